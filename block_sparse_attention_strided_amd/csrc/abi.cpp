@@ -1,0 +1,411 @@
+// C ABI of libxattn: host validation, workspace planning and kernel launches.
+// Every entry point validates all of its arguments on the host before it
+// enqueues anything, so an error return leaves no partial work behind.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <string>
+#include <vector>
+
+#include "../../include/xattn.h"
+#include "xattn_internal.h"
+
+using namespace xattn;
+
+namespace {
+
+thread_local std::string g_last_error;
+
+int fail(int code, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return code;
+}
+
+int hip_fail(hipError_t e, const char* what) {
+  return fail(XATTN_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+constexpr int kMaxKb = 4096;  // select sorts up to this many blocks per row in LDS
+
+// Everything derived from (shape, params) on the host.
+struct Plan {
+  int batch, hq, hkv, d, dtype, elem;
+  int stride, rb;
+  int max_qb, max_kb, max_r;
+  int total_q, total_k;
+  float est_scale, softmax_scale;
+  // workspace layout (byte offsets)
+  size_t off_part, off_bs, off_maskq, off_maskkv, off_hist, off_counts;
+  size_t off_o[3], off_l[3];
+  size_t off_table;
+  size_t total;
+};
+
+size_t align_up(size_t x) { return (x + 255) & ~(size_t)255; }
+
+int make_plan(const XattnShape* sh, const XattnParams* pr, Plan* p) {
+  if (!sh || !pr) return fail(XATTN_ERR_INVALID, "shape and params must not be NULL");
+  if (sh->batch < 1) return fail(XATTN_ERR_INVALID, "batch must be >= 1 (got %d)", sh->batch);
+  if (sh->num_q_heads < 1 || sh->num_kv_heads < 1)
+    return fail(XATTN_ERR_INVALID, "head counts must be >= 1");
+  if (sh->num_q_heads % sh->num_kv_heads != 0)
+    return fail(XATTN_ERR_INVALID, "num_q_heads (%d) must be a multiple of num_kv_heads (%d)",
+                sh->num_q_heads, sh->num_kv_heads);
+  if (sh->head_dim != 64 && sh->head_dim != 128)
+    return fail(XATTN_ERR_UNSUPPORTED, "head_dim must be 64 or 128 (got %d)", sh->head_dim);
+  if (sh->dtype != XATTN_DTYPE_BF16 && sh->dtype != XATTN_DTYPE_F32)
+    return fail(XATTN_ERR_INVALID, "unknown dtype %d", sh->dtype);
+  if (!sh->cu_q_host || !sh->cu_k_host)
+    return fail(XATTN_ERR_INVALID, "cu_q_host and cu_k_host must not be NULL");
+  if (!sh->cu_q || !sh->cu_k) return fail(XATTN_ERR_INVALID, "device cu_q and cu_k must not be NULL");
+  if (pr->block_size != XATTN_BLOCK)
+    return fail(XATTN_ERR_UNSUPPORTED, "block_size must be 128 (got %d)", pr->block_size);
+  if (pr->stride != 4 && pr->stride != 8 && pr->stride != 16)
+    return fail(XATTN_ERR_UNSUPPORTED, "stride must be 4, 8 or 16 (got %d)", pr->stride);
+  if (!std::isfinite(pr->threshold) || pr->threshold < 0.f)
+    return fail(XATTN_ERR_INVALID, "threshold must be finite and >= 0");
+  if (!std::isfinite(pr->est_scale) || pr->est_scale < 0.f)
+    return fail(XATTN_ERR_INVALID, "est_scale must be finite and >= 0 (0 = default)");
+  if (!std::isfinite(pr->softmax_scale) || pr->softmax_scale < 0.f)
+    return fail(XATTN_ERR_INVALID, "softmax_scale must be finite and >= 0 (0 = default)");
+  if (pr->kv_chunk_tokens < 0 || pr->kv_chunk_tokens % XATTN_BLOCK != 0)
+    return fail(XATTN_ERR_INVALID, "kv_chunk_tokens must be a non-negative multiple of 128");
+  if (pr->select_mode != XATTN_SELECT_PER_KVHEAD && pr->select_mode != XATTN_SELECT_CHUNK_VOTE)
+    return fail(XATTN_ERR_INVALID, "unknown select_mode %d", pr->select_mode);
+  if (pr->group_agg != XATTN_GQA_ANY && pr->group_agg != XATTN_GQA_MAJORITY)
+    return fail(XATTN_ERR_INVALID, "unknown group_agg %d", pr->group_agg);
+  if (sh->cu_q_host[0] != 0 || sh->cu_k_host[0] != 0)
+    return fail(XATTN_ERR_INVALID, "cu_q and cu_k must start at 0");
+  int max_lq = 0, max_lk = 0;
+  for (int b = 0; b < sh->batch; ++b) {
+    const long long lq = (long long)sh->cu_q_host[b + 1] - sh->cu_q_host[b];
+    const long long lk = (long long)sh->cu_k_host[b + 1] - sh->cu_k_host[b];
+    if (lq < 0 || lk < 0) return fail(XATTN_ERR_INVALID, "cu_q / cu_k must be non-decreasing (sequence %d)", b);
+    if (lq % XATTN_BLOCK || lk % XATTN_BLOCK)
+      return fail(XATTN_ERR_UNSUPPORTED, "sequence %d: Lq=%lld and Lk=%lld must be multiples of 128", b, lq, lk);
+    if (lk < lq) return fail(XATTN_ERR_INVALID, "sequence %d: Lk=%lld < Lq=%lld", b, lk, lq);
+    if (lq > max_lq) max_lq = (int)lq;
+    if (lk > max_lk) max_lk = (int)lk;
+  }
+  p->batch = sh->batch;
+  p->hq = sh->num_q_heads;
+  p->hkv = sh->num_kv_heads;
+  p->d = sh->head_dim;
+  p->dtype = sh->dtype;
+  p->elem = sh->dtype == XATTN_DTYPE_BF16 ? 2 : 4;
+  p->stride = pr->stride;
+  p->rb = XATTN_BLOCK / pr->stride;
+  p->max_qb = max_lq / XATTN_BLOCK;
+  p->max_kb = max_lk / XATTN_BLOCK;
+  p->max_r = max_lq / pr->stride;
+  p->total_q = sh->cu_q_host[sh->batch];
+  p->total_k = sh->cu_k_host[sh->batch];
+  if (p->max_kb > kMaxKb)
+    return fail(XATTN_ERR_UNSUPPORTED, "key length %d exceeds the supported %d tokens", max_lk, kMaxKb * XATTN_BLOCK);
+  if (sh->block_table) {
+    if (sh->max_blocks_per_seq < p->max_kb)
+      return fail(XATTN_ERR_INVALID, "max_blocks_per_seq (%d) < longest sequence's blocks (%d)",
+                  sh->max_blocks_per_seq, p->max_kb);
+    if (sh->num_phys_blocks < 1) return fail(XATTN_ERR_INVALID, "num_phys_blocks must be >= 1 with a block table");
+  }
+  p->est_scale = pr->est_scale > 0.f ? pr->est_scale : 1.0f / (pr->stride * std::sqrt((float)p->d));
+  p->softmax_scale = pr->softmax_scale > 0.f ? pr->softmax_scale : 1.0f / std::sqrt((float)p->d);
+
+  const size_t B = p->batch;
+  size_t off = 0;
+  p->off_part = off;
+  off = align_up(off + B * p->hq * (size_t)p->max_kb * p->max_r * sizeof(float));
+  p->off_bs = off;
+  off = align_up(off + B * p->hq * (size_t)p->max_qb * p->max_kb * sizeof(float));
+  p->off_maskq = off;
+  off = align_up(off + B * p->hq * (size_t)p->max_qb * p->max_kb);
+  p->off_maskkv = off;
+  off = align_up(off + B * p->hkv * (size_t)p->max_qb * p->max_kb);
+  p->off_hist = off;
+  off = align_up(off + B * (size_t)p->max_kb);
+  p->off_counts = off;
+  off = align_up(off + B * 2 * sizeof(int32_t));
+  for (int x = 0; x < 3; ++x) {
+    p->off_o[x] = off;
+    off = align_up(off + (size_t)p->total_q * p->hq * p->d * sizeof(float));
+    p->off_l[x] = off;
+    off = align_up(off + (size_t)p->hq * p->total_q * sizeof(float));
+  }
+  p->off_table = off;
+  off = align_up(off + (size_t)(p->max_kb + 1) * sizeof(int32_t));
+  p->total = off;
+  return XATTN_OK;
+}
+
+int check_ws(const Plan& p, void* ws, size_t ws_bytes) {
+  if (!ws) return fail(XATTN_ERR_WORKSPACE, "workspace is NULL (need %zu bytes)", p.total);
+  if (ws_bytes < p.total) return fail(XATTN_ERR_WORKSPACE, "workspace has %zu bytes, need %zu", ws_bytes, p.total);
+  if (((uintptr_t)ws) & 255) return fail(XATTN_ERR_INVALID, "workspace must be 256-byte aligned");
+  return XATTN_OK;
+}
+
+template <typename T>
+T* ws_at(void* ws, size_t off) {
+  return (T*)((char*)ws + off);
+}
+
+KvView make_view(const XattnShape* sh, const Plan& p, const void* base) {
+  KvView v;
+  v.base = (const char*)base;
+  v.block_table = sh->block_table;
+  v.cu_k = sh->cu_k;
+  v.max_blocks = sh->max_blocks_per_seq;
+  v.kv_heads = p.hkv;
+  v.head_dim = p.d;
+  v.elem_bytes = p.elem;
+  return v;
+}
+
+hipError_t run_estimate(const XattnShape* sh, const Plan& p, const void* q, KvView kview, int jb0,
+                        int jb_count, float* part, hipStream_t st) {
+  EstArgs ea;
+  ea.q = (const char*)q;
+  ea.k = kview;
+  ea.cu_q = sh->cu_q;
+  ea.cu_k = sh->cu_k;
+  ea.hq = p.hq;
+  ea.group = p.hq / p.hkv;
+  ea.jb0 = jb0;
+  ea.jb_count = jb_count;
+  ea.scale2 = p.est_scale * kLog2e;
+  ea.part = part;
+  ea.max_kb = p.max_kb;
+  ea.max_r = p.max_r;
+  return launch_estimate(ea, p.dtype == XATTN_DTYPE_BF16 ? 0 : 1, p.d, p.stride, p.batch, st);
+}
+
+hipError_t run_block_sums(const XattnShape* sh, const Plan& p, const float* part, float* bs,
+                          hipStream_t st) {
+  BlockSumArgs ba;
+  ba.part = part;
+  ba.cu_q = sh->cu_q;
+  ba.cu_k = sh->cu_k;
+  ba.hq = p.hq;
+  ba.stride = p.stride;
+  ba.max_qb = p.max_qb;
+  ba.max_kb = p.max_kb;
+  ba.max_r = p.max_r;
+  ba.block_sums = bs;
+  return launch_block_sums(ba, p.batch, st);
+}
+
+hipError_t run_select(const XattnShape* sh, const XattnParams* pr, const Plan& p, const float* bs,
+                      uint8_t* maskq, uint8_t* maskkv, uint8_t* hist, int32_t* counts, hipStream_t st) {
+  SelectArgs sa;
+  sa.block_sums = bs;
+  sa.cu_q = sh->cu_q;
+  sa.cu_k = sh->cu_k;
+  sa.hq = p.hq;
+  sa.hkv = p.hkv;
+  sa.max_qb = p.max_qb;
+  sa.max_kb = p.max_kb;
+  sa.threshold = pr->threshold;
+  sa.select_mode = pr->select_mode;
+  sa.group_agg = pr->group_agg;
+  sa.mask_q = maskq;
+  sa.mask_kv = maskkv;
+  sa.hist_sel = hist;
+  sa.counts = counts;
+  return launch_select(sa, p.batch, st);
+}
+
+AttnArgs attn_args(const XattnShape* sh, const Plan& p, const void* q, KvView kv, KvView vv,
+                   const uint8_t* mask, int jb0, int jb1) {
+  AttnArgs aa;
+  aa.q = (const char*)q;
+  aa.k = kv;
+  aa.v = vv;
+  aa.mask = mask;
+  aa.cu_q = sh->cu_q;
+  aa.cu_k = sh->cu_k;
+  aa.hq = p.hq;
+  aa.group = p.hq / p.hkv;
+  aa.max_qb = p.max_qb;
+  aa.max_kb = p.max_kb;
+  aa.jb0 = jb0;
+  aa.jb1 = jb1;
+  aa.scale2 = p.softmax_scale * kLog2e;
+  aa.total_q = p.total_q;
+  aa.out = nullptr;
+  aa.out_f32 = nullptr;
+  aa.lse = nullptr;
+  return aa;
+}
+
+}  // namespace
+
+// ---------------------------------------------------------------------------
+// Ring engine (history streamed from pinned host memory)
+// ---------------------------------------------------------------------------
+struct XattnRing {
+  int num_slots, slot_blocks, hkv, d, dtype, elem;
+  size_t block_bytes;  // one 128-token block of K (or V)
+  char* k_slots = nullptr;
+  char* v_slots = nullptr;
+  hipStream_t xfer = nullptr;
+  std::vector<hipEvent_t> ready, done;
+  hipEvent_t sel_ready = nullptr;
+  uint8_t* host_sel = nullptr;     // pinned, maxKb bytes (grown on demand)
+  int host_sel_cap = 0;
+  int32_t* host_table = nullptr;   // pinned slot tables (grown on demand)
+  size_t host_table_cap = 0;
+  int copy_delay_us = 0;
+};
+
+extern "C" {
+
+const char* xattn_last_error(void) { return g_last_error.c_str(); }
+
+size_t xattn_workspace_size(const XattnShape* shape, const XattnParams* params) {
+  Plan p;
+  if (make_plan(shape, params, &p) != XATTN_OK) return 0;
+  return p.total;
+}
+
+int xattn_estimate(const XattnShape* shape, const XattnParams* params, const void* q, const void* k,
+                   float* block_sums, void* ws, size_t ws_bytes, void* stream) {
+  Plan p;
+  int rc = make_plan(shape, params, &p);
+  if (rc) return rc;
+  if (!q || !k || !block_sums) return fail(XATTN_ERR_INVALID, "q, k and block_sums must not be NULL");
+  if ((rc = check_ws(p, ws, ws_bytes))) return rc;
+  g_last_error.clear();
+  hipStream_t st = (hipStream_t)stream;
+  float* part = ws_at<float>(ws, p.off_part);
+  hipError_t e = run_estimate(shape, p, q, make_view(shape, p, k), 0, p.max_kb, part, st);
+  if (e != hipSuccess) return hip_fail(e, "estimate launch");
+  e = run_block_sums(shape, p, part, block_sums, st);
+  if (e != hipSuccess) return hip_fail(e, "block-sum launch");
+  return XATTN_OK;
+}
+
+int xattn_select(const XattnShape* shape, const XattnParams* params, const float* block_sums,
+                 uint8_t* mask_kv, uint8_t* hist_sel, int32_t* counts, void* ws, size_t ws_bytes,
+                 void* stream) {
+  Plan p;
+  int rc = make_plan(shape, params, &p);
+  if (rc) return rc;
+  if (!block_sums || !mask_kv) return fail(XATTN_ERR_INVALID, "block_sums and mask_kv must not be NULL");
+  if ((rc = check_ws(p, ws, ws_bytes))) return rc;
+  g_last_error.clear();
+  uint8_t* hist = hist_sel ? hist_sel : ws_at<uint8_t>(ws, p.off_hist);
+  int32_t* cnt = counts ? counts : ws_at<int32_t>(ws, p.off_counts);
+  hipError_t e = run_select(shape, params, p, block_sums, ws_at<uint8_t>(ws, p.off_maskq), mask_kv, hist,
+                            cnt, (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "select launch");
+  return XATTN_OK;
+}
+
+int xattn_sparse_attn(const XattnShape* shape, const XattnParams* params, const void* q, const void* k,
+                      const void* v, const uint8_t* mask_kv, void* out, float* lse, void* ws,
+                      size_t ws_bytes, void* stream) {
+  Plan p;
+  int rc = make_plan(shape, params, &p);
+  if (rc) return rc;
+  if (!q || !k || !v || !mask_kv || !out)
+    return fail(XATTN_ERR_INVALID, "q, k, v, mask_kv and out must not be NULL");
+  if ((rc = check_ws(p, ws, ws_bytes))) return rc;
+  g_last_error.clear();
+  AttnArgs aa = attn_args(shape, p, q, make_view(shape, p, k), make_view(shape, p, v), mask_kv, 0, p.max_kb);
+  if (p.dtype == XATTN_DTYPE_BF16) aa.out = out;
+  else aa.out_f32 = (float*)out;
+  aa.lse = lse;
+  hipError_t e = launch_attention(aa, p.dtype == XATTN_DTYPE_BF16 ? 0 : 1, p.d, p.batch, (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "attention launch");
+  return XATTN_OK;
+}
+
+int xattn_merge_attn(int rows, int heads, int head_dim, const float* o_a, const float* lse_a,
+                     const float* o_b, const float* lse_b, float* o, float* lse, void* stream) {
+  if (rows < 0 || heads < 1 || head_dim < 4 || head_dim % 4)
+    return fail(XATTN_ERR_INVALID, "rows >= 0, heads >= 1 and head_dim a positive multiple of 4 required");
+  if (rows == 0) return XATTN_OK;
+  if (!o_a || !lse_a || !o_b || !lse_b || !o || !lse)
+    return fail(XATTN_ERR_INVALID, "merge pointers must not be NULL");
+  g_last_error.clear();
+  MergeArgs ma;
+  ma.rows = rows;
+  ma.heads = heads;
+  ma.head_dim = head_dim;
+  ma.o_a = o_a;
+  ma.lse_a = lse_a;
+  ma.o_b = o_b;
+  ma.lse_b = lse_b;
+  ma.o = o;
+  ma.o_bf16 = nullptr;
+  ma.lse = lse;
+  hipError_t e = launch_merge(ma, (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "merge launch");
+  return XATTN_OK;
+}
+
+int xattn_prefill_chunk(XattnRing* ring, const XattnShape* shape, const XattnParams* params,
+                        const void* q, const void* k, const void* v, const void* k_hist_host,
+                        const void* v_hist_host, int hist_blocks, void* out, float* lse,
+                        int32_t* counts, const XattnAux* aux, void* ws, size_t ws_bytes,
+                        void* stream) {
+  Plan p;
+  int rc = make_plan(shape, params, &p);
+  if (rc) return rc;
+  if (!q || !k || !v || !out) return fail(XATTN_ERR_INVALID, "q, k, v and out must not be NULL");
+  if ((rc = check_ws(p, ws, ws_bytes))) return rc;
+  if (ring) return fail(XATTN_ERR_UNSUPPORTED, "ring mode is not available in this build");
+  (void)k_hist_host;
+  (void)v_hist_host;
+  (void)hist_blocks;
+  g_last_error.clear();
+  hipStream_t st = (hipStream_t)stream;
+  float* part = ws_at<float>(ws, p.off_part);
+  float* bs = (aux && aux->block_sums) ? aux->block_sums : ws_at<float>(ws, p.off_bs);
+  uint8_t* maskkv = (aux && aux->mask_kv) ? aux->mask_kv : ws_at<uint8_t>(ws, p.off_maskkv);
+  uint8_t* hist = (aux && aux->hist_sel) ? aux->hist_sel : ws_at<uint8_t>(ws, p.off_hist);
+  int32_t* cnt = counts ? counts : ws_at<int32_t>(ws, p.off_counts);
+  const KvView kview = make_view(shape, p, k), vview = make_view(shape, p, v);
+  hipError_t e = run_estimate(shape, p, q, kview, 0, p.max_kb, part, st);
+  if (e != hipSuccess) return hip_fail(e, "estimate launch");
+  e = run_block_sums(shape, p, part, bs, st);
+  if (e != hipSuccess) return hip_fail(e, "block-sum launch");
+  e = run_select(shape, params, p, bs, ws_at<uint8_t>(ws, p.off_maskq), maskkv, hist, cnt, st);
+  if (e != hipSuccess) return hip_fail(e, "select launch");
+  AttnArgs aa = attn_args(shape, p, q, kview, vview, maskkv, 0, p.max_kb);
+  if (p.dtype == XATTN_DTYPE_BF16) aa.out = out;
+  else aa.out_f32 = (float*)out;
+  aa.lse = lse;
+  e = launch_attention(aa, p.dtype == XATTN_DTYPE_BF16 ? 0 : 1, p.d, p.batch, st);
+  if (e != hipSuccess) return hip_fail(e, "attention launch");
+  return XATTN_OK;
+}
+
+int xattn_ring_create(int num_slots, int slot_blocks, int num_kv_heads, int head_dim, int dtype,
+                      XattnRing** out) {
+  (void)num_slots;
+  (void)slot_blocks;
+  (void)num_kv_heads;
+  (void)head_dim;
+  (void)dtype;
+  if (out) *out = nullptr;
+  return fail(XATTN_ERR_UNSUPPORTED, "ring mode is not available in this build");
+}
+
+void xattn_ring_destroy(XattnRing* ring) { (void)ring; }
+
+int xattn_ring_set_copy_delay_us(XattnRing* ring, int usec) {
+  if (!ring || usec < 0) return fail(XATTN_ERR_INVALID, "ring must not be NULL and usec >= 0");
+  ring->copy_delay_us = usec;
+  return XATTN_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,298 @@
+// Strided anti-diagonal estimate ("XAttention BSA Policy" design doc, core
+// algorithm Steps 1-2) and the chunked softmax statistics of the stream-fix
+// page (技术细节, 三阶段 KV Chunking).
+//
+// For q head h the reshaped query row r is the s tokens r*s+s-1 .. r*s (in
+// that order) concatenated, and the reshaped key column c is the tokens
+// c*s .. c*s+s-1; S = Qr Kr^T is a GEMM with reduction length s*d.  Instead
+// of writing the fp32 score matrix (Lq*Lk/s^2 floats) and re-reading it, the
+// GEMM epilogue reduces every (row, 128-token key block) to its base-2
+// log-sum-exp over the block's allowed columns: a per-block form of the
+// pages' per-chunk partial statistics, 128/s times smaller than the scores.
+// The block-sum kernel then merges those partials per row (merge of the
+// softmax statistics) and normalises them into block sums.  The result does
+// not depend on how the key range is chunked.
+#include "xattn_internal.h"
+
+namespace xattn {
+namespace {
+
+constexpr float kNegInf = -__builtin_huge_valf();
+constexpr int kEstTile = 128;  // reshaped rows and columns per workgroup
+
+// ---------------------------------------------------------------------------
+// bf16 MFMA score tile + per-block log-sum-exp epilogue.
+// Workgroup: 4 waves, tile 128 (c) x 128 (r); wave w owns the 64 x 64 quarter
+// (c half w&1, r half w>>1) as 2 x 2 MFMA 32x32 accumulators of S^T, so each
+// lane holds one query row r and 16 key columns of every accumulator.
+// ---------------------------------------------------------------------------
+template <int D, int S>
+__global__ __launch_bounds__(256) void est_partial_bf16(EstArgs a) {
+  constexpr int RB = kBlock / S;  // reshaped block
+  constexpr int PITCH = D + 8;    // bf16 per LDS row (padding against bank conflicts)
+  constexpr int CPR = D / 8;      // 16-byte chunks per row
+  __shared__ __align__(16) uint16_t qs[kEstTile * PITCH];
+  __shared__ __align__(16) uint16_t ks[kEstTile * PITCH];
+
+  const int bh = blockIdx.z;
+  const int b = bh / a.hq, h = bh % a.hq, g = h / a.group;
+  const int q0 = a.cu_q[b];
+  const int lq = a.cu_q[b + 1] - q0;
+  const int lk = a.cu_k[b + 1] - a.cu_k[b];
+  const int R = lq / S, C = lk / S, o_s = (lk - lq) / S;
+  const int r0 = blockIdx.y * kEstTile;
+  if (r0 >= R) return;
+  const int c0 = a.jb0 * RB + blockIdx.x * kEstTile;
+  const int c_end = min((a.jb0 + a.jb_count) * RB, C);
+  if (c0 >= c_end) return;
+  const int r_last = min(r0 + kEstTile, R) - 1;
+  if (c0 > r_last + o_s) return;  // whole tile beyond the causal block diagonal
+
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int wc = w & 1, wr = w >> 1;
+  const int l32 = lane & 31, hh = lane >> 5;
+
+  f32x16 acc[2][2];
+#pragma unroll
+  for (int x = 0; x < 2; ++x)
+#pragma unroll
+    for (int y = 0; y < 2; ++y)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) acc[x][y][e] = 0.f;
+
+  const long long q_tok_bytes = (long long)a.hq * D * 2;
+  const char* qbase = a.q + (long long)q0 * q_tok_bytes + (long long)h * D * 2;
+
+  for (int t = 0; t < S; ++t) {
+    for (int it = tid; it < kEstTile * CPR; it += 256) {
+      const int row = it / CPR, part = it - (it / CPR) * CPR;
+      u32x4 vq = {0u, 0u, 0u, 0u};
+      const int r = r0 + row;
+      if (r < R) vq = *(const u32x4*)(qbase + (long long)(r * S + S - 1 - t) * q_tok_bytes + part * 16);
+      *(u32x4*)(&qs[row * PITCH + part * 8]) = vq;
+      u32x4 vk = {0u, 0u, 0u, 0u};
+      const int c = c0 + row;
+      if (c < c_end) {
+        const char* p = a.k.row(b, c * S + t, g);
+        if (p) vk = *(const u32x4*)(p + part * 16);
+      }
+      *(u32x4*)(&ks[row * PITCH + part * 8]) = vk;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int kk = 0; kk < D / 16; ++kk) {
+      bf16x8 af[2], bq[2];
+#pragma unroll
+      for (int x = 0; x < 2; ++x)
+        af[x] = *(const bf16x8*)(&ks[(wc * 64 + x * 32 + l32) * PITCH + kk * 16 + hh * 8]);
+#pragma unroll
+      for (int y = 0; y < 2; ++y)
+        bq[y] = *(const bf16x8*)(&qs[(wr * 64 + y * 32 + l32) * PITCH + kk * 16 + hh * 8]);
+#pragma unroll
+      for (int x = 0; x < 2; ++x)
+#pragma unroll
+        for (int y = 0; y < 2; ++y) acc[x][y] = mfma32(af[x], bq[y], acc[x][y]);
+    }
+    __syncthreads();
+  }
+
+  constexpr int NBLK = 32 / RB;  // key blocks per 32-column accumulator
+  constexpr int IPB = RB / 8;    // accumulator row groups per key block
+  const int j_end = a.jb0 + a.jb_count;
+#pragma unroll
+  for (int y = 0; y < 2; ++y) {
+    const int r = r0 + wr * 64 + y * 32 + l32;
+#pragma unroll
+    for (int x = 0; x < 2; ++x) {
+      const int cblk = c0 + wc * 64 + x * 32;
+      float z[16];
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const int c = cblk + 8 * (e >> 2) + 4 * hh + (e & 3);
+        const bool ok = (r < R) && (c < c_end) && (c <= r + o_s);
+        z[e] = ok ? acc[x][y][e] * a.scale2 : kNegInf;
+      }
+#pragma unroll
+      for (int m = 0; m < NBLK; ++m) {
+        float mx = kNegInf;
+#pragma unroll
+        for (int ii = 0; ii < IPB; ++ii)
+#pragma unroll
+          for (int jj = 0; jj < 4; ++jj) mx = fmaxf(mx, z[(m * IPB + ii) * 4 + jj]);
+        float sm = 0.f;
+        if (mx != kNegInf) {
+#pragma unroll
+          for (int ii = 0; ii < IPB; ++ii)
+#pragma unroll
+            for (int jj = 0; jj < 4; ++jj) sm += exp2f(z[(m * IPB + ii) * 4 + jj] - mx);
+        }
+        const float mo = __shfl_xor(mx, 32, 64);
+        const float so = __shfl_xor(sm, 32, 64);
+        const float M = fmaxf(mx, mo);
+        float lse = kNegInf;
+        if (M != kNegInf) lse = M + log2f(sm * exp2f(mx - M) + so * exp2f(mo - M));
+        const int j = cblk / RB + m;
+        const bool writer = (NBLK == 1) ? (hh == 0) : (hh == (m & 1));
+        if (writer && r < R && j < j_end && j * RB < C)
+          a.part[((long long)bh * a.max_kb + j) * a.max_r + r] = lse;
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// fp32 inputs: plain VALU dot products (tiny workloads; fp32 accuracy).
+// Workgroup = one key block j x (256 / RB) reshaped rows; lane group of RB
+// lanes = one row's RB columns, reduced with cross-lane shuffles.
+// ---------------------------------------------------------------------------
+template <int D, int S>
+__global__ __launch_bounds__(256) void est_partial_f32(EstArgs a) {
+  constexpr int RB = kBlock / S;
+  constexpr int RT = 256 / RB;
+  const int cx = threadIdx.x % RB, ry = threadIdx.x / RB;
+  const int bh = blockIdx.z;
+  const int b = bh / a.hq, h = bh % a.hq, g = h / a.group;
+  const int q0 = a.cu_q[b];
+  const int lq = a.cu_q[b + 1] - q0;
+  const int lk = a.cu_k[b + 1] - a.cu_k[b];
+  const int R = lq / S, C = lk / S, o_s = (lk - lq) / S;
+  const int j = a.jb0 + blockIdx.x;
+  if ((int)blockIdx.y * RT >= R || j * RB >= C) return;
+  const int r = blockIdx.y * RT + ry;
+  const int c = j * RB + cx;
+  float z = kNegInf;
+  if (r < R && c <= r + o_s) {
+    float s = 0.f;
+    for (int t = 0; t < S; ++t) {
+      const float* qp = (const float*)(a.q) + ((long long)(q0 + r * S + S - 1 - t) * a.hq + h) * D;
+      const float* kp = (const float*)a.k.row(b, c * S + t, g);
+      if (!kp) continue;
+#pragma unroll 4
+      for (int e = 0; e < D; e += 4) {
+        const f32x4 qv = *(const f32x4*)(qp + e);
+        const f32x4 kv = *(const f32x4*)(kp + e);
+        s = fmaf(qv[0], kv[0], s);
+        s = fmaf(qv[1], kv[1], s);
+        s = fmaf(qv[2], kv[2], s);
+        s = fmaf(qv[3], kv[3], s);
+      }
+    }
+    z = s * a.scale2;
+  }
+  float mx = z;
+#pragma unroll
+  for (int off = RB / 2; off > 0; off >>= 1) mx = fmaxf(mx, __shfl_xor(mx, off, 64));
+  float e = (mx == kNegInf) ? 0.f : exp2f(z - mx);
+#pragma unroll
+  for (int off = RB / 2; off > 0; off >>= 1) e += __shfl_xor(e, off, 64);
+  if (cx == 0 && r < R)
+    a.part[((long long)bh * a.max_kb + j) * a.max_r + r] = (mx == kNegInf) ? kNegInf : mx + log2f(e);
+}
+
+// ---------------------------------------------------------------------------
+// Merge of the softmax statistics + normalise + block sum.
+// Workgroup (i, h, b): rows r in [i*RB, (i+1)*RB), allowed blocks j <= i+Kh.
+// Phase 1 merges the per-block partial log-sum-exps of each row into its row
+// log-sum-exp; phase 2 writes block_sums[b,h,i,j] = sum_r 2^(part - row).
+// ---------------------------------------------------------------------------
+template <int RB>
+__global__ __launch_bounds__(256) void block_sums_kernel(BlockSumArgs a) {
+  constexpr int JL = 256 / RB;
+  __shared__ float sm_m[JL][RB];
+  __shared__ float sm_l[JL][RB];
+  __shared__ float row_lse[RB];
+  const int i = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+  const int lq = a.cu_q[b + 1] - a.cu_q[b];
+  const int lk = a.cu_k[b + 1] - a.cu_k[b];
+  const int qb = lq / kBlock, kh = (lk - lq) / kBlock;
+  float* out = a.block_sums + (((long long)b * a.hq + h) * a.max_qb + i) * a.max_kb;
+  if (i >= qb) {
+    for (int j = threadIdx.x; j < a.max_kb; j += 256) out[j] = 0.f;
+    return;
+  }
+  const int nj = i + kh + 1;
+  const float* base = a.part + ((long long)(b * a.hq + h) * a.max_kb) * a.max_r + i * RB;
+  const int rr = threadIdx.x % RB, jl = threadIdx.x / RB;
+  float m = kNegInf, l = 0.f;
+  for (int j = jl; j < nj; j += JL) {
+    const float v = base[(long long)j * a.max_r + rr];
+    if (v == kNegInf) continue;
+    if (v > m) {
+      l = l * exp2f(m - v) + 1.f;
+      m = v;
+    } else {
+      l += exp2f(v - m);
+    }
+  }
+  sm_m[jl][rr] = m;
+  sm_l[jl][rr] = l;
+  __syncthreads();
+  if (threadIdx.x < RB) {
+    float M = kNegInf;
+    for (int x = 0; x < JL; ++x) M = fmaxf(M, sm_m[x][threadIdx.x]);
+    float L = 0.f;
+    if (M != kNegInf)
+      for (int x = 0; x < JL; ++x)
+        if (sm_m[x][threadIdx.x] != kNegInf) L += sm_l[x][threadIdx.x] * exp2f(sm_m[x][threadIdx.x] - M);
+    row_lse[threadIdx.x] = (M == kNegInf) ? kNegInf : M + log2f(L);
+  }
+  __syncthreads();
+  for (int j = threadIdx.x; j < a.max_kb; j += 256) {
+    float s = 0.f;
+    if (j < nj) {
+      const float* p = base + (long long)j * a.max_r;
+#pragma unroll
+      for (int x = 0; x < RB; ++x) {
+        const float v = p[x];
+        if (v != kNegInf) s += exp2f(v - row_lse[x]);
+      }
+    }
+    out[j] = s;
+  }
+}
+
+template <int D, int S>
+hipError_t est_dispatch(const EstArgs& a, int dtype, int batch, hipStream_t st) {
+  constexpr int RB = kBlock / S;
+  if (dtype == 0) {
+    dim3 grid((a.jb_count * RB + kEstTile - 1) / kEstTile, (a.max_r + kEstTile - 1) / kEstTile,
+              batch * a.hq);
+    hipLaunchKernelGGL((est_partial_bf16<D, S>), grid, dim3(256), 0, st, a);
+  } else {
+    constexpr int RT = 256 / RB;
+    dim3 grid(a.jb_count, (a.max_r + RT - 1) / RT, batch * a.hq);
+    hipLaunchKernelGGL((est_partial_f32<D, S>), grid, dim3(256), 0, st, a);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_estimate(const EstArgs& a, int dtype, int head_dim, int stride, int batch,
+                           hipStream_t s) {
+  if (a.jb_count <= 0 || a.max_r <= 0 || batch <= 0) return hipSuccess;
+#define XATTN_EST_CASE(D_, S_) \
+  if (head_dim == D_ && stride == S_) return est_dispatch<D_, S_>(a, dtype, batch, s);
+  XATTN_EST_CASE(128, 8)
+  XATTN_EST_CASE(128, 16)
+  XATTN_EST_CASE(128, 4)
+  XATTN_EST_CASE(64, 8)
+  XATTN_EST_CASE(64, 16)
+  XATTN_EST_CASE(64, 4)
+#undef XATTN_EST_CASE
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_block_sums(const BlockSumArgs& a, int batch, hipStream_t s) {
+  if (a.max_qb <= 0 || a.max_kb <= 0 || batch <= 0) return hipSuccess;
+  dim3 grid(a.max_qb, a.hq, batch);
+  switch (kBlock / a.stride) {
+    case 8: hipLaunchKernelGGL((block_sums_kernel<8>), grid, dim3(256), 0, s, a); break;
+    case 16: hipLaunchKernelGGL((block_sums_kernel<16>), grid, dim3(256), 0, s, a); break;
+    case 32: hipLaunchKernelGGL((block_sums_kernel<32>), grid, dim3(256), 0, s, a); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+}  // namespace xattn

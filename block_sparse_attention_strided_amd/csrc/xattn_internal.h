@@ -1,0 +1,103 @@
+// Host-side interface between the C ABI layer and the kernel launchers.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "xattn_device.h"
+
+namespace xattn {
+
+// Partial estimate of one launch: for every (sequence b, q head h, key block j
+// in [jb0, jb0 + jb_count), reshaped query row r) the base-2 log-sum-exp of
+// est_scale*log2(e)*S over the allowed columns of block j.  Stored at
+// part[((b*hq + h)*max_kb + j)*max_r + r].
+struct EstArgs {
+  const char* q;
+  KvView k;
+  const int32_t* cu_q;
+  const int32_t* cu_k;
+  int hq;
+  int group;
+  int jb0;
+  int jb_count;
+  float scale2;
+  float* part;
+  int max_kb;
+  int max_r;
+};
+
+struct BlockSumArgs {
+  const float* part;
+  const int32_t* cu_q;
+  const int32_t* cu_k;
+  int hq;
+  int stride;
+  int max_qb;
+  int max_kb;
+  int max_r;
+  float* block_sums;  // [batch, hq, max_qb, max_kb]
+};
+
+struct SelectArgs {
+  const float* block_sums;  // [batch, hq, max_qb, max_kb]
+  const int32_t* cu_q;
+  const int32_t* cu_k;
+  int hq;
+  int hkv;
+  int max_qb;
+  int max_kb;
+  float threshold;
+  int select_mode;
+  int group_agg;
+  uint8_t* mask_q;   // [batch, hq, max_qb, max_kb]  (workspace)
+  uint8_t* mask_kv;  // [batch, hkv, max_qb, max_kb]
+  uint8_t* hist_sel; // [batch, max_kb]
+  int32_t* counts;   // [batch, 2]
+};
+
+// Attention of one launch.  Keys come from blocks j in [jb0, jb1) whose mask
+// byte is set and whose page is present; rows are (b, q head, query).
+struct AttnArgs {
+  const char* q;
+  KvView k;
+  KvView v;
+  const uint8_t* mask;  // [batch, hkv, max_qb, max_kb]
+  const int32_t* cu_q;
+  const int32_t* cu_k;
+  int hq;
+  int group;
+  int max_qb;
+  int max_kb;
+  int jb0;
+  int jb1;
+  float scale2;       // softmax_scale * log2(e)
+  int total_q;
+  // Output: final (out in input dtype) or partial fp32 (out_f32).
+  void* out;          // [total_q, hq, d] dtype   (nullptr if partial)
+  float* out_f32;     // [total_q, hq, d] fp32    (nullptr if final)
+  float* lse;         // [hq, total_q] natural log (may be nullptr)
+};
+
+struct MergeArgs {
+  int rows;
+  int heads;
+  int head_dim;
+  const float* o_a;
+  const float* lse_a;
+  const float* o_b;
+  const float* lse_b;
+  float* o;        // fp32 out (or nullptr)
+  void* o_bf16;    // bf16 out (or nullptr)
+  float* lse;      // may be nullptr
+};
+
+hipError_t launch_estimate(const EstArgs& a, int dtype, int head_dim, int stride, int batch,
+                           hipStream_t s);
+hipError_t launch_block_sums(const BlockSumArgs& a, int batch, hipStream_t s);
+hipError_t launch_select(const SelectArgs& a, int batch, hipStream_t s);
+hipError_t launch_attention(const AttnArgs& a, int dtype, int head_dim, int batch,
+                            hipStream_t s);
+hipError_t launch_merge(const MergeArgs& a, hipStream_t s);
+
+}  // namespace xattn

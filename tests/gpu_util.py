@@ -1,0 +1,189 @@
+"""Shared plumbing for the GPU parity tests: move a workload to the device,
+run the library's stages through the C ABI, and run the oracle on the same
+inputs with the same float32-rounded parameters."""
+
+import math
+import sys
+
+import numpy as np
+import torch
+
+import block_sparse_attention_strided_amd as X
+import oracle as O
+
+# Tolerances (floating point): block sums |g-o| <= 1e-3*|o| + 1e-7*rb;
+# attention bf16 out 2e-2 abs / lse 1e-3 abs; fp32 out 1e-4 / lse 1e-5.
+BS_RTOL = 1e-3
+OUT_ATOL = {torch.bfloat16: 2e-2, torch.float32: 1e-4}
+LSE_ATOL = {torch.bfloat16: 1e-3, torch.float32: 1e-5}
+
+
+def f32(x):
+    return float(np.float32(x))
+
+
+def say(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+class Run:
+    """A workload resident on the GPU with its C-ABI shape/params/workspace."""
+
+    def __init__(self, w, *, threshold=None, select_mode=None, group_agg=None, device="cuda"):
+        self.w = w
+        self.paged = w.block_table is not None
+        d = w.head_dim
+        self.tau = f32(w.threshold if threshold is None else threshold)
+        self.mode = w.select_mode if select_mode is None else select_mode
+        self.agg = w.group_agg if group_agg is None else group_agg
+        self.est_scale = f32(1.0 / (w.stride * math.sqrt(d)))
+        self.softmax_scale = f32(1.0 / math.sqrt(d))
+        self.q = w.q.to(device)
+        if self.paged:
+            self.k = w.k_cache.to(device)
+            self.v = w.v_cache.to(device)
+            self.table = w.block_table.to(device).contiguous()
+            self.shape = X.Shape(num_q_heads=w.num_q_heads, num_kv_heads=w.num_kv_heads, head_dim=d,
+                                 dtype=w.dtype, cu_q=w.cu_q, cu_k=w.cu_k, device=device,
+                                 block_table=self.table, num_phys_blocks=w.k_cache.shape[0])
+        else:
+            self.k = w.k.to(device)
+            self.v = w.v.to(device)
+            self.shape = X.Shape(num_q_heads=w.num_q_heads, num_kv_heads=w.num_kv_heads, head_dim=d,
+                                 dtype=w.dtype, cu_q=w.cu_q, cu_k=w.cu_k, device=device)
+        self.params = X.make_params(stride=w.stride, threshold=self.tau, est_scale=self.est_scale,
+                                    softmax_scale=self.softmax_scale, kv_chunk_tokens=w.kv_chunk_tokens,
+                                    select_mode=self.mode, group_agg=self.agg)
+        self.ws = X.alloc_workspace(self.shape, self.params, device)
+        sh = self.shape
+        self.B, self.hq, self.hkv = sh.batch, sh.num_q_heads, sh.num_kv_heads
+        self.max_qb, self.max_kb = sh.max_qb, sh.max_kb
+        self.device = device
+
+    # ---- GPU stages
+    def estimate(self):
+        bs = torch.full((self.B, self.hq, self.max_qb, self.max_kb), float("nan"), device=self.device)
+        X.xattn_estimate(self.shape, self.params, self.q, self.k, bs, self.ws)
+        torch.cuda.synchronize()
+        return bs
+
+    def select(self, bs):
+        mask = torch.full((self.B, self.hkv, self.max_qb, self.max_kb), 7, dtype=torch.uint8, device=self.device)
+        hist = torch.full((self.B, max(self.max_kb, 1)), 7, dtype=torch.uint8, device=self.device)
+        counts = torch.full((self.B, 2), -1, dtype=torch.int32, device=self.device)
+        X.xattn_select(self.shape, self.params, bs.to(self.device).contiguous(), mask, hist, counts, self.ws)
+        torch.cuda.synchronize()
+        return mask, hist, counts
+
+    def attend(self, mask):
+        out = torch.full_like(self.q, float("nan"))
+        lse = torch.full((self.hq, self.shape.total_q), float("nan"), device=self.device)
+        X.xattn_sparse_attn(self.shape, self.params, self.q, self.k, self.v,
+                            mask.to(self.device, torch.uint8).contiguous(), out, lse, self.ws)
+        torch.cuda.synchronize()
+        return out, lse
+
+    def prefill(self):
+        out = torch.full_like(self.q, float("nan"))
+        lse = torch.full((self.hq, self.shape.total_q), float("nan"), device=self.device)
+        counts = torch.full((self.B, 2), -1, dtype=torch.int32, device=self.device)
+        aux = {
+            "block_sums": torch.empty((self.B, self.hq, self.max_qb, self.max_kb), device=self.device),
+            "mask_kv": torch.empty((self.B, self.hkv, self.max_qb, self.max_kb), dtype=torch.uint8,
+                                   device=self.device),
+            "hist_sel": torch.empty((self.B, max(self.max_kb, 1)), dtype=torch.uint8, device=self.device),
+        }
+        X.xattn_prefill_chunk(self.shape, self.params, self.q, self.k, self.v, out, lse, counts, self.ws,
+                              aux=aux)
+        torch.cuda.synchronize()
+        return out, lse, counts, aux
+
+    # ---- oracle on the same inputs
+    def oracle(self, attention=True, rows=None):
+        w = self.w
+        kw = dict(num_kv_heads=w.num_kv_heads, stride=w.stride, threshold=self.tau,
+                  est_scale=self.est_scale, softmax_scale=self.softmax_scale,
+                  kv_chunk_tokens=w.kv_chunk_tokens, mode=self.mode, agg=self.agg,
+                  attention=attention, rows=rows)
+        if self.paged:
+            return O.prefill(w.q, None, None, w.cu_q, w.cu_k, block_table=w.block_table.numpy(),
+                             k_cache=w.k_cache, v_cache=w.v_cache, **kw)
+        return O.prefill(w.q, w.k, w.v, w.cu_q, w.cu_k, **kw)
+
+    def oracle_attention(self, mask, rows=None):
+        """Oracle O7 on a given effective mask [B,Hkv,maxQb,maxKb]."""
+        w = self.w
+        q = O.to_f64(w.q)
+        out = np.full(q.shape, np.nan)
+        lse = np.full((w.num_q_heads, q.shape[0]), np.nan)
+        k = v = None
+        if not self.paged:
+            k = O.to_f64(w.k)
+            v = O.to_f64(w.v)
+        kc = O.to_f64(w.k_cache) if self.paged else None
+        vc = O.to_f64(w.v_cache) if self.paged else None
+        m = np.asarray(mask.cpu().numpy(), dtype=bool)
+        for b in range(w.batch):
+            lq, lk = w.lens(b)
+            if lq == 0:
+                continue
+            kb_, vb_ = O.sequence_kv(k, v, w.cu_k, b, None if not self.paged else w.block_table.numpy(),
+                                     kc, vc)
+            r_b = None if rows is None else rows.get(b, [])
+            if r_b is not None and len(r_b) == 0:
+                continue
+            o_b, l_b = O.sparse_attention(q[w.cu_q[b]:w.cu_q[b + 1]], kb_, vb_,
+                                          m[b, :, :lq // 128, :lk // 128],
+                                          softmax_scale=self.softmax_scale,
+                                          group=w.num_q_heads // w.num_kv_heads, rows=r_b)
+            out[w.cu_q[b]:w.cu_q[b + 1]] = o_b
+            lse[:, w.cu_q[b]:w.cu_q[b + 1]] = l_b
+        return out, lse
+
+
+def assert_block_sums_close(gpu, ref, stride, label=""):
+    g = gpu.detach().cpu().double().numpy()
+    rb = 128 // stride
+    err = np.abs(g - ref)
+    tol = BS_RTOL * np.abs(ref) + 1e-7 * rb
+    bad = err > tol
+    assert not np.isnan(g).any(), label + ": NaN in block sums"
+    assert not bad.any(), "%s: %d/%d block sums out of tolerance; worst rel %.3g" % (
+        label, int(bad.sum()), bad.size, float((err / np.maximum(np.abs(ref), 1e-30)).max()))
+
+
+def assert_attention_close(out, lse, ref_out, ref_lse, dtype, rows_idx=None, label=""):
+    o = out.detach().float().cpu().double().numpy()
+    l_ = lse.detach().cpu().double().numpy()
+    if rows_idx is not None:
+        o = o[rows_idx]
+        ref_out = ref_out[rows_idx]
+        l_ = l_[:, rows_idx]
+        ref_lse = ref_lse[:, rows_idx]
+    assert np.isfinite(o).all(), label + ": non-finite output"
+    do = np.abs(o - ref_out).max()
+    dl = np.abs(l_ - ref_lse).max()
+    assert do <= OUT_ATOL[dtype], "%s: max |out - oracle| = %.3g" % (label, do)
+    assert dl <= LSE_ATOL[dtype], "%s: max |lse - oracle| = %.3g" % (label, dl)
+    return do, dl
+
+
+def sample_rows(w, per_seq=96, seed=0):
+    """Query rows spread over every q block of every sequence (first, last and
+    random rows of each block)."""
+    rng = np.random.default_rng(seed)
+    rows = {}
+    flat = []
+    for b in range(w.batch):
+        lq, _ = w.lens(b)
+        if lq == 0:
+            rows[b] = []
+            continue
+        picks = set()
+        for i in range(lq // 128):
+            picks.update({i * 128, i * 128 + 127})
+        picks.update(int(x) for x in rng.choice(lq, size=min(per_seq, lq), replace=False))
+        rows[b] = sorted(picks)
+        flat.extend(w.cu_q[b] + x for x in rows[b])
+    return rows, np.asarray(flat)

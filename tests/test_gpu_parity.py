@@ -1,0 +1,195 @@
+"""GPU parity of every stage (and the whole path) against the float64 oracle.
+
+All calls go through the C ABI of libxattn.so.  Inputs are the seeded
+synthetic workloads; both sides see the identical fp32 / bf16 values.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+from tests.gpu_util import (Run, assert_attention_close, assert_block_sums_close, sample_rows, say)
+from workloads import make_random, make_well_separated, make_workload
+
+pytestmark = [pytest.mark.gpu,
+              pytest.mark.skipif(not torch.cuda.is_available(), reason="needs a GPU")]
+
+
+EST_CASES = {
+    "bf16_s8_d128_varlen": dict(hq=4, hkv=2, d=128, lq=[2048, 384], lk=[4096, 1024], stride=8),
+    "bf16_s16_d128_gqa4": dict(hq=4, hkv=1, d=128, lq=[2048], lk=[3072], stride=16),
+    "bf16_s4_d64": dict(hq=2, hkv=2, d=64, lq=[1024], lk=[2048], stride=4),
+    "bf16_paged_3seq": dict(hq=4, hkv=2, d=128, lq=[512, 256, 128], lk=[2048, 256, 1536], stride=8,
+                            paged=True),
+    "bf16_empty_seqs": dict(hq=2, hkv=1, d=128, lq=[256, 0, 128, 0], lk=[512, 256, 128, 0], stride=8),
+    "f32_s8_d64": dict(hq=2, hkv=1, d=64, lq=[512], lk=[1024], stride=8, dtype=torch.float32),
+    "f32_s16_d128_paged": dict(hq=2, hkv=2, d=128, lq=[256, 128], lk=[512, 384], stride=16,
+                               dtype=torch.float32, paged=True),
+}
+
+
+def _make(name, seed=11, **over):
+    kw = dict(EST_CASES[name])
+    kw.update(over)
+    return make_random(name, seed=seed, **kw)
+
+
+@pytest.mark.parametrize("name", list(EST_CASES))
+def test_estimate_block_sums(name):
+    w = _make(name)
+    r = Run(w)
+    say("estimate " + name)
+    bs = r.estimate()
+    ref = r.oracle(attention=False)["block_sums"]
+    assert_block_sums_close(bs, ref, w.stride, name)
+
+
+def test_estimate_tiny_fp32_workload():
+    w = make_workload("tiny_causal_fp32_1k")
+    r = Run(w)
+    say("estimate tiny fp32")
+    bs = r.estimate()
+    ref = r.oracle(attention=False)["block_sums"]
+    assert_block_sums_close(bs, ref, w.stride, "tiny")
+
+
+@pytest.mark.parametrize("mode", ["per_kvhead", "chunk_vote"])
+@pytest.mark.parametrize("agg", ["any", "majority"])
+@pytest.mark.parametrize("tau", [0.5, 0.9, 0.95, 1.0])
+def test_select_matches_oracle_bit_exact(mode, agg, tau):
+    """The select kernels fed the oracle's block sums (rounded to fp32) make
+    the same float64 decisions as the oracle on those fp32 values."""
+    w = make_random("sel", seed=21, hq=8, hkv=2, d=64, lq=[512, 256, 0], lk=[2048, 256, 384],
+                    dtype=torch.float32, stride=8, select_mode=mode, group_agg=agg)
+    r = Run(w, threshold=tau)
+    bs64 = r.oracle(attention=False)["block_sums"]
+    bs32 = bs64.astype(np.float32)
+    say("select %s %s %g" % (mode, agg, tau))
+    mask, hist, counts = r.select(torch.from_numpy(bs32))
+    # oracle selection on the same fp32 values
+    for b in range(w.batch):
+        lq, lk = w.lens(b)
+        qb, kb = lq // 128, lk // 128
+        if qb == 0:
+            assert (mask[b].cpu() == 0).all()
+            assert counts[b].tolist() == [0, 0]
+            continue
+        sel = O.select_blocks(bs32[b, :, :qb, :kb].astype(np.float64), kh=(lk - lq) // 128, tau=r.tau,
+                              group=w.num_q_heads // w.num_kv_heads, mode=mode, agg=agg)
+        m = mask[b].cpu().numpy().astype(bool)
+        assert (m[:, :qb, :kb] == sel["mask_kv"]).all(), "mask mismatch seq %d" % b
+        assert not m[:, qb:, :].any() and not m[:, :, kb:].any()
+        assert (hist[b, :kb].cpu().numpy().astype(bool) == sel["hist_sel"]).all()
+        assert tuple(counts[b].tolist()) == sel["counts"]
+
+
+def test_select_ties_and_zeros():
+    """Equal values (index order decides) and zero blocks."""
+    w = make_random("ties", seed=22, hq=2, hkv=1, d=64, lq=[256], lk=[1024], dtype=torch.float32,
+                    select_mode="per_kvhead")
+    r = Run(w, threshold=0.5)
+    bs = np.zeros((1, 2, 2, 8), dtype=np.float32)
+    bs[0, 0, 0, :7] = 0.25
+    bs[0, 0, 1, :8] = [0.5, 0.0, 0.5, 0.5, 0.0, 1.0, 0.25, 0.25]
+    bs[0, 1, 0, :7] = [0.0] * 6 + [1.0]
+    bs[0, 1, 1, :8] = 1.0 / 8
+    mask, hist, counts = r.select(torch.from_numpy(bs))
+    sel = O.select_blocks(bs[0].astype(np.float64), kh=6, tau=r.tau, group=2, mode="per_kvhead")
+    assert (mask[0].cpu().numpy().astype(bool) == sel["mask_kv"]).all()
+    assert tuple(counts[0].tolist()) == sel["counts"]
+
+
+ATTN_CASES = {
+    "bf16_d128_gqa2_varlen": dict(hq=4, hkv=2, d=128, lq=[512, 256], lk=[1024, 256]),
+    "bf16_d64_gqa1": dict(hq=2, hkv=2, d=64, lq=[384], lk=[896]),
+    "bf16_paged": dict(hq=4, hkv=1, d=128, lq=[256, 128], lk=[768, 640], paged=True),
+    "f32_d64": dict(hq=2, hkv=1, d=64, lq=[256], lk=[512], dtype=torch.float32),
+}
+
+
+@pytest.mark.parametrize("name", list(ATTN_CASES))
+@pytest.mark.parametrize("mask_kind", ["random", "dense"])
+def test_sparse_attention(name, mask_kind):
+    w = make_random(name, seed=31, **ATTN_CASES[name])
+    r = Run(w)
+    rng = np.random.default_rng(5)
+    mask = np.zeros((r.B, r.hkv, r.max_qb, r.max_kb), dtype=np.uint8)
+    for b in range(w.batch):
+        lq, lk = w.lens(b)
+        kh = (lk - lq) // 128
+        for i in range(lq // 128):
+            n = i + kh + 1
+            row = (rng.random((r.hkv, n)) < 0.5) if mask_kind == "random" else np.ones((r.hkv, n), bool)
+            row[:, i + kh] = True
+            mask[b, :, i, :n] = row
+    mask_t = torch.from_numpy(mask)
+    say("attention %s %s" % (name, mask_kind))
+    out, lse = r.attend(mask_t)
+    ref_o, ref_l = r.oracle_attention(mask_t)
+    assert_attention_close(out, lse, ref_o, ref_l, w.dtype, label=name)
+
+
+def test_merge_attention():
+    import block_sparse_attention_strided_amd as X
+    rng = np.random.default_rng(7)
+    rows, heads, d = 300, 3, 128
+    oa = rng.standard_normal((rows, heads, d))
+    ob = rng.standard_normal((rows, heads, d))
+    la = rng.standard_normal((heads, rows)) * 3
+    lb = rng.standard_normal((heads, rows)) * 3
+    la[0, :10] = -np.inf
+    lb[1, :10] = -np.inf
+    la[2, :5] = lb[2, :5] = -np.inf
+    ref_o, ref_l = O.merge_attention(oa, la, ob, lb)
+    t = lambda a: torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).cuda()
+    o = torch.empty((rows, heads, d), device="cuda")
+    l_ = torch.empty((heads, rows), device="cuda")
+    say("merge")
+    X.xattn_merge_attn(t(oa), t(la), t(ob), t(lb), o, l_)
+    torch.cuda.synchronize()
+    np.testing.assert_allclose(o.cpu().numpy(), ref_o, rtol=1e-5, atol=1e-5)
+    np.testing.assert_allclose(l_.cpu().numpy(), ref_l, rtol=1e-6, atol=1e-5)
+
+
+def _prefill_and_check(w, rows=None, rows_idx=None, max_mismatch=0.0, label=""):
+    r = Run(w)
+    say("prefill " + label)
+    out, lse, counts, aux = r.prefill()
+    ref = r.oracle(attention=False)
+    assert_block_sums_close(aux["block_sums"], ref["block_sums"], w.stride, label)
+    gm = aux["mask_kv"].cpu().numpy().astype(bool)
+    mism = float((gm != ref["mask_kv"]).mean())
+    say("  mask mismatch fraction %.4g, counts %s vs %s" % (mism, counts.tolist(), ref["counts"].tolist()))
+    assert mism <= max_mismatch, "%s: mask mismatch fraction %.4g" % (label, mism)
+    ref_o, ref_l = r.oracle_attention(aux["mask_kv"], rows=rows)
+    assert_attention_close(out, lse, ref_o, ref_l, w.dtype, rows_idx=rows_idx, label=label)
+    return mism
+
+
+def test_prefill_tiny_fp32():
+    _prefill_and_check(make_workload("tiny_causal_fp32_1k"), label="tiny fp32")
+
+
+def test_prefill_qwen06_4k():
+    _prefill_and_check(make_workload("qwen3_0p6b_4k"), max_mismatch=0.01, label="4k")
+
+
+def test_prefill_chunk32k_sampled():
+    w = make_workload("chunked_prefill_32k")
+    rows, idx = sample_rows(w, per_seq=64)
+    _prefill_and_check(w, rows=rows, rows_idx=idx, max_mismatch=0.01, label="32k")
+
+
+def test_prefill_paged_varlen_sampled():
+    w = make_workload("paged_varlen_3seq")
+    rows, idx = sample_rows(w, per_seq=48)
+    _prefill_and_check(w, rows=rows, rows_idx=idx, max_mismatch=0.01, label="paged varlen")
+
+
+@pytest.mark.parametrize("seed", [101, 102, 103])
+@pytest.mark.parametrize("mode", ["per_kvhead", "chunk_vote"])
+def test_well_separated_masks_bit_exact(seed, mode):
+    w = make_well_separated("ws", seed=seed, hq=8, hkv=4, d=128, lq=[1024, 512], lk=[2048, 512],
+                            select_mode=mode)
+    _prefill_and_check(w, max_mismatch=0.0, label="well-separated %d %s" % (seed, mode))
