@@ -46,6 +46,8 @@ struct Plan {
   size_t off_part, off_bs, off_maskq, off_maskkv, off_hist, off_counts;
   size_t off_o[3], off_l[3];
   size_t off_table;
+  size_t off_vt, off_lists;
+  int num_pages;  // 128-key pages of the K/V arrays (contiguous or paged)
   size_t total;
 };
 
@@ -141,6 +143,12 @@ int make_plan(const XattnShape* sh, const XattnParams* pr, Plan* p) {
   }
   p->off_table = off;
   off = align_up(off + (size_t)(p->max_kb + 1) * sizeof(int32_t));
+  p->num_pages = sh->block_table ? sh->num_phys_blocks : p->total_k / XATTN_BLOCK;
+  p->off_vt = off;
+  if (p->dtype == XATTN_DTYPE_BF16)
+    off = align_up(off + (size_t)p->num_pages * p->hkv * p->d * XATTN_BLOCK * 2);
+  p->off_lists = off;
+  off = align_up(off + B * p->hkv * (size_t)p->max_qb * (p->max_kb + 1) * sizeof(int32_t));
   p->total = off;
   return XATTN_OK;
 }
@@ -242,7 +250,45 @@ AttnArgs attn_args(const XattnShape* sh, const Plan& p, const void* q, KvView kv
   aa.out = nullptr;
   aa.out_f32 = nullptr;
   aa.lse = nullptr;
+  aa.vt = nullptr;
+  aa.lists = nullptr;
   return aa;
+}
+
+// Attention over blocks [jb0, jb1) of `mask`: for bf16 first re-lays V out
+// d-major (V^T pages) and builds the per-row block lists, then attends.
+hipError_t run_attention(const XattnShape* sh, const Plan& p, AttnArgs aa, const void* v, int num_pages,
+                         void* ws, bool transpose_v, hipStream_t st) {
+  if (p.dtype == XATTN_DTYPE_BF16) {
+    char* vt = ws_at<char>(ws, p.off_vt);
+    if (transpose_v) {
+      VtArgs va;
+      va.v = (const char*)v;
+      va.vt = vt;
+      va.num_pages = num_pages;
+      va.hkv = p.hkv;
+      va.head_dim = p.d;
+      hipError_t e = launch_vt_transpose(va, st);
+      if (e != hipSuccess) return e;
+    }
+    PlanArgs pa;
+    pa.mask = aa.mask;
+    pa.cu_q = sh->cu_q;
+    pa.cu_k = sh->cu_k;
+    pa.block_table = aa.k.block_table;
+    pa.max_blocks = aa.k.max_blocks;
+    pa.hkv = p.hkv;
+    pa.max_qb = p.max_qb;
+    pa.max_kb = p.max_kb;
+    pa.jb0 = aa.jb0;
+    pa.jb1 = aa.jb1;
+    pa.lists = ws_at<int32_t>(ws, p.off_lists);
+    hipError_t e = launch_plan(pa, p.batch, st);
+    if (e != hipSuccess) return e;
+    aa.vt = vt;
+    aa.lists = pa.lists;
+  }
+  return launch_attention(aa, p.dtype == XATTN_DTYPE_BF16 ? 0 : 1, p.d, p.batch, st);
 }
 
 }  // namespace
@@ -323,7 +369,7 @@ int xattn_sparse_attn(const XattnShape* shape, const XattnParams* params, const 
   if (p.dtype == XATTN_DTYPE_BF16) aa.out = out;
   else aa.out_f32 = (float*)out;
   aa.lse = lse;
-  hipError_t e = launch_attention(aa, p.dtype == XATTN_DTYPE_BF16 ? 0 : 1, p.d, p.batch, (hipStream_t)stream);
+  hipError_t e = run_attention(shape, p, aa, v, p.num_pages, ws, true, (hipStream_t)stream);
   if (e != hipSuccess) return hip_fail(e, "attention launch");
   return XATTN_OK;
 }
@@ -384,7 +430,7 @@ int xattn_prefill_chunk(XattnRing* ring, const XattnShape* shape, const XattnPar
   if (p.dtype == XATTN_DTYPE_BF16) aa.out = out;
   else aa.out_f32 = (float*)out;
   aa.lse = lse;
-  e = launch_attention(aa, p.dtype == XATTN_DTYPE_BF16 ? 0 : 1, p.d, p.batch, st);
+  e = run_attention(shape, p, aa, v, p.num_pages, ws, true, st);
   if (e != hipSuccess) return hip_fail(e, "attention launch");
   return XATTN_OK;
 }

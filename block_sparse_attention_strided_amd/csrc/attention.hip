@@ -2,17 +2,23 @@
 // design doc, section 2: flash_attn_with_lse over the selected blocks) and
 // the LSE merge of two partial results (merge_attention_outputs).
 //
-// bf16 kernel layout (gfx950, wave64, v_mfma_f32_32x32x16_bf16):
-//  * workgroup = one (sequence, q head, 128-query block); wave w owns queries
-//    32w .. 32w+31 of the block.
-//  * key tiles of 64 keys: K staged row-major in LDS, V staged transposed
-//    (d-major) so that both MFMA operands read 16 contiguous bytes per lane.
-//  * S^T = K Q^T: the accumulator puts one query per lane (column) and 32 of
-//    the tile's keys in its registers, so the running max/sum of the online
-//    softmax are per lane, with one exchange between the two half-waves.
-//  * O^T += V^T P^T reuses the S^T accumulator registers as the B operand
-//    directly: the k-slots of P^T are a fixed permutation of the tile's keys,
-//    and V^T is written to LDS in the same permuted key order.
+// bf16 kernel (gfx950, wave64, v_mfma_f32_32x32x16_bf16):
+//  * a workgroup is HPW q heads of one KV group x one 128-query block; wave
+//    w owns 32 queries of head w/4.  The HPW heads share every K/V tile.
+//  * key tiles of 64 keys are copied global -> LDS with direct
+//    (global_load_lds) 16-byte loads into a 3-stage ring, one barrier per tile;
+//    K rows and V^T rows are XOR-swizzled in 16-byte chunks against LDS bank
+//    conflicts.  V is read from a d-major copy (VtArgs) so that its tile is a
+//    plain copy too.
+//  * S^T = K Q^T puts one query per lane (accumulator column) and 32 of the
+//    tile's keys in that lane's registers: the online-softmax max and sum are
+//    per lane plus one exchange between half-waves.  Its registers, rounded to
+//    bf16, are the B operand of O^T += V^T P^T directly (the k-slot order of
+//    P^T is matched by the key order of the V^T copy).
+//  * the running max is refreshed only when a tile raises it by more than 8
+//    (base 2), so the O rescale is rare; probabilities stay below 2^8.
+//  * blockIdx -> (kv head, q block) is XCD-aware: the workgroups of one KV
+//    head land on one XCD and share its L2.
 #include "xattn_internal.h"
 
 namespace xattn {
@@ -21,55 +27,145 @@ namespace {
 constexpr float kNegInf = -__builtin_huge_valf();
 constexpr int kKT = 64;  // keys per tile
 
-// Position of key k (0..63) inside a V^T LDS row: bits 2 and 3 swapped, so
-// the 8 keys of k-slot group (16m + 8hh .. +8) are {16m+4hh+0..3, 16m+8+4hh+0..3}.
-__device__ __forceinline__ int vperm(int k) { return (k & ~12) | ((k & 4) << 1) | ((k & 8) >> 1); }
+// Position of key k inside a 16-key group of a V^T row: bits 2 and 3
+// swapped, so k-slot group hh of MFMA k-step m holds keys
+// {16m + 4hh + 0..3, 16m + 8 + 4hh + 0..3}, the keys a lane's S^T
+// accumulator registers 4*i0 .. 4*i0+7 hold.
+__host__ __device__ __forceinline__ int vperm(int k) {
+  return (k & ~12) | ((k & 4) << 1) | ((k & 8) >> 1);
+}
 
-struct BlockIter {
-  const uint8_t* mrow;
-  const int32_t* table;  // block table row (paged) or nullptr
-  int jend;
-  // First selected block >= j (page present), or jend.
-  __device__ __forceinline__ int next(int j) const {
-    for (; j < jend; ++j) {
-      if (!mrow[j]) continue;
-      if (table && table[j] < 0) continue;
-      return j;
-    }
-    return jend;
-  }
-};
+typedef __attribute__((address_space(3))) void* lds_ptr_t;
 
+__device__ __forceinline__ void load_lds16(const void* g, void* lds) {
+  __builtin_amdgcn_global_load_lds(g, (lds_ptr_t)lds, 16, 0, 0);
+}
+
+// s_waitcnt with only vmcnt constrained (expcnt, lgkmcnt left at maximum).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+// ---------------------------------------------------------------------------
+// V -> V^T pages.  Workgroup (page, kv head): [128 keys][d] -> [d][128].
+// ---------------------------------------------------------------------------
 template <int D>
-__global__ __launch_bounds__(256) void attn_bf16(AttnArgs a) {
-  constexpr int KP = D + 8;    // K LDS pitch (bf16)
-  constexpr int VP = kKT + 8;  // V^T LDS pitch (bf16)
-  constexpr int CPR = D / 8;   // 16-byte chunks per key row
-  constexpr int KLOADS = kKT * CPR / 256;       // K chunks per thread
-  constexpr int VPAIRS = (kKT / 2) * CPR / 256;  // V key-pair chunks per thread
-  __shared__ __align__(16) uint16_t ks[kKT * KP];
-  __shared__ __align__(16) uint16_t vts[D * VP];
+__global__ __launch_bounds__(256) void vt_transpose_kernel(VtArgs a) {
+  constexpr int P = kBlock + 2;  // LDS pitch (bf16) of the [d][key] tile
+  __shared__ uint16_t t[D * P];
+  const int page = blockIdx.x, g = blockIdx.y;
+  const char* src = a.v + ((long long)page * kBlock * a.hkv + g) * D * 2;
+  const long long row_bytes = (long long)a.hkv * D * 2;
+  for (int c = threadIdx.x; c < kBlock * D / 8; c += 256) {
+    const int key = c / (D / 8), part = c % (D / 8);
+    const u32x4 v = *(const u32x4*)(src + key * row_bytes + part * 16);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const uint32_t w = v[e >> 1];
+      t[(part * 8 + e) * P + key] = (uint16_t)((e & 1) ? (w >> 16) : (w & 0xffffu));
+    }
+  }
+  __syncthreads();
+  char* dst = a.vt + ((long long)page * a.hkv + g) * D * kBlock * 2;
+  for (int c = threadIdx.x; c < D * kBlock / 8; c += 256) {
+    const int d = c / (kBlock / 8), chunk = c % (kBlock / 8);
+    u32x4 o;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int p0 = chunk * 8 + 2 * e;  // storage positions p0, p0+1
+      const int k0 = (p0 & ~15) | vperm(p0 & 15), k1 = (p0 & ~15) | vperm((p0 + 1) & 15);
+      o[e] = (uint32_t)t[d * P + k0] | ((uint32_t)t[d * P + k1] << 16);
+    }
+    *(u32x4*)(dst + ((long long)d * kBlock + chunk * 8) * 2) = o;
+  }
+}
 
-  const int i = a.max_qb - 1 - blockIdx.x;  // heaviest causal rows first
-  const int h = blockIdx.y, b = blockIdx.z;
-  const int g = h / a.group;
-  const int q0 = a.cu_q[b];
-  const int lq = a.cu_q[b + 1] - q0;
+// ---------------------------------------------------------------------------
+// Block lists for one attention launch.  One wave per (q block, kv head, b).
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(64) void plan_kernel(PlanArgs a) {
+  const int i = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
+  const int lane = threadIdx.x;
+  const int lq = a.cu_q[b + 1] - a.cu_q[b];
   const int lk = a.cu_k[b + 1] - a.cu_k[b];
   const int qb = lq / kBlock, kh = (lk - lq) / kBlock;
-  if (i >= qb) return;
-  const int o = lk - lq;
+  int32_t* out = a.lists + (((long long)b * a.hkv + g) * a.max_qb + i) * (a.max_kb + 1);
+  if (i >= qb) {
+    if (lane == 0) out[0] = 0;
+    return;
+  }
+  const uint8_t* mrow = a.mask + (((long long)b * a.hkv + g) * a.max_qb + i) * a.max_kb;
+  const int jend = min(a.jb1, i + kh + 1);
+  const int page0 = a.cu_k[b] / kBlock;
+  int n = 0;
+  for (int j0 = a.jb0; j0 < jend; j0 += 64) {
+    const int j = j0 + lane;
+    int page = -1;
+    if (j < jend && mrow[j]) page = a.block_table ? a.block_table[(long long)b * a.max_blocks + j] : page0 + j;
+    const bool take = page >= 0;
+    const unsigned long long bal = __ballot(take);
+    const int before = __popcll(bal & ((1ull << lane) - 1ull));
+    if (take) out[1 + n + before] = (page << 1) | (j == i + kh ? 1 : 0);
+    n += __popcll(bal);
+  }
+  if (lane == 0) out[0] = n;
+}
+
+// ---------------------------------------------------------------------------
+// bf16 MFMA attention.
+// ---------------------------------------------------------------------------
+template <int D, int HPW>
+__global__ __launch_bounds__(256 * HPW) void attn_mfma(AttnArgs a, int hkv) {
+  constexpr int NW = 4 * HPW;          // waves
+  constexpr int KROW = D * 2;          // bytes per K row in LDS
+  constexpr int KCPR = D / 8;          // 16-byte chunks per K row
+  constexpr int TILE = kKT * KROW;     // bytes of one K (or V^T) tile
+  constexpr int CH = TILE / 16;        // 16-byte chunks per tile
+  constexpr int LPW = CH / (64 * NW);  // direct loads per wave per operand
+  static_assert(LPW >= 1 && CH % (64 * NW) == 0, "tile / workgroup mismatch");
+  // Three stage buffers as separate objects: the compiler then knows that the
+  // direct loads into the other two stages do not alias the stage being read
+  // and waits only for the loads of that stage.
+  __shared__ __align__(1024) char stage0[2 * TILE];
+  __shared__ __align__(1024) char stage1[2 * TILE];
+  __shared__ __align__(1024) char stage2[2 * TILE];
+  extern __shared__ int32_t list[];
+
+  // ---- work unit (XCD-aware: the 8 XCDs take consecutive ids round-robin)
+  const int nwg = gridDim.x;
+  const int id = blockIdx.x;
+  const int full = (nwg / 8) * 8;
+  const int logical = id < full ? (id % 8) * (nwg / 8) + id / 8 : id;
+  const int npair = a.group / HPW;
+  const int irev = logical % a.max_qb;
+  int rest = logical / a.max_qb;
+  const int pair = rest % npair;
+  rest /= npair;
+  const int g = rest % hkv;
+  const int b = rest / hkv;
+  const int i = a.max_qb - 1 - irev;  // heaviest (longest causal) rows first
+  const int q0 = a.cu_q[b];
+  const int lq = a.cu_q[b + 1] - q0;
+  if (i >= lq / kBlock) return;
+
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int l32 = lane & 31, hh = lane >> 5;
-  const int x = i * kBlock + w * 32 + l32;  // this lane's query (sequence-relative)
-  const int qpos = o + x;
+  const int hsub = w >> 2, qs = w & 3;
+  const int h = g * a.group + pair * HPW + hsub;
+  const int xq = qs * 32 + l32;  // query within the block
+  const int x = i * kBlock + xq;
 
-  BlockIter it;
-  it.mrow = a.mask + (((long long)b * (a.hq / a.group) + g) * a.max_qb + i) * a.max_kb;
-  it.table = a.k.block_table ? a.k.block_table + (long long)b * a.k.max_blocks : nullptr;
-  it.jend = min(a.jb1, i + kh + 1);
+  // Block list of this row, copied to LDS so the tile loop reads it with LDS
+  // loads (vector-memory reads would be ordered with the direct tile loads).
+  const int32_t* glist = a.lists + (((long long)b * hkv + g) * a.max_qb + i) * (a.max_kb + 1);
+  const int nblk = glist[0];
+  for (int z = tid; z <= nblk; z += 64 * NW) list[z] = glist[z];
+  __syncthreads();
+  const int ntile = 2 * nblk;
 
-  // Q fragments: B operand of S^T = K Q^T (query col = lane%32, d slots 8*hh..).
+  // Q fragments: B operand of S^T (query col = lane%32, d slots 8*hh .. +8).
   bf16x8 qf[D / 16];
   {
     const char* qrow = a.q + ((long long)(q0 + x) * a.hq + h) * D * 2;
@@ -77,140 +173,140 @@ __global__ __launch_bounds__(256) void attn_bf16(AttnArgs a) {
     for (int kk = 0; kk < D / 16; ++kk) qf[kk] = *(const bf16x8*)(qrow + (kk * 16 + hh * 8) * 2);
   }
 
+  // Per-thread constant parts of the direct-load addresses.
+  const long long k_page_bytes = (long long)kBlock * hkv * D * 2;
+  const long long k_row_bytes = (long long)hkv * D * 2;
+  const long long vt_page_bytes = (long long)hkv * D * kBlock * 2;
+  int koff[LPW], voff[LPW];
+#pragma unroll
+  for (int n = 0; n < LPW; ++n) {
+    const int idx = (w * LPW + n) * 64 + lane;
+    const int krow = idx / KCPR, kpch = idx % KCPR;
+    const int kc = (KCPR == 16) ? (kpch ^ (krow & 15)) : (kpch ^ ((krow >> 1) & 7));
+    koff[n] = (int)(krow * k_row_bytes + kc * 16);
+    const int vrow = idx >> 3, vpch = idx & 7;
+    const int vc = vpch ^ ((vrow >> 1) & 7);
+    voff[n] = (vrow * kBlock + vc * 8) * 2;
+  }
+  const char* kbase = a.k.base + (long long)g * D * 2;
+  const char* vbase = a.vt + (long long)g * D * kBlock * 2;
+
+  auto issue = [&](int t, char* kl) {
+    const int e = list[1 + (t >> 1)];
+    const int page = e >> 1, sub = t & 1;
+    const char* kp = kbase + page * k_page_bytes + sub * kKT * k_row_bytes;
+    const char* vp = vbase + page * vt_page_bytes + sub * kKT * 2;
+    char* vl = kl + TILE;
+#pragma unroll
+    for (int n = 0; n < LPW; ++n) load_lds16(kp + koff[n], kl + (w * LPW + n) * 1024);
+#pragma unroll
+    for (int n = 0; n < LPW; ++n) load_lds16(vp + voff[n], vl + (w * LPW + n) * 1024);
+  };
+
+  // LDS read offsets of this lane's MFMA A fragments.
+  const int kswz = (KCPR == 16) ? (l32 & 15) : ((l32 >> 1) & 7);
+  const int vswz = (l32 >> 1) & 7;
+
   f32x16 oacc[D / 32];
 #pragma unroll
   for (int n = 0; n < D / 32; ++n)
 #pragma unroll
     for (int e = 0; e < 16; ++e) oacc[n][e] = 0.f;
   float m_run = kNegInf, l_run = 0.f;
+  const float c2 = a.scale2;
 
-  u32x4 kreg[KLOADS];
-  u32x4 vreg[VPAIRS][2];
-
-  auto fetch = [&](int j, int sub) {
-    const int key0 = j * kBlock + sub * kKT;
+  auto compute = [&](int t, const char* kl) {
+    const char* vl = kl + TILE;
+    const int e = list[1 + (t >> 1)];
+    const bool diag = (e & 1) != 0;
+    const int sub = t & 1;
+    // ---- S^T = K Q^T
+    f32x16 s0, s1;
 #pragma unroll
-    for (int n = 0; n < KLOADS; ++n) {
-      const int c = tid + 256 * n;
-      const int key = c / CPR, part = c % CPR;
-      kreg[n] = *(const u32x4*)(a.k.row(b, key0 + key, g) + part * 16);
+    for (int z = 0; z < 16; ++z) {
+      s0[z] = 0.f;
+      s1[z] = 0.f;
     }
-#pragma unroll
-    for (int n = 0; n < VPAIRS; ++n) {
-      const int p = tid + 256 * n;
-      const int kp = p % (kKT / 2), part = p / (kKT / 2);
-      vreg[n][0] = *(const u32x4*)(a.v.row(b, key0 + 2 * kp, g) + part * 16);
-      vreg[n][1] = *(const u32x4*)(a.v.row(b, key0 + 2 * kp + 1, g) + part * 16);
-    }
-  };
-  auto stage = [&]() {
-#pragma unroll
-    for (int n = 0; n < KLOADS; ++n) {
-      const int c = tid + 256 * n;
-      const int key = c / CPR, part = c % CPR;
-      *(u32x4*)(&ks[key * KP + part * 8]) = kreg[n];
-    }
-#pragma unroll
-    for (int n = 0; n < VPAIRS; ++n) {
-      const int p = tid + 256 * n;
-      const int kp = p % (kKT / 2), part = p / (kKT / 2);
-      const int pos = vperm(2 * kp);  // even; key 2kp+1 lands at pos+1
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const uint32_t w0 = vreg[n][0][e >> 1], w1 = vreg[n][1][e >> 1];
-        const uint32_t lo = (e & 1) ? (w0 >> 16) : (w0 & 0xffffu);
-        const uint32_t hi = (e & 1) ? (w1 & 0xffff0000u) : (w1 << 16);
-        *(uint32_t*)(&vts[(part * 8 + e) * VP + pos]) = lo | hi;
-      }
-    }
-  };
-
-  int j = it.next(a.jb0);
-  int sub = 0;
-  if (j < it.jend) fetch(j, 0);
-  while (j < it.jend) {
-    stage();
-    __syncthreads();
-    const int cj = j, csub = sub;
-    if (sub == 0) {
-      sub = 1;
-    } else {
-      sub = 0;
-      j = it.next(j + 1);
-    }
-    if (j < it.jend) fetch(j, sub);
-
-    // ---- S^T = K Q^T over this 64-key tile
-    f32x16 s[2];
-#pragma unroll
-    for (int cb = 0; cb < 2; ++cb)
-#pragma unroll
-      for (int e = 0; e < 16; ++e) s[cb][e] = 0.f;
 #pragma unroll
     for (int kk = 0; kk < D / 16; ++kk) {
+      const int pc = (2 * kk + hh) ^ kswz;
+      const bf16x8 a0 = *(const bf16x8*)(kl + l32 * KROW + pc * 16);
+      const bf16x8 a1 = *(const bf16x8*)(kl + (32 + l32) * KROW + pc * 16);
+      s0 = mfma32(a0, qf[kk], s0);
+      s1 = mfma32(a1, qf[kk], s1);
+    }
+    // ---- causal mask on the diagonal block only
+    if (diag) {
 #pragma unroll
-      for (int cb = 0; cb < 2; ++cb) {
-        const bf16x8 af = *(const bf16x8*)(&ks[(cb * 32 + l32) * KP + kk * 16 + hh * 8]);
-        s[cb] = mfma32(af, qf[kk], s[cb]);
+      for (int z = 0; z < 16; ++z) {
+        const int key = sub * kKT + 8 * (z >> 2) + 4 * hh + (z & 3);
+        if (key > xq) s0[z] = kNegInf;
+        if (key + 32 > xq) s1[z] = kNegInf;
       }
     }
-    // ---- online softmax (base 2), causal mask on the diagonal block only
-    const int key0 = cj * kBlock + csub * kKT;
-    const bool diag = (cj == i + kh);
-    float mx = kNegInf;
+    float mx = fmaxf(s0[0], s1[0]);
 #pragma unroll
-    for (int cb = 0; cb < 2; ++cb)
-#pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        float v = s[cb][e] * a.scale2;
-        if (diag) {
-          const int key = key0 + cb * 32 + 8 * (e >> 2) + 4 * hh + (e & 3);
-          if (key > qpos) v = kNegInf;
-        }
-        s[cb][e] = v;
-        mx = fmaxf(mx, v);
-      }
+    for (int z = 1; z < 16; ++z) mx = fmaxf(mx, fmaxf(s0[z], s1[z]));
     mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-    const float m_new = fmaxf(m_run, mx);
-    const float m_use = (m_new == kNegInf) ? 0.f : m_new;
-    const float alpha = exp2f(m_run - m_use);
+    const float m_tile = mx * c2;
+    // lazy rescale: refresh the running max only when it would grow by > 8
+    if (__ballot(m_tile > m_run + 8.0f) != 0ull) {
+      const float m_new = fmaxf(m_run, m_tile);
+      const float alpha = exp2f(m_run - m_new);
+      l_run *= alpha;
+#pragma unroll
+      for (int n = 0; n < D / 32; ++n)
+#pragma unroll
+        for (int z = 0; z < 16; ++z) oacc[n][z] *= alpha;
+      m_run = m_new;
+    }
+    const float mneg = (m_run == kNegInf) ? 0.f : -m_run;
     float psum = 0.f;
 #pragma unroll
-    for (int cb = 0; cb < 2; ++cb)
-#pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        const float p = exp2f(s[cb][e] - m_use);
-        s[cb][e] = p;
-        psum += p;
-      }
-    l_run = l_run * alpha + psum;
-    m_run = m_new;
-#pragma unroll
-    for (int n = 0; n < D / 32; ++n)
-#pragma unroll
-      for (int e = 0; e < 16; ++e) oacc[n][e] *= alpha;
-    // ---- P^T fragments (B operand), k-step m covers keys 16m .. 16m+15
+    for (int z = 0; z < 16; ++z) {
+      s0[z] = exp2f(fmaf(s0[z], c2, mneg));
+      s1[z] = exp2f(fmaf(s1[z], c2, mneg));
+      psum += s0[z] + s1[z];
+    }
+    l_run += psum;
+    // ---- P^T fragments: k-step m covers keys 16m .. 16m+15 of the tile
     bf16x8 pb[4];
 #pragma unroll
     for (int m = 0; m < 4; ++m) {
-      const int cb = m >> 1, i0 = 2 * (m & 1);
-      u32x4 u;
-      u[0] = pack_bf16x2(s[cb][4 * i0 + 0], s[cb][4 * i0 + 1]);
-      u[1] = pack_bf16x2(s[cb][4 * i0 + 2], s[cb][4 * i0 + 3]);
-      u[2] = pack_bf16x2(s[cb][4 * i0 + 4], s[cb][4 * i0 + 5]);
-      u[3] = pack_bf16x2(s[cb][4 * i0 + 6], s[cb][4 * i0 + 7]);
-      pb[m] = __builtin_bit_cast(bf16x8, u);
+      const int i0 = 2 * (m & 1);
+#pragma unroll
+      for (int z = 0; z < 8; ++z) pb[m][z] = (__bf16)((m < 2) ? s0[4 * i0 + z] : s1[4 * i0 + z]);
     }
     // ---- O^T += V^T P^T
 #pragma unroll
     for (int m = 0; m < 4; ++m) {
+      const int pc = (2 * m + hh) ^ vswz;
 #pragma unroll
       for (int n = 0; n < D / 32; ++n) {
-        const bf16x8 av = *(const bf16x8*)(&vts[(n * 32 + l32) * VP + m * 16 + hh * 8]);
+        const bf16x8 av = *(const bf16x8*)(vl + (n * 32 + l32) * (kKT * 2) + pc * 16);
         oacc[n] = mfma32(av, pb[m], oacc[n]);
       }
     }
-    __syncthreads();
+  };
+
+  // One tile step with compile-time stage buffers: wait for this wave's loads
+  // of tile t (only tile t+1's may remain in flight), barrier to publish all
+  // waves' parts (a bare s_barrier: a memory fence would drain the loads of
+  // tile t+1 too), refill the stage freed by tile t-1 with tile t+2, compute.
+  auto step = [&](int t, char* cur, char* ahead2) {
+    if (t + 1 < ntile) wait_vmcnt<2 * LPW>();
+    else wait_vmcnt<0>();
+    __builtin_amdgcn_s_barrier();
+    if (t + 2 < ntile) issue(t + 2, ahead2);
+    compute(t, cur);
+  };
+
+  if (ntile > 0) issue(0, stage0);
+  if (ntile > 1) issue(1, stage1);
+  for (int t = 0; t < ntile; t += 3) {
+    step(t, stage0, stage2);
+    if (t + 1 < ntile) step(t + 1, stage1, stage0);
+    if (t + 2 < ntile) step(t + 2, stage2, stage1);
   }
 
   const float l_tot = l_run + __shfl_xor(l_run, 32, 64);
@@ -227,9 +323,13 @@ __global__ __launch_bounds__(256) void attn_bf16(AttnArgs a) {
         f32x4 v = {v0, v1, v2, v3};
         *(f32x4*)(a.out_f32 + orow + d) = v;
       } else {
-        uint32_t* p = (uint32_t*)((char*)a.out + (orow + d) * 2);
-        p[0] = pack_bf16x2(v0, v1);
-        p[1] = pack_bf16x2(v2, v3);
+        typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+        bf16x4 o4;
+        o4[0] = (__bf16)v0;
+        o4[1] = (__bf16)v1;
+        o4[2] = (__bf16)v2;
+        o4[3] = (__bf16)v3;
+        *(bf16x4*)((char*)a.out + (orow + d) * 2) = o4;
       }
     }
   if (a.lse && hh == 0) {
@@ -237,6 +337,21 @@ __global__ __launch_bounds__(256) void attn_bf16(AttnArgs a) {
     a.lse[(long long)h * a.total_q + q0 + x] = lse;
   }
 }
+
+struct BlockIter {
+  const uint8_t* mrow;
+  const int32_t* table;  // block table row (paged) or nullptr
+  int jend;
+  // First selected block >= j (page present), or jend.
+  __device__ __forceinline__ int next(int j) const {
+    for (; j < jend; ++j) {
+      if (!mrow[j]) continue;
+      if (table && table[j] < 0) continue;
+      return j;
+    }
+    return jend;
+  }
+};
 
 // ---------------------------------------------------------------------------
 // fp32 inputs: one thread per query, key tiles of 32 staged in LDS.
@@ -360,9 +475,17 @@ __global__ __launch_bounds__(256) void merge_kernel(MergeArgs a) {
 
 template <int D>
 hipError_t attn_dispatch(const AttnArgs& a, int dtype, int batch, hipStream_t s) {
-  dim3 grid(a.max_qb, a.hq, batch);
-  if (dtype == 0) hipLaunchKernelGGL((attn_bf16<D>), grid, dim3(256), 0, s, a);
-  else hipLaunchKernelGGL((attn_f32<D>), grid, dim3(128), 0, s, a);
+  if (dtype == 0) {
+    const int hkv = a.hq / a.group;
+    const int hpw = (a.group % 2 == 0) ? 2 : 1;
+    const int nwg = batch * hkv * (a.group / hpw) * a.max_qb;
+    const size_t shm = (size_t)(a.max_kb + 1) * sizeof(int32_t);
+    if (hpw == 2) hipLaunchKernelGGL((attn_mfma<D, 2>), dim3(nwg), dim3(512), shm, s, a, hkv);
+    else hipLaunchKernelGGL((attn_mfma<D, 1>), dim3(nwg), dim3(256), shm, s, a, hkv);
+  } else {
+    dim3 grid(a.max_qb, a.hq, batch);
+    hipLaunchKernelGGL((attn_f32<D>), grid, dim3(128), 0, s, a);
+  }
   return hipGetLastError();
 }
 
@@ -374,6 +497,21 @@ hipError_t launch_attention(const AttnArgs& a, int dtype, int head_dim, int batc
   if (head_dim == 128) return attn_dispatch<128>(a, dtype, batch, s);
   if (head_dim == 64) return attn_dispatch<64>(a, dtype, batch, s);
   return hipErrorInvalidValue;
+}
+
+hipError_t launch_vt_transpose(const VtArgs& a, hipStream_t s) {
+  if (a.num_pages <= 0) return hipSuccess;
+  dim3 grid(a.num_pages, a.hkv);
+  if (a.head_dim == 128) hipLaunchKernelGGL((vt_transpose_kernel<128>), grid, dim3(256), 0, s, a);
+  else if (a.head_dim == 64) hipLaunchKernelGGL((vt_transpose_kernel<64>), grid, dim3(256), 0, s, a);
+  else return hipErrorInvalidValue;
+  return hipGetLastError();
+}
+
+hipError_t launch_plan(const PlanArgs& a, int batch, hipStream_t s) {
+  if (a.max_qb <= 0 || batch <= 0) return hipSuccess;
+  hipLaunchKernelGGL(plan_kernel, dim3(a.max_qb, a.hkv, batch), dim3(64), 0, s, a);
+  return hipGetLastError();
 }
 
 hipError_t launch_merge(const MergeArgs& a, hipStream_t s) {

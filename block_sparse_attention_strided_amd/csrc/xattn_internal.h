@@ -56,12 +56,42 @@ struct SelectArgs {
   int32_t* counts;   // [batch, 2]
 };
 
+// V re-laid out for the attention kernel: page p (128 keys) of kv head g is a
+// [d][128] bf16 block at vt + ((p*hkv + g)*d)*128*2, keys of every 16-key
+// group stored in the order the MFMA B operand of P^T consumes them.
+struct VtArgs {
+  const char* v;  // [num_pages, 128, hkv, d] (a contiguous [total_k, hkv, d] array is the same)
+  char* vt;
+  int num_pages;
+  int hkv;
+  int head_dim;
+};
+
+// Per (b, kv head g, q block i) list of the key blocks the attention visits,
+// in increasing j: lists[row*(max_kb+1)] = count, then entries
+// (page << 1) | (j == i + Kh), for selected j in [jb0, min(jb1, i+Kh+1)).
+struct PlanArgs {
+  const uint8_t* mask;  // [batch, hkv, max_qb, max_kb]
+  const int32_t* cu_q;
+  const int32_t* cu_k;
+  const int32_t* block_table;  // [batch, max_blocks] or nullptr (contiguous)
+  int max_blocks;
+  int hkv;
+  int max_qb;
+  int max_kb;
+  int jb0;
+  int jb1;
+  int32_t* lists;
+};
+
 // Attention of one launch.  Keys come from blocks j in [jb0, jb1) whose mask
 // byte is set and whose page is present; rows are (b, q head, query).
 struct AttnArgs {
   const char* q;
   KvView k;
   KvView v;
+  const char* vt;         // bf16 path: transposed V pages (VtArgs layout)
+  const int32_t* lists;   // bf16 path: block lists (PlanArgs layout)
   const uint8_t* mask;  // [batch, hkv, max_qb, max_kb]
   const int32_t* cu_q;
   const int32_t* cu_k;
@@ -96,6 +126,8 @@ hipError_t launch_estimate(const EstArgs& a, int dtype, int head_dim, int stride
                            hipStream_t s);
 hipError_t launch_block_sums(const BlockSumArgs& a, int batch, hipStream_t s);
 hipError_t launch_select(const SelectArgs& a, int batch, hipStream_t s);
+hipError_t launch_vt_transpose(const VtArgs& a, hipStream_t s);
+hipError_t launch_plan(const PlanArgs& a, int batch, hipStream_t s);
 hipError_t launch_attention(const AttnArgs& a, int dtype, int head_dim, int batch,
                             hipStream_t s);
 hipError_t launch_merge(const MergeArgs& a, hipStream_t s);
