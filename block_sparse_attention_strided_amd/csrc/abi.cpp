@@ -7,6 +7,10 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <unistd.h>
+
+#include <algorithm>
+#include <utility>
 #include <string>
 #include <vector>
 
@@ -174,6 +178,7 @@ KvView make_view(const XattnShape* sh, const Plan& p, const void* base) {
   v.kv_heads = p.hkv;
   v.head_dim = p.d;
   v.elem_bytes = p.elem;
+  v.y_offset = 0;
   return v;
 }
 
@@ -294,22 +299,226 @@ hipError_t run_attention(const XattnShape* sh, const Plan& p, AttnArgs aa, const
 }  // namespace
 
 // ---------------------------------------------------------------------------
-// Ring engine (history streamed from pinned host memory)
+// Ring engine: device slots fed from pinned host history on a transfer
+// stream.  Per slot s: the transfer stream waits done[s], copies, records
+// ready[s]; the caller's compute stream waits ready[s], runs every kernel
+// that reads the slot, records done[s].  done[s] is recorded once at
+// creation so the first copy into a slot does not wait.
 // ---------------------------------------------------------------------------
 struct XattnRing {
-  int num_slots, slot_blocks, hkv, d, dtype, elem;
-  size_t block_bytes;  // one 128-token block of K (or V)
+  int num_slots = 0, slot_blocks = 0, hkv = 0, d = 0, dtype = 0, elem = 0;
+  size_t block_bytes = 0;  // one 128-token block of K (or V)
   char* k_slots = nullptr;
   char* v_slots = nullptr;
   hipStream_t xfer = nullptr;
   std::vector<hipEvent_t> ready, done;
   hipEvent_t sel_ready = nullptr;
-  uint8_t* host_sel = nullptr;     // pinned, maxKb bytes (grown on demand)
-  int host_sel_cap = 0;
-  int32_t* host_table = nullptr;   // pinned slot tables (grown on demand)
-  size_t host_table_cap = 0;
+  uint8_t* host_sel = nullptr;    // pinned staging of the selection result
+  int32_t* host_table = nullptr;  // pinned staging of the block -> slot table
+  int host_cap = 0;               // entries of both staging buffers
+  int next_slot = 0;
   int copy_delay_us = 0;
 };
+
+namespace {
+
+void sleep_host_fn(void* arg) { usleep((useconds_t)(*(const int*)arg)); }
+
+int check_pinned(const void* ptr, const char* what) {
+  hipPointerAttribute_t attr;
+  hipError_t e = hipPointerGetAttributes(&attr, ptr);
+  if (e != hipSuccess) {
+    (void)hipGetLastError();
+    return fail(XATTN_ERR_NOT_PINNED, "%s is not pinned host memory", what);
+  }
+  if (attr.type != hipMemoryTypeHost)
+    return fail(XATTN_ERR_NOT_PINNED, "%s is not pinned host memory (memory type %d)", what, (int)attr.type);
+  return XATTN_OK;
+}
+
+// Ring copy of `nb` K/V blocks into slot s, enqueued on the transfer stream;
+// `runs` lists (first history block, count) runs laid out back to back.
+hipError_t ring_fill(XattnRing* r, int s, const char* kh, const char* vh,
+                     const std::vector<std::pair<int, int>>& runs, bool with_v) {
+  hipError_t e = hipStreamWaitEvent(r->xfer, r->done[s], 0);
+  if (e != hipSuccess) return e;
+  if (r->copy_delay_us > 0) {
+    e = hipLaunchHostFunc(r->xfer, sleep_host_fn, &r->copy_delay_us);
+    if (e != hipSuccess) return e;
+  }
+  const size_t slot_bytes = (size_t)r->slot_blocks * r->block_bytes;
+  size_t pos = 0;
+  for (const auto& run : runs) {
+    const size_t off = (size_t)run.first * r->block_bytes, n = (size_t)run.second * r->block_bytes;
+    e = hipMemcpyAsync(r->k_slots + s * slot_bytes + pos, kh + off, n, hipMemcpyHostToDevice, r->xfer);
+    if (e != hipSuccess) return e;
+    if (with_v) {
+      e = hipMemcpyAsync(r->v_slots + s * slot_bytes + pos, vh + off, n, hipMemcpyHostToDevice, r->xfer);
+      if (e != hipSuccess) return e;
+    }
+    pos += n;
+  }
+  return hipEventRecord(r->ready[s], r->xfer);
+}
+
+int prefill_ring(XattnRing* r, const XattnShape* sh, const XattnParams* pr, const Plan& p, const void* q,
+                 const void* k, const void* v, const void* k_hist, const void* v_hist, int hist_blocks,
+                 void* out, float* lse, int32_t* counts, const XattnAux* aux, void* ws, hipStream_t st) {
+  const int lq = sh->cu_q_host[1], lk = sh->cu_k_host[1];
+  const int qb = lq / XATTN_BLOCK, kb = lk / XATTN_BLOCK, kh = kb - qb;
+  if (p.batch != 1 || sh->block_table)
+    return fail(XATTN_ERR_INVALID, "ring mode needs batch == 1 and no block table");
+  if (hist_blocks != kh)
+    return fail(XATTN_ERR_INVALID, "hist_blocks (%d) must equal (Lk - Lq) / 128 = %d", hist_blocks, kh);
+  if (r->hkv != p.hkv || r->d != p.d || r->dtype != p.dtype)
+    return fail(XATTN_ERR_INVALID, "ring geometry (kv heads %d, head_dim %d, dtype %d) does not match the shape",
+                r->hkv, r->d, r->dtype);
+  if (pr->select_mode != XATTN_SELECT_CHUNK_VOTE)
+    return fail(XATTN_ERR_UNSUPPORTED, "ring mode streams the voted history blocks: select_mode must be CHUNK_VOTE");
+  if (kh > 0) {
+    if (!k_hist || !v_hist) return fail(XATTN_ERR_INVALID, "k_hist_host and v_hist_host must not be NULL");
+    int rc = check_pinned(k_hist, "k_hist_host");
+    if (rc) return rc;
+    if ((rc = check_pinned(v_hist, "v_hist_host"))) return rc;
+  }
+  if (r->host_cap < kb) {
+    if (r->host_sel) (void)hipHostFree(r->host_sel);
+    if (r->host_table) (void)hipHostFree(r->host_table);
+    r->host_sel = nullptr;
+    r->host_table = nullptr;
+    r->host_cap = 0;
+    hipError_t e = hipHostMalloc((void**)&r->host_sel, (size_t)kb, hipHostMallocDefault);
+    if (e == hipSuccess) e = hipHostMalloc((void**)&r->host_table, (size_t)kb * sizeof(int32_t), hipHostMallocDefault);
+    if (e != hipSuccess) return hip_fail(e, "ring staging allocation");
+    r->host_cap = kb;
+  }
+  g_last_error.clear();
+  const char* kh_ptr = (const char*)k_hist;
+  const char* vh_ptr = (const char*)v_hist;
+  const size_t slot_bytes = (size_t)r->slot_blocks * r->block_bytes;
+  float* part = ws_at<float>(ws, p.off_part);
+  float* bs = (aux && aux->block_sums) ? aux->block_sums : ws_at<float>(ws, p.off_bs);
+  uint8_t* maskkv = (aux && aux->mask_kv) ? aux->mask_kv : ws_at<uint8_t>(ws, p.off_maskkv);
+  uint8_t* hist = (aux && aux->hist_sel) ? aux->hist_sel : ws_at<uint8_t>(ws, p.off_hist);
+  int32_t* cnt = counts ? counts : ws_at<int32_t>(ws, p.off_counts);
+  int32_t* table = ws_at<int32_t>(ws, p.off_table);
+  hipError_t e;
+
+  // ---- pass 1: history K through the ring, estimate per slot; then the current chunk
+  for (int j0 = 0; j0 < kh; j0 += r->slot_blocks) {
+    const int nb = std::min(r->slot_blocks, kh - j0);
+    const int s = r->next_slot;
+    r->next_slot = (s + 1) % r->num_slots;
+    if ((e = ring_fill(r, s, kh_ptr, vh_ptr, {{j0, nb}}, false)) != hipSuccess) return hip_fail(e, "ring copy");
+    if ((e = hipStreamWaitEvent(st, r->ready[s], 0)) != hipSuccess) return hip_fail(e, "ring wait");
+    KvView kv = make_view(sh, p, r->k_slots + s * slot_bytes);
+    kv.y_offset = j0 * XATTN_BLOCK;
+    if ((e = run_estimate(sh, p, q, kv, j0, nb, part, st)) != hipSuccess) return hip_fail(e, "estimate launch");
+    if ((e = hipEventRecord(r->done[s], st)) != hipSuccess) return hip_fail(e, "ring record");
+  }
+  {
+    KvView kv = make_view(sh, p, k);
+    kv.y_offset = kh * XATTN_BLOCK;
+    if ((e = run_estimate(sh, p, q, kv, kh, qb, part, st)) != hipSuccess) return hip_fail(e, "estimate launch");
+  }
+  if ((e = run_block_sums(sh, p, part, bs, st)) != hipSuccess) return hip_fail(e, "block-sum launch");
+  if ((e = run_select(sh, pr, p, bs, ws_at<uint8_t>(ws, p.off_maskq), maskkv, hist, cnt, st)) != hipSuccess)
+    return hip_fail(e, "select launch");
+
+  // ---- the one host wait: which history blocks were voted in
+  if ((e = hipMemcpyAsync(r->host_sel, hist, (size_t)kb, hipMemcpyDeviceToHost, st)) != hipSuccess)
+    return hip_fail(e, "selection copy");
+  if ((e = hipEventRecord(r->sel_ready, st)) != hipSuccess) return hip_fail(e, "selection record");
+  if ((e = hipEventSynchronize(r->sel_ready)) != hipSuccess) return hip_fail(e, "selection wait");
+  std::vector<int> sel;
+  for (int j = 0; j < kh; ++j)
+    if (r->host_sel[j]) sel.push_back(j);
+  for (int j = 0; j < kb; ++j) r->host_table[j] = -1;
+  for (size_t x = 0; x < sel.size(); ++x) r->host_table[sel[x]] = (int)(x % r->slot_blocks);
+  for (int j = kh; j < kb; ++j) r->host_table[j] = j - kh;
+  if ((e = hipMemcpyAsync(table, r->host_table, (size_t)kb * sizeof(int32_t), hipMemcpyHostToDevice, st)) != hipSuccess)
+    return hip_fail(e, "table copy");
+
+  auto paged_view = [&](const void* base) {
+    KvView kv = make_view(sh, p, base);
+    kv.block_table = table;
+    kv.max_blocks = kb;
+    return kv;
+  };
+  float* o_acc = ws_at<float>(ws, p.off_o[0]);
+  float* l_acc = ws_at<float>(ws, p.off_l[0]);
+  float* o_cur = ws_at<float>(ws, p.off_o[1]);
+  float* l_cur = ws_at<float>(ws, p.off_l[1]);
+  float* o_tmp = ws_at<float>(ws, p.off_o[2]);
+  float* l_tmp = ws_at<float>(ws, p.off_l[2]);
+  const bool bf16 = p.dtype == XATTN_DTYPE_BF16;
+
+  // ---- current chunk (causal), overlapping the first history copies
+  {
+    AttnArgs aa = attn_args(sh, p, q, paged_view(k), paged_view(v), maskkv, kh, kb);
+    if (sel.empty()) {
+      if (bf16) aa.out = out;
+      else aa.out_f32 = (float*)out;
+      aa.lse = lse;
+    } else {
+      aa.out_f32 = o_cur;
+      aa.lse = l_cur;
+    }
+    if ((e = run_attention(sh, p, aa, v, qb, ws, true, st)) != hipSuccess) return hip_fail(e, "attention launch");
+    if (sel.empty()) return XATTN_OK;
+  }
+  // ---- selected history blocks, slot by slot; partials merged history-first
+  for (size_t x0 = 0; x0 < sel.size(); x0 += r->slot_blocks) {
+    const size_t x1 = std::min(sel.size(), x0 + (size_t)r->slot_blocks);
+    std::vector<std::pair<int, int>> runs;
+    for (size_t x = x0; x < x1; ++x) {
+      if (!runs.empty() && runs.back().first + runs.back().second == sel[x]) runs.back().second++;
+      else runs.push_back({sel[x], 1});
+    }
+    const int s = r->next_slot;
+    r->next_slot = (s + 1) % r->num_slots;
+    if ((e = ring_fill(r, s, kh_ptr, vh_ptr, runs, true)) != hipSuccess) return hip_fail(e, "ring copy");
+    if ((e = hipStreamWaitEvent(st, r->ready[s], 0)) != hipSuccess) return hip_fail(e, "ring wait");
+    const bool first = (x0 == 0);
+    AttnArgs aa = attn_args(sh, p, q, paged_view(r->k_slots + s * slot_bytes), paged_view(r->v_slots + s * slot_bytes),
+                            maskkv, sel[x0], sel[x1 - 1] + 1);
+    aa.out_f32 = first ? o_acc : o_tmp;
+    aa.lse = first ? l_acc : l_tmp;
+    if ((e = run_attention(sh, p, aa, r->v_slots + s * slot_bytes, (int)(x1 - x0), ws, true, st)) != hipSuccess)
+      return hip_fail(e, "attention launch");
+    if ((e = hipEventRecord(r->done[s], st)) != hipSuccess) return hip_fail(e, "ring record");
+    if (!first) {
+      MergeArgs ma;
+      ma.rows = p.total_q;
+      ma.heads = p.hq;
+      ma.head_dim = p.d;
+      ma.o_a = o_acc;
+      ma.lse_a = l_acc;
+      ma.o_b = o_tmp;
+      ma.lse_b = l_tmp;
+      ma.o = o_acc;
+      ma.o_bf16 = nullptr;
+      ma.lse = l_acc;
+      if ((e = launch_merge(ma, st)) != hipSuccess) return hip_fail(e, "merge launch");
+    }
+  }
+  // ---- final: history partial, then the current chunk
+  MergeArgs ma;
+  ma.rows = p.total_q;
+  ma.heads = p.hq;
+  ma.head_dim = p.d;
+  ma.o_a = o_acc;
+  ma.lse_a = l_acc;
+  ma.o_b = o_cur;
+  ma.lse_b = l_cur;
+  ma.o = bf16 ? nullptr : (float*)out;
+  ma.o_bf16 = bf16 ? out : nullptr;
+  ma.lse = lse ? lse : l_tmp;
+  if ((e = launch_merge(ma, st)) != hipSuccess) return hip_fail(e, "merge launch");
+  return XATTN_OK;
+}
+
+}  // namespace
 
 extern "C" {
 
@@ -408,10 +617,9 @@ int xattn_prefill_chunk(XattnRing* ring, const XattnShape* shape, const XattnPar
   if (rc) return rc;
   if (!q || !k || !v || !out) return fail(XATTN_ERR_INVALID, "q, k, v and out must not be NULL");
   if ((rc = check_ws(p, ws, ws_bytes))) return rc;
-  if (ring) return fail(XATTN_ERR_UNSUPPORTED, "ring mode is not available in this build");
-  (void)k_hist_host;
-  (void)v_hist_host;
-  (void)hist_blocks;
+  if (ring)
+    return prefill_ring(ring, shape, params, p, q, k, v, k_hist_host, v_hist_host, hist_blocks, out, lse, counts,
+                        aux, ws, (hipStream_t)stream);
   g_last_error.clear();
   hipStream_t st = (hipStream_t)stream;
   float* part = ws_at<float>(ws, p.off_part);
@@ -437,16 +645,55 @@ int xattn_prefill_chunk(XattnRing* ring, const XattnShape* shape, const XattnPar
 
 int xattn_ring_create(int num_slots, int slot_blocks, int num_kv_heads, int head_dim, int dtype,
                       XattnRing** out) {
-  (void)num_slots;
-  (void)slot_blocks;
-  (void)num_kv_heads;
-  (void)head_dim;
-  (void)dtype;
-  if (out) *out = nullptr;
-  return fail(XATTN_ERR_UNSUPPORTED, "ring mode is not available in this build");
+  if (!out) return fail(XATTN_ERR_INVALID, "out must not be NULL");
+  *out = nullptr;
+  if (num_slots < 2 || slot_blocks < 1 || num_kv_heads < 1)
+    return fail(XATTN_ERR_INVALID, "need num_slots >= 2, slot_blocks >= 1, num_kv_heads >= 1");
+  if (head_dim != 64 && head_dim != 128) return fail(XATTN_ERR_UNSUPPORTED, "head_dim must be 64 or 128");
+  if (dtype != XATTN_DTYPE_BF16 && dtype != XATTN_DTYPE_F32) return fail(XATTN_ERR_INVALID, "unknown dtype %d", dtype);
+  XattnRing* r = new XattnRing();
+  r->num_slots = num_slots;
+  r->slot_blocks = slot_blocks;
+  r->hkv = num_kv_heads;
+  r->d = head_dim;
+  r->dtype = dtype;
+  r->elem = dtype == XATTN_DTYPE_BF16 ? 2 : 4;
+  r->block_bytes = (size_t)XATTN_BLOCK * num_kv_heads * head_dim * r->elem;
+  const size_t bytes = (size_t)num_slots * slot_blocks * r->block_bytes;
+  hipError_t e = hipMalloc((void**)&r->k_slots, bytes);
+  if (e == hipSuccess) e = hipMalloc((void**)&r->v_slots, bytes);
+  if (e == hipSuccess) e = hipStreamCreateWithFlags(&r->xfer, hipStreamNonBlocking);
+  for (int s = 0; e == hipSuccess && s < num_slots; ++s) {
+    hipEvent_t a = nullptr, b = nullptr;
+    e = hipEventCreateWithFlags(&a, hipEventDisableTiming);
+    if (e == hipSuccess) e = hipEventCreateWithFlags(&b, hipEventDisableTiming);
+    if (a) r->ready.push_back(a);
+    if (b) r->done.push_back(b);
+    if (e == hipSuccess) e = hipEventRecord(b, r->xfer);  // slot free before its first copy
+  }
+  if (e == hipSuccess) e = hipEventCreateWithFlags(&r->sel_ready, hipEventDisableTiming);
+  if (e != hipSuccess) {
+    int rc = hip_fail(e, "ring creation");
+    xattn_ring_destroy(r);
+    return rc;
+  }
+  *out = r;
+  return XATTN_OK;
 }
 
-void xattn_ring_destroy(XattnRing* ring) { (void)ring; }
+void xattn_ring_destroy(XattnRing* r) {
+  if (!r) return;
+  if (r->xfer) (void)hipStreamSynchronize(r->xfer);
+  for (auto ev : r->ready) (void)hipEventSynchronize(ev), (void)hipEventDestroy(ev);
+  for (auto ev : r->done) (void)hipEventSynchronize(ev), (void)hipEventDestroy(ev);
+  if (r->sel_ready) (void)hipEventDestroy(r->sel_ready);
+  if (r->xfer) (void)hipStreamDestroy(r->xfer);
+  if (r->k_slots) (void)hipFree(r->k_slots);
+  if (r->v_slots) (void)hipFree(r->v_slots);
+  if (r->host_sel) (void)hipHostFree(r->host_sel);
+  if (r->host_table) (void)hipHostFree(r->host_table);
+  delete r;
+}
 
 int xattn_ring_set_copy_delay_us(XattnRing* ring, int usec) {
   if (!ring || usec < 0) return fail(XATTN_ERR_INVALID, "ring must not be NULL and usec >= 0");

@@ -49,6 +49,7 @@ struct KvView {
   int kv_heads;
   int head_dim;
   int elem_bytes;
+  int y_offset;  // contiguous layout: the array starts at key y_offset of the sequence
 
   // Byte address of key `y` (sequence-relative), kv head `g`, element 0.
   // Paged: returns nullptr when the page is unallocated (-1).
@@ -60,7 +61,7 @@ struct KvView {
       return base + ((long long)page * kBlock + (y & (kBlock - 1))) * row_bytes +
              (long long)g * head_dim * elem_bytes;
     }
-    return base + (long long)(cu_k[b] + y) * row_bytes + (long long)g * head_dim * elem_bytes;
+    return base + (long long)(cu_k[b] + y - y_offset) * row_bytes + (long long)g * head_dim * elem_bytes;
   }
 };
 

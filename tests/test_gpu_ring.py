@@ -1,0 +1,137 @@
+"""Ring mode of xattn_prefill_chunk: history K/V in pinned host memory,
+streamed through device slots on a transfer stream with event ordering.
+
+Checks: agreement with the resident-KV path and with the oracle; bit-equal
+results when every slot copy is delayed on the host (a missing wait would
+let a kernel read a stale slot); slot reuse with 2 slots; a pageable history
+is rejected before any work; the 128K-context workload on sampled rows.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import block_sparse_attention_strided_amd as X
+from tests.gpu_util import Run, assert_attention_close, assert_block_sums_close, sample_rows, say
+from workloads import make_random, make_workload
+
+pytestmark = [pytest.mark.gpu,
+              pytest.mark.skipif(not torch.cuda.is_available(), reason="needs a GPU")]
+
+
+def _ring_inputs(w, pinned=True):
+    lq, lk = w.lens(0)
+    kh = (lk - lq) // 128
+    hkv, d = w.num_kv_heads, w.head_dim
+    kh_t = w.k[: lk - lq].reshape(kh, 128, hkv, d)
+    vh_t = w.v[: lk - lq].reshape(kh, 128, hkv, d)
+    if pinned:
+        k_hist = torch.empty(kh_t.shape, dtype=w.dtype, pin_memory=True)
+        v_hist = torch.empty(vh_t.shape, dtype=w.dtype, pin_memory=True)
+        k_hist.copy_(kh_t)
+        v_hist.copy_(vh_t)
+    else:
+        k_hist, v_hist = kh_t.contiguous(), vh_t.contiguous()
+    k_cur = w.k[lk - lq:].cuda()
+    v_cur = w.v[lk - lq:].cuda()
+    return k_hist, v_hist, k_cur, v_cur, kh
+
+
+def _run_ring(r, w, ring, k_hist, v_hist, k_cur, v_cur, kh):
+    out = torch.full_like(r.q, float("nan"))
+    lse = torch.full((r.hq, r.shape.total_q), float("nan"), device="cuda")
+    counts = torch.full((1, 2), -1, dtype=torch.int32, device="cuda")
+    aux = {
+        "block_sums": torch.empty((1, r.hq, r.max_qb, r.max_kb), device="cuda"),
+        "mask_kv": torch.empty((1, r.hkv, r.max_qb, r.max_kb), dtype=torch.uint8, device="cuda"),
+        "hist_sel": torch.empty((1, r.max_kb), dtype=torch.uint8, device="cuda"),
+    }
+    X.xattn_prefill_chunk(r.shape, r.params, r.q, k_cur, v_cur, out, lse, counts, r.ws, aux=aux, ring=ring,
+                          k_hist=k_hist, v_hist=v_hist, hist_blocks=kh)
+    torch.cuda.synchronize()
+    return out, lse, counts, aux
+
+
+def _small():
+    return make_random("ring_small", seed=41, hq=8, hkv=2, d=128, lq=[1024], lk=[16384],
+                       stride=16, threshold=0.95, select_mode="chunk_vote", kv_chunk_tokens=1024)
+
+
+def test_ring_matches_resident_path_and_oracle():
+    w = _small()
+    r = Run(w)
+    k_hist, v_hist, k_cur, v_cur, kh = _ring_inputs(w)
+    ring = X.Ring(4, 8, w.num_kv_heads, w.head_dim, w.dtype)
+    say("ring small: resident path")
+    o_res, l_res, c_res, aux_res = r.prefill()
+    say("ring small: ring path")
+    o_ring, l_ring, c_ring, aux_ring = _run_ring(r, w, ring, k_hist, v_hist, k_cur, v_cur, kh)
+    ring.close()
+    # the estimate and the selection see bit-identical inputs either way
+    assert torch.equal(aux_res["block_sums"], aux_ring["block_sums"])
+    assert torch.equal(aux_res["mask_kv"], aux_ring["mask_kv"])
+    assert torch.equal(c_res, c_ring)
+    assert (o_res.float() - o_ring.float()).abs().max().item() <= 2e-2
+    ref = r.oracle(attention=False)
+    assert_block_sums_close(aux_ring["block_sums"], ref["block_sums"], w.stride, "ring small")
+    ref_o, ref_l = r.oracle_attention(aux_ring["mask_kv"])
+    assert_attention_close(o_ring, l_ring, ref_o, ref_l, w.dtype, label="ring small")
+
+
+@pytest.mark.parametrize("slots", [2, 4])
+def test_ring_delayed_copies_give_identical_results(slots):
+    """A host callback sleeps 2 ms before every slot copy on the transfer
+    stream; with correct event ordering the result is bit-identical."""
+    w = _small()
+    r = Run(w)
+    k_hist, v_hist, k_cur, v_cur, kh = _ring_inputs(w)
+    ring = X.Ring(slots, 8, w.num_kv_heads, w.head_dim, w.dtype)
+    say("ring delay test slots=%d: no delay" % slots)
+    o0, l0, c0, a0 = _run_ring(r, w, ring, k_hist, v_hist, k_cur, v_cur, kh)
+    ring.set_copy_delay_us(2000)
+    say("ring delay test slots=%d: 2 ms delay per copy" % slots)
+    o1, l1, c1, a1 = _run_ring(r, w, ring, k_hist, v_hist, k_cur, v_cur, kh)
+    ring.set_copy_delay_us(0)
+    say("ring delay test slots=%d: back to back" % slots)
+    o2, l2, c2, a2 = _run_ring(r, w, ring, k_hist, v_hist, k_cur, v_cur, kh)
+    ring.close()
+    for o, l_, c, a in ((o1, l1, c1, a1), (o2, l2, c2, a2)):
+        assert torch.equal(a["block_sums"], a0["block_sums"])
+        assert torch.equal(a["mask_kv"], a0["mask_kv"])
+        assert torch.equal(c, c0)
+        assert torch.equal(o, o0)
+        assert torch.equal(l_, l0)
+
+
+def test_ring_rejects_pageable_history():
+    w = make_random("ring_err", seed=42, hq=2, hkv=1, d=128, lq=[256], lk=[1024], stride=8,
+                    select_mode="chunk_vote")
+    r = Run(w)
+    k_hist, v_hist, k_cur, v_cur, kh = _ring_inputs(w, pinned=False)
+    ring = X.Ring(2, 2, 1, 128, w.dtype)
+    with pytest.raises(X.XattnError) as ei:
+        _run_ring(r, w, ring, k_hist, v_hist, k_cur, v_cur, kh)
+    assert ei.value.code == -5
+    ring.close()
+
+
+def test_ring_qwen3_4b_128k_sampled():
+    w = make_workload("qwen3_4b_128k_ring")
+    r = Run(w)
+    k_hist, v_hist, k_cur, v_cur, kh = _ring_inputs(w)
+    ring = X.Ring(w.ring_slots, w.ring_slot_blocks, w.num_kv_heads, w.head_dim, w.dtype)
+    say("ring 128K: ring path")
+    out, lse, counts, aux = _run_ring(r, w, ring, k_hist, v_hist, k_cur, v_cur, kh)
+    ring.close()
+    ref = r.oracle(attention=False)
+    assert_block_sums_close(aux["block_sums"], ref["block_sums"], w.stride, "128K")
+    gm = aux["mask_kv"].cpu().numpy().astype(bool)
+    mism = float((gm != ref["mask_kv"]).mean())
+    say("  mask mismatch %.4g counts %s vs %s" % (mism, counts.tolist(), ref["counts"].tolist()))
+    assert mism <= 0.01
+    rng = np.random.default_rng(3)
+    blocks = sorted(rng.choice(32, size=3, replace=False).tolist())
+    rows = {0: sorted({b * 128 + int(x) for b in blocks for x in rng.choice(128, 16, replace=False)} |
+                      {b * 128 for b in blocks} | {b * 128 + 127 for b in blocks})}
+    ref_o, ref_l = r.oracle_attention(aux["mask_kv"], rows=rows)
+    assert_attention_close(out, lse, ref_o, ref_l, w.dtype, rows_idx=np.asarray(rows[0]), label="128K")
