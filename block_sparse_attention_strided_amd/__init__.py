@@ -143,6 +143,16 @@ def xattn_sparse_attn(shape, params, q, k, v, mask_kv, out, lse, ws, stream=None
                                          _stream(stream)))
 
 
+def xattn_attn_plan(shape, params, v, mask_kv, ws, stream=None):
+    _check(_lib.load().xattn_attn_plan(ctypes.byref(shape.c), ctypes.byref(params), _ptr(v), _ptr(mask_kv),
+                                       _ptr(ws), ws.numel(), _stream(stream)))
+
+
+def xattn_attn_run(shape, params, q, k, v, mask_kv, out, lse, ws, stream=None):
+    _check(_lib.load().xattn_attn_run(ctypes.byref(shape.c), ctypes.byref(params), _ptr(q), _ptr(k), _ptr(v),
+                                      _ptr(mask_kv), _ptr(out), _ptr(lse), _ptr(ws), ws.numel(), _stream(stream)))
+
+
 def xattn_merge_attn(o_a, lse_a, o_b, lse_b, o, lse, stream=None):
     rows, heads, hd = o_a.shape
     _check(_lib.load().xattn_merge_attn(rows, heads, hd, _ptr(o_a), _ptr(lse_a), _ptr(o_b), _ptr(lse_b),

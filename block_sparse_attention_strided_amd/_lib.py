@@ -29,6 +29,8 @@ EXPORTED = (
     "xattn_estimate",
     "xattn_select",
     "xattn_sparse_attn",
+    "xattn_attn_plan",
+    "xattn_attn_run",
     "xattn_merge_attn",
     "xattn_prefill_chunk",
     "xattn_ring_create",
@@ -101,6 +103,10 @@ def load():
     lib.xattn_select.restype = ctypes.c_int
     lib.xattn_sparse_attn.argtypes = [sp, pp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_size_t, vp]
     lib.xattn_sparse_attn.restype = ctypes.c_int
+    lib.xattn_attn_plan.argtypes = [sp, pp, vp, vp, vp, ctypes.c_size_t, vp]
+    lib.xattn_attn_plan.restype = ctypes.c_int
+    lib.xattn_attn_run.argtypes = [sp, pp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_size_t, vp]
+    lib.xattn_attn_run.restype = ctypes.c_int
     lib.xattn_merge_attn.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, vp, vp, vp, vp, vp, vp, vp]
     lib.xattn_merge_attn.restype = ctypes.c_int
     lib.xattn_prefill_chunk.argtypes = [vp, sp, pp, vp, vp, vp, vp, vp, ctypes.c_int, vp, vp, vp,

@@ -260,10 +260,10 @@ AttnArgs attn_args(const XattnShape* sh, const Plan& p, const void* q, KvView kv
   return aa;
 }
 
-// Attention over blocks [jb0, jb1) of `mask`: for bf16 first re-lays V out
-// d-major (V^T pages) and builds the per-row block lists, then attends.
-hipError_t run_attention(const XattnShape* sh, const Plan& p, AttnArgs aa, const void* v, int num_pages,
-                         void* ws, bool transpose_v, hipStream_t st) {
+// bf16 preparation of an attention launch over blocks [jb0, jb1) of
+// aa.mask: V^T pages of `v` (num_pages pages) and the per-row block lists.
+hipError_t plan_attention(const XattnShape* sh, const Plan& p, const AttnArgs& aa, const void* v, int num_pages,
+                          void* ws, bool transpose_v, hipStream_t st) {
   if (p.dtype == XATTN_DTYPE_BF16) {
     char* vt = ws_at<char>(ws, p.off_vt);
     if (transpose_v) {
@@ -288,12 +288,23 @@ hipError_t run_attention(const XattnShape* sh, const Plan& p, AttnArgs aa, const
     pa.jb0 = aa.jb0;
     pa.jb1 = aa.jb1;
     pa.lists = ws_at<int32_t>(ws, p.off_lists);
-    hipError_t e = launch_plan(pa, p.batch, st);
-    if (e != hipSuccess) return e;
-    aa.vt = vt;
-    aa.lists = pa.lists;
+    return launch_plan(pa, p.batch, st);
   }
+  return hipSuccess;
+}
+
+hipError_t launch_planned(const Plan& p, AttnArgs aa, void* ws, hipStream_t st) {
+  aa.vt = ws_at<char>(ws, p.off_vt);
+  aa.lists = ws_at<int32_t>(ws, p.off_lists);
   return launch_attention(aa, p.dtype == XATTN_DTYPE_BF16 ? 0 : 1, p.d, p.batch, st);
+}
+
+// Attention over blocks [jb0, jb1) of `mask`: prepare (bf16), then attend.
+hipError_t run_attention(const XattnShape* sh, const Plan& p, AttnArgs aa, const void* v, int num_pages,
+                         void* ws, bool transpose_v, hipStream_t st) {
+  hipError_t e = plan_attention(sh, p, aa, v, num_pages, ws, transpose_v, st);
+  if (e != hipSuccess) return e;
+  return launch_planned(p, aa, ws, st);
 }
 
 }  // namespace
@@ -579,6 +590,38 @@ int xattn_sparse_attn(const XattnShape* shape, const XattnParams* params, const 
   else aa.out_f32 = (float*)out;
   aa.lse = lse;
   hipError_t e = run_attention(shape, p, aa, v, p.num_pages, ws, true, (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "attention launch");
+  return XATTN_OK;
+}
+
+int xattn_attn_plan(const XattnShape* shape, const XattnParams* params, const void* v, const uint8_t* mask_kv,
+                    void* ws, size_t ws_bytes, void* stream) {
+  Plan p;
+  int rc = make_plan(shape, params, &p);
+  if (rc) return rc;
+  if (!v || !mask_kv) return fail(XATTN_ERR_INVALID, "v and mask_kv must not be NULL");
+  if ((rc = check_ws(p, ws, ws_bytes))) return rc;
+  g_last_error.clear();
+  AttnArgs aa = attn_args(shape, p, nullptr, make_view(shape, p, v), make_view(shape, p, v), mask_kv, 0, p.max_kb);
+  hipError_t e = plan_attention(shape, p, aa, v, p.num_pages, ws, true, (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "attention plan launch");
+  return XATTN_OK;
+}
+
+int xattn_attn_run(const XattnShape* shape, const XattnParams* params, const void* q, const void* k, const void* v,
+                   const uint8_t* mask_kv, void* out, float* lse, void* ws, size_t ws_bytes, void* stream) {
+  Plan p;
+  int rc = make_plan(shape, params, &p);
+  if (rc) return rc;
+  if (!q || !k || !v || !mask_kv || !out)
+    return fail(XATTN_ERR_INVALID, "q, k, v, mask_kv and out must not be NULL");
+  if ((rc = check_ws(p, ws, ws_bytes))) return rc;
+  g_last_error.clear();
+  AttnArgs aa = attn_args(shape, p, q, make_view(shape, p, k), make_view(shape, p, v), mask_kv, 0, p.max_kb);
+  if (p.dtype == XATTN_DTYPE_BF16) aa.out = out;
+  else aa.out_f32 = (float*)out;
+  aa.lse = lse;
+  hipError_t e = launch_planned(p, aa, ws, (hipStream_t)stream);
   if (e != hipSuccess) return hip_fail(e, "attention launch");
   return XATTN_OK;
 }

@@ -124,33 +124,52 @@ __global__ __launch_bounds__(256) void aggregate_kernel(SelectArgs a) {
   }
 }
 
-// Chunk-vote mode: the vote on history column j and the effective mask of
-// the column; per-KV-head mode: clears hist_sel.  One thread per column.
+// Chunk-vote mode: votes of history column j over the Hkv*Qb (kv head,
+// q block) rows.  Workgroup = 64 columns x 4 row lanes; per-KV-head mode
+// clears hist_sel.
 __global__ __launch_bounds__(256) void vote_kernel(SelectArgs a) {
-  const int j = blockIdx.x * 256 + threadIdx.x;
+  __shared__ int part[4][64];
+  const int c = threadIdx.x & 63, rl = threadIdx.x >> 6;
+  const int j = blockIdx.x * 64 + c;
   const int b = blockIdx.y;
-  if (j >= a.max_kb) return;
+  const int lq = a.cu_q[b + 1] - a.cu_q[b];
+  const int lk = a.cu_k[b + 1] - a.cu_k[b];
+  const int qb = lq / kBlock, kh = (lk - lq) / kBlock;
+  int votes = 0;
+  if (a.select_mode == 1 && j < kh) {
+    const int nrows = a.hkv * qb;
+#pragma unroll 8
+    for (int r = rl; r < nrows; r += 4) {
+      const int g = r / qb, i = r - (r / qb) * qb;
+      votes += a.mask_kv[(((long long)b * a.hkv + g) * a.max_qb + i) * a.max_kb + j];
+    }
+  }
+  part[rl][c] = votes;
+  __syncthreads();
+  if (rl == 0 && j < a.max_kb) {
+    uint8_t sel = 0;
+    if (a.select_mode == 1 && qb > 0 && j < kh) {
+      const int v = part[0][c] + part[1][c] + part[2][c] + part[3][c];
+      sel = (2 * v > a.hkv * qb || j == 0 || j == kh - 1) ? 1 : 0;
+    }
+    a.hist_sel[(long long)b * a.max_kb + j] = sel;
+  }
+}
+
+// Chunk-vote mode: effective mask row (g, i): voted history, dense causal
+// current chunk.  One workgroup per (i, g, b).
+__global__ __launch_bounds__(256) void effective_mask_kernel(SelectArgs a) {
+  const int i = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
   const int lq = a.cu_q[b + 1] - a.cu_q[b];
   const int lk = a.cu_k[b + 1] - a.cu_k[b];
   const int qb = lq / kBlock, kb = lk / kBlock, kh = (lk - lq) / kBlock;
-  if (a.select_mode == 0) {
-    if (a.hist_sel) a.hist_sel[(long long)b * a.max_kb + j] = 0;
-    return;
+  uint8_t* row = a.mask_kv + (((long long)b * a.hkv + g) * a.max_qb + i) * a.max_kb;
+  const uint8_t* hs = a.hist_sel + (long long)b * a.max_kb;
+  for (int j = threadIdx.x; j < a.max_kb; j += 256) {
+    uint8_t v = 0;
+    if (i < qb && j < kb) v = (j < kh) ? hs[j] : (j <= i + kh ? 1 : 0);
+    row[j] = v;
   }
-  uint8_t sel = 0;
-  if (qb > 0 && j < kh) {
-    int votes = 0;
-    for (int g = 0; g < a.hkv; ++g)
-      for (int i = 0; i < qb; ++i) votes += a.mask_kv[(((long long)b * a.hkv + g) * a.max_qb + i) * a.max_kb + j];
-    sel = (2 * votes > a.hkv * qb || j == 0 || j == kh - 1) ? 1 : 0;
-  }
-  if (a.hist_sel) a.hist_sel[(long long)b * a.max_kb + j] = sel;
-  for (int g = 0; g < a.hkv; ++g)
-    for (int i = 0; i < a.max_qb; ++i) {
-      uint8_t v = 0;
-      if (i < qb && j < kb) v = (j < kh) ? sel : (j <= i + kh ? 1 : 0);
-      a.mask_kv[(((long long)b * a.hkv + g) * a.max_qb + i) * a.max_kb + j] = v;
-    }
 }
 
 // counts[b] = {selected, available}; one workgroup per sequence.
@@ -202,9 +221,14 @@ hipError_t launch_select(const SelectArgs& a, int batch, hipStream_t s) {
     e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
-  hipLaunchKernelGGL(vote_kernel, dim3((a.max_kb + 255) / 256, batch), dim3(256), 0, s, a);
+  hipLaunchKernelGGL(vote_kernel, dim3((a.max_kb + 63) / 64, batch), dim3(256), 0, s, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
+  if (a.select_mode == 1 && a.max_qb > 0) {
+    hipLaunchKernelGGL(effective_mask_kernel, dim3(a.max_qb, a.hkv, batch), dim3(256), 0, s, a);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
   if (a.counts) {
     hipLaunchKernelGGL(counts_kernel, dim3(batch), dim3(256), 0, s, a);
     e = hipGetLastError();

@@ -157,6 +157,19 @@ int xattn_sparse_attn(const XattnShape *shape, const XattnParams *params, const 
                       const void *k, const void *v, const uint8_t *mask_kv, void *out,
                       float *lse, void *ws, size_t ws_bytes, void *stream);
 
+/* The two halves of xattn_sparse_attn, for callers that reuse V and the
+ * mask across calls (and to time the attention kernel alone).
+ * xattn_attn_plan re-lays V out d-major for the bf16 kernel and builds, in
+ * the workspace, each (sequence, kv head, q block) row's list of blocks to
+ * visit; it is a no-op for fp32.  xattn_attn_run launches only the attention
+ * kernel; its workspace must hold a plan made with the same shape, params,
+ * v and mask_kv contents, with no other call on that workspace in between. */
+int xattn_attn_plan(const XattnShape *shape, const XattnParams *params, const void *v,
+                    const uint8_t *mask_kv, void *ws, size_t ws_bytes, void *stream);
+int xattn_attn_run(const XattnShape *shape, const XattnParams *params, const void *q,
+                   const void *k, const void *v, const uint8_t *mask_kv, void *out,
+                   float *lse, void *ws, size_t ws_bytes, void *stream);
+
 /* LSE merge of two partial attentions over disjoint key sets (design doc
  * section 2, merge_attention_outputs):
  *   lse = max(a,b) + log1p(exp(-|a-b|)),  o = e^(a-lse) o_a + e^(b-lse) o_b;
