@@ -37,6 +37,11 @@ __host__ __device__ __forceinline__ int vperm(int k) {
 
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
 
+// 2^x with the bare v_exp_f32 (results below 2^-126 flush to zero, which is
+// harmless for softmax weights; exp2f would add a denormal range fix-up of
+// five more VALU instructions per call).
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
 __device__ __forceinline__ void load_lds16(const void* g, void* lds) {
   __builtin_amdgcn_global_load_lds(g, (lds_ptr_t)lds, 16, 0, 0);
 }
@@ -217,8 +222,7 @@ __global__ __launch_bounds__(256 * HPW) void attn_mfma(AttnArgs a, int hkv) {
 
   auto compute = [&](int t, const char* kl) {
     const char* vl = kl + TILE;
-    const int e = list[1 + (t >> 1)];
-    const bool diag = (e & 1) != 0;
+    const bool diag = (list[1 + (t >> 1)] & 1) != 0;
     const int sub = t & 1;
     // ---- S^T = K Q^T
     f32x16 s0, s1;
@@ -235,8 +239,10 @@ __global__ __launch_bounds__(256 * HPW) void attn_mfma(AttnArgs a, int hkv) {
       s0 = mfma32(a0, qf[kk], s0);
       s1 = mfma32(a1, qf[kk], s1);
     }
-    // ---- causal mask on the diagonal block only
+    // ---- causal mask on the diagonal block only (a real, uniform branch: the
+    // empty asm keeps the compiler from evaluating the mask on every tile)
     if (diag) {
+      asm volatile("" ::: "memory");
 #pragma unroll
       for (int z = 0; z < 16; ++z) {
         const int key = sub * kKT + 8 * (z >> 2) + 4 * hh + (z & 3);
@@ -252,7 +258,7 @@ __global__ __launch_bounds__(256 * HPW) void attn_mfma(AttnArgs a, int hkv) {
     // lazy rescale: refresh the running max only when it would grow by > 8
     if (__ballot(m_tile > m_run + 8.0f) != 0ull) {
       const float m_new = fmaxf(m_run, m_tile);
-      const float alpha = exp2f(m_run - m_new);
+      const float alpha = fast_exp2(m_run - m_new);
       l_run *= alpha;
 #pragma unroll
       for (int n = 0; n < D / 32; ++n)
@@ -264,8 +270,8 @@ __global__ __launch_bounds__(256 * HPW) void attn_mfma(AttnArgs a, int hkv) {
     float psum = 0.f;
 #pragma unroll
     for (int z = 0; z < 16; ++z) {
-      s0[z] = exp2f(fmaf(s0[z], c2, mneg));
-      s1[z] = exp2f(fmaf(s1[z], c2, mneg));
+      s0[z] = fast_exp2(fmaf(s0[z], c2, mneg));
+      s1[z] = fast_exp2(fmaf(s1[z], c2, mneg));
       psum += s0[z] + s1[z];
     }
     l_run += psum;
