@@ -20,7 +20,7 @@ ARCH = "gfx950"
 FLAGS = [
     "--offload-arch=" + ARCH,
     "-O3",
-    "-std=c++17",
+    "-std=c++20",
     "-fPIC",
     "-ffp-contract=fast",
     # packed fp32 VALU ops are kept out of the generated code

@@ -19,13 +19,15 @@
 //    (base 2), so the O rescale is rare; probabilities stay below 2^8.
 //  * blockIdx -> (kv head, q block) is XCD-aware: the workgroups of one KV
 //    head land on one XCD and share its L2.
+#include <type_traits>
+#include <utility>
+
 #include "xattn_internal.h"
 
 namespace xattn {
 namespace {
 
 constexpr float kNegInf = -__builtin_huge_valf();
-constexpr int kKT = 64;  // keys per tile
 
 // Position of key k inside a 16-key group of a V^T row: bits 2 and 3
 // swapped, so k-slot group hh of MFMA k-step m holds keys
@@ -44,6 +46,42 @@ __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_ex
 
 __device__ __forceinline__ void load_lds16(const void* g, void* lds) {
   __builtin_amdgcn_global_load_lds(g, (lds_ptr_t)lds, 16, 0, 0);
+}
+
+// 16-byte and 4-byte LDS reads issued from inline asm.  The compiler does not
+// see them as LDS accesses, so it never adds a wait for the pending direct
+// (global -> LDS) tile loads in front of them; the kernel orders them itself
+// (s_waitcnt vmcnt + s_barrier before a tile is read, lgkm_wait before use).
+__device__ __forceinline__ u32x4 lds_read16(uint32_t addr) {
+  u32x4 v;
+  asm volatile("ds_read_b128 %0, %1" : "=v"(v) : "v"(addr));
+  return v;
+}
+template <int OFF>
+__device__ __forceinline__ u32x4 lds_read16_at(uint32_t addr) {
+  static_assert(OFF >= 0 && OFF < 65536, "ds offset field");
+  u32x4 v;
+  asm volatile("ds_read_b128 %0, %1 offset:%2" : "=v"(v) : "v"(addr), "i"(OFF));
+  return v;
+}
+__device__ __forceinline__ int lds_read4(uint32_t addr) {
+  int v;
+  asm volatile("ds_read_b32 %0, %1" : "=v"(v) : "v"(addr));
+  return v;
+}
+// Wait until at most N LDS (lgkm) operations are outstanding; the operands
+// tie the values that must have arrived to this point of the program.
+template <int N>
+__device__ __forceinline__ void lgkm_wait(u32x4& a) {
+  asm volatile("s_waitcnt lgkmcnt(%1)" : "+v"(a) : "n"(N));
+}
+template <int N>
+__device__ __forceinline__ void lgkm_wait(u32x4& a, u32x4& b) {
+  asm volatile("s_waitcnt lgkmcnt(%2)" : "+v"(a), "+v"(b) : "n"(N));
+}
+template <int N>
+__device__ __forceinline__ void lgkm_wait(int& a) {
+  asm volatile("s_waitcnt lgkmcnt(%1)" : "+v"(a) : "n"(N));
 }
 
 // s_waitcnt with only vmcnt constrained (expcnt, lgkmcnt left at maximum).
@@ -124,18 +162,17 @@ __global__ __launch_bounds__(64) void plan_kernel(PlanArgs a) {
 template <int D, int HPW>
 __global__ __launch_bounds__(256 * HPW) void attn_mfma(AttnArgs a, int hkv) {
   constexpr int NW = 4 * HPW;          // waves
+  constexpr int KT = 64;               // keys per tile
   constexpr int KROW = D * 2;          // bytes per K row in LDS
   constexpr int KCPR = D / 8;          // 16-byte chunks per K row
-  constexpr int TILE = kKT * KROW;     // bytes of one K (or V^T) tile
+  constexpr int TILE = KT * KROW;      // bytes of one K (or V^T) tile
   constexpr int CH = TILE / 16;        // 16-byte chunks per tile
   constexpr int LPW = CH / (64 * NW);  // direct loads per wave per operand
+  constexpr int STAGES = 3;
   static_assert(LPW >= 1 && CH % (64 * NW) == 0, "tile / workgroup mismatch");
-  // Three stage buffers as separate objects: the compiler then knows that the
-  // direct loads into the other two stages do not alias the stage being read
-  // and waits only for the loads of that stage.
-  __shared__ __align__(1024) char stage0[2 * TILE];
-  __shared__ __align__(1024) char stage1[2 * TILE];
-  __shared__ __align__(1024) char stage2[2 * TILE];
+  // LDS: K tiles of the 3 stages, then V^T tiles of the 3 stages; every read
+  // address is a per-lane base plus an immediate offset below 64 KiB.
+  __shared__ __align__(1024) char tiles[2 * STAGES * TILE];
   extern __shared__ int32_t list[];
 
   // ---- work unit (XCD-aware: the 8 XCDs take consecutive ids round-robin)
@@ -162,13 +199,16 @@ __global__ __launch_bounds__(256 * HPW) void attn_mfma(AttnArgs a, int hkv) {
   const int xq = qs * 32 + l32;  // query within the block
   const int x = i * kBlock + xq;
 
-  // Block list of this row, copied to LDS so the tile loop reads it with LDS
-  // loads (vector-memory reads would be ordered with the direct tile loads).
+  // Block list of this row, copied to LDS.
   const int32_t* glist = a.lists + (((long long)b * hkv + g) * a.max_qb + i) * (a.max_kb + 1);
   const int nblk = glist[0];
   for (int z = tid; z <= nblk; z += 64 * NW) list[z] = glist[z];
   __syncthreads();
   const int ntile = 2 * nblk;
+  // The diagonal block, if present, is the last entry: only its two tiles
+  // need the causal mask.
+  const int first_diag = (nblk > 0 && (list[nblk] & 1)) ? ntile - 2 : ntile;
+  const uint32_t list_lds = (uint32_t)(uintptr_t)(lds_ptr_t)list;
 
   // Q fragments: B operand of S^T (query col = lane%32, d slots 8*hh .. +8).
   bf16x8 qf[D / 16];
@@ -196,21 +236,28 @@ __global__ __launch_bounds__(256 * HPW) void attn_mfma(AttnArgs a, int hkv) {
   const char* kbase = a.k.base + (long long)g * D * 2;
   const char* vbase = a.vt + (long long)g * D * kBlock * 2;
 
-  auto issue = [&](int t, char* kl) {
-    const int e = list[1 + (t >> 1)];
+  auto issue = [&](int t, int e, int stage) {
     const int page = e >> 1, sub = t & 1;
-    const char* kp = kbase + page * k_page_bytes + sub * kKT * k_row_bytes;
-    const char* vp = vbase + page * vt_page_bytes + sub * kKT * 2;
-    char* vl = kl + TILE;
+    const char* kp = kbase + page * k_page_bytes + sub * KT * k_row_bytes;
+    const char* vp = vbase + page * vt_page_bytes + sub * KT * 2;
+    char* kl = tiles + stage * TILE;
+    char* vl = tiles + (STAGES + stage) * TILE;
 #pragma unroll
     for (int n = 0; n < LPW; ++n) load_lds16(kp + koff[n], kl + (w * LPW + n) * 1024);
 #pragma unroll
     for (int n = 0; n < LPW; ++n) load_lds16(vp + voff[n], vl + (w * LPW + n) * 1024);
   };
 
-  // LDS read offsets of this lane's MFMA A fragments.
+  // Per-lane LDS addresses of the MFMA A fragments (stage 0; other stages
+  // and rows 32.. / d-blocks add immediate offsets).
+  const uint32_t lds0 = (uint32_t)(uintptr_t)(lds_ptr_t)tiles;
   const int kswz = (KCPR == 16) ? (l32 & 15) : ((l32 >> 1) & 7);
   const int vswz = (l32 >> 1) & 7;
+  uint32_t kaddr[D / 16], vaddr[4];
+#pragma unroll
+  for (int kk = 0; kk < D / 16; ++kk) kaddr[kk] = lds0 + l32 * KROW + (((2 * kk + hh) ^ kswz) * 16);
+#pragma unroll
+  for (int m = 0; m < 4; ++m) vaddr[m] = lds0 + STAGES * TILE + l32 * (KT * 2) + (((2 * m + hh) ^ vswz) * 16);
 
   f32x16 oacc[D / 32];
 #pragma unroll
@@ -220,24 +267,33 @@ __global__ __launch_bounds__(256 * HPW) void attn_mfma(AttnArgs a, int hkv) {
   float m_run = kNegInf, l_run = 0.f;
   const float c2 = a.scale2;
 
-  auto compute = [&](int t, const char* kl) {
-    const char* vl = kl + TILE;
-    const bool diag = (list[1 + (t >> 1)] & 1) != 0;
+  auto compute = [&](auto stage_tag, int t) {
+    constexpr int S = decltype(stage_tag)::value;
+    const bool diag = t >= first_diag;
     const int sub = t & 1;
-    // ---- S^T = K Q^T
+    // ---- S^T = K Q^T; K fragments read one MFMA pair ahead
     f32x16 s0, s1;
 #pragma unroll
     for (int z = 0; z < 16; ++z) {
       s0[z] = 0.f;
       s1[z] = 0.f;
     }
+    u32x4 ka0 = lds_read16_at<S * TILE>(kaddr[0]);
+    u32x4 ka1 = lds_read16_at<S * TILE + 32 * KROW>(kaddr[0]);
 #pragma unroll
     for (int kk = 0; kk < D / 16; ++kk) {
-      const int pc = (2 * kk + hh) ^ kswz;
-      const bf16x8 a0 = *(const bf16x8*)(kl + l32 * KROW + pc * 16);
-      const bf16x8 a1 = *(const bf16x8*)(kl + (32 + l32) * KROW + pc * 16);
-      s0 = mfma32(a0, qf[kk], s0);
-      s1 = mfma32(a1, qf[kk], s1);
+      u32x4 kb0, kb1;
+      if (kk + 1 < D / 16) {
+        kb0 = lds_read16_at<S * TILE>(kaddr[kk + 1 < D / 16 ? kk + 1 : 0]);
+        kb1 = lds_read16_at<S * TILE + 32 * KROW>(kaddr[kk + 1 < D / 16 ? kk + 1 : 0]);
+        lgkm_wait<2>(ka0, ka1);
+      } else {
+        lgkm_wait<0>(ka0, ka1);
+      }
+      s0 = mfma32(__builtin_bit_cast(bf16x8, ka0), qf[kk], s0);
+      s1 = mfma32(__builtin_bit_cast(bf16x8, ka1), qf[kk], s1);
+      ka0 = kb0;
+      ka1 = kb1;
     }
     // ---- causal mask on the diagonal block only (a real, uniform branch: the
     // empty asm keeps the compiler from evaluating the mask on every tile)
@@ -245,7 +301,7 @@ __global__ __launch_bounds__(256 * HPW) void attn_mfma(AttnArgs a, int hkv) {
       asm volatile("" ::: "memory");
 #pragma unroll
       for (int z = 0; z < 16; ++z) {
-        const int key = sub * kKT + 8 * (z >> 2) + 4 * hh + (z & 3);
+        const int key = sub * KT + 8 * (z >> 2) + 4 * hh + (z & 3);
         if (key > xq) s0[z] = kNegInf;
         if (key + 32 > xq) s1[z] = kNegInf;
       }
@@ -283,36 +339,61 @@ __global__ __launch_bounds__(256 * HPW) void attn_mfma(AttnArgs a, int hkv) {
 #pragma unroll
       for (int z = 0; z < 8; ++z) pb[m][z] = (__bf16)((m < 2) ? s0[4 * i0 + z] : s1[4 * i0 + z]);
     }
-    // ---- O^T += V^T P^T
-#pragma unroll
-    for (int m = 0; m < 4; ++m) {
-      const int pc = (2 * m + hh) ^ vswz;
-#pragma unroll
-      for (int n = 0; n < D / 32; ++n) {
-        const bf16x8 av = *(const bf16x8*)(vl + (n * 32 + l32) * (kKT * 2) + pc * 16);
-        oacc[n] = mfma32(av, pb[m], oacc[n]);
+    // ---- O^T += V^T P^T; V^T fragments read two MFMAs ahead
+    constexpr int NV = 4 * (D / 32);
+    auto vread = [&](auto j_tag) {
+      constexpr int J = decltype(j_tag)::value;
+      constexpr int M = J / (D / 32), N = J % (D / 32);
+      return lds_read16_at<S * TILE + N * 32 * KT * 2>(vaddr[M]);
+    };
+    u32x4 va = vread(std::integral_constant<int, 0>{});
+    u32x4 vb = vread(std::integral_constant<int, 1>{});
+    auto pv_step = [&](auto j_tag) {
+      constexpr int J = decltype(j_tag)::value;
+      u32x4 vc;
+      if constexpr (J + 2 < NV) {
+        vc = vread(std::integral_constant<int, J + 2>{});
+        lgkm_wait<2>(va);
+      } else if constexpr (J + 1 < NV) {
+        lgkm_wait<1>(va);
+      } else {
+        lgkm_wait<0>(va);
       }
-    }
+      oacc[J % (D / 32)] = mfma32(__builtin_bit_cast(bf16x8, va), pb[J / (D / 32)], oacc[J % (D / 32)]);
+      va = vb;
+      vb = vc;
+    };
+    [&]<int... J>(std::integer_sequence<int, J...>) {
+      (pv_step(std::integral_constant<int, J>{}), ...);
+    }(std::make_integer_sequence<int, NV>{});
   };
 
   // One tile step with compile-time stage buffers: wait for this wave's loads
   // of tile t (only tile t+1's may remain in flight), barrier to publish all
   // waves' parts (a bare s_barrier: a memory fence would drain the loads of
   // tile t+1 too), refill the stage freed by tile t-1 with tile t+2, compute.
-  auto step = [&](int t, char* cur, char* ahead2) {
+  // The list entry of tile t+2 was read one step earlier (e_next).
+  int e_next = 0;
+  auto step = [&](auto stage_tag, int t) {
+    constexpr int S = decltype(stage_tag)::value;
     if (t + 1 < ntile) wait_vmcnt<2 * LPW>();
     else wait_vmcnt<0>();
     __builtin_amdgcn_s_barrier();
-    if (t + 2 < ntile) issue(t + 2, ahead2);
-    compute(t, cur);
+    if (t + 2 < ntile) {
+      lgkm_wait<0>(e_next);
+      issue(t + 2, e_next, (S + 2) % STAGES);
+    }
+    if (t + 3 < ntile) e_next = lds_read4(list_lds + 4 * (1 + ((t + 3) >> 1)));
+    compute(stage_tag, t);
   };
 
-  if (ntile > 0) issue(0, stage0);
-  if (ntile > 1) issue(1, stage1);
+  if (ntile > 0) issue(0, list[1], 0);
+  if (ntile > 1) issue(1, list[1], 1);
+  if (ntile > 2) e_next = list[1 + 1];
   for (int t = 0; t < ntile; t += 3) {
-    step(t, stage0, stage2);
-    if (t + 1 < ntile) step(t + 1, stage1, stage0);
-    if (t + 2 < ntile) step(t + 2, stage2, stage1);
+    step(std::integral_constant<int, 0>{}, t);
+    if (t + 1 < ntile) step(std::integral_constant<int, 1>{}, t + 1);
+    if (t + 2 < ntile) step(std::integral_constant<int, 2>{}, t + 2);
   }
 
   const float l_tot = l_run + __shfl_xor(l_run, 32, 64);
