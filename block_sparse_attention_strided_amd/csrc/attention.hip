@@ -28,6 +28,12 @@ namespace xattn {
 namespace {
 
 constexpr float kNegInf = -__builtin_huge_valf();
+#ifndef XATTN_PF
+#define XATTN_PF 6
+#endif
+#ifndef XATTN_SPREAD
+#define XATTN_SPREAD 1
+#endif
 
 // Position of key k inside a 16-key group of a V^T row: bits 2 and 3
 // swapped, so k-slot group hh of MFMA k-step m holds keys
@@ -43,6 +49,26 @@ typedef __attribute__((address_space(3))) void* lds_ptr_t;
 // harmless for softmax weights; exp2f would add a denormal range fix-up of
 // five more VALU instructions per call).
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// Combine the values of lanes l and l ^ 32 with one v_permlane32_swap: after
+// the swap, the two results hold {x[l ^ 32], x[l]} in some order on every lane.
+__device__ __forceinline__ float half_max(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __builtin_elementwise_maximum(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float half_sum(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+// Raw buffer descriptor word 3 for gfx950 (32-bit data format, no swizzle).
+constexpr int kBufFlags = 0x00020000;
+
+// 16 bytes per lane, buffer -> LDS (lane L writes lds + 16 L); offsets at or
+// beyond the descriptor's byte count read as zero.
+__device__ __forceinline__ void buffer_load_lds16(__amdgpu_buffer_rsrc_t r, void* lds, uint32_t voff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_ptr_t)lds, 16, voff, 0, 0, 0);
+}
 
 __device__ __forceinline__ void load_lds16(const void* g, void* lds) {
   __builtin_amdgcn_global_load_lds(g, (lds_ptr_t)lds, 16, 0, 0);
@@ -83,6 +109,12 @@ template <int N>
 __device__ __forceinline__ void lgkm_wait(int& a) {
   asm volatile("s_waitcnt lgkmcnt(%1)" : "+v"(a) : "n"(N));
 }
+
+// Empty asm that needs its operand in registers at this point of the
+// program: values computed before it stay computed before it.
+__device__ __forceinline__ void reg_fence(const f32x16& v) { asm volatile("" ::"v"(v)); }
+__device__ __forceinline__ void reg_fence(const bf16x8& v) { asm volatile("" ::"v"(v)); }
+__device__ __forceinline__ void reg_fence(float v) { asm volatile("" ::"v"(v)); }
 
 // s_waitcnt with only vmcnt constrained (expcnt, lgkmcnt left at maximum).
 template <int N>
@@ -425,6 +457,418 @@ __global__ __launch_bounds__(256 * HPW) void attn_mfma(AttnArgs a, int hkv) {
   }
 }
 
+// ---------------------------------------------------------------------------
+// bf16 MFMA attention, two heads per workgroup, ping-pong schedule.
+//
+// Waves 0-3 (group A, first head of the pair) and waves 4-7 (group B, second
+// head) share the SIMDs pairwise (wave w and w+4 on one SIMD) and run the same
+// per-tile program half a tile apart.  A wave issues nothing but LDS reads and
+// MFMAs in its MFMA phase (O^T += V^T P^T of tile u-1, then S^T = K Q^T of
+// tile u; a wave's own VALU work would serialise with its MFMAs) while the
+// other group runs its softmax on the VALU; a workgroup barrier separates the
+// phases and keeps the groups in anti-phase:
+//   barrier 2u+1 -> A: MFMA(u)     B: softmax(u-1)
+//   barrier 2u+2 -> A: softmax(u)  B: MFMA(u)
+// K and V^T tiles live in two 4-stage LDS rings (tile t in stage t % 4).  The
+// softmax phase of tile g also issues copy group g: K of tile g+3 and V^T of
+// tile g+2 (raw buffer loads straight to LDS, which count on vmcnt only).
+// Each wave waits for its own copies of a tile before the barrier that opens
+// the first phase reading it; register fences keep the compiler from moving
+// phase work across the barriers.
+// ---------------------------------------------------------------------------
+template <int D, int PF>
+__global__ __launch_bounds__(512) void attn_pp(AttnArgs a, int hkv) {
+  constexpr int NW = 8;
+  constexpr int KT = 64;               // keys per tile
+  constexpr int KROW = D * 2;          // bytes per K row in LDS
+  constexpr int KCPR = D / 8;          // 16-byte chunks per K row
+  constexpr int TILE = KT * KROW;      // bytes of one K (or V^T) tile
+  constexpr int CH = TILE / 16;        // 16-byte chunks per tile
+  constexpr int LPW = CH / (64 * NW);  // direct loads per wave per operand
+  constexpr int ST = 4;                // ring stages
+  constexpr int NS = 2 * (D / 16);     // S^T MFMAs per tile
+  constexpr int NPV = 4 * (D / 32);    // O^T MFMAs per tile
+  static_assert(LPW >= 1 && CH % (64 * NW) == 0, "tile / workgroup mismatch");
+  static_assert(NS == NPV, "phase interleave assumes equal MFMA counts");
+  __shared__ __align__(1024) char tiles[2 * ST * TILE];  // K stages, then V^T stages
+  extern __shared__ int32_t list[];
+
+  // ---- work unit (XCD-aware: the 8 XCDs take consecutive ids round-robin)
+  const int nwg = gridDim.x;
+  const int id = blockIdx.x;
+  const int full = (nwg / 8) * 8;
+  const int logical = id < full ? (id % 8) * (nwg / 8) + id / 8 : id;
+  const int npair = a.group / 2;
+  const int irev = logical % a.max_qb;
+  int rest = logical / a.max_qb;
+  const int pair = rest % npair;
+  rest /= npair;
+  const int g = rest % hkv;
+  const int b = rest / hkv;
+  const int i = a.max_qb - 1 - irev;  // heaviest (longest causal) rows first
+  const int q0 = a.cu_q[b];
+  const int lq = a.cu_q[b + 1] - q0;
+  if (i >= lq / kBlock) return;
+
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int l32 = lane & 31, hh = lane >> 5;
+  const int grp = __builtin_amdgcn_readfirstlane(w >> 2), qs = w & 3;
+  const int h = g * a.group + pair * 2 + grp;
+  const int xq = qs * 32 + l32;  // query within the block
+  const int x = i * kBlock + xq;
+
+  // Block list of this row, copied to LDS.
+  const int32_t* glist = a.lists + (((long long)b * hkv + g) * a.max_qb + i) * (a.max_kb + 1);
+  const int nblk = glist[0];
+  for (int z = tid; z <= nblk; z += 64 * NW) list[z] = glist[z];
+  __syncthreads();
+  const int ntile = 2 * nblk;
+  const int first_diag = (nblk > 0 && (list[nblk] & 1)) ? ntile - 2 : ntile;
+  const uint32_t list_lds = (uint32_t)(uintptr_t)(lds_ptr_t)list;
+
+  // Q fragments: B operand of S^T (query col = lane%32, d slots 8*hh .. +8).
+  bf16x8 qf[D / 16];
+  {
+    const char* qrow = a.q + ((long long)(q0 + x) * a.hq + h) * D * 2;
+#pragma unroll
+    for (int kk = 0; kk < D / 16; ++kk) qf[kk] = *(const bf16x8*)(qrow + (kk * 16 + hh * 8) * 2);
+  }
+
+  // Per-thread constant parts of the direct-load addresses.
+  const long long k_page_bytes = (long long)kBlock * hkv * D * 2;
+  const long long k_row_bytes = (long long)hkv * D * 2;
+  const long long vt_page_bytes = (long long)hkv * D * kBlock * 2;
+  int koff[LPW], voff[LPW];
+#pragma unroll
+  for (int n = 0; n < LPW; ++n) {
+    const int idx = (w * LPW + n) * 64 + lane;
+    const int krow = idx / KCPR, kpch = idx % KCPR;
+    const int kc = (KCPR == 16) ? (kpch ^ (krow & 15)) : (kpch ^ ((krow >> 1) & 7));
+    koff[n] = (int)(krow * k_row_bytes + kc * 16);
+    const int vrow = idx >> 3, vpch = idx & 7;
+    const int vc = vpch ^ ((vrow >> 1) & 7);
+    voff[n] = (vrow * kBlock + vc * 8) * 2;
+  }
+  const char* kbase = a.k.base + (long long)g * D * 2;
+  const char* vbase = a.vt + (long long)g * D * kBlock * 2;
+
+  // Tile copies: one raw buffer descriptor per tile (scalar base = the tile's
+  // first row, byte count = the tile's extent), constant per-lane offsets,
+  // LDS destination in m0; no VALU address arithmetic.
+  const int wu = __builtin_amdgcn_readfirstlane(w);
+  const int k_tile_bytes = (int)(KT * k_row_bytes);
+  const int vt_tile_bytes = D * kBlock * 2;
+  __amdgpu_buffer_rsrc_t rk, rv;
+  char* kl = tiles;
+  char* vl = tiles;
+  bool k_on = false, v_on = false;
+  auto setup_k = [&](int t, int e) {
+    const int page = __builtin_amdgcn_readfirstlane(e) >> 1;
+    const char* kp = kbase + page * k_page_bytes + (t & 1) * KT * k_row_bytes;
+    rk = __builtin_amdgcn_make_buffer_rsrc((void*)kp, (short)0, k_tile_bytes, kBufFlags);
+    kl = tiles + (t & (ST - 1)) * TILE + wu * LPW * 1024;
+  };
+  auto setup_v = [&](int t, int e) {
+    const int page = __builtin_amdgcn_readfirstlane(e) >> 1;
+    const char* vp = vbase + page * vt_page_bytes + (t & 1) * KT * 2;
+    rv = __builtin_amdgcn_make_buffer_rsrc((void*)vp, (short)0, vt_tile_bytes, kBufFlags);
+    vl = tiles + (ST + (t & (ST - 1))) * TILE + wu * LPW * 1024;
+  };
+  // part n < LPW: K chunk n, else V^T chunk n - LPW (each if its tile exists)
+  auto copy_part = [&](auto n_tag) {
+    constexpr int N = decltype(n_tag)::value;
+    if constexpr (N < LPW) {
+      if (k_on) buffer_load_lds16(rk, kl + N * 1024, (uint32_t)koff[N]);
+    } else {
+      if (v_on) buffer_load_lds16(rv, vl + (N - LPW) * 1024, (uint32_t)voff[N - LPW]);
+    }
+  };
+  auto copy_parts = [&]() {
+    [&]<int... N>(std::integer_sequence<int, N...>) {
+      (copy_part(std::integral_constant<int, N>{}), ...);
+    }(std::make_integer_sequence<int, 2 * LPW>{});
+  };
+  auto entry = [&](int t) {  // list entry of tile t, waited for
+    int e = lds_read4(list_lds + 4 * (1 + (t >> 1)));
+    lgkm_wait<0>(e);
+    return e;
+  };
+  // Copy group gi (issued in the softmax phase of tile gi, prologue groups
+  // -3..-1):
+  // K of tile gi+3 into K stage (gi+3)%4 and V^T of tile gi+2 into V stage
+  // (gi+2)%4.  Those stages last held K of tile gi-1 and V^T of tile gi-2,
+  // both last read in the MFMA phases of tile gi-1, which both groups have
+  // finished before group gi is issued.
+  auto prologue_group = [&](int gi) {
+    k_on = gi + 3 < ntile;
+    v_on = gi + 2 >= 0 && gi + 2 < ntile;
+    if (k_on) setup_k(gi + 3, entry(gi + 3));
+    if (v_on) setup_v(gi + 2, entry(gi + 2));
+    copy_parts();
+  };
+  int e_k = 0, e_v = 0;  // list entries of tiles gi+3 and gi+2 for the next group
+  auto group_begin = [&](int gi) {
+    lgkm_wait<0>(e_k);  // read during the previous MFMA phase
+    k_on = gi + 3 < ntile;
+    v_on = gi + 2 < ntile;
+    if (k_on) setup_k(gi + 3, e_k);
+    if (v_on) setup_v(gi + 2, e_v);
+    e_v = e_k;
+    if (gi + 4 < ntile) e_k = lds_read4(list_lds + 4 * (1 + ((gi + 4) >> 1)));
+  };
+  // Before the barrier that opens phase 2m+1 (K of tile m and V^T of tile
+  // m-1 are read from then on): this wave's copies of group m-3 are done.
+  // Groups are issued in the softmax phases (A: phase 2g+2, B: phase 2g+3),
+  // so at that barrier A may still have groups m-2 and m-1 in flight, B only
+  // group m-2 (all waves also after the prologue, which issued -3..-1).
+  auto wait_group = [&](int m, bool newest_issued) {
+    int c = (m < ntile) + (m + 1 < ntile);  // group m-2, in units of LPW
+    if (newest_issued) c += (m + 1 < ntile) + (m + 2 < ntile);  // group m-1
+    if (c >= 4) wait_vmcnt<4 * LPW>();
+    else if (c == 3) wait_vmcnt<3 * LPW>();
+    else if (c == 2) wait_vmcnt<2 * LPW>();
+    else if (c == 1) wait_vmcnt<LPW>();
+    else wait_vmcnt<0>();
+  };
+
+  // Per-lane LDS addresses of the MFMA A fragments in stage 0.
+  const uint32_t lds0 = (uint32_t)(uintptr_t)(lds_ptr_t)tiles;
+  const int kswz = (KCPR == 16) ? (l32 & 15) : ((l32 >> 1) & 7);
+  const int vswz = (l32 >> 1) & 7;
+  uint32_t kaddr[D / 16], vaddr[4];
+#pragma unroll
+  for (int kk = 0; kk < D / 16; ++kk) kaddr[kk] = lds0 + l32 * KROW + (((2 * kk + hh) ^ kswz) * 16);
+#pragma unroll
+  for (int m = 0; m < 4; ++m) vaddr[m] = lds0 + ST * TILE + l32 * (KT * 2) + (((2 * m + hh) ^ vswz) * 16);
+
+  f32x16 oacc[D / 32];
+#pragma unroll
+  for (int n = 0; n < D / 32; ++n)
+#pragma unroll
+    for (int e = 0; e < 16; ++e) oacc[n][e] = 0.f;
+  f32x16 s0, s1;
+  bf16x8 pb[4];
+  float m_run = kNegInf, l_run = 0.f;
+  const float c2 = a.scale2;
+
+  // ---- MFMA phase of tile u: O^T += V^T(u-1) P^T(u-1) if PV, S^T(u) = K(u) Q^T
+  // if SS.  The two MFMA streams alternate; LDS fragments are read two ahead.
+  auto mma = [&](auto pv_tag, auto ss_tag, int u, bool cp) {
+    constexpr bool PV = decltype(pv_tag)::value, SS = decltype(ss_tag)::value;
+    constexpr int NOPS = (PV ? NPV : 0) + (SS ? NS : 0);
+    const uint32_t kst = (uint32_t)((u & (ST - 1)) * TILE);
+    const uint32_t vst = (uint32_t)(((u + ST - 1) & (ST - 1)) * TILE);
+    uint32_t ka[D / 16], va4[4];
+    if constexpr (SS) {
+#pragma unroll
+      for (int kk = 0; kk < D / 16; ++kk) ka[kk] = kaddr[kk] + kst;
+#pragma unroll
+      for (int z = 0; z < 16; ++z) {
+        s0[z] = 0.f;
+        s1[z] = 0.f;
+      }
+    }
+    if constexpr (PV) {
+#pragma unroll
+      for (int m = 0; m < 4; ++m) va4[m] = vaddr[m] + vst;
+    }
+    // op J: a PV step when PV and (J even or !SS), else an S step
+    auto is_pv = [](int j) constexpr { return PV && (!SS || (j % 2 == 0)); };
+    auto sub_idx = [](int j) constexpr { return (PV && SS) ? j / 2 : j; };
+    auto frag = [&](auto j_tag) -> u32x4 {
+      constexpr int J = decltype(j_tag)::value;
+      constexpr int I = sub_idx(J);
+      if constexpr (is_pv(J)) {
+        constexpr int M = I / (D / 32), N = I % (D / 32);
+        return lds_read16_at<N * 32 * KT * 2>(va4[M]);
+      } else {
+        constexpr int KK = I >> 1, HALF = I & 1;
+        return lds_read16_at<HALF * 32 * KROW>(ka[KK]);
+      }
+    };
+    // fragment of op J lives in fr[J]; reads run PF ops ahead of the MFMAs
+    if constexpr (!XATTN_SPREAD) {
+      if (cp) copy_parts();
+    }
+    u32x4 fr[NOPS];
+    [&]<int... J>(std::integer_sequence<int, J...>) {
+      ((fr[J] = frag(std::integral_constant<int, J>{})), ...);
+    }(std::make_integer_sequence<int, (PF < NOPS ? PF : NOPS)>{});
+    auto op = [&](auto j_tag) {
+      constexpr int J = decltype(j_tag)::value;
+      constexpr int I = sub_idx(J);
+      if constexpr (J + PF < NOPS) {
+        fr[J + PF] = frag(std::integral_constant<int, J + PF>{});
+        lgkm_wait<PF>(fr[J]);
+      } else {
+        lgkm_wait<NOPS - 1 - J>(fr[J]);
+      }
+      const u32x4 fa = fr[J];
+      if constexpr (is_pv(J)) {
+        constexpr int M = I / (D / 32), N = I % (D / 32);
+        oacc[N] = mfma32(__builtin_bit_cast(bf16x8, fa), pb[M], oacc[N]);
+      } else {
+        constexpr int KK = I >> 1, HALF = I & 1;
+        if constexpr (HALF == 0) s0 = mfma32(__builtin_bit_cast(bf16x8, fa), qf[KK], s0);
+        else s1 = mfma32(__builtin_bit_cast(bf16x8, fa), qf[KK], s1);
+      }
+      // one part of the copy group after every fourth MFMA
+      if constexpr (XATTN_SPREAD && J % 4 == 1 && J / 4 < 2 * LPW) {
+        if (cp) copy_part(std::integral_constant<int, J / 4>{});
+      }
+    };
+    [&]<int... J>(std::integer_sequence<int, J...>) {
+      (op(std::integral_constant<int, J>{}), ...);
+    }(std::make_integer_sequence<int, NOPS>{});
+  };
+
+  // ---- softmax of tile u: S^T registers -> P^T (bf16) in pb
+  auto smax = [&](int u) {
+    const bool diag = u >= first_diag;
+    const int sub = u & 1;
+    if (diag) {
+      asm volatile("" ::: "memory");
+#pragma unroll
+      for (int z = 0; z < 16; ++z) {
+        const int key = sub * KT + 8 * (z >> 2) + 4 * hh + (z & 3);
+        if (key > xq) s0[z] = kNegInf;
+        if (key + 32 > xq) s1[z] = kNegInf;
+      }
+    }
+    // Row max: four independent chains (the wave runs alone on the VALU of
+    // its SIMD in this phase, so dependency latency, not issue, is the cost);
+    // IEEE maximum lowers to v_maximum3_f32 without operand canonicalisation.
+    float mq[4];
+#pragma unroll
+    for (int c = 0; c < 4; ++c) mq[c] = __builtin_elementwise_maximum(s0[c], s1[c]);
+#pragma unroll
+    for (int z = 4; z < 16; ++z)
+      mq[z & 3] = __builtin_elementwise_maximum(mq[z & 3], __builtin_elementwise_maximum(s0[z], s1[z]));
+    float mx = __builtin_elementwise_maximum(__builtin_elementwise_maximum(mq[0], mq[1]),
+                                             __builtin_elementwise_maximum(mq[2], mq[3]));
+    mx = half_max(mx);
+    const float m_tile = mx * c2;
+    if (__ballot(m_tile > m_run + 8.0f) != 0ull) {
+      const float m_new = fmaxf(m_run, m_tile);
+      const float alpha = fast_exp2(m_run - m_new);
+      l_run *= alpha;
+#pragma unroll
+      for (int n = 0; n < D / 32; ++n)
+#pragma unroll
+        for (int z = 0; z < 16; ++z) oacc[n][z] *= alpha;
+      m_run = m_new;
+    }
+    const float mneg = (m_run == kNegInf) ? 0.f : -m_run;
+    // Row sum of the fp32 probabilities (rounding them to bf16 first would
+    // move the LSE of short rows by up to half a bf16 ulp), four chains.
+    float ps[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int z = 0; z < 16; ++z) {
+      s0[z] = fast_exp2(fmaf(s0[z], c2, mneg));
+      s1[z] = fast_exp2(fmaf(s1[z], c2, mneg));
+      ps[z & 3] += s0[z] + s1[z];
+    }
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+      const int i0 = 2 * (m & 1);
+#pragma unroll
+      for (int z = 0; z < 8; ++z) pb[m][z] = (__bf16)((m < 2) ? s0[4 * i0 + z] : s1[4 * i0 + z]);
+    }
+    l_run += (ps[0] + ps[1]) + (ps[2] + ps[3]);
+  };
+
+  // Register fences: the compiler would otherwise move the tail of a phase
+  // (e.g. the exponentials, whose only consumer is the next MFMA phase)
+  // across the barrier into the other phase of the same wave, where it runs
+  // serially with that wave's MFMAs instead of beside the other group's.
+  auto fence_mma = [&]() {
+    reg_fence(s0);
+    reg_fence(s1);
+#pragma unroll
+    for (int n = 0; n < D / 32; ++n) reg_fence(oacc[n]);
+  };
+  auto fence_smax = [&]() {
+#pragma unroll
+    for (int m = 0; m < 4; ++m) reg_fence(pb[m]);
+    reg_fence(l_run);
+    reg_fence(m_run);
+#pragma unroll
+    for (int n = 0; n < D / 32; ++n) reg_fence(oacc[n]);
+  };
+  using T_ = std::integral_constant<bool, true>;
+  using F_ = std::integral_constant<bool, false>;
+  // Prologue: copy groups -3..-1 (K of tiles 0..2, V^T of tiles 0..1).
+  prologue_group(-3);
+  prologue_group(-2);
+  prologue_group(-1);
+  if (2 < ntile) e_v = entry(2);
+  if (3 < ntile) e_k = entry(3);
+  wait_group(0, true);
+  __builtin_amdgcn_s_barrier();
+  if (grp == 1) __builtin_amdgcn_s_barrier();  // B: idle phase 1 (A computes S of tile 0)
+  // Per tile u: MFMA phase (O += V^T(u-1) P(u-1), S(u)), barrier, softmax
+  // phase (copy group u, softmax of S(u)), barrier.  Tile 0 (S only) is
+  // peeled so that the loop has one MFMA-phase shape.
+  auto softmax_phase = [&](int u) {
+    group_begin(u);
+    copy_parts();
+    smax(u);
+    fence_smax();
+  };
+  if (ntile > 0) {
+    __builtin_amdgcn_s_setprio(1);
+    mma(F_{}, T_{}, 0, false);
+    fence_mma();
+    __builtin_amdgcn_s_setprio(0);
+    if (grp == 1) wait_group(1, false);
+    __builtin_amdgcn_s_barrier();
+    softmax_phase(0);
+    if (grp == 0) wait_group(1, true);
+    __builtin_amdgcn_s_barrier();
+  }
+  for (int u = 1; u < ntile; ++u) {
+    __builtin_amdgcn_s_setprio(1);
+    mma(T_{}, T_{}, u, false);
+    fence_mma();
+    __builtin_amdgcn_s_setprio(0);
+    if (grp == 1) wait_group(u + 1, false);
+    __builtin_amdgcn_s_barrier();
+    softmax_phase(u);
+    if (grp == 0) wait_group(u + 1, true);
+    __builtin_amdgcn_s_barrier();
+  }
+  if (ntile > 0) mma(T_{}, F_{}, ntile, false);
+  if (grp == 0) __builtin_amdgcn_s_barrier();  // matches B's last loop barrier
+
+  const float l_tot = half_sum(l_run);
+  const float inv = (l_tot > 0.f) ? 1.f / l_tot : 0.f;
+  const long long orow = ((long long)(q0 + x) * a.hq + h) * D;
+#pragma unroll
+  for (int n = 0; n < D / 32; ++n)
+#pragma unroll
+    for (int ii = 0; ii < 4; ++ii) {
+      const int d = n * 32 + 8 * ii + 4 * hh;
+      const float v0 = oacc[n][4 * ii + 0] * inv, v1 = oacc[n][4 * ii + 1] * inv;
+      const float v2 = oacc[n][4 * ii + 2] * inv, v3 = oacc[n][4 * ii + 3] * inv;
+      if (a.out_f32) {
+        f32x4 v = {v0, v1, v2, v3};
+        *(f32x4*)(a.out_f32 + orow + d) = v;
+      } else {
+        typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+        bf16x4 o4;
+        o4[0] = (__bf16)v0;
+        o4[1] = (__bf16)v1;
+        o4[2] = (__bf16)v2;
+        o4[3] = (__bf16)v3;
+        *(bf16x4*)((char*)a.out + (orow + d) * 2) = o4;
+      }
+    }
+  if (a.lse && hh == 0) {
+    const float lse = (l_tot > 0.f) ? (m_run + log2f(l_tot)) * kLn2 : kNegInf;
+    a.lse[(long long)h * a.total_q + q0 + x] = lse;
+  }
+}
+
 struct BlockIter {
   const uint8_t* mrow;
   const int32_t* table;  // block table row (paged) or nullptr
@@ -567,7 +1011,7 @@ hipError_t attn_dispatch(const AttnArgs& a, int dtype, int batch, hipStream_t s)
     const int hpw = (a.group % 2 == 0) ? 2 : 1;
     const int nwg = batch * hkv * (a.group / hpw) * a.max_qb;
     const size_t shm = (size_t)(a.max_kb + 1) * sizeof(int32_t);
-    if (hpw == 2) hipLaunchKernelGGL((attn_mfma<D, 2>), dim3(nwg), dim3(512), shm, s, a, hkv);
+    if (hpw == 2) hipLaunchKernelGGL((attn_pp<D, XATTN_PF>), dim3(nwg), dim3(512), shm, s, a, hkv);
     else hipLaunchKernelGGL((attn_mfma<D, 1>), dim3(nwg), dim3(256), shm, s, a, hkv);
   } else {
     dim3 grid(a.max_qb, a.hq, batch);
