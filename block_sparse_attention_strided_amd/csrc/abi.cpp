@@ -257,6 +257,7 @@ AttnArgs attn_args(const XattnShape* sh, const Plan& p, const void* q, KvView kv
   aa.lse = nullptr;
   aa.vt = nullptr;
   aa.lists = nullptr;
+  aa.num_pages = p.num_pages;
   return aa;
 }
 
@@ -302,6 +303,7 @@ hipError_t launch_planned(const Plan& p, AttnArgs aa, void* ws, hipStream_t st) 
 // Attention over blocks [jb0, jb1) of `mask`: prepare (bf16), then attend.
 hipError_t run_attention(const XattnShape* sh, const Plan& p, AttnArgs aa, const void* v, int num_pages,
                          void* ws, bool transpose_v, hipStream_t st) {
+  aa.num_pages = num_pages;
   hipError_t e = plan_attention(sh, p, aa, v, num_pages, ws, transpose_v, st);
   if (e != hipSuccess) return e;
   return launch_planned(p, aa, ws, st);

@@ -31,9 +31,7 @@ constexpr float kNegInf = -__builtin_huge_valf();
 #ifndef XATTN_PF
 #define XATTN_PF 6
 #endif
-#ifndef XATTN_SPREAD
-#define XATTN_SPREAD 1
-#endif
+
 
 // Position of key k inside a 16-key group of a V^T row: bits 2 and 3
 // swapped, so k-slot group hh of MFMA k-step m holds keys
@@ -88,6 +86,11 @@ __device__ __forceinline__ u32x4 lds_read16_at(uint32_t addr) {
   static_assert(OFF >= 0 && OFF < 65536, "ds offset field");
   u32x4 v;
   asm volatile("ds_read_b128 %0, %1 offset:%2" : "=v"(v) : "v"(addr), "i"(OFF));
+  return v;
+}
+__device__ __forceinline__ int lds_read4_sync(uint32_t addr) {
+  int v;
+  asm volatile("ds_read_b32 %0, %1\n\ts_waitcnt lgkmcnt(0)" : "=v"(v) : "v"(addr));
   return v;
 }
 __device__ __forceinline__ int lds_read4(uint32_t addr) {
@@ -523,6 +526,8 @@ __global__ __launch_bounds__(512) void attn_pp(AttnArgs a, int hkv) {
   for (int z = tid; z <= nblk; z += 64 * NW) list[z] = glist[z];
   __syncthreads();
   const int ntile = 2 * nblk;
+  // The diagonal block, if present, is the last entry: only its two tiles
+  // need the causal mask.
   const int first_diag = (nblk > 0 && (list[nblk] & 1)) ? ntile - 2 : ntile;
   const uint32_t list_lds = (uint32_t)(uintptr_t)(lds_ptr_t)list;
 
@@ -552,83 +557,67 @@ __global__ __launch_bounds__(512) void attn_pp(AttnArgs a, int hkv) {
   const char* kbase = a.k.base + (long long)g * D * 2;
   const char* vbase = a.vt + (long long)g * D * kBlock * 2;
 
-  // Tile copies: one raw buffer descriptor per tile (scalar base = the tile's
-  // first row, byte count = the tile's extent), constant per-lane offsets,
-  // LDS destination in m0; no VALU address arithmetic.
+  // Tile copies: one raw buffer descriptor per operand for the whole launch
+  // (its K and V^T spans are below 2^31 bytes, checked by the launcher); a
+  // tile is a 32-bit byte offset in soffset plus the constant per-lane
+  // offsets, its LDS destination goes to m0.  Copy group gi copies K of
+  // tile gi+3 into K stage (gi+3)%4 and V^T of tile gi+2 into V^T stage
+  // (gi+2)%4.  Those stages last held K of tile gi-1 and V^T of tile gi-2,
+  // both last read in the MFMA phases of tile gi-1, which both groups have
+  // finished before group gi is issued.  Every group issues all its loads:
+  // a tile past the end (or before the start) re-reads the nearest existing
+  // tile into its own stage, which no later phase reads, so the number of
+  // loads in flight -- and every vmcnt below -- is the same for each group.
   const int wu = __builtin_amdgcn_readfirstlane(w);
-  const int k_tile_bytes = (int)(KT * k_row_bytes);
-  const int vt_tile_bytes = D * kBlock * 2;
-  __amdgpu_buffer_rsrc_t rk, rv;
-  char* kl = tiles;
-  char* vl = tiles;
-  bool k_on = false, v_on = false;
-  auto setup_k = [&](int t, int e) {
-    const int page = __builtin_amdgcn_readfirstlane(e) >> 1;
-    const char* kp = kbase + page * k_page_bytes + (t & 1) * KT * k_row_bytes;
-    rk = __builtin_amdgcn_make_buffer_rsrc((void*)kp, (short)0, k_tile_bytes, kBufFlags);
-    kl = tiles + (t & (ST - 1)) * TILE + wu * LPW * 1024;
+  const __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)kbase, (short)0, (int)(a.num_pages * k_page_bytes - (long long)g * D * 2), kBufFlags);
+  const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)vbase, (short)0, (int)(a.num_pages * vt_page_bytes - (long long)g * D * kBlock * 2), kBufFlags);
+  const int kpb = (int)k_page_bytes, vpb = (int)vt_page_bytes, khalf = (int)(KT * k_row_bytes);
+  char* const kl0 = tiles + wu * LPW * 1024;
+  char* const vl0 = tiles + ST * TILE + wu * LPW * 1024;
+  auto src_tile = [&](int t) { return t < 0 ? 0 : (t < ntile ? t : ntile - 1); };
+  // List entries for the copies: lane j of `eb` holds the entry of block
+  // eb0 + j, loaded by one LDS read that waits for its own result (a read
+  // left in flight in an asm output could be copied by the compiler before
+  // it lands); a group takes its two entries with v_readlane.  Refilled
+  // once per 64 blocks.
+  int eb = 0, eb0 = -64;
+  auto entry_of = [&](int t) {
+    const int blk = t >> 1;
+    if (blk >= eb0 + 64) {
+      eb0 = blk > 0 ? blk - 1 : 0;
+      const int z = eb0 + lane < nblk ? eb0 + lane : nblk - 1;
+      eb = lds_read4_sync(list_lds + 4 * (1 + z));
+    }
+    return __builtin_amdgcn_readlane(eb, blk - eb0);
   };
-  auto setup_v = [&](int t, int e) {
-    const int page = __builtin_amdgcn_readfirstlane(e) >> 1;
-    const char* vp = vbase + page * vt_page_bytes + (t & 1) * KT * 2;
-    rv = __builtin_amdgcn_make_buffer_rsrc((void*)vp, (short)0, vt_tile_bytes, kBufFlags);
-    vl = tiles + (ST + (t & (ST - 1))) * TILE + wu * LPW * 1024;
+  int soff_k = 0, soff_v = 0;
+  char* kl = kl0;
+  char* vl = vl0;
+  auto group_setup = [&](int gi) {
+    const int tv = src_tile(gi + 2), tk = src_tile(gi + 3);
+    const int ev = entry_of(tv), ek = entry_of(tk);
+    soff_k = (ek >> 1) * kpb + (tk & 1) * khalf;
+    soff_v = (ev >> 1) * vpb + (tv & 1) * (KT * 2);
+    kl = kl0 + ((gi + 3) & (ST - 1)) * TILE;
+    vl = vl0 + (gi + 2 < 0 ? 0 : ((gi + 2) & (ST - 1))) * TILE;
   };
-  // part n < LPW: K chunk n, else V^T chunk n - LPW (each if its tile exists)
+  // part n < LPW: K chunk n, else V^T chunk n - LPW
   auto copy_part = [&](auto n_tag) {
     constexpr int N = decltype(n_tag)::value;
     if constexpr (N < LPW) {
-      if (k_on) buffer_load_lds16(rk, kl + N * 1024, (uint32_t)koff[N]);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (lds_ptr_t)(kl + N * 1024), 16, (uint32_t)koff[N], soff_k, 0, 0);
     } else {
-      if (v_on) buffer_load_lds16(rv, vl + (N - LPW) * 1024, (uint32_t)voff[N - LPW]);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (lds_ptr_t)(vl + (N - LPW) * 1024), 16, (uint32_t)voff[N - LPW],
+                                               soff_v, 0, 0);
     }
   };
-  auto copy_parts = [&]() {
+  auto copy_group = [&](int gi) {
+    group_setup(gi);
     [&]<int... N>(std::integer_sequence<int, N...>) {
       (copy_part(std::integral_constant<int, N>{}), ...);
     }(std::make_integer_sequence<int, 2 * LPW>{});
-  };
-  auto entry = [&](int t) {  // list entry of tile t, waited for
-    int e = lds_read4(list_lds + 4 * (1 + (t >> 1)));
-    lgkm_wait<0>(e);
-    return e;
-  };
-  // Copy group gi (issued in the softmax phase of tile gi, prologue groups
-  // -3..-1):
-  // K of tile gi+3 into K stage (gi+3)%4 and V^T of tile gi+2 into V stage
-  // (gi+2)%4.  Those stages last held K of tile gi-1 and V^T of tile gi-2,
-  // both last read in the MFMA phases of tile gi-1, which both groups have
-  // finished before group gi is issued.
-  auto prologue_group = [&](int gi) {
-    k_on = gi + 3 < ntile;
-    v_on = gi + 2 >= 0 && gi + 2 < ntile;
-    if (k_on) setup_k(gi + 3, entry(gi + 3));
-    if (v_on) setup_v(gi + 2, entry(gi + 2));
-    copy_parts();
-  };
-  int e_k = 0, e_v = 0;  // list entries of tiles gi+3 and gi+2 for the next group
-  auto group_begin = [&](int gi) {
-    lgkm_wait<0>(e_k);  // read during the previous MFMA phase
-    k_on = gi + 3 < ntile;
-    v_on = gi + 2 < ntile;
-    if (k_on) setup_k(gi + 3, e_k);
-    if (v_on) setup_v(gi + 2, e_v);
-    e_v = e_k;
-    if (gi + 4 < ntile) e_k = lds_read4(list_lds + 4 * (1 + ((gi + 4) >> 1)));
-  };
-  // Before the barrier that opens phase 2m+1 (K of tile m and V^T of tile
-  // m-1 are read from then on): this wave's copies of group m-3 are done.
-  // Groups are issued in the softmax phases (A: phase 2g+2, B: phase 2g+3),
-  // so at that barrier A may still have groups m-2 and m-1 in flight, B only
-  // group m-2 (all waves also after the prologue, which issued -3..-1).
-  auto wait_group = [&](int m, bool newest_issued) {
-    int c = (m < ntile) + (m + 1 < ntile);  // group m-2, in units of LPW
-    if (newest_issued) c += (m + 1 < ntile) + (m + 2 < ntile);  // group m-1
-    if (c >= 4) wait_vmcnt<4 * LPW>();
-    else if (c == 3) wait_vmcnt<3 * LPW>();
-    else if (c == 2) wait_vmcnt<2 * LPW>();
-    else if (c == 1) wait_vmcnt<LPW>();
-    else wait_vmcnt<0>();
   };
 
   // Per-lane LDS addresses of the MFMA A fragments in stage 0.
@@ -653,7 +642,7 @@ __global__ __launch_bounds__(512) void attn_pp(AttnArgs a, int hkv) {
 
   // ---- MFMA phase of tile u: O^T += V^T(u-1) P^T(u-1) if PV, S^T(u) = K(u) Q^T
   // if SS.  The two MFMA streams alternate; LDS fragments are read two ahead.
-  auto mma = [&](auto pv_tag, auto ss_tag, int u, bool cp) {
+  auto mma = [&](auto pv_tag, auto ss_tag, int u) {
     constexpr bool PV = decltype(pv_tag)::value, SS = decltype(ss_tag)::value;
     constexpr int NOPS = (PV ? NPV : 0) + (SS ? NS : 0);
     const uint32_t kst = (uint32_t)((u & (ST - 1)) * TILE);
@@ -687,9 +676,6 @@ __global__ __launch_bounds__(512) void attn_pp(AttnArgs a, int hkv) {
       }
     };
     // fragment of op J lives in fr[J]; reads run PF ops ahead of the MFMAs
-    if constexpr (!XATTN_SPREAD) {
-      if (cp) copy_parts();
-    }
     u32x4 fr[NOPS];
     [&]<int... J>(std::integer_sequence<int, J...>) {
       ((fr[J] = frag(std::integral_constant<int, J>{})), ...);
@@ -711,10 +697,6 @@ __global__ __launch_bounds__(512) void attn_pp(AttnArgs a, int hkv) {
         constexpr int KK = I >> 1, HALF = I & 1;
         if constexpr (HALF == 0) s0 = mfma32(__builtin_bit_cast(bf16x8, fa), qf[KK], s0);
         else s1 = mfma32(__builtin_bit_cast(bf16x8, fa), qf[KK], s1);
-      }
-      // one part of the copy group after every fourth MFMA
-      if constexpr (XATTN_SPREAD && J % 4 == 1 && J / 4 < 2 * LPW) {
-        if (cp) copy_part(std::integral_constant<int, J / 4>{});
       }
     };
     [&]<int... J>(std::integer_sequence<int, J...>) {
@@ -763,7 +745,13 @@ __global__ __launch_bounds__(512) void attn_pp(AttnArgs a, int hkv) {
     // move the LSE of short rows by up to half a bf16 ulp), four chains.
     float ps[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int z = 0; z < 16; ++z) {
+    for (int z = 0; z < 8; ++z) {
+      s0[z] = fast_exp2(fmaf(s0[z], c2, mneg));
+      s1[z] = fast_exp2(fmaf(s1[z], c2, mneg));
+      ps[z & 3] += s0[z] + s1[z];
+    }
+#pragma unroll
+    for (int z = 8; z < 16; ++z) {
       s0[z] = fast_exp2(fmaf(s0[z], c2, mneg));
       s1[z] = fast_exp2(fmaf(s1[z], c2, mneg));
       ps[z & 3] += s0[z] + s1[z];
@@ -797,48 +785,51 @@ __global__ __launch_bounds__(512) void attn_pp(AttnArgs a, int hkv) {
   };
   using T_ = std::integral_constant<bool, true>;
   using F_ = std::integral_constant<bool, false>;
-  // Prologue: copy groups -3..-1 (K of tiles 0..2, V^T of tiles 0..1).
-  prologue_group(-3);
-  prologue_group(-2);
-  prologue_group(-1);
-  if (2 < ntile) e_v = entry(2);
-  if (3 < ntile) e_k = entry(3);
-  wait_group(0, true);
+  // Prologue: copy groups -3..-1 (K of tiles 0..2, V^T of tiles 0..1);
+  // before the barrier that opens a phase reading K of tile m, every wave
+  // has its copies of group m-3 done: groups m-2 and m-1 may be in flight
+  // for A (it issued group m-1 in the phase just ending), only group m-2 for B.
+  if (ntile > 0) {
+    copy_group(-3);  // V^T part: tile 0, the same bytes as group -2's
+    copy_group(-2);
+    copy_group(-1);
+    wait_vmcnt<4 * LPW>();
+  }
   __builtin_amdgcn_s_barrier();
   if (grp == 1) __builtin_amdgcn_s_barrier();  // B: idle phase 1 (A computes S of tile 0)
   // Per tile u: MFMA phase (O += V^T(u-1) P(u-1), S(u)), barrier, softmax
   // phase (copy group u, softmax of S(u)), barrier.  Tile 0 (S only) is
   // peeled so that the loop has one MFMA-phase shape.
   auto softmax_phase = [&](int u) {
-    group_begin(u);
-    copy_parts();
+    copy_group(u);
     smax(u);
     fence_smax();
   };
   if (ntile > 0) {
     __builtin_amdgcn_s_setprio(1);
-    mma(F_{}, T_{}, 0, false);
+    mma(F_{}, T_{}, 0);
     fence_mma();
     __builtin_amdgcn_s_setprio(0);
-    if (grp == 1) wait_group(1, false);
+    if (grp == 1) wait_vmcnt<2 * LPW>();
     __builtin_amdgcn_s_barrier();
     softmax_phase(0);
-    if (grp == 0) wait_group(1, true);
+    if (grp == 0) wait_vmcnt<4 * LPW>();
     __builtin_amdgcn_s_barrier();
   }
   for (int u = 1; u < ntile; ++u) {
     __builtin_amdgcn_s_setprio(1);
-    mma(T_{}, T_{}, u, false);
+    mma(T_{}, T_{}, u);
     fence_mma();
     __builtin_amdgcn_s_setprio(0);
-    if (grp == 1) wait_group(u + 1, false);
+    if (grp == 1) wait_vmcnt<2 * LPW>();
     __builtin_amdgcn_s_barrier();
     softmax_phase(u);
-    if (grp == 0) wait_group(u + 1, true);
+    if (grp == 0) wait_vmcnt<4 * LPW>();
     __builtin_amdgcn_s_barrier();
   }
-  if (ntile > 0) mma(T_{}, F_{}, ntile, false);
+  if (ntile > 0) mma(T_{}, F_{}, ntile);
   if (grp == 0) __builtin_amdgcn_s_barrier();  // matches B's last loop barrier
+  wait_vmcnt<0>();  // copies of the groups past the end land in LDS before exit
 
   const float l_tot = half_sum(l_run);
   const float inv = (l_tot > 0.f) ? 1.f / l_tot : 0.f;
@@ -1011,7 +1002,10 @@ hipError_t attn_dispatch(const AttnArgs& a, int dtype, int batch, hipStream_t s)
     const int hpw = (a.group % 2 == 0) ? 2 : 1;
     const int nwg = batch * hkv * (a.group / hpw) * a.max_qb;
     const size_t shm = (size_t)(a.max_kb + 1) * sizeof(int32_t);
-    if (hpw == 2) hipLaunchKernelGGL((attn_pp<D, XATTN_PF>), dim3(nwg), dim3(512), shm, s, a, hkv);
+    // The ping-pong kernel addresses K and V^T with 32-bit buffer offsets.
+    const long long span = (long long)a.num_pages * kBlock * hkv * D * 2;
+    if (hpw == 2 && span < (1ll << 31)) hipLaunchKernelGGL((attn_pp<D, XATTN_PF>), dim3(nwg), dim3(512), shm, s, a, hkv);
+    else if (hpw == 2) hipLaunchKernelGGL((attn_mfma<D, 2>), dim3(nwg), dim3(512), shm, s, a, hkv);
     else hipLaunchKernelGGL((attn_mfma<D, 1>), dim3(nwg), dim3(256), shm, s, a, hkv);
   } else {
     dim3 grid(a.max_qb, a.hq, batch);

@@ -92,6 +92,7 @@ struct AttnArgs {
   KvView v;
   const char* vt;         // bf16 path: transposed V pages (VtArgs layout)
   const int32_t* lists;   // bf16 path: block lists (PlanArgs layout)
+  int num_pages;          // 128-key pages addressable through k.base / vt
   const uint8_t* mask;  // [batch, hkv, max_qb, max_kb]
   const int32_t* cu_q;
   const int32_t* cu_k;
