@@ -182,8 +182,9 @@ KvView make_view(const XattnShape* sh, const Plan& p, const void* base) {
   return v;
 }
 
+// k_pages: 128-key pages addressable from kview.base.
 hipError_t run_estimate(const XattnShape* sh, const Plan& p, const void* q, KvView kview, int jb0,
-                        int jb_count, float* part, hipStream_t st) {
+                        int jb_count, int k_pages, float* part, hipStream_t st) {
   EstArgs ea;
   ea.q = (const char*)q;
   ea.k = kview;
@@ -197,6 +198,8 @@ hipError_t run_estimate(const XattnShape* sh, const Plan& p, const void* q, KvVi
   ea.part = part;
   ea.max_kb = p.max_kb;
   ea.max_r = p.max_r;
+  ea.q_bytes = (long long)p.total_q * p.hq * p.d * (p.dtype == XATTN_DTYPE_BF16 ? 2 : 4);
+  ea.k_bytes = (long long)k_pages * XATTN_BLOCK * p.hkv * p.d * (p.dtype == XATTN_DTYPE_BF16 ? 2 : 4);
   return launch_estimate(ea, p.dtype == XATTN_DTYPE_BF16 ? 0 : 1, p.d, p.stride, p.batch, st);
 }
 
@@ -426,13 +429,13 @@ int prefill_ring(XattnRing* r, const XattnShape* sh, const XattnParams* pr, cons
     if ((e = hipStreamWaitEvent(st, r->ready[s], 0)) != hipSuccess) return hip_fail(e, "ring wait");
     KvView kv = make_view(sh, p, r->k_slots + s * slot_bytes);
     kv.y_offset = j0 * XATTN_BLOCK;
-    if ((e = run_estimate(sh, p, q, kv, j0, nb, part, st)) != hipSuccess) return hip_fail(e, "estimate launch");
+    if ((e = run_estimate(sh, p, q, kv, j0, nb, nb, part, st)) != hipSuccess) return hip_fail(e, "estimate launch");
     if ((e = hipEventRecord(r->done[s], st)) != hipSuccess) return hip_fail(e, "ring record");
   }
   {
     KvView kv = make_view(sh, p, k);
     kv.y_offset = kh * XATTN_BLOCK;
-    if ((e = run_estimate(sh, p, q, kv, kh, qb, part, st)) != hipSuccess) return hip_fail(e, "estimate launch");
+    if ((e = run_estimate(sh, p, q, kv, kh, qb, qb, part, st)) != hipSuccess) return hip_fail(e, "estimate launch");
   }
   if ((e = run_block_sums(sh, p, part, bs, st)) != hipSuccess) return hip_fail(e, "block-sum launch");
   if ((e = run_select(sh, pr, p, bs, ws_at<uint8_t>(ws, p.off_maskq), maskkv, hist, cnt, st)) != hipSuccess)
@@ -553,7 +556,7 @@ int xattn_estimate(const XattnShape* shape, const XattnParams* params, const voi
   g_last_error.clear();
   hipStream_t st = (hipStream_t)stream;
   float* part = ws_at<float>(ws, p.off_part);
-  hipError_t e = run_estimate(shape, p, q, make_view(shape, p, k), 0, p.max_kb, part, st);
+  hipError_t e = run_estimate(shape, p, q, make_view(shape, p, k), 0, p.max_kb, p.num_pages, part, st);
   if (e != hipSuccess) return hip_fail(e, "estimate launch");
   e = run_block_sums(shape, p, part, block_sums, st);
   if (e != hipSuccess) return hip_fail(e, "block-sum launch");
@@ -673,7 +676,7 @@ int xattn_prefill_chunk(XattnRing* ring, const XattnShape* shape, const XattnPar
   uint8_t* hist = (aux && aux->hist_sel) ? aux->hist_sel : ws_at<uint8_t>(ws, p.off_hist);
   int32_t* cnt = counts ? counts : ws_at<int32_t>(ws, p.off_counts);
   const KvView kview = make_view(shape, p, k), vview = make_view(shape, p, v);
-  hipError_t e = run_estimate(shape, p, q, kview, 0, p.max_kb, part, st);
+  hipError_t e = run_estimate(shape, p, q, kview, 0, p.max_kb, p.num_pages, part, st);
   if (e != hipSuccess) return hip_fail(e, "estimate launch");
   e = run_block_sums(shape, p, part, bs, st);
   if (e != hipSuccess) return hip_fail(e, "block-sum launch");

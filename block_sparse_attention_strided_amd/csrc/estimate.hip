@@ -19,6 +19,8 @@ namespace {
 
 constexpr float kNegInf = -__builtin_huge_valf();
 constexpr int kEstTile = 128;  // reshaped rows and columns per workgroup
+// Raw buffer descriptor word 3 for gfx950 (32-bit data format, no swizzle).
+constexpr int kEstBufFlags = 0x00020000;
 
 // ---------------------------------------------------------------------------
 // bf16 MFMA score tile + per-block log-sum-exp epilogue.
@@ -141,6 +143,219 @@ __global__ __launch_bounds__(256) void est_partial_bf16(EstArgs a) {
 }
 
 // ---------------------------------------------------------------------------
+// bf16 MFMA score GEMM for large launches.  Workgroup: 8 waves, tile 256
+// reshaped key columns x 256 reshaped query rows; wave w owns 128 columns
+// (half w&1) x 64 rows (quarter w>>1) as 4 x 2 MFMA 32x32 accumulators of
+// S^T.  The reduction (s tokens x d) runs in stages of 64 elements (one
+// token offset t, one half or quarter of d), double-buffered in LDS and
+// filled by direct buffer -> LDS loads: a row's token goes into a per-lane
+// offset computed once, the stage's (t, d) position into the scalar offset,
+// and rows past the end (or unallocated pages) read zeros through the
+// descriptor's byte bound.  LDS rows are 128 B with 16-byte chunks
+// XOR-swizzled by the row's low 3 bits (no bank conflicts for the fragment
+// reads, which are inline asm retired by explicit lgkmcnt waits so that the
+// compiler adds no wait for the in-flight copies).
+// ---------------------------------------------------------------------------
+template <int OFF>
+__device__ __forceinline__ u32x4 est_lds_read16(uint32_t addr) {
+  static_assert(OFF >= 0 && OFF < 65536, "ds offset field");
+  u32x4 v;
+  asm volatile("ds_read_b128 %0, %1 offset:%2" : "=v"(v) : "v"(addr), "i"(OFF));
+  return v;
+}
+template <int N>
+__device__ __forceinline__ void est_lgkm_wait(u32x4& a0, u32x4& a1, u32x4& a2, u32x4& a3, u32x4& a4, u32x4& a5) {
+  asm volatile("s_waitcnt lgkmcnt(%6)" : "+v"(a0), "+v"(a1), "+v"(a2), "+v"(a3), "+v"(a4), "+v"(a5) : "n"(N));
+}
+template <int N>
+__device__ __forceinline__ void est_wait_vmcnt() {
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+constexpr int kEstBig = 256;
+
+template <int D, int S>
+__global__ __launch_bounds__(512) void est_gemm_bf16(EstArgs a) {
+  constexpr int RB = kBlock / S;
+  constexpr int TT = kEstBig;        // rows and columns per workgroup
+  constexpr int BK = 64;             // reduction elements per stage
+  constexpr int TILEB = TT * BK * 2; // bytes of one operand tile (32 KiB)
+  constexpr int DQ = D / BK;         // stages per token offset
+  constexpr int NST = S * DQ;        // stages (even for every supported S, D)
+  static_assert(NST % 2 == 0, "stage loop is unrolled by two");
+  typedef __attribute__((address_space(3))) void* lds_ptr;
+  __shared__ __align__(1024) char lds[4 * TILEB];  // buffer 0: K, Q; buffer 1: K, Q
+
+  const int bh = blockIdx.z;
+  const int b = bh / a.hq, h = bh % a.hq, g = h / a.group;
+  const int q0 = a.cu_q[b];
+  const int lq = a.cu_q[b + 1] - q0;
+  const int lk = a.cu_k[b + 1] - a.cu_k[b];
+  const int R = lq / S, C = lk / S, o_s = (lk - lq) / S;
+  const int r0 = blockIdx.y * TT;
+  if (r0 >= R) return;
+  const int c0 = a.jb0 * RB + blockIdx.x * TT;
+  const int c_end = min((a.jb0 + a.jb_count) * RB, C);
+  if (c0 >= c_end) return;
+  const int r_last = min(r0 + TT, R) - 1;
+  if (c0 > r_last + o_s) return;  // whole tile beyond the causal block diagonal
+
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int wu = __builtin_amdgcn_readfirstlane(w);
+  const int wc = w & 1, wr = w >> 1;
+  const int l32 = lane & 31, hh = lane >> 5;
+
+  // ---- copies: instruction n of wave w fills tile rows (4w+n)*8 .. +8
+  const long long q_tok = (long long)a.hq * D * 2;
+  const long long k_row = (long long)a.k.kv_heads * D * 2;
+  constexpr uint32_t kOut = 0x80000000u;  // beyond either descriptor's bound
+  uint32_t kvo[4], qvo[4];
+#pragma unroll
+  for (int n = 0; n < 4; ++n) {
+    const int row = (w * 4 + n) * 8 + (lane >> 3);
+    const int lc = (lane & 7) ^ (row & 7);  // logical chunk stored at this lane's position
+    const int c = c0 + row, r = r0 + row;
+    kvo[n] = kOut;
+    if (c < c_end) {
+      const char* p = a.k.row(b, c * S, g);
+      if (p) kvo[n] = (uint32_t)(p - a.k.base) + lc * 16;
+    }
+    qvo[n] = kOut;
+    if (r < R) qvo[n] = (uint32_t)(((long long)(q0 + r * S) * a.hq + h) * D * 2) + lc * 16;
+  }
+  const __amdgpu_buffer_rsrc_t rk =
+      __builtin_amdgcn_make_buffer_rsrc((void*)a.k.base, (short)0, (int)a.k_bytes, kEstBufFlags);
+  const __amdgpu_buffer_rsrc_t rq =
+      __builtin_amdgcn_make_buffer_rsrc((void*)a.q, (short)0, (int)a.q_bytes, kEstBufFlags);
+  auto issue = [&](int st, int bf) {
+    const int t = st / DQ, dq = st - (st / DQ) * DQ;
+    const int so_k = (int)(t * k_row) + dq * BK * 2;
+    const int so_q = (int)((S - 1 - t) * q_tok) + dq * BK * 2;
+    char* kd = lds + bf * 2 * TILEB + wu * 4 * 1024;
+    char* qd = kd + TILEB;
+#pragma unroll
+    for (int n = 0; n < 4; ++n) __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (lds_ptr)(kd + n * 1024), 16, kvo[n], so_k, 0, 0);
+#pragma unroll
+    for (int n = 0; n < 4; ++n) __builtin_amdgcn_raw_ptr_buffer_load_lds(rq, (lds_ptr)(qd + n * 1024), 16, qvo[n], so_q, 0, 0);
+  };
+
+  // ---- fragment addresses: row swizzle = l32 & 7 for every tile row a lane reads
+  const uint32_t lds0 = (uint32_t)(uintptr_t)(lds_ptr)lds;
+  uint32_t ka[2][4], qa[2][4];
+#pragma unroll
+  for (int bf = 0; bf < 2; ++bf)
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) {
+      const uint32_t ch = (uint32_t)(((2 * kk + hh) ^ (l32 & 7)) * 16);
+      ka[bf][kk] = lds0 + bf * 2 * TILEB + (wc * 128 + l32) * 128 + ch;
+      qa[bf][kk] = lds0 + bf * 2 * TILEB + TILEB + (wr * 64 + l32) * 128 + ch;
+    }
+
+  f32x16 acc[4][2];
+#pragma unroll
+  for (int x = 0; x < 4; ++x)
+#pragma unroll
+    for (int y = 0; y < 2; ++y)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) acc[x][y][e] = 0.f;
+
+  // one stage: 4 k-steps of 16; k-step kk+1's six fragments are read while
+  // k-step kk's eight MFMAs issue
+  auto compute = [&](auto bf_tag) {
+    constexpr int BF = decltype(bf_tag)::value;
+    u32x4 f0 = est_lds_read16<0>(ka[BF][0]), f1 = est_lds_read16<4096>(ka[BF][0]);
+    u32x4 f2 = est_lds_read16<8192>(ka[BF][0]), f3 = est_lds_read16<12288>(ka[BF][0]);
+    u32x4 f4 = est_lds_read16<0>(qa[BF][0]), f5 = est_lds_read16<4096>(qa[BF][0]);
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) {
+      u32x4 g0, g1, g2, g3, g4, g5;
+      if (kk + 1 < 4) {
+        const int k1 = kk + 1 < 4 ? kk + 1 : 0;
+        g0 = est_lds_read16<0>(ka[BF][k1]);
+        g1 = est_lds_read16<4096>(ka[BF][k1]);
+        g2 = est_lds_read16<8192>(ka[BF][k1]);
+        g3 = est_lds_read16<12288>(ka[BF][k1]);
+        g4 = est_lds_read16<0>(qa[BF][k1]);
+        g5 = est_lds_read16<4096>(qa[BF][k1]);
+        est_lgkm_wait<6>(f0, f1, f2, f3, f4, f5);
+      } else {
+        est_lgkm_wait<0>(f0, f1, f2, f3, f4, f5);
+      }
+      const bf16x8 kf[4] = {__builtin_bit_cast(bf16x8, f0), __builtin_bit_cast(bf16x8, f1),
+                            __builtin_bit_cast(bf16x8, f2), __builtin_bit_cast(bf16x8, f3)};
+      const bf16x8 qf[2] = {__builtin_bit_cast(bf16x8, f4), __builtin_bit_cast(bf16x8, f5)};
+#pragma unroll
+      for (int x = 0; x < 4; ++x)
+#pragma unroll
+        for (int y = 0; y < 2; ++y) acc[x][y] = mfma32(kf[x], qf[y], acc[x][y]);
+      if (kk + 1 < 4) {
+        f0 = g0; f1 = g1; f2 = g2; f3 = g3; f4 = g4; f5 = g5;
+      }
+    }
+  };
+
+  // ---- stage loop: wait for this wave's copies of the stage, barrier (all
+  // copies visible, the other buffer free), copy the next stage, compute
+  issue(0, 0);
+  for (int st = 0; st < NST; st += 2) {
+    est_wait_vmcnt<0>();
+    __builtin_amdgcn_s_barrier();
+    issue(st + 1, 1);
+    compute(std::integral_constant<int, 0>{});
+    est_wait_vmcnt<0>();
+    __builtin_amdgcn_s_barrier();
+    if (st + 2 < NST) issue(st + 2, 0);
+    compute(std::integral_constant<int, 1>{});
+  }
+
+  // ---- epilogue: per (query row, key block) base-2 log-sum-exp over the
+  // block's allowed columns; a block's columns are split between lanes l
+  // and l ^ 32, combined with one swap of the (max, sum) pair
+  constexpr int NBLK = 32 / RB;  // key blocks per 32-column accumulator
+  constexpr int EPB = 16 / NBLK; // accumulator values per lane and block
+  const int j_end = a.jb0 + a.jb_count;
+#pragma unroll
+  for (int y = 0; y < 2; ++y) {
+    const int r = r0 + wr * 64 + y * 32 + l32;
+#pragma unroll
+    for (int x = 0; x < 4; ++x) {
+      const int cblk = c0 + wc * 128 + x * 32;
+#pragma unroll
+      for (int m = 0; m < NBLK; ++m) {
+        float z[EPB];
+        float mx = kNegInf;
+#pragma unroll
+        for (int q = 0; q < EPB; ++q) {
+          const int e = m * EPB + q;
+          const int c = cblk + 8 * (e >> 2) + 4 * hh + (e & 3);
+          const bool ok = (r < R) && (c < c_end) && (c <= r + o_s);
+          z[q] = ok ? acc[x][y][e] * a.scale2 : kNegInf;
+          mx = fmaxf(mx, z[q]);
+        }
+        float sm = 0.f;
+        if (mx != kNegInf) {
+#pragma unroll
+          for (int q = 0; q < EPB; ++q) sm += exp2f(z[q] - mx);
+        }
+        const auto pm = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx), false, false);
+        const auto ps = __builtin_amdgcn_permlane32_swap(__float_as_uint(sm), __float_as_uint(sm), false, false);
+        const float m0 = __uint_as_float(pm[0]), m1 = __uint_as_float(pm[1]);
+        const float s0 = __uint_as_float(ps[0]), s1 = __uint_as_float(ps[1]);
+        const float M = fmaxf(m0, m1);
+        float lse = kNegInf;
+        if (M != kNegInf) {
+          const float tot = (m0 == kNegInf ? 0.f : s0 * exp2f(m0 - M)) + (m1 == kNegInf ? 0.f : s1 * exp2f(m1 - M));
+          lse = M + log2f(tot);
+        }
+        const int j = cblk / RB + m;
+        if (hh == 0 && r < R && j < j_end && j * RB < C)
+          a.part[((long long)bh * a.max_kb + j) * a.max_r + r] = lse;
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
 // fp32 inputs: plain VALU dot products (tiny workloads; fp32 accuracy).
 // Workgroup = one key block j x (256 / RB) reshaped rows; lane group of RB
 // lanes = one row's RB columns, reduced with cross-lane shuffles.
@@ -255,6 +470,14 @@ template <int D, int S>
 hipError_t est_dispatch(const EstArgs& a, int dtype, int batch, hipStream_t st) {
   constexpr int RB = kBlock / S;
   if (dtype == 0) {
+    // Large launches: 256 x 256 tiles when they still fill the chip and both
+    // operands fit 32-bit buffer offsets; otherwise 128 x 128 tiles.
+    dim3 big((a.jb_count * RB + kEstBig - 1) / kEstBig, (a.max_r + kEstBig - 1) / kEstBig, batch * a.hq);
+    const long long nbig = (long long)big.x * big.y * big.z;
+    if (nbig >= 256 && a.q_bytes < (1ll << 31) && a.k_bytes < (1ll << 31)) {
+      hipLaunchKernelGGL((est_gemm_bf16<D, S>), big, dim3(512), 0, st, a);
+      return hipGetLastError();
+    }
     dim3 grid((a.jb_count * RB + kEstTile - 1) / kEstTile, (a.max_r + kEstTile - 1) / kEstTile,
               batch * a.hq);
     hipLaunchKernelGGL((est_partial_bf16<D, S>), grid, dim3(256), 0, st, a);

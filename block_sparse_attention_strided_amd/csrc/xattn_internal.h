@@ -25,6 +25,8 @@ struct EstArgs {
   float* part;
   int max_kb;
   int max_r;
+  long long q_bytes;  // bytes addressable from q
+  long long k_bytes;  // bytes addressable from k.base
 };
 
 struct BlockSumArgs {

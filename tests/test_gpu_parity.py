@@ -24,6 +24,10 @@ EST_CASES = {
                             paged=True),
     "bf16_empty_seqs": dict(hq=2, hkv=1, d=128, lq=[256, 0, 128, 0], lk=[512, 256, 128, 0], stride=8),
     "f32_s8_d64": dict(hq=2, hkv=1, d=64, lq=[512], lk=[1024], stride=8, dtype=torch.float32),
+    # large enough (>= 256 tiles of 256 x 256) for the big-tile GEMM path:
+    # ragged rows/columns, causal tiles, two sequences
+    "bf16_big_s8_varlen": dict(hq=16, hkv=4, d=128, lq=[2432, 640], lk=[8192, 1024], stride=8),
+    "bf16_big_s16_d64": dict(hq=16, hkv=8, d=64, lq=[4096], lk=[65536], stride=16),
     "f32_s16_d128_paged": dict(hq=2, hkv=2, d=128, lq=[256, 128], lk=[512, 384], stride=16,
                                dtype=torch.float32, paged=True),
 }
