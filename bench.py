@@ -11,9 +11,11 @@ Other workloads (--workload) are the 4K layer, the paged varlen batch and the
 128K context streamed from pinned host memory through the 4-slot ring.
 
 Prints one JSON line.  "roofline" is for the dominant kernel, the bf16 sparse
-attention (attn_mfma), timed alone (xattn_attn_run) with HIP events on the
+attention (attn_pp), timed alone (xattn_attn_run) with HIP events on the
 stream it is launched on; algorithmic flops = 4*d per visible selected
-(query, key) pair per q head.  "cpu_baseline" times the float64 oracle on a
+(query, key) pair per q head.  "achievable" states what this machine reaches on
+a large bf16 GEMM (hipBLASLt through torch.matmul) and on a device copy, next
+to the published peaks.  "cpu_baseline" times the float64 oracle on a
 bounded sample of the same workload on the host cores.
 """
 
@@ -43,6 +45,8 @@ def parse():
                     help="query rows of the oracle attention sample (scaled to the chunk)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 512 MiB device copy kernel (reference for PMC byte counters)")
+    ap.add_argument("--no-achievable", action="store_true",
+                    help="skip the large-GEMM and copy rate measurement")
     return ap.parse_args()
 
 
@@ -83,9 +87,35 @@ def profiled_traffic(workload):
     if ("attention.hip %s" % h) not in text:
         return None
     for line in text.splitlines():
-        if line.startswith("attn_mfma traffic_bytes_per_launch:"):
+        if line.startswith("attention traffic_bytes_per_launch:"):
             return int(line.split(":")[1])
     return None
+
+
+def achievable_rates(dev):
+    """This box's rates on a large bf16 GEMM (8192^3, hipBLASLt via
+    torch.matmul) and a 512 MiB device copy, timed with HIP events."""
+    import torch
+
+    n = 8192
+    a = torch.randn(n, n, device=dev, dtype=torch.bfloat16)
+    b = torch.randn(n, n, device=dev, dtype=torch.bfloat16)
+    c = torch.empty(n, n, device=dev, dtype=torch.bfloat16)
+    for _ in range(3):
+        torch.matmul(a, b, out=c)
+    ms_g = time_region(lambda: torch.matmul(a, b, out=c), 10, torch.cuda.current_stream())
+    x = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+    y = torch.empty_like(x)
+    for _ in range(3):
+        y.copy_(x)
+    ms_c = time_region(lambda: y.copy_(x), 10, torch.cuda.current_stream())
+    del a, b, c, x, y
+    gemm = 2.0 * n ** 3 / (ms_g * 1e-3) / 1e12
+    copy = 2.0 * (512 << 20) / (ms_c * 1e-3) / 1e9
+    return {"gemm_bf16_tflops": gemm, "gemm_frac_of_peak": gemm / PEAK_BF16_TFLOPS,
+            "copy_gbs": copy, "copy_frac_of_peak": copy / PEAK_HBM_GBS,
+            "gemm": "bf16 8192x8192x8192 torch.matmul (hipBLASLt), 10 launches",
+            "copy": "512 MiB device-to-device copy_, 10 launches, read+write bytes"}
 
 
 def time_region(fn, steps, stream):
@@ -240,9 +270,10 @@ def main():
         flops = attention_flops(mask, w.cu_q, w.cu_k, hq // hkv, w.head_dim)
         achieved = flops / (ms_attn * 1e-3) / 1e12
         e_fl = estimate_flops(w.cu_q, w.cu_k, hq, w.stride, w.head_dim)
+        stages["estimate_flops"] = e_fl
         stages["estimate_tflops"] = e_fl / (stages["estimate_ms"] * 1e-3) / 1e12
         roofline = {
-            "kernel": "attn_mfma (block-sparse flash attention, bf16 MFMA)",
+            "kernel": "attn_pp (block-sparse flash attention, bf16 MFMA, ping-pong)",
             "bound": "mfma",
             "achieved": achieved,
             "peak": PEAK_BF16_TFLOPS,
@@ -290,6 +321,8 @@ def main():
                                    "kernel": "elementwise mul by 1.0 (torch), 5 launches"}
     if ring is not None:
         ring.close()
+    if not args.no_achievable:
+        res["achievable"] = achievable_rates(dev)
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(w, args.cpu_sample_rows)
     print(json.dumps(res), flush=True)

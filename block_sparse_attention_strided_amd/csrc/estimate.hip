@@ -186,15 +186,24 @@ __global__ __launch_bounds__(512) void est_gemm_bf16(EstArgs a) {
   typedef __attribute__((address_space(3))) void* lds_ptr;
   __shared__ __align__(1024) char lds[4 * TILEB];  // buffer 0: K, Q; buffer 1: K, Q
 
-  const int bh = blockIdx.z;
+  // XCD-aware work unit: the 8 XCDs take consecutive workgroup ids
+  // round-robin, so logical unit (id % 8) * (n / 8) + id / 8 gives each XCD a
+  // contiguous range of (head, row tile, column tile) units -- with the
+  // column tile fastest, an XCD holds whole heads (typically one KV group),
+  // and its L2 fetches their Q and K once.
+  const int ntx = a.tiles_c, nty = a.tiles_r;
+  const int nwg = gridDim.x, id = blockIdx.x;
+  const int full = (nwg / 8) * 8;
+  const int logical = id < full ? (id % 8) * (nwg / 8) + id / 8 : id;
+  const int bx = logical % ntx, by = (logical / ntx) % nty, bh = logical / (ntx * nty);
   const int b = bh / a.hq, h = bh % a.hq, g = h / a.group;
   const int q0 = a.cu_q[b];
   const int lq = a.cu_q[b + 1] - q0;
   const int lk = a.cu_k[b + 1] - a.cu_k[b];
   const int R = lq / S, C = lk / S, o_s = (lk - lq) / S;
-  const int r0 = blockIdx.y * TT;
+  const int r0 = by * TT;
   if (r0 >= R) return;
-  const int c0 = a.jb0 * RB + blockIdx.x * TT;
+  const int c0 = a.jb0 * RB + bx * TT;
   const int c_end = min((a.jb0 + a.jb_count) * RB, C);
   if (c0 >= c_end) return;
   const int r_last = min(r0 + TT, R) - 1;
@@ -475,7 +484,10 @@ hipError_t est_dispatch(const EstArgs& a, int dtype, int batch, hipStream_t st) 
     dim3 big((a.jb_count * RB + kEstBig - 1) / kEstBig, (a.max_r + kEstBig - 1) / kEstBig, batch * a.hq);
     const long long nbig = (long long)big.x * big.y * big.z;
     if (nbig >= 256 && a.q_bytes < (1ll << 31) && a.k_bytes < (1ll << 31)) {
-      hipLaunchKernelGGL((est_gemm_bf16<D, S>), big, dim3(512), 0, st, a);
+      EstArgs a2 = a;
+      a2.tiles_c = (int)big.x;
+      a2.tiles_r = (int)big.y;
+      hipLaunchKernelGGL((est_gemm_bf16<D, S>), dim3((unsigned)nbig), dim3(512), 0, st, a2);
       return hipGetLastError();
     }
     dim3 grid((a.jb_count * RB + kEstTile - 1) / kEstTile, (a.max_r + kEstTile - 1) / kEstTile,

@@ -27,6 +27,8 @@ struct EstArgs {
   int max_r;
   long long q_bytes;  // bytes addressable from q
   long long k_bytes;  // bytes addressable from k.base
+  int tiles_c;        // big-tile GEMM: column tiles per head (set by the launcher)
+  int tiles_r;        // big-tile GEMM: row tiles per head
 };
 
 struct BlockSumArgs {
