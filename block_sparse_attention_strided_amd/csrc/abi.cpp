@@ -261,6 +261,29 @@ AttnArgs attn_args(const XattnShape* sh, const Plan& p, const void* q, KvView kv
   aa.vt = nullptr;
   aa.lists = nullptr;
   aa.num_pages = p.num_pages;
+  // Row order for the bf16 attention launch: (b, i) rows of all sequences,
+  // by the number of key blocks the row may see within [jb0, jb1), longest
+  // first (ties keep sequence order, q blocks descending).  One sequence
+  // keeps the kernel's default order, which is the same thing.
+  aa.n_order = 0;
+  if (p.batch > 1) {
+    std::vector<std::pair<int, int>> rows;  // (-length, b << 16 | i)
+    for (int b = 0; b < p.batch; ++b) {
+      const int lq = sh->cu_q_host[b + 1] - sh->cu_q_host[b];
+      const int lk = sh->cu_k_host[b + 1] - sh->cu_k_host[b];
+      const int qb = lq / XATTN_BLOCK, kh = (lk - lq) / XATTN_BLOCK;
+      for (int i = qb - 1; i >= 0; --i) {
+        const int len = std::max(0, std::min(jb1, i + kh + 1) - jb0);
+        rows.push_back({-len, (b << 16) | i});
+      }
+    }
+    std::stable_sort(rows.begin(), rows.end(),
+                     [](const std::pair<int, int>& x, const std::pair<int, int>& y) { return x.first < y.first; });
+    if (!rows.empty() && rows.size() <= (size_t)kMaxOrder && p.max_qb < 65536) {
+      aa.n_order = (int)rows.size();
+      for (size_t r = 0; r < rows.size(); ++r) aa.order[r] = rows[r].second;
+    }
+  }
   return aa;
 }
 

@@ -126,6 +126,48 @@ __device__ __forceinline__ void wait_vmcnt() {
   __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
 }
 
+// Work unit (sequence b, kv head g, head pair, q block i) of workgroup `id`.
+// With a row order from the host (a.order: (b, i) rows, longest causal row
+// first) and a multiple of 8 kv slots (g, pair), XCD id % 8 takes the slots
+// congruent to it (its L2 serves their K/V) and every XCD walks the same
+// longest-first row order, so heavy and light sequences are spread evenly
+// over the XCDs.  Otherwise: blocks of consecutive units per XCD, rows of
+// each sequence longest first.
+struct WorkUnit {
+  int b, g, pair, i;
+};
+__device__ __forceinline__ WorkUnit work_unit(const AttnArgs& a, int hkv, int npair, int id, int nwg) {
+  WorkUnit u;
+  const int ns = hkv * npair;
+  if (a.n_order > 0) {
+    int slot, r;
+    if (ns % 8 == 0 && nwg % 8 == 0) {
+      const int per = ns / 8, k = id / 8;
+      slot = (id % 8) + 8 * (k % per);
+      r = k / per;
+    } else {
+      slot = id % ns;
+      r = id / ns;
+    }
+    const int bi = a.order[r];
+    u.b = bi >> 16;
+    u.i = bi & 0xffff;
+    u.g = slot % hkv;
+    u.pair = slot / hkv;
+    return u;
+  }
+  const int full = (nwg / 8) * 8;
+  const int logical = id < full ? (id % 8) * (nwg / 8) + id / 8 : id;
+  const int irev = logical % a.max_qb;
+  int rest = logical / a.max_qb;
+  u.pair = rest % npair;
+  rest /= npair;
+  u.g = rest % hkv;
+  u.b = rest / hkv;
+  u.i = a.max_qb - 1 - irev;
+  return u;
+}
+
 // ---------------------------------------------------------------------------
 // V -> V^T pages.  Workgroup (page, kv head): [128 keys][d] -> [d][128].
 // ---------------------------------------------------------------------------
@@ -211,18 +253,9 @@ __global__ __launch_bounds__(256 * HPW) void attn_mfma(AttnArgs a, int hkv) {
   extern __shared__ int32_t list[];
 
   // ---- work unit (XCD-aware: the 8 XCDs take consecutive ids round-robin)
-  const int nwg = gridDim.x;
-  const int id = blockIdx.x;
-  const int full = (nwg / 8) * 8;
-  const int logical = id < full ? (id % 8) * (nwg / 8) + id / 8 : id;
   const int npair = a.group / HPW;
-  const int irev = logical % a.max_qb;
-  int rest = logical / a.max_qb;
-  const int pair = rest % npair;
-  rest /= npair;
-  const int g = rest % hkv;
-  const int b = rest / hkv;
-  const int i = a.max_qb - 1 - irev;  // heaviest (longest causal) rows first
+  const WorkUnit wk = work_unit(a, hkv, npair, blockIdx.x, gridDim.x);
+  const int pair = wk.pair, g = wk.g, b = wk.b, i = wk.i;
   const int q0 = a.cu_q[b];
   const int lq = a.cu_q[b + 1] - q0;
   if (i >= lq / kBlock) return;
@@ -497,18 +530,9 @@ __global__ __launch_bounds__(512) void attn_pp(AttnArgs a, int hkv) {
   extern __shared__ int32_t list[];
 
   // ---- work unit (XCD-aware: the 8 XCDs take consecutive ids round-robin)
-  const int nwg = gridDim.x;
-  const int id = blockIdx.x;
-  const int full = (nwg / 8) * 8;
-  const int logical = id < full ? (id % 8) * (nwg / 8) + id / 8 : id;
   const int npair = a.group / 2;
-  const int irev = logical % a.max_qb;
-  int rest = logical / a.max_qb;
-  const int pair = rest % npair;
-  rest /= npair;
-  const int g = rest % hkv;
-  const int b = rest / hkv;
-  const int i = a.max_qb - 1 - irev;  // heaviest (longest causal) rows first
+  const WorkUnit wk = work_unit(a, hkv, npair, blockIdx.x, gridDim.x);
+  const int pair = wk.pair, g = wk.g, b = wk.b, i = wk.i;
   const int q0 = a.cu_q[b];
   const int lq = a.cu_q[b + 1] - q0;
   if (i >= lq / kBlock) return;
@@ -1000,7 +1024,7 @@ hipError_t attn_dispatch(const AttnArgs& a, int dtype, int batch, hipStream_t s)
   if (dtype == 0) {
     const int hkv = a.hq / a.group;
     const int hpw = (a.group % 2 == 0) ? 2 : 1;
-    const int nwg = batch * hkv * (a.group / hpw) * a.max_qb;
+    const int nwg = (a.n_order > 0 ? a.n_order : batch * a.max_qb) * hkv * (a.group / hpw);
     const size_t shm = (size_t)(a.max_kb + 1) * sizeof(int32_t);
     // The ping-pong kernel addresses K and V^T with 32-bit buffer offsets.
     const long long span = (long long)a.num_pages * kBlock * hkv * D * 2;

@@ -90,6 +90,8 @@ struct PlanArgs {
 
 // Attention of one launch.  Keys come from blocks j in [jb0, jb1) whose mask
 // byte is set and whose page is present; rows are (b, q head, query).
+constexpr int kMaxOrder = 256;
+
 struct AttnArgs {
   const char* q;
   KvView k;
@@ -97,6 +99,10 @@ struct AttnArgs {
   const char* vt;         // bf16 path: transposed V pages (VtArgs layout)
   const int32_t* lists;   // bf16 path: block lists (PlanArgs layout)
   int num_pages;          // 128-key pages addressable through k.base / vt
+  // bf16 path: (b << 16 | i) rows in launch order, longest causal row first
+  // (n_order == 0: the kernel's default order)
+  int n_order;
+  int order[kMaxOrder];
   const uint8_t* mask;  // [batch, hkv, max_qb, max_kb]
   const int32_t* cu_q;
   const int32_t* cu_k;
