@@ -164,25 +164,49 @@ __device__ __forceinline__ u32x4 est_lds_read16(uint32_t addr) {
   return v;
 }
 template <int N>
-__device__ __forceinline__ void est_lgkm_wait(u32x4& a0, u32x4& a1, u32x4& a2, u32x4& a3, u32x4& a4, u32x4& a5) {
-  asm volatile("s_waitcnt lgkmcnt(%6)" : "+v"(a0), "+v"(a1), "+v"(a2), "+v"(a3), "+v"(a4), "+v"(a5) : "n"(N));
-}
-template <int N>
 __device__ __forceinline__ void est_wait_vmcnt() {
   __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
 }
 
+// wait until at most N LDS operations are outstanding; ties the M fragments
+template <int N, int M>
+__device__ __forceinline__ void est_lgkm_wait_arr(u32x4* f) {
+  if constexpr (M == 2) {
+    asm volatile("s_waitcnt lgkmcnt(%2)" : "+v"(f[0]), "+v"(f[1]) : "n"(N));
+  } else if constexpr (M == 4) {
+    asm volatile("s_waitcnt lgkmcnt(%4)" : "+v"(f[0]), "+v"(f[1]), "+v"(f[2]), "+v"(f[3]) : "n"(N));
+  } else {
+    static_assert(M == 6, "fragment count");
+    asm volatile("s_waitcnt lgkmcnt(%6)" : "+v"(f[0]), "+v"(f[1]), "+v"(f[2]), "+v"(f[3]), "+v"(f[4]), "+v"(f[5]) : "n"(N));
+  }
+}
+
+// LPW buffer -> LDS copies of 1 KiB (16 B per lane) to consecutive KiB of LDS
+template <int LPW>
+__device__ __forceinline__ void est_copy_rows(__amdgpu_buffer_rsrc_t r, char* lds, const uint32_t* voff, int soff) {
+  typedef __attribute__((address_space(3))) void* lds_ptr;
+#pragma unroll
+  for (int n = 0; n < LPW; ++n)
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_ptr)(lds + n * 1024), 16, voff[n], soff, 0, 0);
+}
+
 constexpr int kEstBig = 256;
 
-template <int D, int S>
-__global__ __launch_bounds__(512) void est_gemm_bf16(EstArgs a) {
+// TT x TT tile over NW waves: wave w owns TT/2 columns (half w&1) x 2*TT/NW
+// rows (part w>>1); XT x YT accumulators.
+template <int D, int S, int TT, int NW>
+__global__ __launch_bounds__(64 * NW) void est_gemm_bf16(EstArgs a) {
   constexpr int RB = kBlock / S;
-  constexpr int TT = kEstBig;        // rows and columns per workgroup
   constexpr int BK = 64;             // reduction elements per stage
-  constexpr int TILEB = TT * BK * 2; // bytes of one operand tile (32 KiB)
+  constexpr int TILEB = TT * BK * 2; // bytes of one operand tile
   constexpr int DQ = D / BK;         // stages per token offset
   constexpr int NST = S * DQ;        // stages (even for every supported S, D)
+  constexpr int WR = NW / 2;         // wave rows
+  constexpr int XT = TT / 2 / 32;    // 32-column accumulator tiles per wave
+  constexpr int YT = TT / WR / 32;   // 32-row accumulator tiles per wave
+  constexpr int LPW = TT / (8 * NW); // copy instructions per wave per operand
   static_assert(NST % 2 == 0, "stage loop is unrolled by two");
+  static_assert(XT >= 1 && YT >= 1 && LPW >= 1 && TT % (8 * NW) == 0, "tile / wave split");
   typedef __attribute__((address_space(3))) void* lds_ptr;
   __shared__ __align__(1024) char lds[4 * TILEB];  // buffer 0: K, Q; buffer 1: K, Q
 
@@ -214,14 +238,14 @@ __global__ __launch_bounds__(512) void est_gemm_bf16(EstArgs a) {
   const int wc = w & 1, wr = w >> 1;
   const int l32 = lane & 31, hh = lane >> 5;
 
-  // ---- copies: instruction n of wave w fills tile rows (4w+n)*8 .. +8
+  // ---- copies: instruction n of wave w fills tile rows (LPW*w+n)*8 .. +8
   const long long q_tok = (long long)a.hq * D * 2;
   const long long k_row = (long long)a.k.kv_heads * D * 2;
   constexpr uint32_t kOut = 0x80000000u;  // beyond either descriptor's bound
-  uint32_t kvo[4], qvo[4];
+  uint32_t kvo[LPW], qvo[LPW];
 #pragma unroll
-  for (int n = 0; n < 4; ++n) {
-    const int row = (w * 4 + n) * 8 + (lane >> 3);
+  for (int n = 0; n < LPW; ++n) {
+    const int row = (w * LPW + n) * 8 + (lane >> 3);
     const int lc = (lane & 7) ^ (row & 7);  // logical chunk stored at this lane's position
     const int c = c0 + row, r = r0 + row;
     kvo[n] = kOut;
@@ -240,12 +264,10 @@ __global__ __launch_bounds__(512) void est_gemm_bf16(EstArgs a) {
     const int t = st / DQ, dq = st - (st / DQ) * DQ;
     const int so_k = (int)(t * k_row) + dq * BK * 2;
     const int so_q = (int)((S - 1 - t) * q_tok) + dq * BK * 2;
-    char* kd = lds + bf * 2 * TILEB + wu * 4 * 1024;
+    char* kd = lds + bf * 2 * TILEB + wu * LPW * 1024;
     char* qd = kd + TILEB;
-#pragma unroll
-    for (int n = 0; n < 4; ++n) __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (lds_ptr)(kd + n * 1024), 16, kvo[n], so_k, 0, 0);
-#pragma unroll
-    for (int n = 0; n < 4; ++n) __builtin_amdgcn_raw_ptr_buffer_load_lds(rq, (lds_ptr)(qd + n * 1024), 16, qvo[n], so_q, 0, 0);
+    est_copy_rows<LPW>(rk, kd, kvo, so_k);
+    est_copy_rows<LPW>(rq, qd, qvo, so_q);
   };
 
   // ---- fragment addresses: row swizzle = l32 & 7 for every tile row a lane reads
@@ -256,49 +278,49 @@ __global__ __launch_bounds__(512) void est_gemm_bf16(EstArgs a) {
 #pragma unroll
     for (int kk = 0; kk < 4; ++kk) {
       const uint32_t ch = (uint32_t)(((2 * kk + hh) ^ (l32 & 7)) * 16);
-      ka[bf][kk] = lds0 + bf * 2 * TILEB + (wc * 128 + l32) * 128 + ch;
-      qa[bf][kk] = lds0 + bf * 2 * TILEB + TILEB + (wr * 64 + l32) * 128 + ch;
+      ka[bf][kk] = lds0 + bf * 2 * TILEB + (wc * (TT / 2) + l32) * 128 + ch;
+      qa[bf][kk] = lds0 + bf * 2 * TILEB + TILEB + (wr * (YT * 32) + l32) * 128 + ch;
     }
 
-  f32x16 acc[4][2];
+  f32x16 acc[XT][YT];
 #pragma unroll
-  for (int x = 0; x < 4; ++x)
+  for (int x = 0; x < XT; ++x)
 #pragma unroll
-    for (int y = 0; y < 2; ++y)
+    for (int y = 0; y < YT; ++y)
 #pragma unroll
       for (int e = 0; e < 16; ++e) acc[x][y][e] = 0.f;
 
-  // one stage: 4 k-steps of 16; k-step kk+1's six fragments are read while
-  // k-step kk's eight MFMAs issue
+  // one stage: 4 k-steps of 16; k-step kk+1's XT + YT fragments are read
+  // while k-step kk's XT * YT MFMAs issue
+  constexpr int NF = XT + YT;
   auto compute = [&](auto bf_tag) {
     constexpr int BF = decltype(bf_tag)::value;
-    u32x4 f0 = est_lds_read16<0>(ka[BF][0]), f1 = est_lds_read16<4096>(ka[BF][0]);
-    u32x4 f2 = est_lds_read16<8192>(ka[BF][0]), f3 = est_lds_read16<12288>(ka[BF][0]);
-    u32x4 f4 = est_lds_read16<0>(qa[BF][0]), f5 = est_lds_read16<4096>(qa[BF][0]);
+    u32x4 f[NF], gq[NF];
+    auto rd = [&](u32x4* dst, int kk) {
+      [&]<int... X>(std::integer_sequence<int, X...>) {
+        ((dst[X] = est_lds_read16<X * 4096>(ka[BF][kk])), ...);
+      }(std::make_integer_sequence<int, XT>{});
+      [&]<int... Y>(std::integer_sequence<int, Y...>) {
+        ((dst[XT + Y] = est_lds_read16<Y * 4096>(qa[BF][kk])), ...);
+      }(std::make_integer_sequence<int, YT>{});
+    };
+    rd(f, 0);
 #pragma unroll
     for (int kk = 0; kk < 4; ++kk) {
-      u32x4 g0, g1, g2, g3, g4, g5;
       if (kk + 1 < 4) {
-        const int k1 = kk + 1 < 4 ? kk + 1 : 0;
-        g0 = est_lds_read16<0>(ka[BF][k1]);
-        g1 = est_lds_read16<4096>(ka[BF][k1]);
-        g2 = est_lds_read16<8192>(ka[BF][k1]);
-        g3 = est_lds_read16<12288>(ka[BF][k1]);
-        g4 = est_lds_read16<0>(qa[BF][k1]);
-        g5 = est_lds_read16<4096>(qa[BF][k1]);
-        est_lgkm_wait<6>(f0, f1, f2, f3, f4, f5);
+        rd(gq, kk + 1 < 4 ? kk + 1 : 0);
+        est_lgkm_wait_arr<NF, NF>(f);
       } else {
-        est_lgkm_wait<0>(f0, f1, f2, f3, f4, f5);
+        est_lgkm_wait_arr<0, NF>(f);
       }
-      const bf16x8 kf[4] = {__builtin_bit_cast(bf16x8, f0), __builtin_bit_cast(bf16x8, f1),
-                            __builtin_bit_cast(bf16x8, f2), __builtin_bit_cast(bf16x8, f3)};
-      const bf16x8 qf[2] = {__builtin_bit_cast(bf16x8, f4), __builtin_bit_cast(bf16x8, f5)};
 #pragma unroll
-      for (int x = 0; x < 4; ++x)
+      for (int x = 0; x < XT; ++x)
 #pragma unroll
-        for (int y = 0; y < 2; ++y) acc[x][y] = mfma32(kf[x], qf[y], acc[x][y]);
+        for (int y = 0; y < YT; ++y)
+          acc[x][y] = mfma32(__builtin_bit_cast(bf16x8, f[x]), __builtin_bit_cast(bf16x8, f[XT + y]), acc[x][y]);
       if (kk + 1 < 4) {
-        f0 = g0; f1 = g1; f2 = g2; f3 = g3; f4 = g4; f5 = g5;
+#pragma unroll
+        for (int z = 0; z < NF; ++z) f[z] = gq[z];
       }
     }
   };
@@ -324,11 +346,11 @@ __global__ __launch_bounds__(512) void est_gemm_bf16(EstArgs a) {
   constexpr int EPB = 16 / NBLK; // accumulator values per lane and block
   const int j_end = a.jb0 + a.jb_count;
 #pragma unroll
-  for (int y = 0; y < 2; ++y) {
-    const int r = r0 + wr * 64 + y * 32 + l32;
+  for (int y = 0; y < YT; ++y) {
+    const int r = r0 + wr * (YT * 32) + y * 32 + l32;
 #pragma unroll
-    for (int x = 0; x < 4; ++x) {
-      const int cblk = c0 + wc * 128 + x * 32;
+    for (int x = 0; x < XT; ++x) {
+      const int cblk = c0 + wc * (TT / 2) + x * 32;
 #pragma unroll
       for (int m = 0; m < NBLK; ++m) {
         float z[EPB];
@@ -479,15 +501,22 @@ template <int D, int S>
 hipError_t est_dispatch(const EstArgs& a, int dtype, int batch, hipStream_t st) {
   constexpr int RB = kBlock / S;
   if (dtype == 0) {
-    // Large launches: 256 x 256 tiles when they still fill the chip and both
-    // operands fit 32-bit buffer offsets; otherwise 128 x 128 tiles.
-    dim3 big((a.jb_count * RB + kEstBig - 1) / kEstBig, (a.max_r + kEstBig - 1) / kEstBig, batch * a.hq);
-    const long long nbig = (long long)big.x * big.y * big.z;
-    if (nbig >= 256 && a.q_bytes < (1ll << 31) && a.k_bytes < (1ll << 31)) {
+    // 256 x 256 tiles (8 waves) when they still fill the chip, else 128 x 128
+    // tiles (4 waves); both need Q and K spans within 31-bit buffer offsets.
+    if (a.q_bytes < (1ll << 31) && a.k_bytes < (1ll << 31)) {
+      dim3 big((a.jb_count * RB + kEstBig - 1) / kEstBig, (a.max_r + kEstBig - 1) / kEstBig, batch * a.hq);
+      const long long nbig = (long long)big.x * big.y * big.z;
       EstArgs a2 = a;
-      a2.tiles_c = (int)big.x;
-      a2.tiles_r = (int)big.y;
-      hipLaunchKernelGGL((est_gemm_bf16<D, S>), dim3((unsigned)nbig), dim3(512), 0, st, a2);
+      if (nbig >= 256) {
+        a2.tiles_c = (int)big.x;
+        a2.tiles_r = (int)big.y;
+        hipLaunchKernelGGL((est_gemm_bf16<D, S, kEstBig, 8>), dim3((unsigned)nbig), dim3(512), 0, st, a2);
+      } else {
+        a2.tiles_c = (a.jb_count * RB + kEstTile - 1) / kEstTile;
+        a2.tiles_r = (a.max_r + kEstTile - 1) / kEstTile;
+        const long long n = (long long)a2.tiles_c * a2.tiles_r * batch * a.hq;
+        hipLaunchKernelGGL((est_gemm_bf16<D, S, kEstTile, 4>), dim3((unsigned)n), dim3(256), 0, st, a2);
+      }
       return hipGetLastError();
     }
     dim3 grid((a.jb_count * RB + kEstTile - 1) / kEstTile, (a.max_r + kEstTile - 1) / kEstTile,
