@@ -261,28 +261,10 @@ AttnArgs attn_args(const XattnShape* sh, const Plan& p, const void* q, KvView kv
   aa.vt = nullptr;
   aa.lists = nullptr;
   aa.num_pages = p.num_pages;
-  // Row order for the bf16 attention launch: (b, i) rows of all sequences,
-  // by the number of key blocks the row may see within [jb0, jb1), longest
-  // first (ties keep sequence order, q blocks descending).  One sequence
-  // keeps the kernel's default order, which is the same thing.
   aa.n_order = 0;
-  if (p.batch > 1) {
-    std::vector<std::pair<int, int>> rows;  // (-length, b << 16 | i)
-    for (int b = 0; b < p.batch; ++b) {
-      const int lq = sh->cu_q_host[b + 1] - sh->cu_q_host[b];
-      const int lk = sh->cu_k_host[b + 1] - sh->cu_k_host[b];
-      const int qb = lq / XATTN_BLOCK, kh = (lk - lq) / XATTN_BLOCK;
-      for (int i = qb - 1; i >= 0; --i) {
-        const int len = std::max(0, std::min(jb1, i + kh + 1) - jb0);
-        rows.push_back({-len, (b << 16) | i});
-      }
-    }
-    std::stable_sort(rows.begin(), rows.end(),
-                     [](const std::pair<int, int>& x, const std::pair<int, int>& y) { return x.first < y.first; });
-    if (!rows.empty() && rows.size() <= (size_t)kMaxOrder && p.max_qb < 65536) {
-      aa.n_order = (int)rows.size();
-      for (size_t r = 0; r < rows.size(); ++r) aa.order[r] = rows[r].second;
-    }
+  for (int x = 0; x < 3; ++x) {
+    aa.split_o[x] = nullptr;
+    aa.split_l[x] = nullptr;
   }
   return aa;
 }
@@ -320,10 +302,107 @@ hipError_t plan_attention(const XattnShape* sh, const Plan& p, const AttnArgs& a
   return hipSuccess;
 }
 
-hipError_t launch_planned(const Plan& p, AttnArgs aa, void* ws, hipStream_t st) {
+int device_cu_count() {
+  static int cache[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
+  if (cache[dev] == 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) n = 0;
+    cache[dev] = n;
+  }
+  return cache[dev];
+}
+
+// Launch order of the bf16 attention's rows and the split of long rows.
+// A row's length is the number of key blocks it may see in [jb0, jb1) (the
+// causal bound; the selection only shortens it).  Rows go longest first
+// (ties keep sequence order, q blocks descending), so that the workgroups
+// dispatched last are the short ones.  When the launch writes the final
+// output and its longest row is well above the per-CU share of the launch
+// (total row-blocks x workgroups per row / CUs) -- a single causal sequence
+// whose long rows would set the launch time -- rows longer than
+// bmax = max(share, longest / 3) are cut into ns = ceil(length / bmax) <= 3
+// parts whose partial outputs a split merge combines (the merge rule of
+// partial attention results).  One sequence without splits keeps the
+// kernel's default order, which is the same order.
+void set_order(const XattnShape* sh, const Plan& p, AttnArgs& aa, void* ws, SplitMergeArgs* sm) {
+  sm->n = 0;
+  aa.n_order = 0;
+  struct Row {
+    int len, b, i;
+  };
+  std::vector<Row> rows;
+  long long total = 0;
+  int lmax = 0;
+  for (int b = 0; b < p.batch; ++b) {
+    const int lq = sh->cu_q_host[b + 1] - sh->cu_q_host[b];
+    const int lk = sh->cu_k_host[b + 1] - sh->cu_k_host[b];
+    const int qb = lq / XATTN_BLOCK, kh = (lk - lq) / XATTN_BLOCK;
+    for (int i = qb - 1; i >= 0; --i) {
+      const int len = std::max(0, std::min(aa.jb1, i + kh + 1) - aa.jb0);
+      rows.push_back({len, b, i});
+      total += len;
+      lmax = std::max(lmax, len);
+    }
+  }
+  if (rows.empty() || p.batch >= 4096 || p.max_qb >= 65536) return;
+  const int group = p.hq / p.hkv;
+  const int per_row = p.hkv * (group / ((group % 2 == 0) ? 2 : 1));
+  const int cus = device_cu_count();
+  int bmax = 0;  // 0: no splits
+  if (aa.out && !aa.out_f32 && cus > 0) {
+    const double share = (double)total * per_row / cus;
+    if (lmax >= 4 && lmax > 1.25 * share) bmax = std::max({(int)std::ceil(share), (lmax + 2) / 3, 2});
+  }
+  std::vector<std::pair<int, uint32_t>> items;  // (-part length, order entry)
+  int nsplit = 0;
+  for (const Row& r : rows) {
+    const int ns = (bmax > 0 && r.len > bmax) ? std::min(3, (r.len + bmax - 1) / bmax) : 1;
+    for (int x = 0; x < ns; ++x)
+      items.push_back({-(((x + 1) * r.len) / ns - (x * r.len) / ns), order_entry(r.b, r.i, x, ns)});
+    if (ns > 1) {
+      if (nsplit < kMaxOrder) sm->rows[nsplit] = (sh->cu_q_host[r.b] / XATTN_BLOCK + r.i) | ((ns - 1) << 28);
+      ++nsplit;
+    }
+  }
+  if (items.size() > (size_t)kMaxOrder) {
+    // too many parts for the order table: no splits, plain rows if they fit
+    if (p.batch == 1 || rows.size() > (size_t)kMaxOrder) return;
+    items.clear();
+    for (const Row& r : rows) items.push_back({-r.len, order_entry(r.b, r.i, 0, 1)});
+    nsplit = 0;
+  }
+  if (p.batch == 1 && nsplit == 0) return;
+  std::stable_sort(items.begin(), items.end(),
+                   [](const std::pair<int, uint32_t>& x, const std::pair<int, uint32_t>& y) { return x.first < y.first; });
+  aa.n_order = (int)items.size();
+  for (size_t r = 0; r < items.size(); ++r) aa.order[r] = (int)items[r].second;
+  if (nsplit > 0) {
+    for (int x = 0; x < 3; ++x) {
+      aa.split_o[x] = ws_at<float>(ws, p.off_o[x]);
+      aa.split_l[x] = ws_at<float>(ws, p.off_l[x]);
+      sm->o[x] = aa.split_o[x];
+      sm->l[x] = aa.split_l[x];
+    }
+    sm->n = nsplit;
+    sm->heads = p.hq;
+    sm->head_dim = p.d;
+    sm->total_q = p.total_q;
+    sm->out = aa.out;
+    sm->lse = aa.lse;
+  }
+}
+
+hipError_t launch_planned(const XattnShape* sh, const Plan& p, AttnArgs aa, void* ws, hipStream_t st) {
   aa.vt = ws_at<char>(ws, p.off_vt);
   aa.lists = ws_at<int32_t>(ws, p.off_lists);
-  return launch_attention(aa, p.dtype == XATTN_DTYPE_BF16 ? 0 : 1, p.d, p.batch, st);
+  SplitMergeArgs sm;
+  sm.n = 0;
+  if (p.dtype == XATTN_DTYPE_BF16) set_order(sh, p, aa, ws, &sm);
+  hipError_t e = launch_attention(aa, p.dtype == XATTN_DTYPE_BF16 ? 0 : 1, p.d, p.batch, st);
+  if (e != hipSuccess || sm.n == 0) return e;
+  return launch_split_merge(sm, st);
 }
 
 // Attention over blocks [jb0, jb1) of `mask`: prepare (bf16), then attend.
@@ -332,7 +411,7 @@ hipError_t run_attention(const XattnShape* sh, const Plan& p, AttnArgs aa, const
   aa.num_pages = num_pages;
   hipError_t e = plan_attention(sh, p, aa, v, num_pages, ws, transpose_v, st);
   if (e != hipSuccess) return e;
-  return launch_planned(p, aa, ws, st);
+  return launch_planned(sh, p, aa, ws, st);
 }
 
 }  // namespace
@@ -649,7 +728,7 @@ int xattn_attn_run(const XattnShape* shape, const XattnParams* params, const voi
   if (p.dtype == XATTN_DTYPE_BF16) aa.out = out;
   else aa.out_f32 = (float*)out;
   aa.lse = lse;
-  hipError_t e = launch_planned(p, aa, ws, (hipStream_t)stream);
+  hipError_t e = launch_planned(shape, p, aa, ws, (hipStream_t)stream);
   if (e != hipSuccess) return hip_fail(e, "attention launch");
   return XATTN_OK;
 }

@@ -28,6 +28,9 @@ namespace xattn {
 namespace {
 
 constexpr float kNegInf = -__builtin_huge_valf();
+#ifndef XATTN_ILV
+#define XATTN_ILV 0
+#endif
 #ifndef XATTN_PF
 #define XATTN_PF 6
 #endif
@@ -133,8 +136,10 @@ __device__ __forceinline__ void wait_vmcnt() {
 // longest-first row order, so heavy and light sequences are spread evenly
 // over the XCDs.  Otherwise: blocks of consecutive units per XCD, rows of
 // each sequence longest first.
+// A row may be split into ns parts (part s of ns equal parts of its block
+// list); the host splits only rows it lists in the order.
 struct WorkUnit {
-  int b, g, pair, i;
+  int b, g, pair, i, s, ns;
 };
 __device__ __forceinline__ WorkUnit work_unit(const AttnArgs& a, int hkv, int npair, int id, int nwg) {
   WorkUnit u;
@@ -149,9 +154,11 @@ __device__ __forceinline__ WorkUnit work_unit(const AttnArgs& a, int hkv, int np
       slot = id % ns;
       r = id / ns;
     }
-    const int bi = a.order[r];
-    u.b = bi >> 16;
-    u.i = bi & 0xffff;
+    const uint32_t e = (uint32_t)a.order[r];
+    u.b = (int)((e >> 16) & 0xfffu);
+    u.i = (int)(e & 0xffffu);
+    u.s = (int)((e >> 28) & 3u);
+    u.ns = (int)(e >> 30) + 1;
     u.g = slot % hkv;
     u.pair = slot / hkv;
     return u;
@@ -165,7 +172,22 @@ __device__ __forceinline__ WorkUnit work_unit(const AttnArgs& a, int hkv, int np
   u.g = rest % hkv;
   u.b = rest / hkv;
   u.i = a.max_qb - 1 - irev;
+  u.s = 0;
+  u.ns = 1;
   return u;
+}
+
+// Part s of ns of a row's block list, copied to LDS: list[0] = its count,
+// list[1..] its entries.  The parts are consecutive runs of the list, as even
+// as integer division makes them; the diagonal block (the last entry) falls
+// in the last part.  The caller synchronises before reading `list`.
+__device__ __forceinline__ int load_row_list(const int32_t* glist, int32_t* list, int s, int ns, int tid,
+                                             int nthreads) {
+  const int nall = glist[0];
+  const int z0 = (s * nall) / ns;
+  const int n = ((s + 1) * nall) / ns - z0;
+  for (int z = tid; z <= n; z += nthreads) list[z] = (z == 0) ? n : glist[z0 + z];
+  return n;
 }
 
 // ---------------------------------------------------------------------------
@@ -269,8 +291,7 @@ __global__ __launch_bounds__(256 * HPW) void attn_mfma(AttnArgs a, int hkv) {
 
   // Block list of this row, copied to LDS.
   const int32_t* glist = a.lists + (((long long)b * hkv + g) * a.max_qb + i) * (a.max_kb + 1);
-  const int nblk = glist[0];
-  for (int z = tid; z <= nblk; z += 64 * NW) list[z] = glist[z];
+  const int nblk = load_row_list(glist, list, wk.s, wk.ns, tid, 64 * NW);
   __syncthreads();
   const int ntile = 2 * nblk;
   // The diagonal block, if present, is the last entry: only its two tiles
@@ -467,6 +488,8 @@ __global__ __launch_bounds__(256 * HPW) void attn_mfma(AttnArgs a, int hkv) {
   const float l_tot = l_run + __shfl_xor(l_run, 32, 64);
   const float inv = (l_tot > 0.f) ? 1.f / l_tot : 0.f;
   const long long orow = ((long long)(q0 + x) * a.hq + h) * D;
+  float* const of32 = wk.ns > 1 ? a.split_o[wk.s] : a.out_f32;
+  float* const lsep = wk.ns > 1 ? a.split_l[wk.s] : a.lse;
 #pragma unroll
   for (int n = 0; n < D / 32; ++n)
 #pragma unroll
@@ -474,9 +497,9 @@ __global__ __launch_bounds__(256 * HPW) void attn_mfma(AttnArgs a, int hkv) {
       const int d = n * 32 + 8 * ii + 4 * hh;
       const float v0 = oacc[n][4 * ii + 0] * inv, v1 = oacc[n][4 * ii + 1] * inv;
       const float v2 = oacc[n][4 * ii + 2] * inv, v3 = oacc[n][4 * ii + 3] * inv;
-      if (a.out_f32) {
+      if (of32) {
         f32x4 v = {v0, v1, v2, v3};
-        *(f32x4*)(a.out_f32 + orow + d) = v;
+        *(f32x4*)(of32 + orow + d) = v;
       } else {
         typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
         bf16x4 o4;
@@ -487,9 +510,9 @@ __global__ __launch_bounds__(256 * HPW) void attn_mfma(AttnArgs a, int hkv) {
         *(bf16x4*)((char*)a.out + (orow + d) * 2) = o4;
       }
     }
-  if (a.lse && hh == 0) {
+  if (lsep && hh == 0) {
     const float lse = (l_tot > 0.f) ? (m_run + log2f(l_tot)) * kLn2 : kNegInf;
-    a.lse[(long long)h * a.total_q + q0 + x] = lse;
+    lsep[(long long)h * a.total_q + q0 + x] = lse;
   }
 }
 
@@ -546,8 +569,7 @@ __global__ __launch_bounds__(512) void attn_pp(AttnArgs a, int hkv) {
 
   // Block list of this row, copied to LDS.
   const int32_t* glist = a.lists + (((long long)b * hkv + g) * a.max_qb + i) * (a.max_kb + 1);
-  const int nblk = glist[0];
-  for (int z = tid; z <= nblk; z += 64 * NW) list[z] = glist[z];
+  const int nblk = load_row_list(glist, list, wk.s, wk.ns, tid, 64 * NW);
   __syncthreads();
   const int ntile = 2 * nblk;
   // The diagonal block, if present, is the last entry: only its two tiles
@@ -728,8 +750,9 @@ __global__ __launch_bounds__(512) void attn_pp(AttnArgs a, int hkv) {
     }(std::make_integer_sequence<int, NOPS>{});
   };
 
-  // ---- softmax of tile u: S^T registers -> P^T (bf16) in pb
-  auto smax = [&](int u) {
+  // ---- softmax of tile u: S^T registers -> P^T (bf16) in pb; hook(C) runs
+  // before exponential chunk C (of 4)
+  auto smax = [&](int u, auto hook) {
     const bool diag = u >= first_diag;
     const int sub = u & 1;
     if (diag) {
@@ -741,17 +764,21 @@ __global__ __launch_bounds__(512) void attn_pp(AttnArgs a, int hkv) {
         if (key + 32 > xq) s1[z] = kNegInf;
       }
     }
-    // Row max: four independent chains (the wave runs alone on the VALU of
-    // its SIMD in this phase, so dependency latency, not issue, is the cost);
-    // IEEE maximum lowers to v_maximum3_f32 without operand canonicalisation.
-    float mq[4];
+    // Row max as a tree of three-input maxima (IEEE maximum lowers to
+    // v_maximum3_f32 without operand canonicalisation): 17 instructions for
+    // the 32 values of a lane.
+    auto mx3 = [](float p, float q, float r) {
+      return __builtin_elementwise_maximum(__builtin_elementwise_maximum(p, q), r);
+    };
+    float t[11];
 #pragma unroll
-    for (int c = 0; c < 4; ++c) mq[c] = __builtin_elementwise_maximum(s0[c], s1[c]);
-#pragma unroll
-    for (int z = 4; z < 16; ++z)
-      mq[z & 3] = __builtin_elementwise_maximum(mq[z & 3], __builtin_elementwise_maximum(s0[z], s1[z]));
-    float mx = __builtin_elementwise_maximum(__builtin_elementwise_maximum(mq[0], mq[1]),
-                                             __builtin_elementwise_maximum(mq[2], mq[3]));
+    for (int k = 0; k < 5; ++k) {
+      t[k] = mx3(s0[3 * k], s0[3 * k + 1], s0[3 * k + 2]);
+      t[5 + k] = mx3(s1[3 * k], s1[3 * k + 1], s1[3 * k + 2]);
+    }
+    t[10] = __builtin_elementwise_maximum(s0[15], s1[15]);
+    float mx = __builtin_elementwise_maximum(mx3(mx3(t[0], t[1], t[2]), mx3(t[3], t[4], t[5]), mx3(t[6], t[7], t[8])),
+                                             __builtin_elementwise_maximum(t[9], t[10]));
     mx = half_max(mx);
     const float m_tile = mx * c2;
     if (__ballot(m_tile > m_run + 8.0f) != 0ull) {
@@ -767,19 +794,22 @@ __global__ __launch_bounds__(512) void attn_pp(AttnArgs a, int hkv) {
     const float mneg = (m_run == kNegInf) ? 0.f : -m_run;
     // Row sum of the fp32 probabilities (rounding them to bf16 first would
     // move the LSE of short rows by up to half a bf16 ulp), four chains.
-    float ps[4] = {0.f, 0.f, 0.f, 0.f};
+    float ps[4];
+    auto chunk = [&](auto c_tag) {
+      constexpr int C = decltype(c_tag)::value;
+      hook(c_tag);
 #pragma unroll
-    for (int z = 0; z < 8; ++z) {
-      s0[z] = fast_exp2(fmaf(s0[z], c2, mneg));
-      s1[z] = fast_exp2(fmaf(s1[z], c2, mneg));
-      ps[z & 3] += s0[z] + s1[z];
-    }
-#pragma unroll
-    for (int z = 8; z < 16; ++z) {
-      s0[z] = fast_exp2(fmaf(s0[z], c2, mneg));
-      s1[z] = fast_exp2(fmaf(s1[z], c2, mneg));
-      ps[z & 3] += s0[z] + s1[z];
-    }
+      for (int z = 4 * C; z < 4 * C + 4; ++z) {
+        s0[z] = fast_exp2(fmaf(s0[z], c2, mneg));
+        s1[z] = fast_exp2(fmaf(s1[z], c2, mneg));
+        if constexpr (C == 0) ps[z & 3] = s0[z] + s1[z];
+        else ps[z & 3] += s0[z] + s1[z];
+      }
+    };
+    chunk(std::integral_constant<int, 0>{});
+    chunk(std::integral_constant<int, 1>{});
+    chunk(std::integral_constant<int, 2>{});
+    chunk(std::integral_constant<int, 3>{});
 #pragma unroll
     for (int m = 0; m < 4; ++m) {
       const int i0 = 2 * (m & 1);
@@ -825,8 +855,24 @@ __global__ __launch_bounds__(512) void attn_pp(AttnArgs a, int hkv) {
   // phase (copy group u, softmax of S(u)), barrier.  Tile 0 (S only) is
   // peeled so that the loop has one MFMA-phase shape.
   auto softmax_phase = [&](int u) {
-    copy_group(u);
-    smax(u);
+    if constexpr (XATTN_ILV) {
+      // copy parts spread over the exponentials: a burst of direct loads
+      // stalls the issuing wave until the vector memory path drains
+      group_setup(u);
+      smax(u, [&](auto c_tag) {
+        constexpr int C = decltype(c_tag)::value, P = 2 * LPW;
+        if constexpr ((C * P) % 4 == 0) {
+          __builtin_amdgcn_sched_barrier(0);
+          [&]<int... N>(std::integer_sequence<int, N...>) {
+            (copy_part(std::integral_constant<int, C * P / 4 + N>{}), ...);
+          }(std::make_integer_sequence<int, (P >= 4 ? P / 4 : 1)>{});
+          __builtin_amdgcn_sched_barrier(0);
+        }
+      });
+    } else {
+      copy_group(u);
+      smax(u, [](auto) {});
+    }
     fence_smax();
   };
   if (ntile > 0) {
@@ -858,6 +904,8 @@ __global__ __launch_bounds__(512) void attn_pp(AttnArgs a, int hkv) {
   const float l_tot = half_sum(l_run);
   const float inv = (l_tot > 0.f) ? 1.f / l_tot : 0.f;
   const long long orow = ((long long)(q0 + x) * a.hq + h) * D;
+  float* const of32 = wk.ns > 1 ? a.split_o[wk.s] : a.out_f32;
+  float* const lsep = wk.ns > 1 ? a.split_l[wk.s] : a.lse;
 #pragma unroll
   for (int n = 0; n < D / 32; ++n)
 #pragma unroll
@@ -865,9 +913,9 @@ __global__ __launch_bounds__(512) void attn_pp(AttnArgs a, int hkv) {
       const int d = n * 32 + 8 * ii + 4 * hh;
       const float v0 = oacc[n][4 * ii + 0] * inv, v1 = oacc[n][4 * ii + 1] * inv;
       const float v2 = oacc[n][4 * ii + 2] * inv, v3 = oacc[n][4 * ii + 3] * inv;
-      if (a.out_f32) {
+      if (of32) {
         f32x4 v = {v0, v1, v2, v3};
-        *(f32x4*)(a.out_f32 + orow + d) = v;
+        *(f32x4*)(of32 + orow + d) = v;
       } else {
         typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
         bf16x4 o4;
@@ -878,9 +926,9 @@ __global__ __launch_bounds__(512) void attn_pp(AttnArgs a, int hkv) {
         *(bf16x4*)((char*)a.out + (orow + d) * 2) = o4;
       }
     }
-  if (a.lse && hh == 0) {
+  if (lsep && hh == 0) {
     const float lse = (l_tot > 0.f) ? (m_run + log2f(l_tot)) * kLn2 : kNegInf;
-    a.lse[(long long)h * a.total_q + q0 + x] = lse;
+    lsep[(long long)h * a.total_q + q0 + x] = lse;
   }
 }
 
@@ -1019,6 +1067,54 @@ __global__ __launch_bounds__(256) void merge_kernel(MergeArgs a) {
   if (a.lse && dv == 0) a.lse[(long long)h * a.rows + r] = lse;
 }
 
+// Split rows: one thread per 4 consecutive d of one (query, head) of a
+// listed row (grid y: the row); the ns partial LSEs give the weights exp(lse_s - lse) with
+// lse = m + log(sum_s exp(lse_s - m)), m the largest partial LSE.
+__global__ __launch_bounds__(256) void split_merge_kernel(SplitMergeArgs a) {
+  const int dq = a.head_dim / 4;
+  const int per_row = kBlock * a.heads * dq;
+  const int r = blockIdx.y;
+  const int rem = blockIdx.x * 256 + threadIdx.x;
+  if (rem >= per_row) return;
+  const int dv = rem % dq, qh = rem / dq;
+  const int h = qh % a.heads, xq = qh / a.heads;
+  const uint32_t e = (uint32_t)a.rows[r];
+  const int ns = (int)(e >> 28) + 1;
+  const long long tok = (long long)(e & 0x0fffffffu) * kBlock + xq;
+  const long long li = (long long)h * a.total_q + tok;
+  const long long off = (tok * a.heads + h) * a.head_dim + dv * 4;
+  // fixed trip counts keep the per-part values in registers
+  float l[3], w[3];
+  float mx = kNegInf;
+#pragma unroll
+  for (int s = 0; s < 3; ++s) {
+    l[s] = (s < ns) ? a.l[s][li] : kNegInf;
+    mx = fmaxf(mx, l[s]);
+  }
+  float lse = kNegInf;
+  f32x4 res = {0.f, 0.f, 0.f, 0.f};
+  if (mx != kNegInf) {
+    float sum = 0.f;
+#pragma unroll
+    for (int s = 0; s < 3; ++s) sum += (l[s] == kNegInf) ? 0.f : expf(l[s] - mx);
+    lse = mx + logf(sum);
+#pragma unroll
+    for (int s = 0; s < 3; ++s) w[s] = (l[s] == kNegInf) ? 0.f : expf(l[s] - lse);
+#pragma unroll
+    for (int s = 0; s < 3; ++s) {
+      if (w[s] != 0.f) {
+        const f32x4 o = *(const f32x4*)(a.o[s] + off);
+#pragma unroll
+        for (int c = 0; c < 4; ++c) res[c] = fmaf(w[s], o[c], res[c]);
+      }
+    }
+  }
+  uint32_t* p = (uint32_t*)((char*)a.out + off * 2);
+  p[0] = pack_bf16x2(res[0], res[1]);
+  p[1] = pack_bf16x2(res[2], res[3]);
+  if (a.lse && dv == 0) a.lse[(long long)h * a.total_q + tok] = lse;
+}
+
 template <int D>
 hipError_t attn_dispatch(const AttnArgs& a, int dtype, int batch, hipStream_t s) {
   if (dtype == 0) {
@@ -1060,6 +1156,14 @@ hipError_t launch_vt_transpose(const VtArgs& a, hipStream_t s) {
 hipError_t launch_plan(const PlanArgs& a, int batch, hipStream_t s) {
   if (a.max_qb <= 0 || batch <= 0) return hipSuccess;
   hipLaunchKernelGGL(plan_kernel, dim3(a.max_qb, a.hkv, batch), dim3(64), 0, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_split_merge(const SplitMergeArgs& a, hipStream_t s) {
+  const long long per_row = (long long)kBlock * a.heads * (a.head_dim / 4);
+  if (a.n <= 0 || per_row <= 0) return hipSuccess;
+  if (per_row >= (1ll << 31)) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(split_merge_kernel, dim3((unsigned)((per_row + 255) / 256), a.n), dim3(256), 0, s, a);
   return hipGetLastError();
 }
 

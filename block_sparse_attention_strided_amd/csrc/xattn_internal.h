@@ -99,10 +99,16 @@ struct AttnArgs {
   const char* vt;         // bf16 path: transposed V pages (VtArgs layout)
   const int32_t* lists;   // bf16 path: block lists (PlanArgs layout)
   int num_pages;          // 128-key pages addressable through k.base / vt
-  // bf16 path: (b << 16 | i) rows in launch order, longest causal row first
-  // (n_order == 0: the kernel's default order)
+  // bf16 path: work rows in launch order, longest first (n_order == 0: the
+  // kernel's default order).  Entry: i | b << 16 | s << 28 | (ns - 1) << 30,
+  // part s of ns equal parts of row (b, i)'s block list (see order_entry).
   int n_order;
   int order[kMaxOrder];
+  // Rows split into ns > 1 parts write part s as a normalised fp32 output
+  // and its natural-log LSE to split_o[s] / split_l[s] (layouts of out_f32 /
+  // lse); a split merge then writes the final output.
+  float* split_o[3];
+  float* split_l[3];
   const uint8_t* mask;  // [batch, hkv, max_qb, max_kb]
   const int32_t* cu_q;
   const int32_t* cu_k;
@@ -118,6 +124,25 @@ struct AttnArgs {
   void* out;          // [total_q, hq, d] dtype   (nullptr if partial)
   float* out_f32;     // [total_q, hq, d] fp32    (nullptr if final)
   float* lse;         // [hq, total_q] natural log (may be nullptr)
+};
+
+constexpr uint32_t order_entry(int b, int i, int s, int ns) {
+  return (uint32_t)i | ((uint32_t)b << 16) | ((uint32_t)s << 28) | ((uint32_t)(ns - 1) << 30);
+}
+
+// Final output of the rows an attention launch split: for each listed row
+// (first query token / 128, ns) the LSE-weighted sum of its ns partial
+// outputs, written to out (bf16) and lse.
+struct SplitMergeArgs {
+  int n;
+  int heads;
+  int head_dim;
+  int total_q;
+  const float* o[3];
+  const float* l[3];
+  void* out;   // bf16 [total_q, heads, d]
+  float* lse;  // [heads, total_q] or nullptr
+  int rows[kMaxOrder];  // q block (global) | (ns - 1) << 28
 };
 
 struct MergeArgs {
@@ -142,5 +167,6 @@ hipError_t launch_plan(const PlanArgs& a, int batch, hipStream_t s);
 hipError_t launch_attention(const AttnArgs& a, int dtype, int head_dim, int batch,
                             hipStream_t s);
 hipError_t launch_merge(const MergeArgs& a, hipStream_t s);
+hipError_t launch_split_merge(const SplitMergeArgs& a, hipStream_t s);
 
 }  // namespace xattn

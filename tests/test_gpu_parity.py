@@ -107,14 +107,18 @@ def test_select_ties_and_zeros():
 ATTN_CASES = {
     "bf16_d128_gqa2_varlen": dict(hq=4, hkv=2, d=128, lq=[512, 256], lk=[1024, 256]),
     "bf16_d64_gqa1": dict(hq=2, hkv=2, d=64, lq=[384], lk=[896]),
+    "bf16_d128_gqa2_causal": dict(hq=4, hkv=2, d=128, lq=[1280], lk=[1280]),
     "bf16_paged": dict(hq=4, hkv=1, d=128, lq=[256, 128], lk=[768, 640], paged=True),
     "f32_d64": dict(hq=2, hkv=1, d=64, lq=[256], lk=[512], dtype=torch.float32),
 }
 
 
 @pytest.mark.parametrize("name", list(ATTN_CASES))
-@pytest.mark.parametrize("mask_kind", ["random", "dense"])
+@pytest.mark.parametrize("mask_kind", ["random", "dense", "diag"])
 def test_sparse_attention(name, mask_kind):
+    """Single sequences much longer than a CU's share of the launch are split
+    into up to 3 parts per row and merged; "diag" (only the diagonal block)
+    leaves the leading parts of split rows empty."""
     w = make_random(name, seed=31, **ATTN_CASES[name])
     r = Run(w)
     rng = np.random.default_rng(5)
@@ -124,7 +128,12 @@ def test_sparse_attention(name, mask_kind):
         kh = (lk - lq) // 128
         for i in range(lq // 128):
             n = i + kh + 1
-            row = (rng.random((r.hkv, n)) < 0.5) if mask_kind == "random" else np.ones((r.hkv, n), bool)
+            if mask_kind == "random":
+                row = rng.random((r.hkv, n)) < 0.5
+            elif mask_kind == "dense":
+                row = np.ones((r.hkv, n), bool)
+            else:
+                row = np.zeros((r.hkv, n), bool)
             row[:, i + kh] = True
             mask[b, :, i, :n] = row
     mask_t = torch.from_numpy(mask)
