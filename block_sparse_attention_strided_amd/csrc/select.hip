@@ -14,6 +14,9 @@
 namespace xattn {
 namespace {
 
+constexpr int kSelMaxWaves = 16;           // q heads per KV group in the fused kernel
+constexpr size_t kSelMaxLds = 64 * 1024;  // dynamic LDS limit of the fused kernel
+
 // Order-preserving map of a float to uint32 (-0 canonicalised to +0).
 __device__ __forceinline__ uint32_t orderable(float v) {
   uint32_t u = __float_as_uint(v == 0.f ? 0.f : v);
@@ -102,6 +105,157 @@ __global__ __launch_bounds__(256) void select_rows_kernel(SelectArgs a, int n2) 
   }
 }
 
+// Orders LDS accesses of one wave: its LDS instructions execute in issue
+// order, so only the compiler has to be kept from moving them across.
+__device__ __forceinline__ void wave_lds_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+// Threshold selection and GQA aggregation fused.  One workgroup per (q block
+// i, kv head g, sequence b) with one wave per q head of the group; wave w
+// works on row (b, h = g*G + w, i) in its own LDS region:
+//   keys   (orderable(v_j) << 32) | ~j for the allowed j (descending order =
+//          value desc, index asc); zero keys pad to n2 and sort last
+//   sort   bitonic, wave-synchronous (no workgroup barriers)
+//   scan   the values as float64 in sorted order (converted by all lanes in
+//          place of their keys, indices kept aside); one lane accumulates
+//          them in that order, so before[x] and the total T round exactly
+//          as a left-to-right float64 cumulative sum
+//   keep   before[x] < tau * T
+// After one workgroup barrier every thread combines the waves' flags for its
+// columns (ANY or MAJORITY), ORs in the forced blocks in per-KV-head mode,
+// and writes the mask_kv row.  In per-KV-head mode workgroup (0, 0, b) also
+// clears hist_sel[b].  Dynamic LDS per wave: n2 8-byte keys (then values)
+// and n2 16-bit indices; then G * max_kb flag bytes.
+template <int PPL>  // compare-exchange pairs per lane and sort step: max(1, n2 / 128)
+__global__ __launch_bounds__(64 * kSelMaxWaves) void select_group_kernel(SelectArgs a, int n2) {
+  extern __shared__ __align__(16) unsigned char smem[];
+  const int G = a.hq / a.hkv;
+  const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
+  const int i = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
+  const int lq = a.cu_q[b + 1] - a.cu_q[b];
+  const int lk = a.cu_k[b + 1] - a.cu_k[b];
+  const int qb = lq / kBlock, kh = (lk - lq) / kBlock;
+  const int nthr = 64 * G;
+  if (a.select_mode == 0 && i == 0 && g == 0)
+    for (int j = tid; j < a.max_kb; j += nthr) a.hist_sel[(long long)b * a.max_kb + j] = 0;
+  uint8_t* out = a.mask_kv + (((long long)b * a.hkv + g) * a.max_qb + i) * a.max_kb;
+  if (i >= qb) {
+    for (int j = tid; j < a.max_kb; j += nthr) out[j] = 0;
+    return;
+  }
+  const int n = i + kh + 1;
+  uint64_t* keys = (uint64_t*)(smem + (size_t)w * n2 * 8);
+  double* vals = (double*)keys;  // values replace the keys after the sort
+  uint16_t* idx = (uint16_t*)(smem + (size_t)G * n2 * 8) + (size_t)w * n2;
+  uint8_t* fl = smem + (size_t)G * n2 * 10 + (size_t)w * a.max_kb;
+  const int h = g * G + w;
+  const float* row = a.block_sums + (((long long)b * a.hq + h) * a.max_qb + i) * a.max_kb;
+  if (a.threshold >= 1.0f) {
+    for (int j = lane; j < a.max_kb; j += 64) fl[j] = (j < n) ? 1 : 0;
+  } else {
+    // all of a lane's row loads in flight at once
+#pragma unroll
+    for (int p = 0; p < 2 * PPL; ++p) {
+      const int x = lane + 64 * p;
+      if (x < n2) {
+        uint64_t key = 0;
+        if (x < n) key = ((uint64_t)orderable(row[x]) << 32) | (uint64_t)(0xffffffffu - (uint32_t)x);
+        keys[x] = key;
+      }
+    }
+    wave_lds_sync();
+    // a step's pairs are disjoint: every read of the step is issued before
+    // its first write
+    for (int k = 2; k <= n2; k <<= 1) {
+      for (int js = k >> 1; js > 0; js >>= 1) {
+        uint64_t xs[PPL], ys[PPL];
+#pragma unroll
+        for (int p = 0; p < PPL; ++p) {
+          const int idx = lane + 64 * p;
+          const int lo = 2 * idx - (idx & (js - 1));
+          if (idx < (n2 >> 1)) {
+            xs[p] = keys[lo];
+            ys[p] = keys[lo + js];
+          }
+        }
+#pragma unroll
+        for (int p = 0; p < PPL; ++p) {
+          const int idx = lane + 64 * p;
+          const int lo = 2 * idx - (idx & (js - 1));
+          const bool desc = (lo & k) == 0;
+          if (idx < (n2 >> 1) && (xs[p] < ys[p]) == desc) {
+            keys[lo] = ys[p];
+            keys[lo + js] = xs[p];
+          }
+        }
+        wave_lds_sync();
+      }
+    }
+    for (int x = lane; x < n; x += 64) {
+      const uint64_t key = keys[x];
+      idx[x] = (uint16_t)(0xffffffffu - (uint32_t)(key & 0xffffffffu));
+      vals[x] = (double)from_orderable((uint32_t)(key >> 32));
+    }
+    for (int j = n + lane; j < a.max_kb; j += 64) fl[j] = 0;
+    wave_lds_sync();
+    double total = 0.0;
+    if (lane == 0) {
+      // blocks of 8 values, the next block's loads issued before the
+      // current block's additions (the additions are the serial chain)
+      double acc = 0.0;
+      const int nfull = n & ~7;
+      double cur[8] = {}, nxt[8] = {};
+      if (nfull > 0)
+#pragma unroll
+        for (int k = 0; k < 8; ++k) cur[k] = vals[k];
+      for (int x0 = 0; x0 < nfull; x0 += 8) {
+        if (x0 + 8 < nfull)
+#pragma unroll
+          for (int k = 0; k < 8; ++k) nxt[k] = vals[x0 + 8 + k];
+        double bef[8];
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+          bef[k] = acc;
+          acc += cur[k];
+        }
+#pragma unroll
+        for (int k = 0; k < 8; ++k) vals[x0 + k] = bef[k];
+#pragma unroll
+        for (int k = 0; k < 8; ++k) cur[k] = nxt[k];
+      }
+      for (int x = nfull; x < n; ++x) {
+        const double v0 = vals[x];
+        vals[x] = acc;
+        acc += v0;
+      }
+      total = acc;
+    }
+    // lane 0's total to every lane
+    const uint64_t tb = (uint64_t)__double_as_longlong(total);
+    const uint32_t t_lo = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)tb);
+    const uint32_t t_hi = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(tb >> 32));
+    const double thr = (double)a.threshold * __longlong_as_double((long long)(((uint64_t)t_hi << 32) | t_lo));
+    wave_lds_sync();
+    for (int x = lane; x < n; x += 64) fl[idx[x]] = vals[x] < thr ? 1 : 0;
+  }
+  __syncthreads();
+  const uint8_t* flags = smem + (size_t)G * n2 * 10;
+  for (int j = tid; j < a.max_kb; j += nthr) {
+    uint8_t val = 0;
+    if (j < n) {
+      int cnt = 0;
+      for (int x = 0; x < G; ++x) cnt += flags[x * a.max_kb + j];
+      bool keep = (a.group_agg == 1) ? (2 * cnt > G) : (cnt > 0);
+      if (a.select_mode == 0) keep = keep || j == 0 || j == i + kh;
+      val = keep ? 1 : 0;
+    }
+    out[j] = val;
+  }
+}
+
 // GQA aggregation (+ per-KV-head forced sink and diagonal), per (i, g, b).
 __global__ __launch_bounds__(256) void aggregate_kernel(SelectArgs a) {
   const int i = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
@@ -124,11 +278,11 @@ __global__ __launch_bounds__(256) void aggregate_kernel(SelectArgs a) {
   }
 }
 
-// Chunk-vote mode: votes of history column j over the Hkv*Qb (kv head,
-// q block) rows.  Workgroup = 64 columns x 4 row lanes; per-KV-head mode
-// clears hist_sel.
-__global__ __launch_bounds__(256) void vote_kernel(SelectArgs a) {
-  __shared__ int part[4][64];
+// Votes of history column j over the Hkv*Qb (kv head, q block) rows and the
+// chunk-vote hist_sel (per-KV-head mode: hist_sel cleared).  Workgroup = 64
+// columns x 16 row lanes; the 16 partial counts of a column meet in LDS.
+__global__ __launch_bounds__(1024) void vote_kernel(SelectArgs a) {
+  __shared__ int part[16][64];
   const int c = threadIdx.x & 63, rl = threadIdx.x >> 6;
   const int j = blockIdx.x * 64 + c;
   const int b = blockIdx.y;
@@ -139,7 +293,7 @@ __global__ __launch_bounds__(256) void vote_kernel(SelectArgs a) {
   if (a.select_mode == 1 && j < kh) {
     const int nrows = a.hkv * qb;
 #pragma unroll 8
-    for (int r = rl; r < nrows; r += 4) {
+    for (int r = rl; r < nrows; r += 16) {
       const int g = r / qb, i = r - (r / qb) * qb;
       votes += a.mask_kv[(((long long)b * a.hkv + g) * a.max_qb + i) * a.max_kb + j];
     }
@@ -149,7 +303,9 @@ __global__ __launch_bounds__(256) void vote_kernel(SelectArgs a) {
   if (rl == 0 && j < a.max_kb) {
     uint8_t sel = 0;
     if (a.select_mode == 1 && qb > 0 && j < kh) {
-      const int v = part[0][c] + part[1][c] + part[2][c] + part[3][c];
+      int v = 0;
+#pragma unroll
+      for (int x = 0; x < 16; ++x) v += part[x][c];
       sel = (2 * v > a.hkv * qb || j == 0 || j == kh - 1) ? 1 : 0;
     }
     a.hist_sel[(long long)b * a.max_kb + j] = sel;
@@ -172,36 +328,46 @@ __global__ __launch_bounds__(256) void effective_mask_kernel(SelectArgs a) {
   }
 }
 
-// counts[b] = {selected, available}; one workgroup per sequence.
-__global__ __launch_bounds__(256) void counts_kernel(SelectArgs a) {
-  __shared__ long long red[256];
-  const int b = blockIdx.x;
+// counts[b] = {selected, available}; one workgroup of 1024 threads per
+// sequence.  Mask bytes are 0 or 1, so a 16-byte word's selected count is
+// the population count of its bits.
+__global__ __launch_bounds__(1024) void counts_kernel(SelectArgs a) {
+  __shared__ long long red[16];
+  const int b = blockIdx.x, tid = threadIdx.x;
   const int lq = a.cu_q[b + 1] - a.cu_q[b];
   const int lk = a.cu_k[b + 1] - a.cu_k[b];
   const int qb = lq / kBlock, kh = (lk - lq) / kBlock;
   long long sel = 0;
   if (qb > 0) {
     if (a.select_mode == 1) {
-      for (int j = threadIdx.x; j < kh; j += 256) sel += a.hist_sel[(long long)b * a.max_kb + j];
+      for (int j = tid; j < kh; j += 1024) sel += a.hist_sel[(long long)b * a.max_kb + j];
     } else {
       const long long n = (long long)a.hkv * a.max_qb * a.max_kb;
       const uint8_t* m = a.mask_kv + (long long)b * n;
-      for (long long x = threadIdx.x; x < n; x += 256) sel += m[x];
+      const int head = (int)min(n, (long long)((16 - ((uintptr_t)m & 15)) & 15));
+      if (tid < head) sel += m[tid];
+      const long long nw = (n - head) / 16;
+      const u32x4* wp = (const u32x4*)(m + head);
+#pragma unroll 4
+      for (long long x = tid; x < nw; x += 1024) {
+        const u32x4 v = wp[x];
+        sel += __popc(v[0]) + __popc(v[1]) + __popc(v[2]) + __popc(v[3]);
+      }
+      for (long long x = head + nw * 16 + tid; x < n; x += 1024) sel += m[x];
     }
   }
-  red[threadIdx.x] = sel;
+  for (int off = 32; off > 0; off >>= 1) sel += __shfl_xor(sel, off, 64);
+  if ((tid & 63) == 0) red[tid >> 6] = sel;
   __syncthreads();
-  for (int s = 128; s > 0; s >>= 1) {
-    if (threadIdx.x < s) red[threadIdx.x] += red[threadIdx.x + s];
-    __syncthreads();
-  }
-  if (threadIdx.x == 0) {
+  if (tid == 0) {
+    long long tot = 0;
+    for (int x = 0; x < 16; ++x) tot += red[x];
     long long avail = 0;
     if (qb > 0) {
       if (a.select_mode == 1) avail = kh;
       else avail = (long long)a.hkv * ((long long)qb * (kh + 1) + (long long)qb * (qb - 1) / 2);
     }
-    a.counts[2 * b] = (int32_t)red[0];
+    a.counts[2 * b] = (int32_t)tot;
     a.counts[2 * b + 1] = (int32_t)avail;
   }
 }
@@ -212,25 +378,41 @@ hipError_t launch_select(const SelectArgs& a, int batch, hipStream_t s) {
   if (a.max_kb <= 0 || batch <= 0) return hipSuccess;
   int n2 = 1;
   while (n2 < a.max_kb) n2 <<= 1;
+  const int group = a.hq / a.hkv;
+  const size_t fused_lds = (size_t)group * n2 * 10 + (size_t)group * a.max_kb;
+  const bool fused = group <= kSelMaxWaves && fused_lds <= kSelMaxLds;
+  hipError_t e = hipSuccess;
   if (a.max_qb > 0) {
-    const size_t shm = (size_t)n2 * (sizeof(uint64_t) + sizeof(double));
-    hipLaunchKernelGGL(select_rows_kernel, dim3(a.max_qb, a.hq, batch), dim3(256), shm, s, a, n2);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(aggregate_kernel, dim3(a.max_qb, a.hkv, batch), dim3(256), 0, s, a);
-    e = hipGetLastError();
-    if (e != hipSuccess) return e;
+    if (fused) {
+      const dim3 grid(a.max_qb, a.hkv, batch), block(64 * group);
+      switch (n2 <= 128 ? 1 : n2 / 128) {
+        case 1: hipLaunchKernelGGL(select_group_kernel<1>, grid, block, fused_lds, s, a, n2); break;
+        case 2: hipLaunchKernelGGL(select_group_kernel<2>, grid, block, fused_lds, s, a, n2); break;
+        case 4: hipLaunchKernelGGL(select_group_kernel<4>, grid, block, fused_lds, s, a, n2); break;
+        case 8: hipLaunchKernelGGL(select_group_kernel<8>, grid, block, fused_lds, s, a, n2); break;
+        case 16: hipLaunchKernelGGL(select_group_kernel<16>, grid, block, fused_lds, s, a, n2); break;
+        default: hipLaunchKernelGGL(select_group_kernel<32>, grid, block, fused_lds, s, a, n2); break;
+      }
+      if ((e = hipGetLastError()) != hipSuccess) return e;
+    } else {
+      const size_t shm = (size_t)n2 * (sizeof(uint64_t) + sizeof(double));
+      hipLaunchKernelGGL(select_rows_kernel, dim3(a.max_qb, a.hq, batch), dim3(256), shm, s, a, n2);
+      if ((e = hipGetLastError()) != hipSuccess) return e;
+      hipLaunchKernelGGL(aggregate_kernel, dim3(a.max_qb, a.hkv, batch), dim3(256), 0, s, a);
+      if ((e = hipGetLastError()) != hipSuccess) return e;
+    }
   }
-  hipLaunchKernelGGL(vote_kernel, dim3((a.max_kb + 63) / 64, batch), dim3(256), 0, s, a);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
+  // the fused kernel clears hist_sel itself in per-KV-head mode
+  if (a.select_mode == 1 || !fused || a.max_qb == 0) {
+    hipLaunchKernelGGL(vote_kernel, dim3((a.max_kb + 63) / 64, batch), dim3(1024), 0, s, a);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+  }
   if (a.select_mode == 1 && a.max_qb > 0) {
     hipLaunchKernelGGL(effective_mask_kernel, dim3(a.max_qb, a.hkv, batch), dim3(256), 0, s, a);
-    e = hipGetLastError();
-    if (e != hipSuccess) return e;
+    if ((e = hipGetLastError()) != hipSuccess) return e;
   }
   if (a.counts) {
-    hipLaunchKernelGGL(counts_kernel, dim3(batch), dim3(256), 0, s, a);
+    hipLaunchKernelGGL(counts_kernel, dim3(batch), dim3(1024), 0, s, a);
     e = hipGetLastError();
   }
   return e;

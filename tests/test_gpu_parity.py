@@ -88,6 +88,35 @@ def test_select_matches_oracle_bit_exact(mode, agg, tau):
         assert tuple(counts[b].tolist()) == sel["counts"]
 
 
+@pytest.mark.parametrize("case", [
+    dict(hq=16, hkv=1, lq=[512], lk=[8192]),        # 16 q heads per group: the fused kernel's widest group
+    dict(hq=8, hkv=1, lq=[256], lk=[131072]),       # 1024-block rows x 8 heads: two-kernel path (LDS)
+    dict(hq=32, hkv=1, lq=[256], lk=[16384]),       # 32 q heads per group: two-kernel path (group size)
+    dict(hq=1, hkv=1, lq=[128, 256], lk=[384000, 1024]),  # 3000-block rows: 4096-key sort
+])
+@pytest.mark.parametrize("mode", ["per_kvhead", "chunk_vote"])
+def test_select_wide_rows_and_groups(case, mode):
+    """Selection on seeded block sums (exponential, with ties) for row widths
+    and group sizes on both sides of the fused kernel's limits."""
+    w = make_random("selw", seed=23, d=64, dtype=torch.float32, stride=8, select_mode=mode, **case)
+    r = Run(w, threshold=0.9)
+    rng = np.random.default_rng(24)
+    bs32 = rng.exponential(1.0, size=(r.B, r.hq, r.max_qb, r.max_kb)).astype(np.float32)
+    bs32[..., ::7] = bs32[..., 3:4]  # repeated values: index order decides
+    say("select wide %s %s" % (case, mode))
+    mask, hist, counts = r.select(torch.from_numpy(bs32))
+    for b in range(w.batch):
+        lq, lk = w.lens(b)
+        qb, kb = lq // 128, lk // 128
+        sel = O.select_blocks(bs32[b, :, :qb, :kb].astype(np.float64), kh=(lk - lq) // 128, tau=r.tau,
+                              group=w.num_q_heads // w.num_kv_heads, mode=mode)
+        m = mask[b].cpu().numpy().astype(bool)
+        assert (m[:, :qb, :kb] == sel["mask_kv"]).all(), "mask mismatch seq %d" % b
+        assert not m[:, qb:, :].any() and not m[:, :, kb:].any()
+        assert (hist[b, :kb].cpu().numpy().astype(bool) == sel["hist_sel"]).all()
+        assert tuple(counts[b].tolist()) == sel["counts"]
+
+
 def test_select_ties_and_zeros():
     """Equal values (index order decides) and zero blocks."""
     w = make_random("ties", seed=22, hq=2, hkv=1, d=64, lq=[256], lk=[1024], dtype=torch.float32,
