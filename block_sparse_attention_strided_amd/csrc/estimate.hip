@@ -497,6 +497,71 @@ __global__ __launch_bounds__(256) void block_sums_kernel(BlockSumArgs a) {
   }
 }
 
+// The same in one read: workgroup (i, h, b) of 1024 threads, thread (jl, rr)
+// holds the partial log-sum-exps of row rr for blocks jl, jl + JL, ... in
+// registers (NV * JL >= max_kb).  Row maxima and row sums meet in LDS; then
+// each thread scales its 2^(part - max) by 1 / row sum and the RB lanes of a
+// block add them with cross-lane shuffles.
+template <int RB, int NV>
+__global__ __launch_bounds__(1024) void block_sums_reg_kernel(BlockSumArgs a) {
+  constexpr int JL = 1024 / RB;
+  __shared__ float red[JL][RB];
+  __shared__ float row_v[RB];
+  const int i = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+  const int lq = a.cu_q[b + 1] - a.cu_q[b];
+  const int lk = a.cu_k[b + 1] - a.cu_k[b];
+  const int qb = lq / kBlock, kh = (lk - lq) / kBlock;
+  const int tid = threadIdx.x;
+  float* out = a.block_sums + (((long long)b * a.hq + h) * a.max_qb + i) * a.max_kb;
+  if (i >= qb) {
+    for (int j = tid; j < a.max_kb; j += 1024) out[j] = 0.f;
+    return;
+  }
+  const int nj = i + kh + 1;
+  const float* base = a.part + ((long long)(b * a.hq + h) * a.max_kb) * a.max_r + i * RB;
+  const int rr = tid % RB, jl = tid / RB;
+  float v[NV];
+  float m = kNegInf;
+#pragma unroll
+  for (int t = 0; t < NV; ++t) {
+    const int j = jl + t * JL;
+    v[t] = (j < nj) ? base[(long long)j * a.max_r + rr] : kNegInf;
+    m = fmaxf(m, v[t]);
+  }
+  red[jl][rr] = m;
+  __syncthreads();
+  if (tid < RB) {
+    float M = kNegInf;
+    for (int x = 0; x < JL; ++x) M = fmaxf(M, red[x][tid]);
+    row_v[tid] = M;
+  }
+  __syncthreads();
+  const float M = row_v[rr];
+  float l = 0.f;
+#pragma unroll
+  for (int t = 0; t < NV; ++t) {
+    v[t] = (v[t] == kNegInf) ? 0.f : exp2f(v[t] - M);
+    l += v[t];
+  }
+  red[jl][rr] = l;
+  __syncthreads();
+  if (tid < RB) {
+    float L = 0.f;
+    for (int x = 0; x < JL; ++x) L += red[x][tid];
+    row_v[tid] = (L > 0.f) ? 1.f / L : 0.f;
+  }
+  __syncthreads();
+  const float inv = row_v[rr];
+#pragma unroll
+  for (int t = 0; t < NV; ++t) {
+    float sb = v[t] * inv;
+#pragma unroll
+    for (int off = RB / 2; off > 0; off >>= 1) sb += __shfl_xor(sb, off, RB);
+    const int j = jl + t * JL;
+    if (rr == 0 && j < a.max_kb) out[j] = (j < nj) ? sb : 0.f;
+  }
+}
+
 template <int D, int S>
 hipError_t est_dispatch(const EstArgs& a, int dtype, int batch, hipStream_t st) {
   constexpr int RB = kBlock / S;
@@ -550,7 +615,20 @@ hipError_t launch_estimate(const EstArgs& a, int dtype, int head_dim, int stride
 hipError_t launch_block_sums(const BlockSumArgs& a, int batch, hipStream_t s) {
   if (a.max_qb <= 0 || a.max_kb <= 0 || batch <= 0) return hipSuccess;
   dim3 grid(a.max_qb, a.hq, batch);
-  switch (kBlock / a.stride) {
+  const int rb = kBlock / a.stride;
+  const int jl = 1024 / rb;
+  int nv = 1;
+  while (nv * jl < a.max_kb) nv <<= 1;
+#define XATTN_BS_CASE(RB_, NV_)                                                                  \
+  if (rb == RB_ && nv == NV_) {                                                                  \
+    hipLaunchKernelGGL((block_sums_reg_kernel<RB_, NV_>), grid, dim3(1024), 0, s, a);           \
+    return hipGetLastError();                                                                    \
+  }
+  XATTN_BS_CASE(8, 1) XATTN_BS_CASE(8, 2) XATTN_BS_CASE(8, 4) XATTN_BS_CASE(8, 8) XATTN_BS_CASE(8, 16)
+  XATTN_BS_CASE(16, 1) XATTN_BS_CASE(16, 2) XATTN_BS_CASE(16, 4) XATTN_BS_CASE(16, 8) XATTN_BS_CASE(16, 16)
+  XATTN_BS_CASE(32, 1) XATTN_BS_CASE(32, 2) XATTN_BS_CASE(32, 4) XATTN_BS_CASE(32, 8) XATTN_BS_CASE(32, 16)
+#undef XATTN_BS_CASE
+  switch (rb) {
     case 8: hipLaunchKernelGGL((block_sums_kernel<8>), grid, dim3(256), 0, s, a); break;
     case 16: hipLaunchKernelGGL((block_sums_kernel<16>), grid, dim3(256), 0, s, a); break;
     case 32: hipLaunchKernelGGL((block_sums_kernel<32>), grid, dim3(256), 0, s, a); break;

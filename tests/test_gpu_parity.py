@@ -28,6 +28,8 @@ EST_CASES = {
     # ragged rows/columns, causal tiles, two sequences
     "bf16_big_s8_varlen": dict(hq=16, hkv=4, d=128, lq=[2432, 640], lk=[8192, 1024], stride=8),
     "bf16_big_s16_d64": dict(hq=16, hkv=8, d=64, lq=[4096], lk=[65536], stride=16),
+    # 640-block rows at stride 4: the block-sum kernel that re-reads the partials
+    "bf16_s4_long_rows": dict(hq=2, hkv=1, d=64, lq=[256], lk=[81920], stride=4),
     "f32_s16_d128_paged": dict(hq=2, hkv=2, d=128, lq=[256, 128], lk=[512, 384], stride=16,
                                dtype=torch.float32, paged=True),
 }
