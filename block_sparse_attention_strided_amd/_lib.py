@@ -69,6 +69,7 @@ class XattnParams(ctypes.Structure):
         ("kv_chunk_tokens", ctypes.c_int),
         ("select_mode", ctypes.c_int),
         ("group_agg", ctypes.c_int),
+        ("num_to_choose", ctypes.c_int),
     ]
 
 

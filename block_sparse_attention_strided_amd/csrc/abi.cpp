@@ -78,6 +78,7 @@ int make_plan(const XattnShape* sh, const XattnParams* pr, Plan* p) {
     return fail(XATTN_ERR_UNSUPPORTED, "stride must be 4, 8 or 16 (got %d)", pr->stride);
   if (!std::isfinite(pr->threshold) || pr->threshold < 0.f)
     return fail(XATTN_ERR_INVALID, "threshold must be finite and >= 0");
+  if (pr->num_to_choose < 0) return fail(XATTN_ERR_INVALID, "num_to_choose must be >= 0 (0 = threshold rule)");
   if (!std::isfinite(pr->est_scale) || pr->est_scale < 0.f)
     return fail(XATTN_ERR_INVALID, "est_scale must be finite and >= 0 (0 = default)");
   if (!std::isfinite(pr->softmax_scale) || pr->softmax_scale < 0.f)
@@ -229,6 +230,7 @@ hipError_t run_select(const XattnShape* sh, const XattnParams* pr, const Plan& p
   sa.max_qb = p.max_qb;
   sa.max_kb = p.max_kb;
   sa.threshold = pr->threshold;
+  sa.num_to_choose = pr->num_to_choose;
   sa.select_mode = pr->select_mode;
   sa.group_agg = pr->group_agg;
   sa.mask_q = maskq;

@@ -47,7 +47,7 @@ __global__ __launch_bounds__(256) void select_rows_kernel(SelectArgs a, int n2) 
   }
   const int n = i + kh + 1;
   const float* row = a.block_sums + (((long long)b * a.hq + h) * a.max_qb + i) * a.max_kb;
-  if (a.threshold >= 1.0f) {
+  if (a.num_to_choose > 0 ? a.num_to_choose >= n : a.threshold >= 1.0f) {
     for (int j = tid; j < a.max_kb; j += 256) out[j] = (j < n) ? 1 : 0;
     return;
   }
@@ -73,7 +73,8 @@ __global__ __launch_bounds__(256) void select_rows_kernel(SelectArgs a, int n2) 
       __syncthreads();
     }
   }
-  if (tid == 0) {
+  if (tid == 0) thr_s = 0.0;
+  if (tid == 0 && a.num_to_choose == 0) {
     double acc = 0.0;
     int x = 0;
     for (; x + 4 <= n; x += 4) {
@@ -98,7 +99,7 @@ __global__ __launch_bounds__(256) void select_rows_kernel(SelectArgs a, int n2) 
   for (int x = tid; x < a.max_kb; x += 256) {
     if (x < n) {
       const int j = (int)(0xffffffffu - (uint32_t)(keys[x] & 0xffffffffu));
-      out[j] = before[x] < thr ? 1 : 0;
+      out[j] = (a.num_to_choose > 0 ? x < a.num_to_choose : before[x] < thr) ? 1 : 0;
     } else {
       out[x] = 0;  // not allowed (positions >= n hold only padding keys)
     }
@@ -129,6 +130,51 @@ __device__ __forceinline__ void wave_lds_sync() {
 // and writes the mask_kv row.  In per-KV-head mode workgroup (0, 0, b) also
 // clears hist_sel[b].  Dynamic LDS per wave: n2 8-byte keys (then values)
 // and n2 16-bit indices; then G * max_kb flag bytes.
+// Wave-synchronous bitonic sort of one row's keys in LDS: key x < n is
+// (orderable(row[x]) << 32) | ~x, keys n..n2-1 are 0; descending order =
+// value desc, index asc, padding last.
+template <int PPL>
+__device__ __forceinline__ void sort_row_keys(uint64_t* keys, const float* row, int n, int n2, int lane) {
+  // all of a lane's row loads in flight at once
+#pragma unroll
+  for (int p = 0; p < 2 * PPL; ++p) {
+    const int x = lane + 64 * p;
+    if (x < n2) {
+      uint64_t key = 0;
+      if (x < n) key = ((uint64_t)orderable(row[x]) << 32) | (uint64_t)(0xffffffffu - (uint32_t)x);
+      keys[x] = key;
+    }
+  }
+  wave_lds_sync();
+  // a step's pairs are disjoint: every read of the step is issued before
+  // its first write
+  for (int k = 2; k <= n2; k <<= 1) {
+    for (int js = k >> 1; js > 0; js >>= 1) {
+      uint64_t xs[PPL], ys[PPL];
+#pragma unroll
+      for (int p = 0; p < PPL; ++p) {
+        const int idx = lane + 64 * p;
+        const int lo = 2 * idx - (idx & (js - 1));
+        if (idx < (n2 >> 1)) {
+          xs[p] = keys[lo];
+          ys[p] = keys[lo + js];
+        }
+      }
+#pragma unroll
+      for (int p = 0; p < PPL; ++p) {
+        const int idx = lane + 64 * p;
+        const int lo = 2 * idx - (idx & (js - 1));
+        const bool desc = (lo & k) == 0;
+        if (idx < (n2 >> 1) && (xs[p] < ys[p]) == desc) {
+          keys[lo] = ys[p];
+          keys[lo + js] = xs[p];
+        }
+      }
+      wave_lds_sync();
+    }
+  }
+}
+
 template <int PPL>  // compare-exchange pairs per lane and sort step: max(1, n2 / 128)
 __global__ __launch_bounds__(64 * kSelMaxWaves) void select_group_kernel(SelectArgs a, int n2) {
   extern __shared__ __align__(16) unsigned char smem[];
@@ -153,47 +199,18 @@ __global__ __launch_bounds__(64 * kSelMaxWaves) void select_group_kernel(SelectA
   uint8_t* fl = smem + (size_t)G * n2 * 10 + (size_t)w * a.max_kb;
   const int h = g * G + w;
   const float* row = a.block_sums + (((long long)b * a.hq + h) * a.max_qb + i) * a.max_kb;
-  if (a.threshold >= 1.0f) {
+  if (a.num_to_choose > 0 ? a.num_to_choose >= n : a.threshold >= 1.0f) {
     for (int j = lane; j < a.max_kb; j += 64) fl[j] = (j < n) ? 1 : 0;
+  } else if (a.num_to_choose > 0) {
+    // top-k rule: the first num_to_choose keys of the sorted order
+    sort_row_keys<PPL>(keys, row, n, n2, lane);
+    for (int j = n + lane; j < a.max_kb; j += 64) fl[j] = 0;
+    for (int x = lane; x < n; x += 64) {
+      const uint64_t key = keys[x];
+      fl[0xffffffffu - (uint32_t)(key & 0xffffffffu)] = (x < a.num_to_choose) ? 1 : 0;
+    }
   } else {
-    // all of a lane's row loads in flight at once
-#pragma unroll
-    for (int p = 0; p < 2 * PPL; ++p) {
-      const int x = lane + 64 * p;
-      if (x < n2) {
-        uint64_t key = 0;
-        if (x < n) key = ((uint64_t)orderable(row[x]) << 32) | (uint64_t)(0xffffffffu - (uint32_t)x);
-        keys[x] = key;
-      }
-    }
-    wave_lds_sync();
-    // a step's pairs are disjoint: every read of the step is issued before
-    // its first write
-    for (int k = 2; k <= n2; k <<= 1) {
-      for (int js = k >> 1; js > 0; js >>= 1) {
-        uint64_t xs[PPL], ys[PPL];
-#pragma unroll
-        for (int p = 0; p < PPL; ++p) {
-          const int idx = lane + 64 * p;
-          const int lo = 2 * idx - (idx & (js - 1));
-          if (idx < (n2 >> 1)) {
-            xs[p] = keys[lo];
-            ys[p] = keys[lo + js];
-          }
-        }
-#pragma unroll
-        for (int p = 0; p < PPL; ++p) {
-          const int idx = lane + 64 * p;
-          const int lo = 2 * idx - (idx & (js - 1));
-          const bool desc = (lo & k) == 0;
-          if (idx < (n2 >> 1) && (xs[p] < ys[p]) == desc) {
-            keys[lo] = ys[p];
-            keys[lo + js] = xs[p];
-          }
-        }
-        wave_lds_sync();
-      }
-    }
+    sort_row_keys<PPL>(keys, row, n, n2, lane);
     for (int x = lane; x < n; x += 64) {
       const uint64_t key = keys[x];
       idx[x] = (uint16_t)(0xffffffffu - (uint32_t)(key & 0xffffffffu));

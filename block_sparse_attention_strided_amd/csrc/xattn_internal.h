@@ -52,6 +52,7 @@ struct SelectArgs {
   int max_qb;
   int max_kb;
   float threshold;
+  int num_to_choose;  // > 0: top-k rule instead of the threshold
   int select_mode;
   int group_agg;
   uint8_t* mask_q;   // [batch, hq, max_qb, max_kb]  (workspace)

@@ -99,6 +99,11 @@ typedef struct XattnParams {
   int kv_chunk_tokens; /* estimate KV chunk (ring slot size); multiple of 128   */
   int select_mode;     /* XATTN_SELECT_*                                        */
   int group_agg;       /* XATTN_GQA_*                                           */
+  int num_to_choose;   /* > 0: keep the num_to_choose largest allowed blocks of
+                          each (q head, q block) row (value desc, index asc)
+                          instead of the threshold rule -- the fixed-count
+                          argument of find_blocks_chunked (design doc 核心算法
+                          Step 3); 0: threshold rule                        */
 } XattnParams;
 
 /* Optional extra outputs of xattn_prefill_chunk (any field may be NULL). */

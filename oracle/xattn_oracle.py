@@ -36,6 +36,10 @@ R5  threshold selection: per row, over allowed blocks ``j <= i + Kh``, order
     the items before it, accumulated in that order, is ``< tau * T`` where
     ``T`` is the float64 sum of all allowed items in the same order.
     ``tau >= 1`` keeps every allowed block.
+R20 top-k selection (``num_to_choose``, named but unused in the pages' call):
+    when it is k > 0 it replaces the threshold: the k largest allowed blocks
+    of the row in R5's order are kept (all of them if k >= their count); the
+    aggregation, forcing and voting that follow are unchanged.
 R6  forced blocks: chunk-vote mode forces the first and last history block
     after voting; per-KV-head mode forces the sink (j = 0) and the diagonal
     block (j = i + Kh).
@@ -248,13 +252,29 @@ def threshold_select_row(v, tau):
     return keep
 
 
+def topk_select_row(v, k):
+    """Boolean keep-mask of the k largest allowed blocks of one row: the
+    fixed-count alternative (``num_to_choose``) to the threshold in the
+    find_blocks_chunked call ([BSA] 核心算法 §1 Step 3).  Order as in R5
+    (value desc, index asc on ties); k >= n keeps every allowed block."""
+    v = np.asarray(v, dtype=np.float64)
+    n = v.shape[0]
+    keep = np.zeros(n, dtype=bool)
+    if n == 0 or k <= 0:
+        return keep
+    order = np.argsort(-v, kind="stable")
+    keep[order[:min(k, n)]] = True
+    return keep
+
+
 # ---------------------------------------------------------------------------
 # O4-O6: GQA aggregation, forced blocks, majority vote, effective mask
 # ([BSA] 核心算法 §1 Step 4) and O9 counts ([BSA] Density 统计 API).
 # ---------------------------------------------------------------------------
 
-def select_blocks(bs, *, kh, tau, group, mode, agg=AGG_ANY):
-    """bs: [Hq, Qb, Kb] block sums of one sequence.
+def select_blocks(bs, *, kh, tau, group, mode, agg=AGG_ANY, num_to_choose=0):
+    """bs: [Hq, Qb, Kb] block sums of one sequence.  ``num_to_choose`` > 0
+    replaces the threshold rule by the top-k rule (topk_select_row).
 
     Returns dict(mask_q [Hq,Qb,Kb], mask_kv [Hkv,Qb,Kb] effective attention
     mask, hist_sel [Kb], counts (selected, available)).
@@ -266,7 +286,10 @@ def select_blocks(bs, *, kh, tau, group, mode, agg=AGG_ANY):
     for h in range(hq):
         for i in range(qb):
             n = i + kh + 1
-            mask_q[h, i, :n] = threshold_select_row(bs[h, i, :n], tau)
+            if num_to_choose > 0:
+                mask_q[h, i, :n] = topk_select_row(bs[h, i, :n], num_to_choose)
+            else:
+                mask_q[h, i, :n] = threshold_select_row(bs[h, i, :n], tau)
     cnt = mask_q.reshape(hkv, group, qb, kb).sum(axis=1)
     if agg == AGG_ANY:
         per_kv = cnt > 0
@@ -420,7 +443,7 @@ def sequence_kv(k, v, cu_k, b, block_table=None, k_cache=None, v_cache=None, blo
 def prefill(q, k, v, cu_q, cu_k, *, num_kv_heads, stride, block=BLOCK, threshold,
             est_scale=None, softmax_scale=None, kv_chunk_tokens=0, mode=PER_KVHEAD,
             agg=AGG_ANY, block_table=None, k_cache=None, v_cache=None, rows=None,
-            attention=True, pages_order=False):
+            attention=True, pages_order=False, num_to_choose=0):
     """Estimate -> select -> attend for every sequence of a packed batch.
 
     q: [total_q, Hq, d]; k, v: [total_k, Hkv, d] (or paged caches via
@@ -474,7 +497,8 @@ def prefill(q, k, v, cu_q, cu_k, *, num_kv_heads, stride, block=BLOCK, threshold
         else:
             bs = estimate_block_sums(q_b, k_b, stride=stride, block=block,
                                      est_scale=est_scale, group=group)
-        sel = select_blocks(bs, kh=kh, tau=threshold, group=group, mode=mode, agg=agg)
+        sel = select_blocks(bs, kh=kh, tau=threshold, group=group, mode=mode, agg=agg,
+                            num_to_choose=num_to_choose)
         res["block_sums"][b, :, :qb_, :kb_] = bs
         res["mask_q"][b, :, :qb_, :kb_] = sel["mask_q"]
         res["mask_kv"][b, :, :qb_, :kb_] = sel["mask_kv"]

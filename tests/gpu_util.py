@@ -30,13 +30,14 @@ def say(msg):
 class Run:
     """A workload resident on the GPU with its C-ABI shape/params/workspace."""
 
-    def __init__(self, w, *, threshold=None, select_mode=None, group_agg=None, device="cuda"):
+    def __init__(self, w, *, threshold=None, select_mode=None, group_agg=None, num_to_choose=0, device="cuda"):
         self.w = w
         self.paged = w.block_table is not None
         d = w.head_dim
         self.tau = f32(w.threshold if threshold is None else threshold)
         self.mode = w.select_mode if select_mode is None else select_mode
         self.agg = w.group_agg if group_agg is None else group_agg
+        self.num_to_choose = num_to_choose
         self.est_scale = f32(1.0 / (w.stride * math.sqrt(d)))
         self.softmax_scale = f32(1.0 / math.sqrt(d))
         self.q = w.q.to(device)
@@ -54,7 +55,7 @@ class Run:
                                  dtype=w.dtype, cu_q=w.cu_q, cu_k=w.cu_k, device=device)
         self.params = X.make_params(stride=w.stride, threshold=self.tau, est_scale=self.est_scale,
                                     softmax_scale=self.softmax_scale, kv_chunk_tokens=w.kv_chunk_tokens,
-                                    select_mode=self.mode, group_agg=self.agg)
+                                    select_mode=self.mode, group_agg=self.agg, num_to_choose=num_to_choose)
         self.ws = X.alloc_workspace(self.shape, self.params, device)
         sh = self.shape
         self.B, self.hq, self.hkv = sh.batch, sh.num_q_heads, sh.num_kv_heads

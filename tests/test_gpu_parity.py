@@ -119,6 +119,33 @@ def test_select_wide_rows_and_groups(case, mode):
         assert tuple(counts[b].tolist()) == sel["counts"]
 
 
+@pytest.mark.parametrize("k", [1, 3, 9, 5000])
+@pytest.mark.parametrize("case", [
+    dict(hq=8, hkv=2, lq=[512, 256], lk=[2048, 256]),  # fused kernel
+    dict(hq=32, hkv=1, lq=[256], lk=[16384]),           # two-kernel path (group size)
+])
+@pytest.mark.parametrize("mode", ["per_kvhead", "chunk_vote"])
+def test_select_topk(k, case, mode):
+    """Top-k rule (num_to_choose) on seeded block sums with ties, both
+    kernel paths, k below, inside and above the row widths."""
+    w = make_random("topk", seed=25, d=64, dtype=torch.float32, stride=8, select_mode=mode, **case)
+    r = Run(w, threshold=0.9, num_to_choose=k)
+    rng = np.random.default_rng(26)
+    bs32 = rng.exponential(1.0, size=(r.B, r.hq, r.max_qb, r.max_kb)).astype(np.float32)
+    bs32[..., ::5] = bs32[..., 2:3]
+    say("select top-%d %s %s" % (k, case, mode))
+    mask, hist, counts = r.select(torch.from_numpy(bs32))
+    for b in range(w.batch):
+        lq, lk = w.lens(b)
+        qb, kb = lq // 128, lk // 128
+        sel = O.select_blocks(bs32[b, :, :qb, :kb].astype(np.float64), kh=(lk - lq) // 128, tau=r.tau,
+                              group=w.num_q_heads // w.num_kv_heads, mode=mode, num_to_choose=k)
+        m = mask[b].cpu().numpy().astype(bool)
+        assert (m[:, :qb, :kb] == sel["mask_kv"]).all(), "mask mismatch seq %d" % b
+        assert (hist[b, :kb].cpu().numpy().astype(bool) == sel["hist_sel"]).all()
+        assert tuple(counts[b].tolist()) == sel["counts"]
+
+
 def test_select_ties_and_zeros():
     """Equal values (index order decides) and zero blocks."""
     w = make_random("ties", seed=22, hq=2, hkv=1, d=64, lq=[256], lk=[1024], dtype=torch.float32,

@@ -195,6 +195,45 @@ def test_threshold_special_cases():
     assert O.threshold_select_row([0.5, 0.25, 0.25], 0.75).tolist() == [True, True, False]
 
 
+def test_topk_select_bruteforce():
+    """Top-k keeps a k-subset of maximum sum; among maximum-sum subsets the
+    one whose sorted index list is smallest (ties toward the lower index)."""
+    rng = np.random.default_rng(17)
+    for trial in range(300):
+        n = int(rng.integers(1, 9))
+        v = (rng.integers(0, 8, size=n) / 8.0).tolist()  # dyadic, many ties
+        k = int(rng.integers(0, n + 3))
+        keep = O.topk_select_row(v, k)
+        m = min(max(k, 0), n)
+        assert keep.sum() == m
+        best = max(itertools.combinations(range(n), m), key=lambda sub: (sum(v[j] for j in sub), [-j for j in sub]))
+        assert set(np.flatnonzero(keep)) == set(best), (v, k)
+
+
+def test_topk_special_cases_and_threshold_relation():
+    v = [0.1, 0.4, 0.2, 0.3]
+    assert O.topk_select_row(v, 0).tolist() == [False] * 4
+    assert O.topk_select_row(v, 1).tolist() == [False, True, False, False]
+    assert O.topk_select_row(v, 2).tolist() == [False, True, False, True]
+    assert O.topk_select_row(v, 9).all()
+    assert O.topk_select_row([1.0, 1.0, 1.0], 2).tolist() == [True, True, False]
+    # the threshold rule keeps a prefix of the same order: top-k with k = its
+    # count reproduces it
+    rng = np.random.default_rng(18)
+    for trial in range(200):
+        w = rng.exponential(size=int(rng.integers(1, 40)))
+        tau = float(rng.uniform(0.1, 0.99))
+        keep = O.threshold_select_row(w, tau)
+        assert (O.topk_select_row(w, int(keep.sum())) == keep).all()
+    # top-k mode feeds the same aggregation and forcing as the threshold mode
+    bs = np.zeros((2, 2, 4))
+    bs[0, 1] = [0.1, 0.2, 0.3, 0.4]
+    bs[1, 1] = [0.4, 0.3, 0.2, 0.1]
+    sel = O.select_blocks(bs, kh=2, tau=0.9, group=2, mode=O.PER_KVHEAD, num_to_choose=1)
+    # row 1: heads pick j=3 and j=0; ANY -> {0, 3}; forced sink 0 and diagonal 3
+    assert sel["mask_kv"][0, 1].tolist() == [True, False, False, True]
+
+
 def test_threshold_mutants_rejected():
     def le_mutant(v, tau):  # <= instead of <
         v = np.asarray(v, float)
