@@ -36,7 +36,7 @@ R5  threshold selection: per row, over allowed blocks ``j <= i + Kh``, order
     the items before it, accumulated in that order, is ``< tau * T`` where
     ``T`` is the float64 sum of all allowed items in the same order.
     ``tau >= 1`` keeps every allowed block.
-R20 top-k selection (``num_to_choose``, named but unused in the pages' call):
+R22 top-k selection (``num_to_choose``, named but unused in the pages' call):
     when it is k > 0 it replaces the threshold: the k largest allowed blocks
     of the row in R5's order are kept (all of them if k >= their count); the
     aggregation, forcing and voting that follow are unchanged.
