@@ -320,6 +320,21 @@ def main():
         res["copy_calibration"] = {"bytes_read": x.numel() * 4, "bytes_written": y.numel() * 4,
                                    "kernel": "elementwise mul by 1.0 (torch), 5 launches"}
     if ring is not None:
+        # write-back of the chunk's K/V to pinned host memory (offload stream),
+        # timed alone: D2H link rate of the step after the path
+        nb = lq0 // 128
+        k_dst = torch.empty((nb, 128, hkv, w.head_dim), dtype=w.dtype, pin_memory=True)
+        v_dst = torch.empty_like(k_dst, pin_memory=True)
+
+        def wb():
+            ring.offload_chunk(k, v, k_dst, v_dst, nb)
+            ring.offload_wait()
+
+        wb()
+        torch.cuda.synchronize()
+        wb_ms = time_region(wb, 5, stream)
+        res["stages"]["writeback_ms"] = wb_ms
+        res["stages"]["writeback_gbs"] = 2 * k_dst.numel() * k_dst.element_size() / (wb_ms * 1e-3) / 1e9
         ring.close()
     if not args.no_achievable:
         res["achievable"] = achievable_rates(dev)

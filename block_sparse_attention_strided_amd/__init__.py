@@ -172,6 +172,14 @@ class Ring:
     def set_copy_delay_us(self, usec):
         _check(_lib.load().xattn_ring_set_copy_delay_us(self.handle, usec))
 
+    def offload_chunk(self, k, v, k_host_dst, v_host_dst, num_blocks, stream=None):
+        """Write a prefilled chunk's K/V back to pinned host history."""
+        _check(_lib.load().xattn_ring_offload_chunk(self.handle, _ptr(k), _ptr(v), _ptr(k_host_dst),
+                                                    _ptr(v_host_dst), int(num_blocks), _stream(stream)))
+
+    def offload_wait(self, stream=None):
+        _check(_lib.load().xattn_ring_offload_wait(self.handle, _stream(stream)))
+
     def close(self):
         if self.handle:
             _lib.load().xattn_ring_destroy(self.handle)

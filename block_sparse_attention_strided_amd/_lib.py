@@ -36,6 +36,8 @@ EXPORTED = (
     "xattn_ring_create",
     "xattn_ring_destroy",
     "xattn_ring_set_copy_delay_us",
+    "xattn_ring_offload_chunk",
+    "xattn_ring_offload_wait",
     "xattn_last_error",
 )
 
@@ -119,6 +121,10 @@ def load():
     lib.xattn_ring_destroy.argtypes = [vp]
     lib.xattn_ring_destroy.restype = None
     lib.xattn_ring_set_copy_delay_us.argtypes = [vp, ctypes.c_int]
+    lib.xattn_ring_offload_chunk.argtypes = [vp, vp, vp, vp, vp, ctypes.c_int, vp]
+    lib.xattn_ring_offload_chunk.restype = ctypes.c_int
+    lib.xattn_ring_offload_wait.argtypes = [vp, vp]
+    lib.xattn_ring_offload_wait.restype = ctypes.c_int
     lib.xattn_ring_set_copy_delay_us.restype = ctypes.c_int
     lib.xattn_last_error.argtypes = []
     lib.xattn_last_error.restype = ctypes.c_char_p

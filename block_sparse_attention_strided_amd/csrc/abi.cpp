@@ -438,6 +438,10 @@ struct XattnRing {
   int host_cap = 0;               // entries of both staging buffers
   int next_slot = 0;
   int copy_delay_us = 0;
+  // write-back of prefilled chunks to the host history (offload stream)
+  hipStream_t offload = nullptr;
+  hipEvent_t chunk_ready = nullptr;  // recorded on the caller's stream
+  hipEvent_t offload_done = nullptr; // recorded after the last write-back
 };
 
 namespace {
@@ -462,6 +466,8 @@ hipError_t ring_fill(XattnRing* r, int s, const char* kh, const char* vh,
                      const std::vector<std::pair<int, int>>& runs, bool with_v) {
   hipError_t e = hipStreamWaitEvent(r->xfer, r->done[s], 0);
   if (e != hipSuccess) return e;
+  // history written back by an earlier call may be among the blocks read
+  if ((e = hipStreamWaitEvent(r->xfer, r->offload_done, 0)) != hipSuccess) return e;
   if (r->copy_delay_us > 0) {
     e = hipLaunchHostFunc(r->xfer, sleep_host_fn, &r->copy_delay_us);
     if (e != hipSuccess) return e;
@@ -824,6 +830,10 @@ int xattn_ring_create(int num_slots, int slot_blocks, int num_kv_heads, int head
     if (e == hipSuccess) e = hipEventRecord(b, r->xfer);  // slot free before its first copy
   }
   if (e == hipSuccess) e = hipEventCreateWithFlags(&r->sel_ready, hipEventDisableTiming);
+  if (e == hipSuccess) e = hipStreamCreateWithFlags(&r->offload, hipStreamNonBlocking);
+  if (e == hipSuccess) e = hipEventCreateWithFlags(&r->chunk_ready, hipEventDisableTiming);
+  if (e == hipSuccess) e = hipEventCreateWithFlags(&r->offload_done, hipEventDisableTiming);
+  if (e == hipSuccess) e = hipEventRecord(r->offload_done, r->offload);  // nothing written back yet
   if (e != hipSuccess) {
     int rc = hip_fail(e, "ring creation");
     xattn_ring_destroy(r);
@@ -839,12 +849,44 @@ void xattn_ring_destroy(XattnRing* r) {
   for (auto ev : r->ready) (void)hipEventSynchronize(ev), (void)hipEventDestroy(ev);
   for (auto ev : r->done) (void)hipEventSynchronize(ev), (void)hipEventDestroy(ev);
   if (r->sel_ready) (void)hipEventDestroy(r->sel_ready);
+  if (r->offload) (void)hipStreamSynchronize(r->offload);
+  if (r->chunk_ready) (void)hipEventDestroy(r->chunk_ready);
+  if (r->offload_done) (void)hipEventDestroy(r->offload_done);
+  if (r->offload) (void)hipStreamDestroy(r->offload);
   if (r->xfer) (void)hipStreamDestroy(r->xfer);
   if (r->k_slots) (void)hipFree(r->k_slots);
   if (r->v_slots) (void)hipFree(r->v_slots);
   if (r->host_sel) (void)hipHostFree(r->host_sel);
   if (r->host_table) (void)hipHostFree(r->host_table);
   delete r;
+}
+
+int xattn_ring_offload_chunk(XattnRing* ring, const void* k, const void* v, void* k_host_dst, void* v_host_dst,
+                             int num_blocks, void* stream) {
+  if (!ring) return fail(XATTN_ERR_INVALID, "ring must not be NULL");
+  if (num_blocks < 0) return fail(XATTN_ERR_INVALID, "num_blocks must be >= 0");
+  if (num_blocks == 0) return XATTN_OK;
+  if (!k || !v || !k_host_dst || !v_host_dst) return fail(XATTN_ERR_INVALID, "k, v and the host destinations must not be NULL");
+  int rc = check_pinned(k_host_dst, "k_host_dst");
+  if (rc) return rc;
+  if ((rc = check_pinned(v_host_dst, "v_host_dst"))) return rc;
+  g_last_error.clear();
+  const size_t bytes = (size_t)num_blocks * ring->block_bytes;
+  hipError_t e = hipEventRecord(ring->chunk_ready, (hipStream_t)stream);
+  if (e == hipSuccess) e = hipStreamWaitEvent(ring->offload, ring->chunk_ready, 0);
+  if (e == hipSuccess && ring->copy_delay_us > 0) e = hipLaunchHostFunc(ring->offload, sleep_host_fn, &ring->copy_delay_us);
+  if (e == hipSuccess) e = hipMemcpyAsync(k_host_dst, k, bytes, hipMemcpyDeviceToHost, ring->offload);
+  if (e == hipSuccess) e = hipMemcpyAsync(v_host_dst, v, bytes, hipMemcpyDeviceToHost, ring->offload);
+  if (e == hipSuccess) e = hipEventRecord(ring->offload_done, ring->offload);
+  if (e != hipSuccess) return hip_fail(e, "write-back");
+  return XATTN_OK;
+}
+
+int xattn_ring_offload_wait(XattnRing* ring, void* stream) {
+  if (!ring) return fail(XATTN_ERR_INVALID, "ring must not be NULL");
+  hipError_t e = hipStreamWaitEvent((hipStream_t)stream, ring->offload_done, 0);
+  if (e != hipSuccess) return hip_fail(e, "write-back wait");
+  return XATTN_OK;
 }
 
 int xattn_ring_set_copy_delay_us(XattnRing* ring, int usec) {

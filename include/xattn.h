@@ -216,8 +216,27 @@ int xattn_ring_create(int num_slots, int slot_blocks, int num_kv_heads, int head
 /* Waits for the ring's pending copies, then frees it.  NULL is a no-op. */
 void xattn_ring_destroy(XattnRing *ring);
 /* Test hook: sleep `usec` microseconds on the transfer stream before every
- * slot copy (a host callback), widening any missing-wait race.  0 = off. */
+ * slot copy, and on the offload stream before every write-back (a host
+ * callback), widening any missing-wait race.  0 = off. */
 int xattn_ring_set_copy_delay_us(XattnRing *ring, int usec);
+
+/* Write-back of a prefilled chunk's K/V into the pinned host history: the
+ * design doc's offload step after prefill (the per-chunk D2H offload of the
+ * [Stream fix] stream table, offload_layer_kv_async / wait_layer_offload of
+ * the layerwise plan 1.2).  Enqueues on the ring's offload stream (default
+ * priority), after everything already enqueued on `stream`, the copies of
+ * num_blocks 128-token blocks of k and v (device, [num_blocks*128, Hkv, d]
+ * in the ring's dtype) to k_host_dst and v_host_dst (PINNED host memory of
+ * the same layout, typically the history arrays at block hist_blocks), and
+ * returns without waiting.  Every later slot copy of this ring waits for it,
+ * so the next chunk's prefill reads the written-back blocks; the caller keeps
+ * k and v unchanged until xattn_ring_offload_wait has ordered a stream after
+ * it.  Errors (nothing enqueued): NULL ring or pointers, num_blocks < 0
+ * (INVALID); destinations not pinned (NOT_PINNED). */
+int xattn_ring_offload_chunk(XattnRing *ring, const void *k, const void *v, void *k_host_dst,
+                             void *v_host_dst, int num_blocks, void *stream);
+/* Makes `stream` wait for the ring's last write-back. */
+int xattn_ring_offload_wait(XattnRing *ring, void *stream);
 
 /* Message of the last error on the calling thread ("" if none). */
 const char *xattn_last_error(void);

@@ -103,6 +103,59 @@ def test_ring_delayed_copies_give_identical_results(slots):
         assert torch.equal(l_, l0)
 
 
+def test_ring_write_back_feeds_the_next_chunk():
+    """Chunk 1's K/V, written back into the pinned history on the ring's
+    offload stream (every copy delayed 2 ms by a host callback), are read by
+    chunk 2's ring prefill: its estimate, selection and output equal chunk 2
+    with all K/V resident, and the host history holds chunk 1's K/V."""
+    L, lq = 16384, 1024
+    kw = dict(hq=8, hkv=2, d=128, stride=16, threshold=0.95, select_mode="chunk_vote", kv_chunk_tokens=1024)
+    w2 = make_random("wb2", seed=43, lq=[lq], lk=[L], **kw)
+    w1 = make_random("wb1", seed=44, lq=[lq], lk=[L - lq], **kw)
+    w1.k = w2.k[: L - lq].clone()  # chunk 1 sees the first L - lq keys of the same sequence
+    w1.v = w2.v[: L - lq].clone()
+    r1, r2 = Run(w1), Run(w2)
+    hkv, d = w2.num_kv_heads, w2.head_dim
+    nh, h1 = (L - lq) // 128, (L - 2 * lq) // 128
+    k_host = torch.empty((nh, 128, hkv, d), dtype=w2.dtype, pin_memory=True).fill_(float("nan"))
+    v_host = torch.empty((nh, 128, hkv, d), dtype=w2.dtype, pin_memory=True).fill_(float("nan"))
+    k_host[:h1].copy_(w2.k[: L - 2 * lq].reshape(h1, 128, hkv, d))
+    v_host[:h1].copy_(w2.v[: L - 2 * lq].reshape(h1, 128, hkv, d))
+    ring = X.Ring(4, 8, hkv, d, w2.dtype)
+    ring.set_copy_delay_us(2000)
+    k1, v1 = w2.k[L - 2 * lq: L - lq].cuda(), w2.v[L - 2 * lq: L - lq].cuda()
+    say("write-back: chunk 1 through the ring")
+    _run_ring(r1, w1, ring, k_host[:h1], v_host[:h1], k1, v1, h1)
+    say("write-back: chunk 1 K/V to host blocks %d..%d" % (h1, nh))
+    ring.offload_chunk(k1, v1, k_host[h1:], v_host[h1:], lq // 128)
+    k2, v2 = w2.k[L - lq:].cuda(), w2.v[L - lq:].cuda()
+    say("write-back: chunk 2 through the ring")
+    o2, l2, c2, a2 = _run_ring(r2, w2, ring, k_host, v_host, k2, v2, nh)
+    ring.offload_wait()
+    torch.cuda.synchronize()
+    ring.close()
+    assert torch.equal(k_host.reshape(-1, hkv, d), w2.k[: L - lq])
+    assert torch.equal(v_host.reshape(-1, hkv, d), w2.v[: L - lq])
+    say("write-back: chunk 2 resident")
+    o_res, l_res, c_res, a_res = r2.prefill()
+    assert torch.equal(a2["block_sums"], a_res["block_sums"])
+    assert torch.equal(a2["mask_kv"], a_res["mask_kv"])
+    assert torch.equal(c2, c_res)
+    assert (o2.float() - o_res.float()).abs().max().item() <= 2e-2
+
+
+def test_ring_write_back_rejects_pageable_destination():
+    ring = X.Ring(2, 2, 1, 128, torch.bfloat16)
+    k = torch.zeros((128, 1, 128), dtype=torch.bfloat16, device="cuda")
+    dst = torch.zeros((1, 128, 1, 128), dtype=torch.bfloat16)
+    with pytest.raises(X.XattnError) as ei:
+        ring.offload_chunk(k, k, dst, dst, 1)
+    assert ei.value.code == -5
+    with pytest.raises(X.XattnError):
+        ring.offload_chunk(k, k, dst, dst, -1)
+    ring.close()
+
+
 def test_ring_rejects_pageable_history():
     w = make_random("ring_err", seed=42, hq=2, hkv=1, d=128, lq=[256], lk=[1024], stride=8,
                     select_mode="chunk_vote")
