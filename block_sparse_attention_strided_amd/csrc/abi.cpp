@@ -277,7 +277,9 @@ hipError_t plan_attention(const XattnShape* sh, const Plan& p, const AttnArgs& a
                           void* ws, bool transpose_v, hipStream_t st) {
   if (p.dtype == XATTN_DTYPE_BF16) {
     char* vt = ws_at<char>(ws, p.off_vt);
-    if (transpose_v) {
+    AttnArgs probe = aa;
+    probe.num_pages = num_pages;
+    if (transpose_v && attention_reads_vt(probe, 0, p.d)) {
       VtArgs va;
       va.v = (const char*)v;
       va.vt = vt;

@@ -32,7 +32,7 @@ constexpr float kNegInf = -__builtin_huge_valf();
 #define XATTN_ILV 0
 #endif
 #ifndef XATTN_PF
-#define XATTN_PF 6
+#define XATTN_PF 3
 #endif
 
 
@@ -109,6 +109,21 @@ __device__ __forceinline__ void lgkm_wait(u32x4& a) {
 }
 template <int N>
 __device__ __forceinline__ void lgkm_wait(u32x4& a, u32x4& b) {
+  asm volatile("s_waitcnt lgkmcnt(%2)" : "+v"(a), "+v"(b) : "n"(N));
+}
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+// 8-byte transposing LDS read (gfx950): within each group of 16 lanes, lane
+// i receives 16-bit element i % 4 of the 8-byte chunks addressed by lanes
+// i / 4 + 4 e, e = 0..3 (element e of the result).
+template <int OFF>
+__device__ __forceinline__ u32x2 lds_read8_tr_at(uint32_t addr) {
+  static_assert(OFF >= 0 && OFF < 65536, "ds offset field");
+  u32x2 v;
+  asm volatile("ds_read_b64_tr_b16 %0, %1 offset:%2" : "=v"(v) : "v"(addr), "i"(OFF));
+  return v;
+}
+template <int N>
+__device__ __forceinline__ void lgkm_wait(u32x2& a, u32x2& b) {
   asm volatile("s_waitcnt lgkmcnt(%2)" : "+v"(a), "+v"(b) : "n"(N));
 }
 template <int N>
@@ -528,8 +543,10 @@ __global__ __launch_bounds__(256 * HPW) void attn_mfma(AttnArgs a, int hkv) {
 // phases and keeps the groups in anti-phase:
 //   barrier 2u+1 -> A: MFMA(u)     B: softmax(u-1)
 //   barrier 2u+2 -> A: softmax(u)  B: MFMA(u)
-// K and V^T tiles live in two 4-stage LDS rings (tile t in stage t % 4).  The
-// softmax phase of tile g also issues copy group g: K of tile g+3 and V^T of
+// K and V tiles (both in the caller's [key][kv head][d] layout) live in two
+// 4-stage LDS rings (tile t in stage t % 4); V^T fragments of the PV MFMAs
+// come from transposing LDS reads.  The softmax phase of tile g also issues
+// copy group g: K of tile g+3 and V of
 // tile g+2 (raw buffer loads straight to LDS, which count on vmcnt only).
 // Each wave waits for its own copies of a tile before the barrier that opens
 // the first phase reading it; register fences keep the compiler from moving
@@ -541,7 +558,7 @@ __global__ __launch_bounds__(512) void attn_pp(AttnArgs a, int hkv) {
   constexpr int KT = 64;               // keys per tile
   constexpr int KROW = D * 2;          // bytes per K row in LDS
   constexpr int KCPR = D / 8;          // 16-byte chunks per K row
-  constexpr int TILE = KT * KROW;      // bytes of one K (or V^T) tile
+  constexpr int TILE = KT * KROW;      // bytes of one K (or V) tile
   constexpr int CH = TILE / 16;        // 16-byte chunks per tile
   constexpr int LPW = CH / (64 * NW);  // direct loads per wave per operand
   constexpr int ST = 4;                // ring stages
@@ -549,7 +566,7 @@ __global__ __launch_bounds__(512) void attn_pp(AttnArgs a, int hkv) {
   constexpr int NPV = 4 * (D / 32);    // O^T MFMAs per tile
   static_assert(LPW >= 1 && CH % (64 * NW) == 0, "tile / workgroup mismatch");
   static_assert(NS == NPV, "phase interleave assumes equal MFMA counts");
-  __shared__ __align__(1024) char tiles[2 * ST * TILE];  // K stages, then V^T stages
+  __shared__ __align__(1024) char tiles[2 * ST * TILE];  // K stages, then V stages
   extern __shared__ int32_t list[];
 
   // ---- work unit (XCD-aware: the 8 XCDs take consecutive ids round-robin)
@@ -588,7 +605,10 @@ __global__ __launch_bounds__(512) void attn_pp(AttnArgs a, int hkv) {
   // Per-thread constant parts of the direct-load addresses.
   const long long k_page_bytes = (long long)kBlock * hkv * D * 2;
   const long long k_row_bytes = (long long)hkv * D * 2;
-  const long long vt_page_bytes = (long long)hkv * D * kBlock * 2;
+  // V row swizzle of the transposing reads: the rows one read instruction
+  // touches (4hh + c/4 plus a multiple of 8) spread over all 64 banks, two
+  // lanes per bank (the minimum for 512 bytes)
+  auto vn_swz = [](int row) { return (KCPR == 16) ? 4 * (row & 3) : 4 * ((row >> 1) & 1); };
   int koff[LPW], voff[LPW];
 #pragma unroll
   for (int n = 0; n < LPW; ++n) {
@@ -596,19 +616,19 @@ __global__ __launch_bounds__(512) void attn_pp(AttnArgs a, int hkv) {
     const int krow = idx / KCPR, kpch = idx % KCPR;
     const int kc = (KCPR == 16) ? (kpch ^ (krow & 15)) : (kpch ^ ((krow >> 1) & 7));
     koff[n] = (int)(krow * k_row_bytes + kc * 16);
-    const int vrow = idx >> 3, vpch = idx & 7;
-    const int vc = vpch ^ ((vrow >> 1) & 7);
-    voff[n] = (vrow * kBlock + vc * 8) * 2;
+    // V in its own layout, 16-byte chunks of a row XOR-swizzled for the
+    // transposing reads
+    voff[n] = (int)(krow * k_row_bytes + (kpch ^ vn_swz(krow)) * 16);
   }
   const char* kbase = a.k.base + (long long)g * D * 2;
-  const char* vbase = a.vt + (long long)g * D * kBlock * 2;
+  const char* vbase = a.v.base + (long long)g * D * 2;
 
   // Tile copies: one raw buffer descriptor per operand for the whole launch
-  // (its K and V^T spans are below 2^31 bytes, checked by the launcher); a
+  // (its K and V spans are below 2^31 bytes, checked by the launcher); a
   // tile is a 32-bit byte offset in soffset plus the constant per-lane
   // offsets, its LDS destination goes to m0.  Copy group gi copies K of
-  // tile gi+3 into K stage (gi+3)%4 and V^T of tile gi+2 into V^T stage
-  // (gi+2)%4.  Those stages last held K of tile gi-1 and V^T of tile gi-2,
+  // tile gi+3 into K stage (gi+3)%4 and V of tile gi+2 into V stage
+  // (gi+2)%4.  Those stages last held K of tile gi-1 and V of tile gi-2,
   // both last read in the MFMA phases of tile gi-1, which both groups have
   // finished before group gi is issued.  Every group issues all its loads:
   // a tile past the end (or before the start) re-reads the nearest existing
@@ -618,8 +638,8 @@ __global__ __launch_bounds__(512) void attn_pp(AttnArgs a, int hkv) {
   const __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc(
       (void*)kbase, (short)0, (int)(a.num_pages * k_page_bytes - (long long)g * D * 2), kBufFlags);
   const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc(
-      (void*)vbase, (short)0, (int)(a.num_pages * vt_page_bytes - (long long)g * D * kBlock * 2), kBufFlags);
-  const int kpb = (int)k_page_bytes, vpb = (int)vt_page_bytes, khalf = (int)(KT * k_row_bytes);
+      (void*)vbase, (short)0, (int)(a.num_pages * k_page_bytes - (long long)g * D * 2), kBufFlags);
+  const int kpb = (int)k_page_bytes, khalf = (int)(KT * k_row_bytes);
   char* const kl0 = tiles + wu * LPW * 1024;
   char* const vl0 = tiles + ST * TILE + wu * LPW * 1024;
   auto src_tile = [&](int t) { return t < 0 ? 0 : (t < ntile ? t : ntile - 1); };
@@ -645,11 +665,11 @@ __global__ __launch_bounds__(512) void attn_pp(AttnArgs a, int hkv) {
     const int tv = src_tile(gi + 2), tk = src_tile(gi + 3);
     const int ev = entry_of(tv), ek = entry_of(tk);
     soff_k = (ek >> 1) * kpb + (tk & 1) * khalf;
-    soff_v = (ev >> 1) * vpb + (tv & 1) * (KT * 2);
+    soff_v = (ev >> 1) * kpb + (tv & 1) * khalf;
     kl = kl0 + ((gi + 3) & (ST - 1)) * TILE;
     vl = vl0 + (gi + 2 < 0 ? 0 : ((gi + 2) & (ST - 1))) * TILE;
   };
-  // part n < LPW: K chunk n, else V^T chunk n - LPW
+  // part n < LPW: K chunk n, else V chunk n - LPW
   auto copy_part = [&](auto n_tag) {
     constexpr int N = decltype(n_tag)::value;
     if constexpr (N < LPW) {
@@ -669,12 +689,23 @@ __global__ __launch_bounds__(512) void attn_pp(AttnArgs a, int hkv) {
   // Per-lane LDS addresses of the MFMA A fragments in stage 0.
   const uint32_t lds0 = (uint32_t)(uintptr_t)(lds_ptr_t)tiles;
   const int kswz = (KCPR == 16) ? (l32 & 15) : ((l32 >> 1) & 7);
-  const int vswz = (l32 >> 1) & 7;
-  uint32_t kaddr[D / 16], vaddr[4];
+  uint32_t kaddr[D / 16], vaddr[4] = {0u, 0u, 0u, 0u};
 #pragma unroll
   for (int kk = 0; kk < D / 16; ++kk) kaddr[kk] = lds0 + l32 * KROW + (((2 * kk + hh) ^ kswz) * 16);
+  {
+    // Transposing reads of V rows: for d block n and read r of key chunk m,
+    // lane c of 16-lane group G (c = lane % 16) addresses key row
+    // 16m + 8r + 4hh + c/4 at d = 32n + 16 (G % 2) + 4 (c % 4); lane l then
+    // holds V[16m + 8r + 4hh + e][32n + l % 32], e = 0..3, in k-slots
+    // 8hh + 4r + e: the keys P^T's k-slots hold (see vperm).  The row part
+    // 16m + 8r is an immediate offset; vaddr[n] carries the rest.
+    const int c = lane & 15, row0 = 4 * hh + (c >> 2);
 #pragma unroll
-  for (int m = 0; m < 4; ++m) vaddr[m] = lds0 + ST * TILE + l32 * (KT * 2) + (((2 * m + hh) ^ vswz) * 16);
+    for (int n = 0; n < D / 32; ++n) {
+      const int d = 32 * n + 16 * ((lane >> 4) & 1) + 4 * (c & 3);
+      vaddr[n] = lds0 + ST * TILE + row0 * KROW + (((d >> 3) ^ vn_swz(row0)) * 16) + ((d >> 2) & 1) * 8;
+    }
+  }
 
   f32x16 oacc[D / 32];
 #pragma unroll
@@ -710,32 +741,45 @@ __global__ __launch_bounds__(512) void attn_pp(AttnArgs a, int hkv) {
     // op J: a PV step when PV and (J even or !SS), else an S step
     auto is_pv = [](int j) constexpr { return PV && (!SS || (j % 2 == 0)); };
     auto sub_idx = [](int j) constexpr { return (PV && SS) ? j / 2 : j; };
-    auto frag = [&](auto j_tag) -> u32x4 {
+    // LDS read instructions of op j (a PV step reads two halves when V is
+    // read transposed), and those of ops J+1 .. J+PF (issued before op J's
+    // wait)
+    auto after = [=](int j) constexpr {
+      int c = 0;
+      for (int x = j + 1; x < NOPS && x <= j + PF; ++x) c += is_pv(x) ? 2 : 1;
+      return c < 15 ? c : 15;  // lgkmcnt field limit; a smaller count only waits longer
+    };
+    // fragment of op J: fr[J] (16-byte read) or fl[J], fh[J] (transposing
+    // halves); reads run PF ops ahead of the MFMAs
+    u32x4 fr[NOPS];
+    u32x2 fl[NOPS], fh[NOPS];
+    auto frag = [&](auto j_tag) {
       constexpr int J = decltype(j_tag)::value;
       constexpr int I = sub_idx(J);
       if constexpr (is_pv(J)) {
         constexpr int M = I / (D / 32), N = I % (D / 32);
-        return lds_read16_at<N * 32 * KT * 2>(va4[M]);
+        fl[J] = lds_read8_tr_at<(16 * M) * KROW>(va4[N]);
+        fh[J] = lds_read8_tr_at<(16 * M + 8) * KROW>(va4[N]);
       } else {
         constexpr int KK = I >> 1, HALF = I & 1;
-        return lds_read16_at<HALF * 32 * KROW>(ka[KK]);
+        fr[J] = lds_read16_at<HALF * 32 * KROW>(ka[KK]);
       }
     };
-    // fragment of op J lives in fr[J]; reads run PF ops ahead of the MFMAs
-    u32x4 fr[NOPS];
     [&]<int... J>(std::integer_sequence<int, J...>) {
-      ((fr[J] = frag(std::integral_constant<int, J>{})), ...);
+      (frag(std::integral_constant<int, J>{}), ...);
     }(std::make_integer_sequence<int, (PF < NOPS ? PF : NOPS)>{});
     auto op = [&](auto j_tag) {
       constexpr int J = decltype(j_tag)::value;
       constexpr int I = sub_idx(J);
-      if constexpr (J + PF < NOPS) {
-        fr[J + PF] = frag(std::integral_constant<int, J + PF>{});
-        lgkm_wait<PF>(fr[J]);
+      if constexpr (J + PF < NOPS) frag(std::integral_constant<int, J + PF>{});
+      u32x4 fa;
+      if constexpr (is_pv(J)) {
+        lgkm_wait<after(J)>(fl[J], fh[J]);
+        fa = u32x4{fl[J][0], fl[J][1], fh[J][0], fh[J][1]};
       } else {
-        lgkm_wait<NOPS - 1 - J>(fr[J]);
+        lgkm_wait<after(J)>(fr[J]);
+        fa = fr[J];
       }
-      const u32x4 fa = fr[J];
       if constexpr (is_pv(J)) {
         constexpr int M = I / (D / 32), N = I % (D / 32);
         oacc[N] = mfma32(__builtin_bit_cast(bf16x8, fa), pb[M], oacc[N]);
@@ -839,12 +883,12 @@ __global__ __launch_bounds__(512) void attn_pp(AttnArgs a, int hkv) {
   };
   using T_ = std::integral_constant<bool, true>;
   using F_ = std::integral_constant<bool, false>;
-  // Prologue: copy groups -3..-1 (K of tiles 0..2, V^T of tiles 0..1);
+  // Prologue: copy groups -3..-1 (K of tiles 0..2, V of tiles 0..1);
   // before the barrier that opens a phase reading K of tile m, every wave
   // has its copies of group m-3 done: groups m-2 and m-1 may be in flight
   // for A (it issued group m-1 in the phase just ending), only group m-2 for B.
   if (ntile > 0) {
-    copy_group(-3);  // V^T part: tile 0, the same bytes as group -2's
+    copy_group(-3);  // V part: tile 0, the same bytes as group -2's
     copy_group(-2);
     copy_group(-1);
     wait_vmcnt<4 * LPW>();
@@ -1115,6 +1159,14 @@ __global__ __launch_bounds__(256) void split_merge_kernel(SplitMergeArgs a) {
   if (a.lse && dv == 0) a.lse[(long long)h * a.total_q + tok] = lse;
 }
 
+// The ping-pong kernel serves even GQA groups whose K/V spans fit 32-bit
+// buffer offsets.
+bool uses_attn_pp(const AttnArgs& a, int head_dim) {
+  const int hkv = a.hq / a.group;
+  const long long span = (long long)a.num_pages * kBlock * hkv * head_dim * 2;
+  return a.group % 2 == 0 && span < (1ll << 31);
+}
+
 template <int D>
 hipError_t attn_dispatch(const AttnArgs& a, int dtype, int batch, hipStream_t s) {
   if (dtype == 0) {
@@ -1122,9 +1174,7 @@ hipError_t attn_dispatch(const AttnArgs& a, int dtype, int batch, hipStream_t s)
     const int hpw = (a.group % 2 == 0) ? 2 : 1;
     const int nwg = (a.n_order > 0 ? a.n_order : batch * a.max_qb) * hkv * (a.group / hpw);
     const size_t shm = (size_t)(a.max_kb + 1) * sizeof(int32_t);
-    // The ping-pong kernel addresses K and V^T with 32-bit buffer offsets.
-    const long long span = (long long)a.num_pages * kBlock * hkv * D * 2;
-    if (hpw == 2 && span < (1ll << 31)) hipLaunchKernelGGL((attn_pp<D, XATTN_PF>), dim3(nwg), dim3(512), shm, s, a, hkv);
+    if (uses_attn_pp(a, D)) hipLaunchKernelGGL((attn_pp<D, XATTN_PF>), dim3(nwg), dim3(512), shm, s, a, hkv);
     else if (hpw == 2) hipLaunchKernelGGL((attn_mfma<D, 2>), dim3(nwg), dim3(512), shm, s, a, hkv);
     else hipLaunchKernelGGL((attn_mfma<D, 1>), dim3(nwg), dim3(256), shm, s, a, hkv);
   } else {
@@ -1135,6 +1185,10 @@ hipError_t attn_dispatch(const AttnArgs& a, int dtype, int batch, hipStream_t s)
 }
 
 }  // namespace
+
+bool attention_reads_vt(const AttnArgs& a, int dtype, int head_dim) {
+  return dtype == 0 && !uses_attn_pp(a, head_dim);
+}
 
 hipError_t launch_attention(const AttnArgs& a, int dtype, int head_dim, int batch,
                             hipStream_t s) {

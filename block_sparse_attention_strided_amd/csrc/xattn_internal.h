@@ -167,6 +167,8 @@ hipError_t launch_vt_transpose(const VtArgs& a, hipStream_t s);
 hipError_t launch_plan(const PlanArgs& a, int batch, hipStream_t s);
 hipError_t launch_attention(const AttnArgs& a, int dtype, int head_dim, int batch,
                             hipStream_t s);
+// Whether the attention launch for `a` reads the V^T pages (a.vt).
+bool attention_reads_vt(const AttnArgs& a, int dtype, int head_dim);
 hipError_t launch_merge(const MergeArgs& a, hipStream_t s);
 hipError_t launch_split_merge(const SplitMergeArgs& a, hipStream_t s);
 

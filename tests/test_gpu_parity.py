@@ -166,6 +166,7 @@ ATTN_CASES = {
     "bf16_d128_gqa2_varlen": dict(hq=4, hkv=2, d=128, lq=[512, 256], lk=[1024, 256]),
     "bf16_d64_gqa1": dict(hq=2, hkv=2, d=64, lq=[384], lk=[896]),
     "bf16_d128_gqa2_causal": dict(hq=4, hkv=2, d=128, lq=[1280], lk=[1280]),
+    "bf16_d64_gqa2_varlen": dict(hq=4, hkv=2, d=64, lq=[640, 128], lk=[1408, 384]),
     "bf16_paged": dict(hq=4, hkv=1, d=128, lq=[256, 128], lk=[768, 640], paged=True),
     "f32_d64": dict(hq=2, hkv=1, d=64, lq=[256], lk=[512], dtype=torch.float32),
 }
