@@ -191,10 +191,14 @@ __device__ __forceinline__ void est_copy_rows(__amdgpu_buffer_rsrc_t r, char* ld
 }
 
 constexpr int kEstBig = 256;
+#ifndef XATTN_EST_NBUF
+#define XATTN_EST_NBUF 4  // stage buffers of the 128 x 128 tile kernel
+#endif
 
 // TT x TT tile over NW waves: wave w owns TT/2 columns (half w&1) x 2*TT/NW
-// rows (part w>>1); XT x YT accumulators.
-template <int D, int S, int TT, int NW>
+// rows (part w>>1); XT x YT accumulators.  NBUF LDS stage buffers: NBUF - 1
+// stages of copies are in flight while one is computed.
+template <int D, int S, int TT, int NW, int NBUF>
 __global__ __launch_bounds__(64 * NW) void est_gemm_bf16(EstArgs a) {
   constexpr int RB = kBlock / S;
   constexpr int BK = 64;             // reduction elements per stage
@@ -205,10 +209,10 @@ __global__ __launch_bounds__(64 * NW) void est_gemm_bf16(EstArgs a) {
   constexpr int XT = TT / 2 / 32;    // 32-column accumulator tiles per wave
   constexpr int YT = TT / WR / 32;   // 32-row accumulator tiles per wave
   constexpr int LPW = TT / (8 * NW); // copy instructions per wave per operand
-  static_assert(NST % 2 == 0, "stage loop is unrolled by two");
+  static_assert(NST % NBUF == 0, "stage loop is unrolled by NBUF");
   static_assert(XT >= 1 && YT >= 1 && LPW >= 1 && TT % (8 * NW) == 0, "tile / wave split");
   typedef __attribute__((address_space(3))) void* lds_ptr;
-  __shared__ __align__(1024) char lds[4 * TILEB];  // buffer 0: K, Q; buffer 1: K, Q
+  __shared__ __align__(1024) char lds[2 * NBUF * TILEB];  // buffer b: K, then Q
 
   // XCD-aware work unit: the 8 XCDs take consecutive workgroup ids
   // round-robin, so logical unit (id % 8) * (n / 8) + id / 8 gives each XCD a
@@ -272,9 +276,9 @@ __global__ __launch_bounds__(64 * NW) void est_gemm_bf16(EstArgs a) {
 
   // ---- fragment addresses: row swizzle = l32 & 7 for every tile row a lane reads
   const uint32_t lds0 = (uint32_t)(uintptr_t)(lds_ptr)lds;
-  uint32_t ka[2][4], qa[2][4];
+  uint32_t ka[NBUF][4], qa[NBUF][4];
 #pragma unroll
-  for (int bf = 0; bf < 2; ++bf)
+  for (int bf = 0; bf < NBUF; ++bf)
 #pragma unroll
     for (int kk = 0; kk < 4; ++kk) {
       const uint32_t ch = (uint32_t)(((2 * kk + hh) ^ (l32 & 7)) * 16);
@@ -325,18 +329,24 @@ __global__ __launch_bounds__(64 * NW) void est_gemm_bf16(EstArgs a) {
     }
   };
 
-  // ---- stage loop: wait for this wave's copies of the stage, barrier (all
-  // copies visible, the other buffer free), copy the next stage, compute
-  issue(0, 0);
-  for (int st = 0; st < NST; st += 2) {
-    est_wait_vmcnt<0>();
-    __builtin_amdgcn_s_barrier();
-    issue(st + 1, 1);
-    compute(std::integral_constant<int, 0>{});
-    est_wait_vmcnt<0>();
-    __builtin_amdgcn_s_barrier();
-    if (st + 2 < NST) issue(st + 2, 0);
-    compute(std::integral_constant<int, 1>{});
+  // ---- stage loop: wait for this wave's copies of stage st (the copies of
+  // the NBUF - 2 later stages may stay in flight), barrier (every wave's
+  // copies of stage st visible; buffer (st - 1) % NBUF, computed in the
+  // previous step, free), copy stage st + NBUF - 1 into it, compute st
+  constexpr int PER = 2 * LPW;  // copy instructions per wave and stage
+#pragma unroll
+  for (int x = 0; x < NBUF - 1; ++x) issue(x, x);
+  for (int st0 = 0; st0 < NST; st0 += NBUF) {
+    [&]<int... B>(std::integer_sequence<int, B...>) {
+      ([&] {
+        const int st = st0 + B;
+        if (st + NBUF - 2 < NST) est_wait_vmcnt<(NBUF - 2) * PER>();
+        else est_wait_vmcnt<0>();
+        __builtin_amdgcn_s_barrier();
+        if (st + NBUF - 1 < NST) issue(st + NBUF - 1, (B + NBUF - 1) % NBUF);
+        compute(std::integral_constant<int, B>{});
+      }(), ...);
+    }(std::make_integer_sequence<int, NBUF>{});
   }
 
   // ---- epilogue: per (query row, key block) base-2 log-sum-exp over the
@@ -345,6 +355,13 @@ __global__ __launch_bounds__(64 * NW) void est_gemm_bf16(EstArgs a) {
   constexpr int NBLK = 32 / RB;  // key blocks per 32-column accumulator
   constexpr int EPB = 16 / NBLK; // accumulator values per lane and block
   const int j_end = a.jb0 + a.jb_count;
+  // Whole tile inside the rows, the launch's columns and the causal bound
+  // (the common case): no per-element masks.  Exponentials and logarithm
+  // are the bare hardware instructions (v_exp_f32 / v_log_f32): every term
+  // is 2^(z - max) <= 1 and the sum is >= 1, so flushing terms below 2^-126
+  // to zero changes nothing at fp32 resolution.
+  const bool unmasked = (r0 + TT <= R) && (c0 + TT <= c_end) && (c0 + TT - 1 <= r0 + o_s);
+  const float sc = a.scale2;
 #pragma unroll
   for (int y = 0; y < YT; ++y) {
     const int r = r0 + wr * (YT * 32) + y * 32 + l32;
@@ -353,20 +370,28 @@ __global__ __launch_bounds__(64 * NW) void est_gemm_bf16(EstArgs a) {
       const int cblk = c0 + wc * (TT / 2) + x * 32;
 #pragma unroll
       for (int m = 0; m < NBLK; ++m) {
-        float z[EPB];
-        float mx = kNegInf;
+        float mx = kNegInf, sm = 0.f;
+        if (unmasked) {
+          float am = acc[x][y][m * EPB];
 #pragma unroll
-        for (int q = 0; q < EPB; ++q) {
-          const int e = m * EPB + q;
-          const int c = cblk + 8 * (e >> 2) + 4 * hh + (e & 3);
-          const bool ok = (r < R) && (c < c_end) && (c <= r + o_s);
-          z[q] = ok ? acc[x][y][e] * a.scale2 : kNegInf;
-          mx = fmaxf(mx, z[q]);
-        }
-        float sm = 0.f;
-        if (mx != kNegInf) {
+          for (int q = 1; q < EPB; ++q) am = fmaxf(am, acc[x][y][m * EPB + q]);
+          mx = am * sc;
 #pragma unroll
-          for (int q = 0; q < EPB; ++q) sm += exp2f(z[q] - mx);
+          for (int q = 0; q < EPB; ++q) sm += __builtin_amdgcn_exp2f(fmaf(acc[x][y][m * EPB + q], sc, -mx));
+        } else {
+          float z[EPB];
+#pragma unroll
+          for (int q = 0; q < EPB; ++q) {
+            const int e = m * EPB + q;
+            const int c = cblk + 8 * (e >> 2) + 4 * hh + (e & 3);
+            const bool ok = (r < R) && (c < c_end) && (c <= r + o_s);
+            z[q] = ok ? acc[x][y][e] * sc : kNegInf;
+            mx = fmaxf(mx, z[q]);
+          }
+          if (mx != kNegInf) {
+#pragma unroll
+            for (int q = 0; q < EPB; ++q) sm += __builtin_amdgcn_exp2f(z[q] - mx);
+          }
         }
         const auto pm = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx), false, false);
         const auto ps = __builtin_amdgcn_permlane32_swap(__float_as_uint(sm), __float_as_uint(sm), false, false);
@@ -375,8 +400,9 @@ __global__ __launch_bounds__(64 * NW) void est_gemm_bf16(EstArgs a) {
         const float M = fmaxf(m0, m1);
         float lse = kNegInf;
         if (M != kNegInf) {
-          const float tot = (m0 == kNegInf ? 0.f : s0 * exp2f(m0 - M)) + (m1 == kNegInf ? 0.f : s1 * exp2f(m1 - M));
-          lse = M + log2f(tot);
+          const float tot = (m0 == kNegInf ? 0.f : s0 * __builtin_amdgcn_exp2f(m0 - M)) +
+                            (m1 == kNegInf ? 0.f : s1 * __builtin_amdgcn_exp2f(m1 - M));
+          lse = M + __builtin_amdgcn_logf(tot);
         }
         const int j = cblk / RB + m;
         if (hh == 0 && r < R && j < j_end && j * RB < C)
@@ -575,12 +601,12 @@ hipError_t est_dispatch(const EstArgs& a, int dtype, int batch, hipStream_t st) 
       if (nbig >= 256) {
         a2.tiles_c = (int)big.x;
         a2.tiles_r = (int)big.y;
-        hipLaunchKernelGGL((est_gemm_bf16<D, S, kEstBig, 8>), dim3((unsigned)nbig), dim3(512), 0, st, a2);
+        hipLaunchKernelGGL((est_gemm_bf16<D, S, kEstBig, 8, 2>), dim3((unsigned)nbig), dim3(512), 0, st, a2);
       } else {
         a2.tiles_c = (a.jb_count * RB + kEstTile - 1) / kEstTile;
         a2.tiles_r = (a.max_r + kEstTile - 1) / kEstTile;
         const long long n = (long long)a2.tiles_c * a2.tiles_r * batch * a.hq;
-        hipLaunchKernelGGL((est_gemm_bf16<D, S, kEstTile, 4>), dim3((unsigned)n), dim3(256), 0, st, a2);
+        hipLaunchKernelGGL((est_gemm_bf16<D, S, kEstTile, 4, XATTN_EST_NBUF>), dim3((unsigned)n), dim3(256), 0, st, a2);
       }
       return hipGetLastError();
     }
