@@ -194,23 +194,37 @@ constexpr int kEstBig = 256;
 #ifndef XATTN_EST_NBUF
 #define XATTN_EST_NBUF 4  // stage buffers of the 128 x 128 tile kernel
 #endif
+// 256 x 256 tiles: 2 stage buffers of 64 reduction elements (measured at
+// 32K: 4 buffers of 32 elements 0.082 ms, 2 of 32 0.088, 2 of 64 0.078)
+#ifndef XATTN_EST_BIG_NBUF
+#define XATTN_EST_BIG_NBUF 2
+#endif
+#ifndef XATTN_EST_BIG_BK
+#define XATTN_EST_BIG_BK 64
+#endif
 
 // TT x TT tile over NW waves: wave w owns TT/2 columns (half w&1) x 2*TT/NW
-// rows (part w>>1); XT x YT accumulators.  NBUF LDS stage buffers: NBUF - 1
-// stages of copies are in flight while one is computed.
-template <int D, int S, int TT, int NW, int NBUF>
+// rows (part w>>1); XT x YT accumulators.  A stage covers BK reduction
+// elements (LDS rows of 2*BK bytes); NBUF LDS stage buffers: NBUF - 1 stages
+// of copies are in flight while one is computed.
+template <int D, int S, int TT, int NW, int NBUF, int BK>
 __global__ __launch_bounds__(64 * NW) void est_gemm_bf16(EstArgs a) {
   constexpr int RB = kBlock / S;
-  constexpr int BK = 64;             // reduction elements per stage
   constexpr int TILEB = TT * BK * 2; // bytes of one operand tile
+  constexpr int CPR = BK / 8;        // 16-byte chunks per LDS row
+  constexpr int RPI = 64 / CPR;      // rows per copy instruction (1 KiB)
+  constexpr int KS = BK / 16;        // MFMA k-steps per stage
   constexpr int DQ = D / BK;         // stages per token offset
   constexpr int NST = S * DQ;        // stages (even for every supported S, D)
   constexpr int WR = NW / 2;         // wave rows
   constexpr int XT = TT / 2 / 32;    // 32-column accumulator tiles per wave
   constexpr int YT = TT / WR / 32;   // 32-row accumulator tiles per wave
-  constexpr int LPW = TT / (8 * NW); // copy instructions per wave per operand
+  constexpr int LPW = TT / (RPI * NW); // copy instructions per wave per operand
+  static_assert(BK == 32 || BK == 64, "stage width");
   static_assert(NST % NBUF == 0, "stage loop is unrolled by NBUF");
-  static_assert(XT >= 1 && YT >= 1 && LPW >= 1 && TT % (8 * NW) == 0, "tile / wave split");
+  static_assert(XT >= 1 && YT >= 1 && LPW >= 1 && TT % (RPI * NW) == 0, "tile / wave split");
+  // 16-byte chunk swizzle of LDS row `row` (conflict-free fragment reads)
+  auto swz = [](int row) { return BK == 64 ? (row & 7) : ((row >> 2) & 3); };
   typedef __attribute__((address_space(3))) void* lds_ptr;
   __shared__ __align__(1024) char lds[2 * NBUF * TILEB];  // buffer b: K, then Q
 
@@ -242,15 +256,15 @@ __global__ __launch_bounds__(64 * NW) void est_gemm_bf16(EstArgs a) {
   const int wc = w & 1, wr = w >> 1;
   const int l32 = lane & 31, hh = lane >> 5;
 
-  // ---- copies: instruction n of wave w fills tile rows (LPW*w+n)*8 .. +8
+  // ---- copies: instruction n of wave w fills tile rows (LPW*w+n)*RPI .. +RPI
   const long long q_tok = (long long)a.hq * D * 2;
   const long long k_row = (long long)a.k.kv_heads * D * 2;
   constexpr uint32_t kOut = 0x80000000u;  // beyond either descriptor's bound
   uint32_t kvo[LPW], qvo[LPW];
 #pragma unroll
   for (int n = 0; n < LPW; ++n) {
-    const int row = (w * LPW + n) * 8 + (lane >> 3);
-    const int lc = (lane & 7) ^ (row & 7);  // logical chunk stored at this lane's position
+    const int row = (w * LPW + n) * RPI + lane / CPR;
+    const int lc = (lane % CPR) ^ swz(row);  // logical chunk stored at this lane's position
     const int c = c0 + row, r = r0 + row;
     kvo[n] = kOut;
     if (c < c_end) {
@@ -274,16 +288,17 @@ __global__ __launch_bounds__(64 * NW) void est_gemm_bf16(EstArgs a) {
     est_copy_rows<LPW>(rq, qd, qvo, so_q);
   };
 
-  // ---- fragment addresses: row swizzle = l32 & 7 for every tile row a lane reads
+  // ---- fragment addresses: every tile row a lane reads has the swizzle of
+  // row l32 (rows differ by multiples of 32)
   const uint32_t lds0 = (uint32_t)(uintptr_t)(lds_ptr)lds;
-  uint32_t ka[NBUF][4], qa[NBUF][4];
+  uint32_t ka[NBUF][KS], qa[NBUF][KS];
 #pragma unroll
   for (int bf = 0; bf < NBUF; ++bf)
 #pragma unroll
-    for (int kk = 0; kk < 4; ++kk) {
-      const uint32_t ch = (uint32_t)(((2 * kk + hh) ^ (l32 & 7)) * 16);
-      ka[bf][kk] = lds0 + bf * 2 * TILEB + (wc * (TT / 2) + l32) * 128 + ch;
-      qa[bf][kk] = lds0 + bf * 2 * TILEB + TILEB + (wr * (YT * 32) + l32) * 128 + ch;
+    for (int kk = 0; kk < KS; ++kk) {
+      const uint32_t ch = (uint32_t)(((2 * kk + hh) ^ swz(l32)) * 16);
+      ka[bf][kk] = lds0 + bf * 2 * TILEB + (wc * (TT / 2) + l32) * (BK * 2) + ch;
+      qa[bf][kk] = lds0 + bf * 2 * TILEB + TILEB + (wr * (YT * 32) + l32) * (BK * 2) + ch;
     }
 
   f32x16 acc[XT][YT];
@@ -294,7 +309,7 @@ __global__ __launch_bounds__(64 * NW) void est_gemm_bf16(EstArgs a) {
 #pragma unroll
       for (int e = 0; e < 16; ++e) acc[x][y][e] = 0.f;
 
-  // one stage: 4 k-steps of 16; k-step kk+1's XT + YT fragments are read
+  // one stage: KS k-steps of 16; k-step kk+1's XT + YT fragments are read
   // while k-step kk's XT * YT MFMAs issue
   constexpr int NF = XT + YT;
   auto compute = [&](auto bf_tag) {
@@ -302,17 +317,17 @@ __global__ __launch_bounds__(64 * NW) void est_gemm_bf16(EstArgs a) {
     u32x4 f[NF], gq[NF];
     auto rd = [&](u32x4* dst, int kk) {
       [&]<int... X>(std::integer_sequence<int, X...>) {
-        ((dst[X] = est_lds_read16<X * 4096>(ka[BF][kk])), ...);
+        ((dst[X] = est_lds_read16<X * 32 * BK * 2>(ka[BF][kk])), ...);
       }(std::make_integer_sequence<int, XT>{});
       [&]<int... Y>(std::integer_sequence<int, Y...>) {
-        ((dst[XT + Y] = est_lds_read16<Y * 4096>(qa[BF][kk])), ...);
+        ((dst[XT + Y] = est_lds_read16<Y * 32 * BK * 2>(qa[BF][kk])), ...);
       }(std::make_integer_sequence<int, YT>{});
     };
     rd(f, 0);
 #pragma unroll
-    for (int kk = 0; kk < 4; ++kk) {
-      if (kk + 1 < 4) {
-        rd(gq, kk + 1 < 4 ? kk + 1 : 0);
+    for (int kk = 0; kk < KS; ++kk) {
+      if (kk + 1 < KS) {
+        rd(gq, kk + 1 < KS ? kk + 1 : 0);
         est_lgkm_wait_arr<NF, NF>(f);
       } else {
         est_lgkm_wait_arr<0, NF>(f);
@@ -322,7 +337,7 @@ __global__ __launch_bounds__(64 * NW) void est_gemm_bf16(EstArgs a) {
 #pragma unroll
         for (int y = 0; y < YT; ++y)
           acc[x][y] = mfma32(__builtin_bit_cast(bf16x8, f[x]), __builtin_bit_cast(bf16x8, f[XT + y]), acc[x][y]);
-      if (kk + 1 < 4) {
+      if (kk + 1 < KS) {
 #pragma unroll
         for (int z = 0; z < NF; ++z) f[z] = gq[z];
       }
@@ -601,12 +616,13 @@ hipError_t est_dispatch(const EstArgs& a, int dtype, int batch, hipStream_t st) 
       if (nbig >= 256) {
         a2.tiles_c = (int)big.x;
         a2.tiles_r = (int)big.y;
-        hipLaunchKernelGGL((est_gemm_bf16<D, S, kEstBig, 8, 2>), dim3((unsigned)nbig), dim3(512), 0, st, a2);
+        hipLaunchKernelGGL((est_gemm_bf16<D, S, kEstBig, 8, XATTN_EST_BIG_NBUF, XATTN_EST_BIG_BK>), dim3((unsigned)nbig),
+                           dim3(512), 0, st, a2);
       } else {
         a2.tiles_c = (a.jb_count * RB + kEstTile - 1) / kEstTile;
         a2.tiles_r = (a.max_r + kEstTile - 1) / kEstTile;
         const long long n = (long long)a2.tiles_c * a2.tiles_r * batch * a.hq;
-        hipLaunchKernelGGL((est_gemm_bf16<D, S, kEstTile, 4, XATTN_EST_NBUF>), dim3((unsigned)n), dim3(256), 0, st, a2);
+        hipLaunchKernelGGL((est_gemm_bf16<D, S, kEstTile, 4, XATTN_EST_NBUF, 64>), dim3((unsigned)n), dim3(256), 0, st, a2);
       }
       return hipGetLastError();
     }
