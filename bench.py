@@ -247,6 +247,24 @@ def main():
     cnt = counts.cpu().tolist()
 
     stages = {}
+    # the same step reusing this step's selection (another layer sharing it):
+    # no estimate, no selection, and in ring mode no history K streamed for them
+    pr_reuse = X.make_params(stride=w.stride, threshold=w.threshold, kv_chunk_tokens=w.kv_chunk_tokens,
+                             select_mode=w.select_mode, group_agg=w.group_agg, reuse_selection=1)
+    aux_reuse = {"mask_kv": mask, "hist_sel": hist}
+
+    def step_reuse():
+        if ring is None:
+            X.xattn_prefill_chunk(sh, pr_reuse, q, k, v, out, lse, None, ws, aux=aux_reuse)
+        else:
+            X.xattn_prefill_chunk(sh, pr_reuse, q, k, v, out, lse, None, ws, aux=aux_reuse, ring=ring,
+                                  k_hist=k_hist, v_hist=v_hist, hist_blocks=(lk0 - lq0) // 128)
+
+    step_reuse()
+    torch.cuda.synchronize()
+    stages["reuse_selection_step_ms"] = time_region(step_reuse, max(1, min(args.steps, 10)), stream)
+    step()
+    torch.cuda.synchronize()
     roofline = None
     if ring is None:
         def est():

@@ -99,7 +99,8 @@ class Shape:
 
 
 def make_params(*, stride=8, threshold=0.9, est_scale=0.0, softmax_scale=0.0, kv_chunk_tokens=4096,
-                select_mode="chunk_vote", group_agg="any", block_size=128, num_to_choose=0):
+                select_mode="chunk_vote", group_agg="any", block_size=128, num_to_choose=0,
+                reuse_selection=0):
     p = XattnParams()
     p.stride = stride
     p.block_size = block_size
@@ -110,6 +111,7 @@ def make_params(*, stride=8, threshold=0.9, est_scale=0.0, softmax_scale=0.0, kv
     p.select_mode = _MODES.get(select_mode, select_mode) if isinstance(select_mode, str) else select_mode
     p.group_agg = _AGGS.get(group_agg, group_agg) if isinstance(group_agg, str) else group_agg
     p.num_to_choose = num_to_choose
+    p.reuse_selection = int(reuse_selection)
     return p
 
 

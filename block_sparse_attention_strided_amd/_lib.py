@@ -72,6 +72,7 @@ class XattnParams(ctypes.Structure):
         ("select_mode", ctypes.c_int),
         ("group_agg", ctypes.c_int),
         ("num_to_choose", ctypes.c_int),
+        ("reuse_selection", ctypes.c_int),
     ]
 
 

@@ -79,6 +79,8 @@ int make_plan(const XattnShape* sh, const XattnParams* pr, Plan* p) {
   if (!std::isfinite(pr->threshold) || pr->threshold < 0.f)
     return fail(XATTN_ERR_INVALID, "threshold must be finite and >= 0");
   if (pr->num_to_choose < 0) return fail(XATTN_ERR_INVALID, "num_to_choose must be >= 0 (0 = threshold rule)");
+  if (pr->reuse_selection != 0 && pr->reuse_selection != 1)
+    return fail(XATTN_ERR_INVALID, "reuse_selection must be 0 or 1");
   if (!std::isfinite(pr->est_scale) || pr->est_scale < 0.f)
     return fail(XATTN_ERR_INVALID, "est_scale must be finite and >= 0 (0 = default)");
   if (!std::isfinite(pr->softmax_scale) || pr->softmax_scale < 0.f)
@@ -503,6 +505,9 @@ int prefill_ring(XattnRing* r, const XattnShape* sh, const XattnParams* pr, cons
                 r->hkv, r->d, r->dtype);
   if (pr->select_mode != XATTN_SELECT_CHUNK_VOTE)
     return fail(XATTN_ERR_UNSUPPORTED, "ring mode streams the voted history blocks: select_mode must be CHUNK_VOTE");
+  const bool reuse = pr->reuse_selection == 1;
+  if (reuse && (!aux || !aux->mask_kv || !aux->hist_sel))
+    return fail(XATTN_ERR_INVALID, "reuse_selection in ring mode needs aux->mask_kv and aux->hist_sel");
   if (kh > 0) {
     if (!k_hist || !v_hist) return fail(XATTN_ERR_INVALID, "k_hist_host and v_hist_host must not be NULL");
     int rc = check_pinned(k_hist, "k_hist_host");
@@ -533,7 +538,8 @@ int prefill_ring(XattnRing* r, const XattnShape* sh, const XattnParams* pr, cons
   hipError_t e;
 
   // ---- pass 1: history K through the ring, estimate per slot; then the current chunk
-  for (int j0 = 0; j0 < kh; j0 += r->slot_blocks) {
+  // (skipped when an earlier selection is reused)
+  for (int j0 = 0; !reuse && j0 < kh; j0 += r->slot_blocks) {
     const int nb = std::min(r->slot_blocks, kh - j0);
     const int s = r->next_slot;
     r->next_slot = (s + 1) % r->num_slots;
@@ -544,14 +550,14 @@ int prefill_ring(XattnRing* r, const XattnShape* sh, const XattnParams* pr, cons
     if ((e = run_estimate(sh, p, q, kv, j0, nb, nb, part, st)) != hipSuccess) return hip_fail(e, "estimate launch");
     if ((e = hipEventRecord(r->done[s], st)) != hipSuccess) return hip_fail(e, "ring record");
   }
-  {
+  if (!reuse) {
     KvView kv = make_view(sh, p, k);
     kv.y_offset = kh * XATTN_BLOCK;
     if ((e = run_estimate(sh, p, q, kv, kh, qb, qb, part, st)) != hipSuccess) return hip_fail(e, "estimate launch");
+    if ((e = run_block_sums(sh, p, part, bs, st)) != hipSuccess) return hip_fail(e, "block-sum launch");
+    if ((e = run_select(sh, pr, p, bs, ws_at<uint8_t>(ws, p.off_maskq), maskkv, hist, cnt, st)) != hipSuccess)
+      return hip_fail(e, "select launch");
   }
-  if ((e = run_block_sums(sh, p, part, bs, st)) != hipSuccess) return hip_fail(e, "block-sum launch");
-  if ((e = run_select(sh, pr, p, bs, ws_at<uint8_t>(ws, p.off_maskq), maskkv, hist, cnt, st)) != hipSuccess)
-    return hip_fail(e, "select launch");
 
   // ---- the one host wait: which history blocks were voted in
   if ((e = hipMemcpyAsync(r->host_sel, hist, (size_t)kb, hipMemcpyDeviceToHost, st)) != hipSuccess)
@@ -788,12 +794,17 @@ int xattn_prefill_chunk(XattnRing* ring, const XattnShape* shape, const XattnPar
   uint8_t* hist = (aux && aux->hist_sel) ? aux->hist_sel : ws_at<uint8_t>(ws, p.off_hist);
   int32_t* cnt = counts ? counts : ws_at<int32_t>(ws, p.off_counts);
   const KvView kview = make_view(shape, p, k), vview = make_view(shape, p, v);
-  hipError_t e = run_estimate(shape, p, q, kview, 0, p.max_kb, p.num_pages, part, st);
-  if (e != hipSuccess) return hip_fail(e, "estimate launch");
-  e = run_block_sums(shape, p, part, bs, st);
-  if (e != hipSuccess) return hip_fail(e, "block-sum launch");
-  e = run_select(shape, params, p, bs, ws_at<uint8_t>(ws, p.off_maskq), maskkv, hist, cnt, st);
-  if (e != hipSuccess) return hip_fail(e, "select launch");
+  hipError_t e = hipSuccess;
+  if (params->reuse_selection) {
+    if (!aux || !aux->mask_kv) return fail(XATTN_ERR_INVALID, "reuse_selection needs aux->mask_kv");
+  } else {
+    e = run_estimate(shape, p, q, kview, 0, p.max_kb, p.num_pages, part, st);
+    if (e != hipSuccess) return hip_fail(e, "estimate launch");
+    e = run_block_sums(shape, p, part, bs, st);
+    if (e != hipSuccess) return hip_fail(e, "block-sum launch");
+    e = run_select(shape, params, p, bs, ws_at<uint8_t>(ws, p.off_maskq), maskkv, hist, cnt, st);
+    if (e != hipSuccess) return hip_fail(e, "select launch");
+  }
   AttnArgs aa = attn_args(shape, p, q, kview, vview, maskkv, 0, p.max_kb);
   if (p.dtype == XATTN_DTYPE_BF16) aa.out = out;
   else aa.out_f32 = (float*)out;

@@ -104,6 +104,13 @@ typedef struct XattnParams {
                           instead of the threshold rule -- the fixed-count
                           argument of find_blocks_chunked (design doc 核心算法
                           Step 3); 0: threshold rule                        */
+  int reuse_selection; /* xattn_prefill_chunk only.  1: skip the estimate and
+                          the selection and attend over aux->mask_kv (and,
+                          in ring mode, stream the blocks aux->hist_sel
+                          marks) as produced by an earlier call -- the
+                          design doc's sharing of one layer's estimate with
+                          the other layers (性能分析, 优化方向 1).  Counts and
+                          block sums are not written.  0: full path.       */
 } XattnParams;
 
 /* Optional extra outputs of xattn_prefill_chunk (any field may be NULL). */

@@ -58,6 +58,7 @@ def test_workspace_size_is_positive_and_grows():
     ({}, dict(kv_chunk_tokens=100), _lib.XATTN_ERR_INVALID),
     ({}, dict(select_mode=7), _lib.XATTN_ERR_INVALID),
     ({}, dict(num_to_choose=-1), _lib.XATTN_ERR_INVALID),
+    ({}, dict(reuse_selection=2), _lib.XATTN_ERR_INVALID),
     (dict(lq=(128,), lk=(128 * 4097,)), {}, _lib.XATTN_ERR_UNSUPPORTED),  # too long
 ])
 def test_invalid_arguments_are_rejected_before_any_work(kw, pk, code):

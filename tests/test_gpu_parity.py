@@ -8,6 +8,7 @@ import numpy as np
 import pytest
 import torch
 
+import block_sparse_attention_strided_amd as X
 import oracle as O
 from tests.gpu_util import (Run, assert_attention_close, assert_block_sums_close, sample_rows, say)
 from workloads import make_random, make_well_separated, make_workload
@@ -257,6 +258,35 @@ def test_prefill_paged_varlen_sampled():
     w = make_workload("paged_varlen_3seq")
     rows, idx = sample_rows(w, per_seq=48)
     _prefill_and_check(w, rows=rows, rows_idx=idx, max_mismatch=0.01, label="paged varlen")
+
+
+@pytest.mark.parametrize("mode", ["per_kvhead", "chunk_vote"])
+def test_prefill_reusing_another_layers_selection(mode):
+    """reuse_selection: layer B attends over layer A's effective mask with no
+    estimate or selection of its own -- equal to the oracle's attention of B
+    over A's mask; B's block sums and counts are left untouched."""
+    kw = dict(hq=8, hkv=2, d=128, lq=[1024, 512], lk=[2048, 512], select_mode=mode)
+    wa = make_random("layerA", seed=51, **kw)
+    wb = make_random("layerB", seed=52, **kw)
+    ra, rb = Run(wa), Run(wb)
+    say("reuse %s: layer A full path" % mode)
+    _, _, _, aux_a = ra.prefill()
+    mask_a = aux_a["mask_kv"]
+    out = torch.full_like(rb.q, float("nan"))
+    lse = torch.full((rb.hq, rb.shape.total_q), float("nan"), device="cuda")
+    counts = torch.full((rb.B, 2), -7, dtype=torch.int32, device="cuda")
+    bs = torch.full((rb.B, rb.hq, rb.max_qb, rb.max_kb), -3.0, device="cuda")
+    params = X.make_params(stride=wb.stride, threshold=rb.tau, est_scale=rb.est_scale, softmax_scale=rb.softmax_scale,
+                           kv_chunk_tokens=wb.kv_chunk_tokens, select_mode=mode, reuse_selection=1)
+    say("reuse %s: layer B over layer A's mask" % mode)
+    X.xattn_prefill_chunk(rb.shape, params, rb.q, rb.k, rb.v, out, lse, counts, rb.ws,
+                          aux={"mask_kv": mask_a, "block_sums": bs})
+    torch.cuda.synchronize()
+    assert (counts == -7).all() and (bs == -3.0).all()
+    ref_o, ref_l = rb.oracle_attention(mask_a)
+    assert_attention_close(out, lse, ref_o, ref_l, wb.dtype, label="reuse " + mode)
+    with pytest.raises(X.XattnError):
+        X.xattn_prefill_chunk(rb.shape, params, rb.q, rb.k, rb.v, out, lse, counts, rb.ws)
 
 
 @pytest.mark.parametrize("seed", [101, 102, 103])

@@ -144,6 +144,32 @@ def test_ring_write_back_feeds_the_next_chunk():
     assert (o2.float() - o_res.float()).abs().max().item() <= 2e-2
 
 
+def test_ring_reusing_a_selection_skips_the_estimate():
+    """reuse_selection in ring mode: the selection of a first ring call
+    (mask_kv and hist_sel) drives a second call that streams no history K for
+    an estimate; same output, block sums untouched."""
+    w = _small()
+    r = Run(w)
+    k_hist, v_hist, k_cur, v_cur, kh = _ring_inputs(w)
+    ring = X.Ring(4, 8, w.num_kv_heads, w.head_dim, w.dtype)
+    say("ring reuse: full path")
+    o0, l0, c0, a0 = _run_ring(r, w, ring, k_hist, v_hist, k_cur, v_cur, kh)
+    params = X.make_params(stride=w.stride, threshold=r.tau, est_scale=r.est_scale, softmax_scale=r.softmax_scale,
+                           kv_chunk_tokens=w.kv_chunk_tokens, select_mode=w.select_mode, reuse_selection=1)
+    out = torch.full_like(r.q, float("nan"))
+    lse = torch.full((r.hq, r.shape.total_q), float("nan"), device="cuda")
+    bs = torch.full_like(a0["block_sums"], -3.0)
+    say("ring reuse: reusing the selection")
+    X.xattn_prefill_chunk(r.shape, params, r.q, k_cur, v_cur, out, lse, None, r.ws,
+                          aux={"mask_kv": a0["mask_kv"], "hist_sel": a0["hist_sel"], "block_sums": bs},
+                          ring=ring, k_hist=k_hist, v_hist=v_hist, hist_blocks=kh)
+    torch.cuda.synchronize()
+    ring.close()
+    assert (bs == -3.0).all()
+    assert torch.equal(out, o0)
+    assert torch.equal(lse, l0)
+
+
 def test_ring_write_back_rejects_pageable_destination():
     ring = X.Ring(2, 2, 1, 128, torch.bfloat16)
     k = torch.zeros((128, 1, 128), dtype=torch.bfloat16, device="cuda")
