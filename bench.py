@@ -354,6 +354,18 @@ def main():
         res["stages"]["writeback_ms"] = wb_ms
         res["stages"]["writeback_gbs"] = 2 * k_dst.numel() * k_dst.element_size() / (wb_ms * 1e-3) / 1e9
         ring.close()
+        # the same step through a staged ring: history K in one bulk copy,
+        # voted V blocks gathered from mapped pinned memory by a kernel
+        staged = X.Ring(1, lk0 // 128, w.num_kv_heads, w.head_dim, w.dtype, staged=True)
+
+        def step_staged():
+            X.xattn_prefill_chunk(sh, pr, q, k, v, out, lse, counts, ws, aux=aux, ring=staged,
+                                  k_hist=k_hist, v_hist=v_hist, hist_blocks=(lk0 - lq0) // 128)
+
+        step_staged()
+        torch.cuda.synchronize()
+        res["stages"]["staged_step_ms"] = time_region(step_staged, max(1, min(args.steps, 10)), stream)
+        staged.close()
     if not args.no_achievable:
         res["achievable"] = achievable_rates(dev)
     if not args.no_cpu_baseline:

@@ -165,11 +165,17 @@ def xattn_merge_attn(o_a, lse_a, o_b, lse_b, o, lse, stream=None):
 class Ring:
     """Device ring of slots for streaming pinned host K/V history."""
 
-    def __init__(self, num_slots, slot_blocks, num_kv_heads, head_dim, dtype):
+    def __init__(self, num_slots, slot_blocks, num_kv_heads, head_dim, dtype, *, staged=False):
+        """staged=True: xattn_ring_create_staged with slot_blocks = max_blocks
+        (num_slots is ignored)."""
         self.handle = ctypes.c_void_p()
         code = {torch.bfloat16: DTYPE_BF16, torch.float32: DTYPE_F32}.get(dtype, 99)
-        _check(_lib.load().xattn_ring_create(num_slots, slot_blocks, num_kv_heads, head_dim, code,
-                                             ctypes.byref(self.handle)))
+        if staged:
+            _check(_lib.load().xattn_ring_create_staged(slot_blocks, num_kv_heads, head_dim, code,
+                                                        ctypes.byref(self.handle)))
+        else:
+            _check(_lib.load().xattn_ring_create(num_slots, slot_blocks, num_kv_heads, head_dim, code,
+                                                 ctypes.byref(self.handle)))
 
     def set_copy_delay_us(self, usec):
         _check(_lib.load().xattn_ring_set_copy_delay_us(self.handle, usec))

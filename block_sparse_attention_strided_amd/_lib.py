@@ -35,6 +35,7 @@ EXPORTED = (
     "xattn_prefill_chunk",
     "xattn_ring_create",
     "xattn_ring_destroy",
+    "xattn_ring_create_staged",
     "xattn_ring_set_copy_delay_us",
     "xattn_ring_offload_chunk",
     "xattn_ring_offload_wait",
@@ -120,6 +121,9 @@ def load():
                                       ctypes.POINTER(vp)]
     lib.xattn_ring_create.restype = ctypes.c_int
     lib.xattn_ring_destroy.argtypes = [vp]
+    lib.xattn_ring_create_staged.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                             ctypes.POINTER(ctypes.c_void_p)]
+    lib.xattn_ring_create_staged.restype = ctypes.c_int
     lib.xattn_ring_destroy.restype = None
     lib.xattn_ring_set_copy_delay_us.argtypes = [vp, ctypes.c_int]
     lib.xattn_ring_offload_chunk.argtypes = [vp, vp, vp, vp, vp, ctypes.c_int, vp]

@@ -38,6 +38,7 @@ int hip_fail(hipError_t e, const char* what) {
 }
 
 constexpr int kMaxKb = 4096;  // select sorts up to this many blocks per row in LDS
+constexpr int kStageChunk = 128;  // history blocks per pipeline step of a staged ring
 
 // Everything derived from (shape, params) on the host.
 struct Plan {
@@ -431,6 +432,12 @@ hipError_t run_attention(const XattnShape* sh, const Plan& p, AttnArgs aa, const
 // ---------------------------------------------------------------------------
 struct XattnRing {
   int num_slots = 0, slot_blocks = 0, hkv = 0, d = 0, dtype = 0, elem = 0;
+  // staged mode: one slot holding a whole sequence (history + chunk); the
+  // history K arrives in one bulk copy, the selected V blocks are gathered
+  // from the mapped pinned host memory by a kernel
+  bool staged = false;
+  std::vector<hipEvent_t> stage_k, stage_v;  // per history chunk: K landed, V gathered
+  hipEvent_t sel_done = nullptr;             // selection written (gather may start)
   size_t block_bytes = 0;  // one 128-token block of K (or V)
   char* k_slots = nullptr;
   char* v_slots = nullptr;
@@ -652,6 +659,212 @@ int prefill_ring(XattnRing* r, const XattnShape* sh, const XattnParams* pr, cons
   return XATTN_OK;
 }
 
+// Staged ring prefill: history K in one bulk copy on the transfer stream,
+// the current chunk copied behind it, the resident estimate and selection
+// over the whole sequence, then a gather kernel reads exactly the voted
+// history V blocks from the mapped pinned host memory (no host wait), and one
+// resident attention launch writes the final output.
+int prefill_staged(XattnRing* r, const XattnShape* sh, const XattnParams* pr, const Plan& p, const void* q,
+                   const void* k, const void* v, const void* k_hist, const void* v_hist, int hist_blocks,
+                   void* out, float* lse, int32_t* counts, const XattnAux* aux, void* ws, hipStream_t st) {
+  const int lq = sh->cu_q_host[1], lk = sh->cu_k_host[1];
+  const int qb = lq / XATTN_BLOCK, kb = lk / XATTN_BLOCK, kh = kb - qb;
+  if (p.batch != 1 || sh->block_table)
+    return fail(XATTN_ERR_INVALID, "ring mode needs batch == 1 and no block table");
+  if (hist_blocks != kh)
+    return fail(XATTN_ERR_INVALID, "hist_blocks (%d) must equal (Lk - Lq) / 128 = %d", hist_blocks, kh);
+  if (r->hkv != p.hkv || r->d != p.d || r->dtype != p.dtype)
+    return fail(XATTN_ERR_INVALID, "ring geometry (kv heads %d, head_dim %d, dtype %d) does not match the shape",
+                r->hkv, r->d, r->dtype);
+  if (pr->select_mode != XATTN_SELECT_CHUNK_VOTE)
+    return fail(XATTN_ERR_UNSUPPORTED, "ring mode streams the voted history blocks: select_mode must be CHUNK_VOTE");
+  if (kb > r->slot_blocks)
+    return fail(XATTN_ERR_INVALID, "the sequence has %d blocks; the staged ring holds %d", kb, r->slot_blocks);
+  const bool reuse = pr->reuse_selection == 1;
+  if (reuse && (!aux || !aux->mask_kv || !aux->hist_sel))
+    return fail(XATTN_ERR_INVALID, "reuse_selection in ring mode needs aux->mask_kv and aux->hist_sel");
+  void* kh_dev = nullptr;
+  void* vh_dev = nullptr;
+  if (kh > 0) {
+    if (!k_hist || !v_hist) return fail(XATTN_ERR_INVALID, "k_hist_host and v_hist_host must not be NULL");
+    int rc = check_pinned(k_hist, "k_hist_host");
+    if (rc) return rc;
+    if ((rc = check_pinned(v_hist, "v_hist_host"))) return rc;
+    if (hipHostGetDevicePointer(&kh_dev, const_cast<void*>(k_hist), 0) != hipSuccess ||
+        hipHostGetDevicePointer(&vh_dev, const_cast<void*>(v_hist), 0) != hipSuccess) {
+      (void)hipGetLastError();
+      return fail(XATTN_ERR_NOT_PINNED, "the history arrays are not mapped into the device address space");
+    }
+  }
+  g_last_error.clear();
+  const size_t bb = r->block_bytes;
+  char* sk = r->k_slots;
+  char* sv = r->v_slots;
+  float* part = ws_at<float>(ws, p.off_part);
+  float* bs = (aux && aux->block_sums) ? aux->block_sums : ws_at<float>(ws, p.off_bs);
+  uint8_t* maskkv = (aux && aux->mask_kv) ? aux->mask_kv : ws_at<uint8_t>(ws, p.off_maskkv);
+  uint8_t* hist = (aux && aux->hist_sel) ? aux->hist_sel : ws_at<uint8_t>(ws, p.off_hist);
+  int32_t* cnt = counts ? counts : ws_at<int32_t>(ws, p.off_counts);
+  float* o_acc = ws_at<float>(ws, p.off_o[0]);
+  float* l_acc = ws_at<float>(ws, p.off_l[0]);
+  float* o_cur = ws_at<float>(ws, p.off_o[1]);
+  float* l_cur = ws_at<float>(ws, p.off_l[1]);
+  float* o_tmp = ws_at<float>(ws, p.off_o[2]);
+  float* l_tmp = ws_at<float>(ws, p.off_l[2]);
+  const bool bf16 = p.dtype == XATTN_DTYPE_BF16;
+  const int nch = (kh + kStageChunk - 1) / kStageChunk;
+  hipError_t e;
+  // Pipeline (transfer stream X, caller's stream S):
+  //   X: history K chunk c -> stage_k[c], for every c (skipped on reuse)
+  //   S: chunk K/V copied in; estimate of K chunk c as it lands; the current
+  //      chunk's estimate; block sums; selection -> sel_done
+  //   X: after sel_done, gather of the voted V (and, on reuse, K) blocks of
+  //      chunk c from mapped host memory -> stage_v[c]
+  //   S: current chunk attention (partial), then chunk c's history attention
+  //      after stage_v[c], merged history-first, then with the current chunk
+  if ((e = hipStreamWaitEvent(r->xfer, r->done[0], 0)) != hipSuccess) return hip_fail(e, "ring wait");
+  if ((e = hipStreamWaitEvent(r->xfer, r->offload_done, 0)) != hipSuccess) return hip_fail(e, "ring wait");
+  for (int c = 0; !reuse && c < nch; ++c) {
+    const int j0 = c * kStageChunk, nb = std::min(kStageChunk, kh - j0);
+    if (r->copy_delay_us > 0 && (e = hipLaunchHostFunc(r->xfer, sleep_host_fn, &r->copy_delay_us)) != hipSuccess)
+      return hip_fail(e, "ring delay");
+    if ((e = hipMemcpyAsync(sk + (size_t)j0 * bb, (const char*)k_hist + (size_t)j0 * bb, (size_t)nb * bb,
+                            hipMemcpyHostToDevice, r->xfer)) != hipSuccess)
+      return hip_fail(e, "history copy");
+    if ((e = hipEventRecord(r->stage_k[c], r->xfer)) != hipSuccess) return hip_fail(e, "ring record");
+  }
+  if ((e = hipStreamWaitEvent(st, r->done[0], 0)) != hipSuccess) return hip_fail(e, "ring wait");
+  if ((e = hipMemcpyAsync(sk + (size_t)kh * bb, k, (size_t)qb * bb, hipMemcpyDeviceToDevice, st)) != hipSuccess ||
+      (e = hipMemcpyAsync(sv + (size_t)kh * bb, v, (size_t)qb * bb, hipMemcpyDeviceToDevice, st)) != hipSuccess)
+    return hip_fail(e, "chunk copy");
+  const KvView kview = make_view(sh, p, sk), vview = make_view(sh, p, sv);
+  if (!reuse) {
+    for (int c = 0; c < nch; ++c) {
+      const int j0 = c * kStageChunk, nb = std::min(kStageChunk, kh - j0);
+      if ((e = hipStreamWaitEvent(st, r->stage_k[c], 0)) != hipSuccess) return hip_fail(e, "ring wait");
+      if ((e = run_estimate(sh, p, q, kview, j0, nb, kb, part, st)) != hipSuccess) return hip_fail(e, "estimate launch");
+    }
+    if ((e = run_estimate(sh, p, q, kview, kh, qb, kb, part, st)) != hipSuccess) return hip_fail(e, "estimate launch");
+    if ((e = run_block_sums(sh, p, part, bs, st)) != hipSuccess) return hip_fail(e, "block-sum launch");
+    if ((e = run_select(sh, pr, p, bs, ws_at<uint8_t>(ws, p.off_maskq), maskkv, hist, cnt, st)) != hipSuccess)
+      return hip_fail(e, "select launch");
+  }
+  if ((e = hipEventRecord(r->sel_done, st)) != hipSuccess) return hip_fail(e, "ring record");
+  if ((e = hipStreamWaitEvent(r->xfer, r->sel_done, 0)) != hipSuccess) return hip_fail(e, "ring wait");
+  for (int c = 0; c < nch; ++c) {
+    const int j0 = c * kStageChunk, nb = std::min(kStageChunk, kh - j0);
+    const size_t off = (size_t)j0 * bb;
+    if ((e = launch_gather_blocks(hist + j0, nb, (const char*)vh_dev + off, sv + off, bb, r->xfer)) != hipSuccess)
+      return hip_fail(e, "gather launch");
+    if (reuse &&
+        (e = launch_gather_blocks(hist + j0, nb, (const char*)kh_dev + off, sk + off, bb, r->xfer)) != hipSuccess)
+      return hip_fail(e, "gather launch");
+    if ((e = hipEventRecord(r->stage_v[c], r->xfer)) != hipSuccess) return hip_fail(e, "ring record");
+  }
+  // ---- current chunk (causal) while the first gathers run
+  {
+    AttnArgs aa = attn_args(sh, p, q, kview, vview, maskkv, kh, kb);
+    if (nch == 0) {
+      if (bf16) aa.out = out;
+      else aa.out_f32 = (float*)out;
+      aa.lse = lse;
+    } else {
+      aa.out_f32 = o_cur;
+      aa.lse = l_cur;
+    }
+    if ((e = run_attention(sh, p, aa, sv, kb, ws, true, st)) != hipSuccess) return hip_fail(e, "attention launch");
+  }
+  MergeArgs ma;
+  ma.rows = p.total_q;
+  ma.heads = p.hq;
+  ma.head_dim = p.d;
+  for (int c = 0; c < nch; ++c) {
+    const int j0 = c * kStageChunk, j1 = std::min(kh, j0 + kStageChunk);
+    if ((e = hipStreamWaitEvent(st, r->stage_v[c], 0)) != hipSuccess) return hip_fail(e, "ring wait");
+    AttnArgs aa = attn_args(sh, p, q, kview, vview, maskkv, j0, j1);
+    aa.out_f32 = c == 0 ? o_acc : o_tmp;
+    aa.lse = c == 0 ? l_acc : l_tmp;
+    if ((e = run_attention(sh, p, aa, sv, kb, ws, true, st)) != hipSuccess) return hip_fail(e, "attention launch");
+    if (c > 0) {
+      ma.o_a = o_acc;
+      ma.lse_a = l_acc;
+      ma.o_b = o_tmp;
+      ma.lse_b = l_tmp;
+      ma.o = o_acc;
+      ma.o_bf16 = nullptr;
+      ma.lse = l_acc;
+      if ((e = launch_merge(ma, st)) != hipSuccess) return hip_fail(e, "merge launch");
+    }
+  }
+  if (nch > 0) {
+    ma.o_a = o_acc;
+    ma.lse_a = l_acc;
+    ma.o_b = o_cur;
+    ma.lse_b = l_cur;
+    ma.o = bf16 ? nullptr : (float*)out;
+    ma.o_bf16 = bf16 ? out : nullptr;
+    ma.lse = lse ? lse : l_tmp;
+    if ((e = launch_merge(ma, st)) != hipSuccess) return hip_fail(e, "merge launch");
+  }
+  if ((e = hipEventRecord(r->done[0], st)) != hipSuccess) return hip_fail(e, "ring record");
+  return XATTN_OK;
+}
+
+int ring_create(int num_slots, int slot_blocks, int num_kv_heads, int head_dim, int dtype, bool staged,
+                XattnRing** out) {
+  if (!out) return fail(XATTN_ERR_INVALID, "out must not be NULL");
+  *out = nullptr;
+  if (num_slots < 1 || slot_blocks < 1 || num_kv_heads < 1)
+    return fail(XATTN_ERR_INVALID, "need slot_blocks >= 1, num_kv_heads >= 1");
+  if (head_dim != 64 && head_dim != 128) return fail(XATTN_ERR_UNSUPPORTED, "head_dim must be 64 or 128");
+  if (dtype != XATTN_DTYPE_BF16 && dtype != XATTN_DTYPE_F32) return fail(XATTN_ERR_INVALID, "unknown dtype %d", dtype);
+  XattnRing* r = new XattnRing();
+  r->staged = staged;
+  r->num_slots = num_slots;
+  r->slot_blocks = slot_blocks;
+  r->hkv = num_kv_heads;
+  r->d = head_dim;
+  r->dtype = dtype;
+  r->elem = dtype == XATTN_DTYPE_BF16 ? 2 : 4;
+  r->block_bytes = (size_t)XATTN_BLOCK * num_kv_heads * head_dim * r->elem;
+  const size_t bytes = (size_t)num_slots * slot_blocks * r->block_bytes;
+  hipError_t e = hipMalloc((void**)&r->k_slots, bytes);
+  if (e == hipSuccess) e = hipMalloc((void**)&r->v_slots, bytes);
+  if (e == hipSuccess) e = hipStreamCreateWithFlags(&r->xfer, hipStreamNonBlocking);
+  for (int s = 0; e == hipSuccess && s < num_slots; ++s) {
+    hipEvent_t a = nullptr, b = nullptr;
+    e = hipEventCreateWithFlags(&a, hipEventDisableTiming);
+    if (e == hipSuccess) e = hipEventCreateWithFlags(&b, hipEventDisableTiming);
+    if (a) r->ready.push_back(a);
+    if (b) r->done.push_back(b);
+    if (e == hipSuccess) e = hipEventRecord(b, r->xfer);  // slot free before its first copy
+  }
+  if (e == hipSuccess) e = hipEventCreateWithFlags(&r->sel_ready, hipEventDisableTiming);
+  if (e == hipSuccess) e = hipStreamCreateWithFlags(&r->offload, hipStreamNonBlocking);
+  if (e == hipSuccess) e = hipEventCreateWithFlags(&r->chunk_ready, hipEventDisableTiming);
+  if (e == hipSuccess) e = hipEventCreateWithFlags(&r->offload_done, hipEventDisableTiming);
+  if (e == hipSuccess) e = hipEventRecord(r->offload_done, r->offload);  // nothing written back yet
+  if (e == hipSuccess && staged) {
+    e = hipEventCreateWithFlags(&r->sel_done, hipEventDisableTiming);
+    const int nch = (slot_blocks + kStageChunk - 1) / kStageChunk;
+    for (int c = 0; e == hipSuccess && c < nch; ++c) {
+      hipEvent_t a = nullptr, b = nullptr;
+      e = hipEventCreateWithFlags(&a, hipEventDisableTiming);
+      if (e == hipSuccess) e = hipEventCreateWithFlags(&b, hipEventDisableTiming);
+      if (a) r->stage_k.push_back(a);
+      if (b) r->stage_v.push_back(b);
+    }
+  }
+  if (e != hipSuccess) {
+    int rc = hip_fail(e, "ring creation");
+    xattn_ring_destroy(r);
+    return rc;
+  }
+  *out = r;
+  return XATTN_OK;
+}
+
+
 }  // namespace
 
 extern "C" {
@@ -783,6 +996,9 @@ int xattn_prefill_chunk(XattnRing* ring, const XattnShape* shape, const XattnPar
   if (rc) return rc;
   if (!q || !k || !v || !out) return fail(XATTN_ERR_INVALID, "q, k, v and out must not be NULL");
   if ((rc = check_ws(p, ws, ws_bytes))) return rc;
+  if (ring && ring->staged)
+    return prefill_staged(ring, shape, params, p, q, k, v, k_hist_host, v_hist_host, hist_blocks, out, lse, counts,
+                          aux, ws, (hipStream_t)stream);
   if (ring)
     return prefill_ring(ring, shape, params, p, q, k, v, k_hist_host, v_hist_host, hist_blocks, out, lse, counts,
                         aux, ws, (hipStream_t)stream);
@@ -816,44 +1032,12 @@ int xattn_prefill_chunk(XattnRing* ring, const XattnShape* shape, const XattnPar
 
 int xattn_ring_create(int num_slots, int slot_blocks, int num_kv_heads, int head_dim, int dtype,
                       XattnRing** out) {
-  if (!out) return fail(XATTN_ERR_INVALID, "out must not be NULL");
-  *out = nullptr;
-  if (num_slots < 2 || slot_blocks < 1 || num_kv_heads < 1)
-    return fail(XATTN_ERR_INVALID, "need num_slots >= 2, slot_blocks >= 1, num_kv_heads >= 1");
-  if (head_dim != 64 && head_dim != 128) return fail(XATTN_ERR_UNSUPPORTED, "head_dim must be 64 or 128");
-  if (dtype != XATTN_DTYPE_BF16 && dtype != XATTN_DTYPE_F32) return fail(XATTN_ERR_INVALID, "unknown dtype %d", dtype);
-  XattnRing* r = new XattnRing();
-  r->num_slots = num_slots;
-  r->slot_blocks = slot_blocks;
-  r->hkv = num_kv_heads;
-  r->d = head_dim;
-  r->dtype = dtype;
-  r->elem = dtype == XATTN_DTYPE_BF16 ? 2 : 4;
-  r->block_bytes = (size_t)XATTN_BLOCK * num_kv_heads * head_dim * r->elem;
-  const size_t bytes = (size_t)num_slots * slot_blocks * r->block_bytes;
-  hipError_t e = hipMalloc((void**)&r->k_slots, bytes);
-  if (e == hipSuccess) e = hipMalloc((void**)&r->v_slots, bytes);
-  if (e == hipSuccess) e = hipStreamCreateWithFlags(&r->xfer, hipStreamNonBlocking);
-  for (int s = 0; e == hipSuccess && s < num_slots; ++s) {
-    hipEvent_t a = nullptr, b = nullptr;
-    e = hipEventCreateWithFlags(&a, hipEventDisableTiming);
-    if (e == hipSuccess) e = hipEventCreateWithFlags(&b, hipEventDisableTiming);
-    if (a) r->ready.push_back(a);
-    if (b) r->done.push_back(b);
-    if (e == hipSuccess) e = hipEventRecord(b, r->xfer);  // slot free before its first copy
-  }
-  if (e == hipSuccess) e = hipEventCreateWithFlags(&r->sel_ready, hipEventDisableTiming);
-  if (e == hipSuccess) e = hipStreamCreateWithFlags(&r->offload, hipStreamNonBlocking);
-  if (e == hipSuccess) e = hipEventCreateWithFlags(&r->chunk_ready, hipEventDisableTiming);
-  if (e == hipSuccess) e = hipEventCreateWithFlags(&r->offload_done, hipEventDisableTiming);
-  if (e == hipSuccess) e = hipEventRecord(r->offload_done, r->offload);  // nothing written back yet
-  if (e != hipSuccess) {
-    int rc = hip_fail(e, "ring creation");
-    xattn_ring_destroy(r);
-    return rc;
-  }
-  *out = r;
-  return XATTN_OK;
+  if (num_slots < 2) return fail(XATTN_ERR_INVALID, "need num_slots >= 2");
+  return ring_create(num_slots, slot_blocks, num_kv_heads, head_dim, dtype, false, out);
+}
+
+int xattn_ring_create_staged(int max_blocks, int num_kv_heads, int head_dim, int dtype, XattnRing** out) {
+  return ring_create(1, max_blocks, num_kv_heads, head_dim, dtype, true, out);
 }
 
 void xattn_ring_destroy(XattnRing* r) {
@@ -863,6 +1047,9 @@ void xattn_ring_destroy(XattnRing* r) {
   for (auto ev : r->done) (void)hipEventSynchronize(ev), (void)hipEventDestroy(ev);
   if (r->sel_ready) (void)hipEventDestroy(r->sel_ready);
   if (r->offload) (void)hipStreamSynchronize(r->offload);
+  for (auto ev : r->stage_k) (void)hipEventDestroy(ev);
+  for (auto ev : r->stage_v) (void)hipEventDestroy(ev);
+  if (r->sel_done) (void)hipEventDestroy(r->sel_done);
   if (r->chunk_ready) (void)hipEventDestroy(r->chunk_ready);
   if (r->offload_done) (void)hipEventDestroy(r->offload_done);
   if (r->offload) (void)hipStreamDestroy(r->offload);

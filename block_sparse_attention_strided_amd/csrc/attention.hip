@@ -31,6 +31,9 @@ constexpr float kNegInf = -__builtin_huge_valf();
 #ifndef XATTN_ILV
 #define XATTN_ILV 0
 #endif
+#ifndef XATTN_GATHER_WGS
+#define XATTN_GATHER_WGS 16
+#endif
 #ifndef XATTN_PF
 #define XATTN_PF 3
 #endif
@@ -1210,6 +1213,49 @@ hipError_t launch_vt_transpose(const VtArgs& a, hipStream_t s) {
 hipError_t launch_plan(const PlanArgs& a, int batch, hipStream_t s) {
   if (a.max_qb <= 0 || batch <= 0) return hipSuccess;
   hipLaunchKernelGGL(plan_kernel, dim3(a.max_qb, a.hkv, batch), dim3(64), 0, s, a);
+  return hipGetLastError();
+}
+
+// Selected-block gather: block j of `src` (host memory mapped into the
+// device address space, read over the link by the kernel itself) is copied
+// to block j of `dst` when sel[j] is set.  A small grid (kGatherWgs
+// workgroups) walks the 16 KiB pieces of all blocks, four 16-byte loads per
+// thread in flight before their stores: 256 KiB of outstanding reads keep
+// the link busy, and the CUs stay with the attention kernels running beside
+// it (a workgroup per piece filled the CUs with waves stalled on the link
+// and slowed the concurrent attention launches several-fold).
+constexpr int kGatherWgs = XATTN_GATHER_WGS;  // 16: 13.8 ms per 128K staged step; 32: 14.4; 64: 15.2; 128: 15.8
+__global__ __launch_bounds__(256) void gather_blocks_kernel(const uint8_t* sel, int nblocks, const char* src,
+                                                            char* dst, long long block_bytes) {
+  const long long parts = (block_bytes + 16383) / 16384;
+  for (long long it = blockIdx.x; it < (long long)nblocks * parts; it += gridDim.x) {
+    const int j = (int)(it / parts);
+    if (!sel[j]) continue;
+    const long long piece = it - (long long)j * parts;
+    const long long base = (long long)j * block_bytes + piece * 16384;
+    const u32x4* s = (const u32x4*)(src + base);
+    u32x4* d = (u32x4*)(dst + base);
+    const long long n = min(16384ll, block_bytes - piece * 16384) / 16;
+    u32x4 v[4];
+#pragma unroll
+    for (int x = 0; x < 4; ++x) {
+      const long long i = threadIdx.x + 256 * x;
+      if (i < n) v[x] = __builtin_nontemporal_load(s + i);
+    }
+#pragma unroll
+    for (int x = 0; x < 4; ++x) {
+      const long long i = threadIdx.x + 256 * x;
+      if (i < n) d[i] = v[x];
+    }
+  }
+}
+
+hipError_t launch_gather_blocks(const uint8_t* sel, int nblocks, const void* src, void* dst, size_t block_bytes,
+                                hipStream_t s) {
+  if (nblocks <= 0) return hipSuccess;
+  if (block_bytes % 16) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(gather_blocks_kernel, dim3(kGatherWgs), dim3(256), 0, s, sel, nblocks, (const char*)src,
+                     (char*)dst, (long long)block_bytes);
   return hipGetLastError();
 }
 

@@ -220,6 +220,21 @@ int xattn_prefill_chunk(XattnRing *ring, const XattnShape *shape, const XattnPar
  * XATTN_OK and *out, or an error (nothing allocated). */
 int xattn_ring_create(int num_slots, int slot_blocks, int num_kv_heads, int head_dim,
                       int dtype, XattnRing **out);
+/* Staged variant for the same calls (NEXT step of the ring: a zero-copy
+ * selected-block gather that removes the host wait of the selection).  Owns
+ * one device region for max_blocks 128-token blocks of K and of V -- the
+ * history plus the current chunk of a sequence -- a transfer stream and
+ * events.  xattn_prefill_chunk with it: history K in one bulk copy on the
+ * transfer stream, the chunk copied behind it, estimate and selection over the
+ * whole sequence as in resident mode, then a kernel gathers the voted history
+ * V blocks straight from the pinned host array (mapped into the device
+ * address space; read over the link by the kernel, driven by the device-side
+ * selection, no host wait) and one attention launch writes the output.  With
+ * reuse_selection it gathers the K and V blocks aux->hist_sel marks and copies
+ * no history in bulk.  Errors as xattn_ring_create; a sequence longer than
+ * max_blocks is rejected (INVALID) by xattn_prefill_chunk. */
+int xattn_ring_create_staged(int max_blocks, int num_kv_heads, int head_dim, int dtype,
+                             XattnRing **out);
 /* Waits for the ring's pending copies, then frees it.  NULL is a no-op. */
 void xattn_ring_destroy(XattnRing *ring);
 /* Test hook: sleep `usec` microseconds on the transfer stream before every

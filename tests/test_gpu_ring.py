@@ -170,6 +170,84 @@ def test_ring_reusing_a_selection_skips_the_estimate():
     assert torch.equal(lse, l0)
 
 
+def test_staged_ring_matches_resident_path():
+    """Staged ring (history K in chunks, device-driven gather of the voted V
+    blocks from mapped pinned memory, chunked attention with merges):
+    estimate and selection bit-identical to the resident path, output within
+    the bf16 tolerance of it and of the oracle; bit-identical to itself with
+    every copy delayed 2 ms and with a reused selection."""
+    w = _small()
+    r = Run(w)
+    k_hist, v_hist, k_cur, v_cur, kh = _ring_inputs(w)
+    lq, lk = w.lens(0)
+    ring = X.Ring(1, lk // 128, w.num_kv_heads, w.head_dim, w.dtype, staged=True)
+    say("staged ring: resident path")
+    o_res, l_res, c_res, a_res = r.prefill()
+    say("staged ring: staged path")
+    o_st, l_st, c_st, a_st = _run_ring(r, w, ring, k_hist, v_hist, k_cur, v_cur, kh)
+    for a in ("block_sums", "mask_kv", "hist_sel"):
+        assert torch.equal(a_st[a], a_res[a]), a
+    assert torch.equal(c_st, c_res)
+    assert (o_st.float() - o_res.float()).abs().max().item() <= 2e-2
+    ref_o, ref_l = r.oracle_attention(a_st["mask_kv"])
+    assert_attention_close(o_st, l_st, ref_o, ref_l, w.dtype, label="staged ring")
+    ring.set_copy_delay_us(2000)
+    say("staged ring: 2 ms delay per copy")
+    o_d, l_d, c_d, a_d = _run_ring(r, w, ring, k_hist, v_hist, k_cur, v_cur, kh)
+    ring.set_copy_delay_us(0)
+    assert torch.equal(o_d, o_st) and torch.equal(a_d["block_sums"], a_res["block_sums"])
+    params = X.make_params(stride=w.stride, threshold=r.tau, est_scale=r.est_scale, softmax_scale=r.softmax_scale,
+                           kv_chunk_tokens=w.kv_chunk_tokens, select_mode=w.select_mode, reuse_selection=1)
+    out = torch.full_like(r.q, float("nan"))
+    lse = torch.full((r.hq, r.shape.total_q), float("nan"), device="cuda")
+    say("staged ring: reused selection")
+    X.xattn_prefill_chunk(r.shape, params, r.q, k_cur, v_cur, out, lse, None, r.ws,
+                          aux={"mask_kv": a_res["mask_kv"], "hist_sel": a_res["hist_sel"]},
+                          ring=ring, k_hist=k_hist, v_hist=v_hist, hist_blocks=kh)
+    torch.cuda.synchronize()
+    ring.close()
+    assert torch.equal(out, o_st) and torch.equal(lse, l_st)
+    small = X.Ring(1, lk // 128 - 1, w.num_kv_heads, w.head_dim, w.dtype, staged=True)
+    with pytest.raises(X.XattnError):
+        _run_ring(r, w, small, k_hist, v_hist, k_cur, v_cur, kh)
+    small.close()
+
+
+def test_staged_ring_write_back_feeds_the_next_chunk():
+    """Chunk 1 through the staged ring, its K/V written back (delayed 2 ms per
+    copy) into the pinned history, chunk 2 through the staged ring: equal to
+    chunk 2 with all K/V resident."""
+    L, lq = 16384, 1024
+    kw = dict(hq=8, hkv=2, d=128, stride=16, threshold=0.95, select_mode="chunk_vote", kv_chunk_tokens=1024)
+    w2 = make_random("swb2", seed=45, lq=[lq], lk=[L], **kw)
+    w1 = make_random("swb1", seed=46, lq=[lq], lk=[L - lq], **kw)
+    w1.k = w2.k[: L - lq].clone()
+    w1.v = w2.v[: L - lq].clone()
+    r1, r2 = Run(w1), Run(w2)
+    hkv, d = w2.num_kv_heads, w2.head_dim
+    nh, h1 = (L - lq) // 128, (L - 2 * lq) // 128
+    k_host = torch.empty((nh, 128, hkv, d), dtype=w2.dtype, pin_memory=True).fill_(float("nan"))
+    v_host = torch.empty((nh, 128, hkv, d), dtype=w2.dtype, pin_memory=True).fill_(float("nan"))
+    k_host[:h1].copy_(w2.k[: L - 2 * lq].reshape(h1, 128, hkv, d))
+    v_host[:h1].copy_(w2.v[: L - 2 * lq].reshape(h1, 128, hkv, d))
+    ring = X.Ring(1, L // 128, hkv, d, w2.dtype, staged=True)
+    ring.set_copy_delay_us(2000)
+    k1, v1 = w2.k[L - 2 * lq: L - lq].cuda(), w2.v[L - 2 * lq: L - lq].cuda()
+    say("staged write-back: chunk 1")
+    _run_ring(r1, w1, ring, k_host[:h1], v_host[:h1], k1, v1, h1)
+    ring.offload_chunk(k1, v1, k_host[h1:], v_host[h1:], lq // 128)
+    k2, v2 = w2.k[L - lq:].cuda(), w2.v[L - lq:].cuda()
+    say("staged write-back: chunk 2")
+    o2, l2, c2, a2 = _run_ring(r2, w2, ring, k_host, v_host, k2, v2, nh)
+    ring.offload_wait()
+    torch.cuda.synchronize()
+    ring.close()
+    o_res, l_res, c_res, a_res = r2.prefill()
+    assert torch.equal(a2["block_sums"], a_res["block_sums"])
+    assert torch.equal(a2["mask_kv"], a_res["mask_kv"])
+    assert (o2.float() - o_res.float()).abs().max().item() <= 2e-2
+
+
 def test_ring_write_back_rejects_pageable_destination():
     ring = X.Ring(2, 2, 1, 128, torch.bfloat16)
     k = torch.zeros((128, 1, 128), dtype=torch.bfloat16, device="cuda")
