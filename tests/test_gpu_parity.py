@@ -63,7 +63,7 @@ def test_estimate_tiny_fp32_workload():
 
 @pytest.mark.parametrize("mode", ["per_kvhead", "chunk_vote"])
 @pytest.mark.parametrize("agg", ["any", "majority"])
-@pytest.mark.parametrize("tau", [0.5, 0.9, 0.95, 1.0])
+@pytest.mark.parametrize("tau", [0.0, 0.5, 0.9, 0.95, 1.0])
 def test_select_matches_oracle_bit_exact(mode, agg, tau):
     """The select kernels fed the oracle's block sums (rounded to fp32) make
     the same float64 decisions as the oracle on those fp32 values."""
@@ -258,6 +258,31 @@ def test_prefill_paged_varlen_sampled():
     w = make_workload("paged_varlen_3seq")
     rows, idx = sample_rows(w, per_seq=48)
     _prefill_and_check(w, rows=rows, rows_idx=idx, max_mismatch=0.01, label="paged varlen")
+
+
+@pytest.mark.parametrize("case", [
+    # the widest rows the library accepts: 4096 key blocks (512K tokens)
+    dict(name="max_width_g2", hq=2, hkv=1, d=64, lq=[128], lk=[524288], mode="chunk_vote", tau=0.9),
+    dict(name="max_width_g1", hq=1, hkv=1, d=64, lq=[256], lk=[524288], mode="per_kvhead", tau=0.9),
+    # tau = 0: no block passes the threshold, only the forced ones remain
+    dict(name="tau0_vote", hq=4, hkv=2, d=128, lq=[512], lk=[2048], mode="chunk_vote", tau=0.0),
+    dict(name="tau0_kvhead", hq=4, hkv=2, d=128, lq=[512], lk=[2048], mode="per_kvhead", tau=0.0),
+    # a lone block, and a batch whose only non-empty sequence is one block
+    dict(name="one_block", hq=2, hkv=1, d=128, lq=[128], lk=[128], mode="per_kvhead", tau=0.9),
+    dict(name="one_block_in_empties", hq=2, hkv=1, d=128, lq=[0, 128, 0], lk=[0, 256, 128], mode="chunk_vote",
+         tau=0.9),
+], ids=lambda c: c["name"])
+def test_prefill_limits_and_degenerate_cases(case):
+    """Whole path at the size limits and in the degenerate cases of the
+    method, against the oracle (estimate, masks bit-exact on these inputs,
+    attention on every row; the 512K rows on sampled rows)."""
+    c = dict(case)
+    name, mode, tau = c.pop("name"), c.pop("mode"), c.pop("tau")
+    w = make_random(name, seed=61, select_mode=mode, threshold=tau, **c)
+    rows = rows_idx = None
+    if c["lk"][0] >= 65536:
+        rows, rows_idx = sample_rows(w, per_seq=32)
+    _prefill_and_check(w, rows=rows, rows_idx=rows_idx, max_mismatch=0.0, label=name)
 
 
 @pytest.mark.parametrize("mode", ["per_kvhead", "chunk_vote"])
