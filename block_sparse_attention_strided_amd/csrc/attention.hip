@@ -28,9 +28,6 @@ namespace xattn {
 namespace {
 
 constexpr float kNegInf = -__builtin_huge_valf();
-#ifndef XATTN_ILV
-#define XATTN_ILV 0
-#endif
 #ifndef XATTN_GATHER_WGS
 #define XATTN_GATHER_WGS 16
 #endif
@@ -589,12 +586,12 @@ __global__ __launch_bounds__(512) void attn_pp(AttnArgs a, int hkv) {
 
   // Block list of this row, copied to LDS.
   const int32_t* glist = a.lists + (((long long)b * hkv + g) * a.max_qb + i) * (a.max_kb + 1);
-  const int nblk = load_row_list(glist, list, wk.s, wk.ns, tid, 64 * NW);
+  const int nblk = __builtin_amdgcn_readfirstlane(load_row_list(glist, list, wk.s, wk.ns, tid, 64 * NW));
   __syncthreads();
   const int ntile = 2 * nblk;
   // The diagonal block, if present, is the last entry: only its two tiles
   // need the causal mask.
-  const int first_diag = (nblk > 0 && (list[nblk] & 1)) ? ntile - 2 : ntile;
+  const int first_diag = __builtin_amdgcn_readfirstlane((nblk > 0 && (list[nblk] & 1)) ? ntile - 2 : ntile);
   const uint32_t list_lds = (uint32_t)(uintptr_t)(lds_ptr_t)list;
 
   // Q fragments: B operand of S^T (query col = lane%32, d slots 8*hh .. +8).
@@ -634,8 +631,8 @@ __global__ __launch_bounds__(512) void attn_pp(AttnArgs a, int hkv) {
   // (gi+2)%4.  Those stages last held K of tile gi-1 and V of tile gi-2,
   // both last read in the MFMA phases of tile gi-1, which both groups have
   // finished before group gi is issued.  Every group issues all its loads:
-  // a tile past the end (or before the start) re-reads the nearest existing
-  // tile into its own stage, which no later phase reads, so the number of
+  // a tile past the end (or before the start) re-reads an existing tile
+  // into its own stage, which no later phase reads, so the number of
   // loads in flight -- and every vmcnt below -- is the same for each group.
   const int wu = __builtin_amdgcn_readfirstlane(w);
   const __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc(
@@ -643,52 +640,66 @@ __global__ __launch_bounds__(512) void attn_pp(AttnArgs a, int hkv) {
   const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc(
       (void*)vbase, (short)0, (int)(a.num_pages * k_page_bytes - (long long)g * D * 2), kBufFlags);
   const int kpb = (int)k_page_bytes, khalf = (int)(KT * k_row_bytes);
-  char* const kl0 = tiles + wu * LPW * 1024;
-  char* const vl0 = tiles + ST * TILE + wu * LPW * 1024;
-  auto src_tile = [&](int t) { return t < 0 ? 0 : (t < ntile ? t : ntile - 1); };
-  // List entries for the copies: lane j of `eb` holds the entry of block
-  // eb0 + j, loaded by one LDS read that waits for its own result (a read
-  // left in flight in an asm output could be copied by the compiler before
-  // it lands); a group takes its two entries with v_readlane.  Refilled
-  // once per 64 blocks.
-  int eb = 0, eb0 = -64;
-  auto entry_of = [&](int t) {
-    const int blk = t >> 1;
-    if (blk >= eb0 + 64) {
-      eb0 = blk > 0 ? blk - 1 : 0;
-      const int z = eb0 + lane < nblk ? eb0 + lane : nblk - 1;
-      eb = lds_read4_sync(list_lds + 4 * (1 + z));
-    }
-    return __builtin_amdgcn_readlane(eb, blk - eb0);
+  char* const kl0 = tiles + wu * LPW * 1024;  // this wave's part of K stage 0 (V stage 0 at + ST * TILE)
+  // Copy sources.  Lane j of `eb` holds the byte offset of the page of block
+  // eb0 + j (the last block's for lanes past the end), read from the list in
+  // LDS by one read that waits for its own result (a read left in flight in
+  // an asm output could be copied by the compiler before it lands) and
+  // refilled once per 64 blocks; a group takes its offsets with v_readlane.
+  // Tile t is half t & 1 of block t >> 1.  A group past the last tile copies
+  // a tile of the last block into a stage that no later phase reads.
+  int eb = 0, eb0 = 0;
+  auto refill = [&](int base) __attribute__((always_inline)) {
+    eb0 = base;
+    const int z = base + lane < nblk ? base + lane : nblk - 1;
+    eb = (lds_read4_sync(list_lds + 4 * (1 + z)) >> 1) * kpb;
   };
   int soff_k = 0, soff_v = 0;
-  char* kl = kl0;
-  char* vl = vl0;
-  auto group_setup = [&](int gi) {
-    const int tv = src_tile(gi + 2), tk = src_tile(gi + 3);
-    const int ev = entry_of(tv), ek = entry_of(tk);
-    soff_k = (ek >> 1) * kpb + (tk & 1) * khalf;
-    soff_v = (ev >> 1) * kpb + (tv & 1) * khalf;
-    kl = kl0 + ((gi + 3) & (ST - 1)) * TILE;
-    vl = vl0 + (gi + 2 < 0 ? 0 : ((gi + 2) & (ST - 1))) * TILE;
-  };
-  // part n < LPW: K chunk n, else V chunk n - LPW
-  auto copy_part = [&](auto n_tag) {
-    constexpr int N = decltype(n_tag)::value;
-    if constexpr (N < LPW) {
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (lds_ptr_t)(kl + N * 1024), 16, (uint32_t)koff[N], soff_k, 0, 0);
-    } else {
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (lds_ptr_t)(vl + (N - LPW) * 1024), 16, (uint32_t)voff[N - LPW],
-                                               soff_v, 0, 0);
-    }
-  };
-  auto copy_group = [&](int gi) {
-    group_setup(gi);
+  // The loads of one copy group: K into stage KS, V into stage VS.
+  auto issue = [&](int ks, int vs) __attribute__((always_inline)) {
+    const uint32_t lk = (uint32_t)(uintptr_t)(lds_ptr_t)kl0 + ks * TILE;
+    const uint32_t lv = (uint32_t)(uintptr_t)(lds_ptr_t)kl0 + (ST + vs) * TILE;
     [&]<int... N>(std::integer_sequence<int, N...>) {
-      (copy_part(std::integral_constant<int, N>{}), ...);
-    }(std::make_integer_sequence<int, 2 * LPW>{});
+      (__builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (lds_ptr_t)(uintptr_t)(lk + N * 1024), 16, (uint32_t)koff[N],
+                                                soff_k, 0, 0),
+       ...);
+      (__builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (lds_ptr_t)(uintptr_t)(lv + N * 1024), 16, (uint32_t)voff[N],
+                                                soff_v, 0, 0),
+       ...);
+    }(std::make_integer_sequence<int, LPW>{});
   };
-
+  // Groups -3..-1 (G = gi + 3 = 0..2): K of tile G into stage G, V of tile
+  // max(G - 1, 0) into stage max(G - 1, 0), tiles clamped to the last one.
+  auto copy_prologue = [&](auto g_tag) __attribute__((always_inline)) {
+    constexpr int G = decltype(g_tag)::value, GV = G > 1 ? G - 1 : 0;
+    const int tk = G < ntile ? G : ntile - 1;
+    const int tv = GV < ntile ? GV : ntile - 1;
+    soff_k = __builtin_amdgcn_readlane(eb, tk >> 1) + (tk & 1) * khalf;
+    soff_v = __builtin_amdgcn_readlane(eb, tv >> 1) + (tv & 1) * khalf;
+    issue(G, GV);
+  };
+  // Group gi >= 0 (P = gi % 2): K of tile gi + 3 into stage (gi + 3) % 4, V
+  // of tile gi + 2 into stage (gi + 2) % 4.  For even gi both tiles are the
+  // halves of block (gi + 3) >> 1, whose offset the previous group took
+  // (e_last); for odd gi the K tile opens the next block and the V tile is
+  // the second half of e_last's.  li = ((gi + 3) >> 1) - eb0.
+  int e_last = 0, li = 1;
+  auto copy_group = [&](auto p_tag, int gi) __attribute__((always_inline)) {
+    if constexpr (decltype(p_tag)::value) {
+      if (++li == 64) {
+        refill(eb0 + 64);
+        li = 0;
+      }
+      const int e = __builtin_amdgcn_readlane(eb, li);
+      soff_k = e;
+      soff_v = e_last + khalf;
+      e_last = e;
+    } else {
+      soff_k = e_last + khalf;
+      soff_v = e_last;
+    }
+    issue((gi + 3) & (ST - 1), (gi + 2) & (ST - 1));
+  };
   // Per-lane LDS addresses of the MFMA A fragments in stage 0.
   const uint32_t lds0 = (uint32_t)(uintptr_t)(lds_ptr_t)tiles;
   const int kswz = (KCPR == 16) ? (l32 & 15) : ((l32 >> 1) & 7);
@@ -718,13 +729,15 @@ __global__ __launch_bounds__(512) void attn_pp(AttnArgs a, int hkv) {
   f32x16 s0, s1;
   bf16x8 pb[4];
   float m_run = kNegInf, l_run = 0.f;
+  float mneg = 0.f, m_thr = kNegInf;  // -m_run (0 while it is -inf); (m_run + 8) / c2
   const float c2 = a.scale2;
 
   // ---- MFMA phase of tile u: O^T += V^T(u-1) P^T(u-1) if PV, S^T(u) = K(u) Q^T
   // if SS.  The two MFMA streams alternate; LDS fragments are read two ahead.
-  auto mma = [&](auto pv_tag, auto ss_tag, int u) {
+  auto mma = [&](auto pv_tag, auto ss_tag, int u) __attribute__((always_inline)) {
     constexpr bool PV = decltype(pv_tag)::value, SS = decltype(ss_tag)::value;
     constexpr int NOPS = (PV ? NPV : 0) + (SS ? NS : 0);
+    // K(u) in stage u % 4, V(u - 1) in stage (u - 1) % 4
     const uint32_t kst = (uint32_t)((u & (ST - 1)) * TILE);
     const uint32_t vst = (uint32_t)(((u + ST - 1) & (ST - 1)) * TILE);
     uint32_t ka[D / 16], va4[4];
@@ -797,18 +810,21 @@ __global__ __launch_bounds__(512) void attn_pp(AttnArgs a, int hkv) {
     }(std::make_integer_sequence<int, NOPS>{});
   };
 
-  // ---- softmax of tile u: S^T registers -> P^T (bf16) in pb; hook(C) runs
-  // before exponential chunk C (of 4)
-  auto smax = [&](int u, auto hook) {
+  // ---- softmax of tile u (P = u % 2): S^T registers -> P^T (bf16) in pb
+  auto smax = [&](auto p_tag, int u) __attribute__((always_inline)) {
+    constexpr int sub = decltype(p_tag)::value;
     const bool diag = u >= first_diag;
-    const int sub = u & 1;
     if (diag) {
-      asm volatile("" ::: "memory");
+      // key = kc + 4 hh > xq with kc a constant: compare kc with xq - 4 hh,
+      // which passes through an empty asm so that neither the keys nor the
+      // compares are hoisted out of the loop into 64 registers or lane masks
+      int xt = xq - 4 * hh;
+      asm volatile("" : "+v"(xt)::"memory");
 #pragma unroll
       for (int z = 0; z < 16; ++z) {
-        const int key = sub * KT + 8 * (z >> 2) + 4 * hh + (z & 3);
-        if (key > xq) s0[z] = kNegInf;
-        if (key + 32 > xq) s1[z] = kNegInf;
+        const int kc = sub * KT + 8 * (z >> 2) + (z & 3);
+        if (kc > xt) s0[z] = kNegInf;
+        if (kc + 32 > xt) s1[z] = kNegInf;
       }
     }
     // Row max as a tree of three-input maxima (IEEE maximum lowers to
@@ -827,9 +843,11 @@ __global__ __launch_bounds__(512) void attn_pp(AttnArgs a, int hkv) {
     float mx = __builtin_elementwise_maximum(mx3(mx3(t[0], t[1], t[2]), mx3(t[3], t[4], t[5]), mx3(t[6], t[7], t[8])),
                                              __builtin_elementwise_maximum(t[9], t[10]));
     mx = half_max(mx);
-    const float m_tile = mx * c2;
-    if (__ballot(m_tile > m_run + 8.0f) != 0ull) {
-      const float m_new = fmaxf(m_run, m_tile);
+    // Lazy rescale: the running max moves only when the tile's exceeds it by
+    // more than 8 (weights stay below 2^8); m_thr is that bound on the
+    // unscaled scores.
+    if (__ballot(mx > m_thr) != 0ull) {
+      const float m_new = fmaxf(m_run, mx * c2);
       const float alpha = fast_exp2(m_run - m_new);
       l_run *= alpha;
 #pragma unroll
@@ -837,14 +855,14 @@ __global__ __launch_bounds__(512) void attn_pp(AttnArgs a, int hkv) {
 #pragma unroll
         for (int z = 0; z < 16; ++z) oacc[n][z] *= alpha;
       m_run = m_new;
+      mneg = (m_new == kNegInf) ? 0.f : -m_new;
+      m_thr = (m_new + 8.0f) / c2;
     }
-    const float mneg = (m_run == kNegInf) ? 0.f : -m_run;
     // Row sum of the fp32 probabilities (rounding them to bf16 first would
     // move the LSE of short rows by up to half a bf16 ulp), four chains.
     float ps[4];
     auto chunk = [&](auto c_tag) {
       constexpr int C = decltype(c_tag)::value;
-      hook(c_tag);
 #pragma unroll
       for (int z = 4 * C; z < 4 * C + 4; ++z) {
         s0[z] = fast_exp2(fmaf(s0[z], c2, mneg));
@@ -870,13 +888,13 @@ __global__ __launch_bounds__(512) void attn_pp(AttnArgs a, int hkv) {
   // (e.g. the exponentials, whose only consumer is the next MFMA phase)
   // across the barrier into the other phase of the same wave, where it runs
   // serially with that wave's MFMAs instead of beside the other group's.
-  auto fence_mma = [&]() {
+  auto fence_mma = [&]() __attribute__((always_inline)) {
     reg_fence(s0);
     reg_fence(s1);
 #pragma unroll
     for (int n = 0; n < D / 32; ++n) reg_fence(oacc[n]);
   };
-  auto fence_smax = [&]() {
+  auto fence_smax = [&]() __attribute__((always_inline)) {
 #pragma unroll
     for (int m = 0; m < 4; ++m) reg_fence(pb[m]);
     reg_fence(l_run);
@@ -891,60 +909,46 @@ __global__ __launch_bounds__(512) void attn_pp(AttnArgs a, int hkv) {
   // has its copies of group m-3 done: groups m-2 and m-1 may be in flight
   // for A (it issued group m-1 in the phase just ending), only group m-2 for B.
   if (ntile > 0) {
-    copy_group(-3);  // V part: tile 0, the same bytes as group -2's
-    copy_group(-2);
-    copy_group(-1);
+    refill(0);
+    e_last = __builtin_amdgcn_readlane(eb, 1);  // block 1 (or the last)
+    copy_prologue(std::integral_constant<int, 0>{});  // V part: tile 0, the same bytes as group -2's
+    copy_prologue(std::integral_constant<int, 1>{});
+    copy_prologue(std::integral_constant<int, 2>{});
     wait_vmcnt<4 * LPW>();
   }
   __builtin_amdgcn_s_barrier();
   if (grp == 1) __builtin_amdgcn_s_barrier();  // B: idle phase 1 (A computes S of tile 0)
   // Per tile u: MFMA phase (O += V^T(u-1) P(u-1), S(u)), barrier, softmax
   // phase (copy group u, softmax of S(u)), barrier.  Tile 0 (S only) is
-  // peeled so that the loop has one MFMA-phase shape.
-  auto softmax_phase = [&](int u) {
-    if constexpr (XATTN_ILV) {
-      // copy parts spread over the exponentials: a burst of direct loads
-      // stalls the issuing wave until the vector memory path drains
-      group_setup(u);
-      smax(u, [&](auto c_tag) {
-        constexpr int C = decltype(c_tag)::value, P = 2 * LPW;
-        if constexpr ((C * P) % 4 == 0) {
-          __builtin_amdgcn_sched_barrier(0);
-          [&]<int... N>(std::integer_sequence<int, N...>) {
-            (copy_part(std::integral_constant<int, C * P / 4 + N>{}), ...);
-          }(std::make_integer_sequence<int, (P >= 4 ? P / 4 : 1)>{});
-          __builtin_amdgcn_sched_barrier(0);
-        }
-      });
-    } else {
-      copy_group(u);
-      smax(u, [](auto) {});
-    }
+  // peeled so that the loop has one MFMA-phase shape; the loop is unrolled
+  // by two so that the tile parity (the copy sources' bookkeeping and the
+  // diagonal mask) is a constant.
+  auto softmax_phase = [&](auto p_tag, int u) __attribute__((always_inline)) {
+    copy_group(p_tag, u);
+    smax(p_tag, u);
     fence_smax();
   };
-  if (ntile > 0) {
+  auto tile = [&](auto pv_tag, auto p_tag, int u) __attribute__((always_inline)) {
     __builtin_amdgcn_s_setprio(1);
-    mma(F_{}, T_{}, 0);
+    mma(pv_tag, T_{}, u);
     fence_mma();
     __builtin_amdgcn_s_setprio(0);
     if (grp == 1) wait_vmcnt<2 * LPW>();
     __builtin_amdgcn_s_barrier();
-    softmax_phase(0);
+    softmax_phase(p_tag, u);
     if (grp == 0) wait_vmcnt<4 * LPW>();
     __builtin_amdgcn_s_barrier();
+  };
+  using Even = std::integral_constant<int, 0>;
+  using Odd = std::integral_constant<int, 1>;
+  if (ntile > 0) tile(F_{}, Even{}, 0);
+  int u = 1;
+  for (; u + 1 < ntile; u += 2) {
+    tile(T_{}, Odd{}, u);
+    tile(T_{}, Even{}, u + 1);
   }
-  for (int u = 1; u < ntile; ++u) {
-    __builtin_amdgcn_s_setprio(1);
-    mma(T_{}, T_{}, u);
-    fence_mma();
-    __builtin_amdgcn_s_setprio(0);
-    if (grp == 1) wait_vmcnt<2 * LPW>();
-    __builtin_amdgcn_s_barrier();
-    softmax_phase(u);
-    if (grp == 0) wait_vmcnt<4 * LPW>();
-    __builtin_amdgcn_s_barrier();
-  }
-  if (ntile > 0) mma(T_{}, F_{}, ntile);
+  if (u < ntile) tile(T_{}, Odd{}, u);
+  if (ntile > 0) mma(T_{}, F_{}, ntile);  // PV of the last tile
   if (grp == 0) __builtin_amdgcn_s_barrier();  // matches B's last loop barrier
   wait_vmcnt<0>();  // copies of the groups past the end land in LDS before exit
 
