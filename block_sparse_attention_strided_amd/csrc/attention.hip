@@ -536,21 +536,20 @@ __global__ __launch_bounds__(256 * HPW) void attn_mfma(AttnArgs a, int hkv) {
 //
 // Waves 0-3 (group A, first head of the pair) and waves 4-7 (group B, second
 // head) share the SIMDs pairwise (wave w and w+4 on one SIMD) and run the same
-// per-tile program half a tile apart.  A wave issues nothing but LDS reads and
+// per-tile work half a tile apart.  A wave issues nothing but LDS reads and
 // MFMAs in its MFMA phase (O^T += V^T P^T of tile u-1, then S^T = K Q^T of
 // tile u; a wave's own VALU work would serialise with its MFMAs) while the
-// other group runs its softmax on the VALU; a workgroup barrier separates the
-// phases and keeps the groups in anti-phase:
-//   barrier 2u+1 -> A: MFMA(u)     B: softmax(u-1)
-//   barrier 2u+2 -> A: softmax(u)  B: MFMA(u)
+// other group runs its softmax on the VALU.  Per tile, A runs MFMA(u) then
+// softmax(u) and B runs softmax(u-1) then MFMA(u); one workgroup barrier per
+// tile realigns the two halves (a second barrier between the halves cost
+// more in waiting than it gained in alignment).
 // K and V tiles (both in the caller's [key][kv head][d] layout) live in two
 // 4-stage LDS rings (tile t in stage t % 4); V^T fragments of the PV MFMAs
 // come from transposing LDS reads.  The softmax phase of tile g also issues
-// copy group g: K of tile g+3 and V of
-// tile g+2 (raw buffer loads straight to LDS, which count on vmcnt only).
-// Each wave waits for its own copies of a tile before the barrier that opens
-// the first phase reading it; register fences keep the compiler from moving
-// phase work across the barriers.
+// copy group g: K of tile g+3 and V of tile g+2 (raw buffer loads straight
+// to LDS, which count on vmcnt only).  Each wave waits for its own copies of
+// a tile before the barrier after which the tile is read; register fences
+// keep the compiler from moving phase work between phases.
 // ---------------------------------------------------------------------------
 template <int D, int PF>
 __global__ __launch_bounds__(512) void attn_pp(AttnArgs a, int hkv) {
@@ -904,10 +903,21 @@ __global__ __launch_bounds__(512) void attn_pp(AttnArgs a, int hkv) {
   };
   using T_ = std::integral_constant<bool, true>;
   using F_ = std::integral_constant<bool, false>;
-  // Prologue: copy groups -3..-1 (K of tiles 0..2, V of tiles 0..1);
-  // before the barrier that opens a phase reading K of tile m, every wave
-  // has its copies of group m-3 done: groups m-2 and m-1 may be in flight
-  // for A (it issued group m-1 in the phase just ending), only group m-2 for B.
+  // Schedule.  Per tile u, group A (waves 0-3) runs the MFMA phase of u
+  // (O += V^T(u-1) P(u-1) and S(u)) and then the softmax phase of u (copy
+  // group u, P(u) from S(u)); group B runs the softmax phase of u - 1 and
+  // then the MFMA phase of u; one workgroup barrier ends the tile.  On each
+  // SIMD the A wave's MFMAs thus run beside the B wave's softmax and vice
+  // versa; the barrier realigns the two halves once per tile.
+  // Copies: before barrier u, every wave has its copy group u - 2 done (A
+  // has issued up to group u and waits for all but two groups, B up to
+  // u - 1 and waits for all but one), so after it both operands of MFMA
+  // phase u + 1 (K(u + 1), V(u), from group u - 2) are in LDS.  Group g
+  // overwrites K(g - 1) and V(g - 2), which only MFMA phase g - 1 reads:
+  // A issues it after barrier g - 1, B after barrier g, and every wave's
+  // MFMA phase g - 1 precedes barrier g - 1.
+  // Prologue: copy groups -3..-1 (K of tiles 0..2, V of tiles 0..1); the
+  // barrier after it makes group -3 (K(0)) visible.
   if (ntile > 0) {
     refill(0);
     e_last = __builtin_amdgcn_readlane(eb, 1);  // block 1 (or the last)
@@ -917,39 +927,58 @@ __global__ __launch_bounds__(512) void attn_pp(AttnArgs a, int hkv) {
     wait_vmcnt<4 * LPW>();
   }
   __builtin_amdgcn_s_barrier();
-  if (grp == 1) __builtin_amdgcn_s_barrier();  // B: idle phase 1 (A computes S of tile 0)
-  // Per tile u: MFMA phase (O += V^T(u-1) P(u-1), S(u)), barrier, softmax
-  // phase (copy group u, softmax of S(u)), barrier.  Tile 0 (S only) is
-  // peeled so that the loop has one MFMA-phase shape; the loop is unrolled
-  // by two so that the tile parity (the copy sources' bookkeeping and the
-  // diagonal mask) is a constant.
+  // Tile 0 has no PV part; the loops are unrolled by two so that the tile
+  // parity (the copy sources' bookkeeping and the diagonal mask) is a
+  // constant.
   auto softmax_phase = [&](auto p_tag, int u) __attribute__((always_inline)) {
     copy_group(p_tag, u);
     smax(p_tag, u);
     fence_smax();
   };
-  auto tile = [&](auto pv_tag, auto p_tag, int u) __attribute__((always_inline)) {
+  auto mma_phase = [&](auto pv_tag, int u) __attribute__((always_inline)) {
     __builtin_amdgcn_s_setprio(1);
     mma(pv_tag, T_{}, u);
     fence_mma();
     __builtin_amdgcn_s_setprio(0);
-    if (grp == 1) wait_vmcnt<2 * LPW>();
-    __builtin_amdgcn_s_barrier();
-    softmax_phase(p_tag, u);
-    if (grp == 0) wait_vmcnt<4 * LPW>();
-    __builtin_amdgcn_s_barrier();
   };
   using Even = std::integral_constant<int, 0>;
   using Odd = std::integral_constant<int, 1>;
-  if (ntile > 0) tile(F_{}, Even{}, 0);
-  int u = 1;
-  for (; u + 1 < ntile; u += 2) {
-    tile(T_{}, Odd{}, u);
-    tile(T_{}, Even{}, u + 1);
+  if (ntile > 0) {
+    if (grp == 0) {
+      auto step = [&](auto pv_tag, auto p_tag, int u) __attribute__((always_inline)) {
+        mma_phase(pv_tag, u);
+        softmax_phase(p_tag, u);
+        wait_vmcnt<4 * LPW>();
+        __builtin_amdgcn_s_barrier();
+      };
+      step(F_{}, Even{}, 0);
+      int u = 1;
+      for (; u + 1 < ntile; u += 2) {
+        step(T_{}, Odd{}, u);
+        step(T_{}, Even{}, u + 1);
+      }
+      if (u < ntile) step(T_{}, Odd{}, u);
+    } else {
+      mma_phase(F_{}, 0);
+      wait_vmcnt<2 * LPW>();
+      __builtin_amdgcn_s_barrier();
+      auto step = [&](auto p_tag, int u) __attribute__((always_inline)) {
+        softmax_phase(p_tag, u - 1);  // p_tag: parity of u - 1
+        mma_phase(T_{}, u);
+        wait_vmcnt<2 * LPW>();
+        __builtin_amdgcn_s_barrier();
+      };
+      int u = 1;
+      for (; u + 1 < ntile; u += 2) {
+        step(Even{}, u);
+        step(Odd{}, u + 1);
+      }
+      if (u < ntile) step(Even{}, u);
+      if (ntile & 1) softmax_phase(Even{}, ntile - 1);
+      else softmax_phase(Odd{}, ntile - 1);
+    }
+    mma(T_{}, F_{}, ntile);  // PV of the last tile
   }
-  if (u < ntile) tile(T_{}, Odd{}, u);
-  if (ntile > 0) mma(T_{}, F_{}, ntile);  // PV of the last tile
-  if (grp == 0) __builtin_amdgcn_s_barrier();  // matches B's last loop barrier
   wait_vmcnt<0>();  // copies of the groups past the end land in LDS before exit
 
   const float l_tot = half_sum(l_run);
