@@ -245,7 +245,7 @@ hipError_t run_select(const XattnShape* sh, const XattnParams* pr, const Plan& p
 
 AttnArgs attn_args(const XattnShape* sh, const Plan& p, const void* q, KvView kv, KvView vv,
                    const uint8_t* mask, int jb0, int jb1) {
-  AttnArgs aa;
+  AttnArgs aa{};
   aa.q = (const char*)q;
   aa.k = kv;
   aa.v = vv;
@@ -331,8 +331,13 @@ int device_cu_count() {
 // whose long rows would set the launch time -- rows longer than
 // bmax = max(share, longest / 3) are cut into ns = ceil(length / bmax) <= 3
 // parts whose partial outputs a split merge combines (the merge rule of
-// partial attention results).  One sequence without splits keeps the
-// kernel's default order, which is the same order.
+// partial attention results).  Otherwise, when all workgroups fit on the
+// CUs at once (one round) and the longest row exceeds the share by at least
+// 4 blocks and 2%, rows longer than the share keep a head of `share` blocks
+// and move the rest into a tail part; longest first, the tails start on the
+// CUs whose short rows finish first, which evens out the CUs' totals.  One
+// sequence without splits keeps the kernel's default order, which is the
+// same order.
 void set_order(const XattnShape* sh, const Plan& p, AttnArgs& aa, void* ws, SplitMergeArgs* sm) {
   sm->n = 0;
   aa.n_order = 0;
@@ -357,17 +362,39 @@ void set_order(const XattnShape* sh, const Plan& p, AttnArgs& aa, void* ws, Spli
   const int group = p.hq / p.hkv;
   const int per_row = p.hkv * (group / ((group % 2 == 0) ? 2 : 1));
   const int cus = device_cu_count();
-  int bmax = 0;  // 0: no splits
+  int bmax = 0;     // > 0: equal parts of at most bmax blocks
+  int head = 0;     // > 0: head + tail parts
   if (aa.out && !aa.out_f32 && cus > 0) {
     const double share = (double)total * per_row / cus;
-    if (lmax >= 4 && lmax > 1.25 * share) bmax = std::max({(int)std::ceil(share), (lmax + 2) / 3, 2});
+    if (lmax >= 4 && lmax > 1.25 * share) {
+      bmax = std::max({(int)std::ceil(share), (lmax + 2) / 3, 2});
+    } else if ((long long)rows.size() * per_row <= cus && lmax >= share + 4 && lmax >= 1.02 * share) {
+      head = (int)std::ceil(share);
+    }
   }
-  std::vector<std::pair<int, uint32_t>> items;  // (-part length, order entry)
+  struct Item {
+    int neg_len;
+    uint32_t entry;
+    uint8_t cut;
+  };
+  std::vector<Item> items;  // longest part first
   int nsplit = 0;
   for (const Row& r : rows) {
-    const int ns = (bmax > 0 && r.len > bmax) ? std::min(3, (r.len + bmax - 1) / bmax) : 1;
-    for (int x = 0; x < ns; ++x)
-      items.push_back({-(((x + 1) * r.len) / ns - (x * r.len) / ns), order_entry(r.b, r.i, x, ns)});
+    int ns = 1;
+    if (bmax > 0 && r.len > bmax) {
+      ns = std::min(3, (r.len + bmax - 1) / bmax);
+      for (int x = 0; x < ns; ++x)
+        items.push_back({-(((x + 1) * r.len) / ns - (x * r.len) / ns), order_entry(r.b, r.i, x, ns), 0});
+    } else if (head > 0 && r.len > head) {
+      // cut = 256 * head / len, rounded, so that part 0 holds about `head`
+      // of the listed blocks (the selection may list fewer than len)
+      const int cut = std::min(255, std::max(1, (int)((256LL * head + r.len / 2) / r.len)));
+      ns = 2;
+      items.push_back({-head, order_entry(r.b, r.i, 0, 2), (uint8_t)cut});
+      items.push_back({-(r.len - head), order_entry(r.b, r.i, 1, 2), (uint8_t)cut});
+    } else {
+      items.push_back({-r.len, order_entry(r.b, r.i, 0, 1), 0});
+    }
     if (ns > 1) {
       if (nsplit < kMaxOrder) sm->rows[nsplit] = (sh->cu_q_host[r.b] / XATTN_BLOCK + r.i) | ((ns - 1) << 28);
       ++nsplit;
@@ -377,14 +404,16 @@ void set_order(const XattnShape* sh, const Plan& p, AttnArgs& aa, void* ws, Spli
     // too many parts for the order table: no splits, plain rows if they fit
     if (p.batch == 1 || rows.size() > (size_t)kMaxOrder) return;
     items.clear();
-    for (const Row& r : rows) items.push_back({-r.len, order_entry(r.b, r.i, 0, 1)});
+    for (const Row& r : rows) items.push_back({-r.len, order_entry(r.b, r.i, 0, 1), 0});
     nsplit = 0;
   }
   if (p.batch == 1 && nsplit == 0) return;
-  std::stable_sort(items.begin(), items.end(),
-                   [](const std::pair<int, uint32_t>& x, const std::pair<int, uint32_t>& y) { return x.first < y.first; });
+  std::stable_sort(items.begin(), items.end(), [](const Item& x, const Item& y) { return x.neg_len < y.neg_len; });
   aa.n_order = (int)items.size();
-  for (size_t r = 0; r < items.size(); ++r) aa.order[r] = (int)items[r].second;
+  for (size_t r = 0; r < items.size(); ++r) {
+    aa.order[r] = (int)items[r].entry;
+    aa.order_cut[r] = items[r].cut;
+  }
   if (nsplit > 0) {
     for (int x = 0; x < 3; ++x) {
       aa.split_o[x] = ws_at<float>(ws, p.off_o[x]);

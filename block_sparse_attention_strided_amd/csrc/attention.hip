@@ -154,7 +154,7 @@ __device__ __forceinline__ void wait_vmcnt() {
 // A row may be split into ns parts (part s of ns equal parts of its block
 // list); the host splits only rows it lists in the order.
 struct WorkUnit {
-  int b, g, pair, i, s, ns;
+  int b, g, pair, i, s, ns, cut;
 };
 __device__ __forceinline__ WorkUnit work_unit(const AttnArgs& a, int hkv, int npair, int id, int nwg) {
   WorkUnit u;
@@ -174,6 +174,7 @@ __device__ __forceinline__ WorkUnit work_unit(const AttnArgs& a, int hkv, int np
     u.i = (int)(e & 0xffffu);
     u.s = (int)((e >> 28) & 3u);
     u.ns = (int)(e >> 30) + 1;
+    u.cut = a.order_cut[r];
     u.g = slot % hkv;
     u.pair = slot / hkv;
     return u;
@@ -189,18 +190,28 @@ __device__ __forceinline__ WorkUnit work_unit(const AttnArgs& a, int hkv, int np
   u.i = a.max_qb - 1 - irev;
   u.s = 0;
   u.ns = 1;
+  u.cut = 0;
   return u;
 }
 
 // Part s of ns of a row's block list, copied to LDS: list[0] = its count,
 // list[1..] its entries.  The parts are consecutive runs of the list, as even
-// as integer division makes them; the diagonal block (the last entry) falls
-// in the last part.  The caller synchronises before reading `list`.
-__device__ __forceinline__ int load_row_list(const int32_t* glist, int32_t* list, int s, int ns, int tid,
+// as integer division makes them, or for two parts with cut > 0 the first
+// (count * cut) / 256 entries and the rest; the diagonal block (the last
+// entry) falls in the last part.  The caller synchronises before reading
+// `list`.
+__device__ __forceinline__ int load_row_list(const int32_t* glist, int32_t* list, int s, int ns, int cut, int tid,
                                              int nthreads) {
   const int nall = glist[0];
-  const int z0 = (s * nall) / ns;
-  const int n = ((s + 1) * nall) / ns - z0;
+  int z0, n;
+  if (ns == 2 && cut > 0) {
+    const int c = (nall * cut) >> 8;
+    z0 = s ? c : 0;
+    n = s ? nall - c : c;
+  } else {
+    z0 = (s * nall) / ns;
+    n = ((s + 1) * nall) / ns - z0;
+  }
   for (int z = tid; z <= n; z += nthreads) list[z] = (z == 0) ? n : glist[z0 + z];
   return n;
 }
@@ -306,7 +317,7 @@ __global__ __launch_bounds__(256 * HPW) void attn_mfma(AttnArgs a, int hkv) {
 
   // Block list of this row, copied to LDS.
   const int32_t* glist = a.lists + (((long long)b * hkv + g) * a.max_qb + i) * (a.max_kb + 1);
-  const int nblk = load_row_list(glist, list, wk.s, wk.ns, tid, 64 * NW);
+  const int nblk = load_row_list(glist, list, wk.s, wk.ns, wk.cut, tid, 64 * NW);
   __syncthreads();
   const int ntile = 2 * nblk;
   // The diagonal block, if present, is the last entry: only its two tiles
@@ -585,7 +596,7 @@ __global__ __launch_bounds__(512) void attn_pp(AttnArgs a, int hkv) {
 
   // Block list of this row, copied to LDS.
   const int32_t* glist = a.lists + (((long long)b * hkv + g) * a.max_qb + i) * (a.max_kb + 1);
-  const int nblk = __builtin_amdgcn_readfirstlane(load_row_list(glist, list, wk.s, wk.ns, tid, 64 * NW));
+  const int nblk = __builtin_amdgcn_readfirstlane(load_row_list(glist, list, wk.s, wk.ns, wk.cut, tid, 64 * NW));
   __syncthreads();
   const int ntile = 2 * nblk;
   // The diagonal block, if present, is the last entry: only its two tiles

@@ -105,6 +105,9 @@ struct AttnArgs {
   // part s of ns equal parts of row (b, i)'s block list (see order_entry).
   int n_order;
   int order[kMaxOrder];
+  // For an entry with ns == 2: part 0 takes the first (count * cut) / 256
+  // entries of the row's block list and part 1 the rest (cut 0: halves).
+  uint8_t order_cut[kMaxOrder];
   // Rows split into ns > 1 parts write part s as a normalised fp32 output
   // and its natural-log LSE to split_o[s] / split_l[s] (layouts of out_f32 /
   // lse); a split merge then writes the final output.
