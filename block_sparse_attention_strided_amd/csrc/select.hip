@@ -116,7 +116,8 @@ __device__ __forceinline__ void wave_lds_sync() {
 
 // Threshold selection and GQA aggregation fused.  One workgroup per (q block
 // i, kv head g, sequence b) with one wave per q head of the group; wave w
-// works on row (b, h = g*G + w, i) in its own LDS region:
+// works on row (b, h = g*G + w, i) in its own LDS region (the aggregated row
+// goes to mask_kv, or in chunk-vote mode to the mask_q scratch):
 //   keys   (orderable(v_j) << 32) | ~j for the allowed j (descending order =
 //          value desc, index asc); zero keys pad to n2 and sort last
 //   sort   bitonic, wave-synchronous (no workgroup barriers)
@@ -187,7 +188,10 @@ __global__ __launch_bounds__(64 * kSelMaxWaves) void select_group_kernel(SelectA
   const int nthr = 64 * G;
   if (a.select_mode == 0 && i == 0 && g == 0)
     for (int j = tid; j < a.max_kb; j += nthr) a.hist_sel[(long long)b * a.max_kb + j] = 0;
-  uint8_t* out = a.mask_kv + (((long long)b * a.hkv + g) * a.max_qb + i) * a.max_kb;
+  // chunk-vote mode: the per-KV-head rows go to the mask_q scratch (same
+  // layout), which chunk_vote_mask_kernel turns into the effective mask_kv
+  uint8_t* const dst = a.select_mode == 1 ? a.mask_q : a.mask_kv;
+  uint8_t* out = dst + (((long long)b * a.hkv + g) * a.max_qb + i) * a.max_kb;
   if (i >= qb) {
     for (int j = tid; j < a.max_kb; j += nthr) out[j] = 0;
     return;
@@ -389,6 +393,88 @@ __global__ __launch_bounds__(1024) void counts_kernel(SelectArgs a) {
   }
 }
 
+// Chunk-vote mode after select_group_kernel, which left the per-KV-head
+// rows in the mask_q scratch: one workgroup per (q block i, kv head g,
+// sequence b) counts the votes of every history column over the sequence's
+// Hkv*Qb rows itself (16 row lanes x 16 chunks of 16 columns per pass,
+// partial counts met in LDS; the rows are 57 KiB at 32K, read from L2 by
+// every workgroup), then writes its effective mask_kv row (voted history,
+// dense causal current chunk; zeros past the sequence).  Workgroup (0, 0, b)
+// also writes hist_sel and counts = {selected history blocks, history
+// blocks}.  One launch instead of vote + effective mask + counts.
+__global__ __launch_bounds__(256) void chunk_vote_mask_kernel(SelectArgs a) {
+  extern __shared__ uint8_t hs[];  // max_kb voted history flags
+  __shared__ int part[16][256];
+  __shared__ int nsel[4];
+  const int i = blockIdx.x, g = blockIdx.y, b = blockIdx.z, tid = threadIdx.x;
+  const int lq = a.cu_q[b + 1] - a.cu_q[b];
+  const int lk = a.cu_k[b + 1] - a.cu_k[b];
+  const int qb = lq / kBlock, kb = lk / kBlock, kh = (lk - lq) / kBlock;
+  const bool lead = (i == 0 && g == 0);
+  uint8_t* out = a.mask_kv + (((long long)b * a.hkv + g) * a.max_qb + i) * a.max_kb;
+  if (i >= qb && !lead) {
+    for (int j = tid; j < a.max_kb; j += 256) out[j] = 0;
+    return;
+  }
+  const int nrows = a.hkv * qb;
+  const uint8_t* sel = a.mask_q + (long long)b * a.hkv * a.max_qb * a.max_kb;
+  const bool vec = (a.max_kb & 15) == 0 && ((uintptr_t)a.mask_q & 15) == 0;
+  const int rl = tid >> 4, cc = tid & 15;
+  int mine = 0;  // this thread's selected history columns (lead workgroup)
+  for (int j0 = 0; j0 < a.max_kb; j0 += 256) {
+    int cnt[16];
+#pragma unroll
+    for (int e = 0; e < 16; ++e) cnt[e] = 0;
+    const int jc = j0 + 16 * cc;
+    if (jc < kh) {
+#pragma unroll 4
+      for (int r = rl; r < nrows; r += 16) {
+        const int gg = r / qb, ii = r - gg * qb;
+        const uint8_t* row = sel + ((long long)gg * a.max_qb + ii) * a.max_kb + jc;
+        if (vec) {
+          const u32x4 w = *(const u32x4*)row;
+#pragma unroll
+          for (int e = 0; e < 16; ++e) cnt[e] += (w[e >> 2] >> (8 * (e & 3))) & 0xffu;
+        } else {
+#pragma unroll
+          for (int e = 0; e < 16; ++e)
+            if (jc + e < a.max_kb) cnt[e] += row[e];
+        }
+      }
+    }
+#pragma unroll
+    for (int e = 0; e < 16; ++e) part[rl][16 * cc + e] = cnt[e];
+    __syncthreads();
+    const int j = j0 + tid;
+    if (j < a.max_kb) {
+      uint8_t v = 0;
+      if (qb > 0 && j < kh) {
+        int votes = 0;
+#pragma unroll
+        for (int x = 0; x < 16; ++x) votes += part[x][tid];
+        v = (2 * votes > nrows || j == 0 || j == kh - 1) ? 1 : 0;
+      }
+      hs[j] = v;
+      if (lead) {
+        a.hist_sel[(long long)b * a.max_kb + j] = v;
+        mine += v;
+      }
+    }
+    __syncthreads();  // part[] reused; hs[] complete after the last pass
+  }
+  for (int j = tid; j < a.max_kb; j += 256)
+    out[j] = (i < qb && j < kb) ? ((j < kh) ? hs[j] : (j <= i + kh ? 1 : 0)) : 0;
+  if (lead && a.counts) {
+    for (int off = 32; off > 0; off >>= 1) mine += __shfl_xor(mine, off, 64);
+    if ((tid & 63) == 0) nsel[tid >> 6] = mine;
+    __syncthreads();
+    if (tid == 0) {
+      a.counts[2 * b] = nsel[0] + nsel[1] + nsel[2] + nsel[3];
+      a.counts[2 * b + 1] = qb > 0 ? kh : 0;
+    }
+  }
+}
+
 }  // namespace
 
 hipError_t launch_select(const SelectArgs& a, int batch, hipStream_t s) {
@@ -411,6 +497,10 @@ hipError_t launch_select(const SelectArgs& a, int batch, hipStream_t s) {
         default: hipLaunchKernelGGL(select_group_kernel<32>, grid, block, fused_lds, s, a, n2); break;
       }
       if ((e = hipGetLastError()) != hipSuccess) return e;
+      if (a.select_mode == 1) {
+        hipLaunchKernelGGL(chunk_vote_mask_kernel, dim3(a.max_qb, a.hkv, batch), dim3(256), (size_t)a.max_kb, s, a);
+        return hipGetLastError();
+      }
     } else {
       const size_t shm = (size_t)n2 * (sizeof(uint64_t) + sizeof(double));
       hipLaunchKernelGGL(select_rows_kernel, dim3(a.max_qb, a.hq, batch), dim3(256), shm, s, a, n2);
