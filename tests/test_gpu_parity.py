@@ -203,6 +203,34 @@ def test_sparse_attention(name, mask_kind):
     assert_attention_close(out, lse, ref_o, ref_l, w.dtype, label=name)
 
 
+@pytest.mark.parametrize("mask_kind", ["dense", "random"])
+def test_attention_head_tail_split(mask_kind):
+    """Two sequences whose 32 q blocks x 8 kv heads = 256 workgroups fill a
+    256-CU launch in one round, rows of 61..86 key blocks: rows longer than
+    the per-CU share (73.5 blocks) keep a 74-block head and queue the rest as
+    a tail part (uneven two-part split), which the split merge combines.
+    Sampled rows (first and last of every q block) against the oracle."""
+    w = make_random("head_tail", seed=41, hq=16, hkv=8, d=128, lq=[2048, 2048],
+                    lk=[2048 + 128 * 60, 2048 + 128 * 70])
+    r = Run(w)
+    rng = np.random.default_rng(9)
+    mask = np.zeros((r.B, r.hkv, r.max_qb, r.max_kb), dtype=np.uint8)
+    for b in range(w.batch):
+        lq, lk = w.lens(b)
+        kh = (lk - lq) // 128
+        for i in range(lq // 128):
+            n = i + kh + 1
+            row = np.ones((r.hkv, n), bool) if mask_kind == "dense" else rng.random((r.hkv, n)) < 0.7
+            row[:, i + kh] = True
+            mask[b, :, i, :n] = row
+    mask_t = torch.from_numpy(mask)
+    rows, idx = sample_rows(w, per_seq=24)
+    say("attention head/tail %s" % mask_kind)
+    out, lse = r.attend(mask_t)
+    ref_o, ref_l = r.oracle_attention(mask_t, rows=rows)
+    assert_attention_close(out, lse, ref_o, ref_l, w.dtype, rows_idx=idx, label="head/tail " + mask_kind)
+
+
 def test_merge_attention():
     import block_sparse_attention_strided_amd as X
     rng = np.random.default_rng(7)
