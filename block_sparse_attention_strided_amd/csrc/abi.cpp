@@ -52,6 +52,7 @@ struct Plan {
   size_t off_o[3], off_l[3];
   size_t off_table;
   size_t off_vt, off_lists;
+  size_t off_ctr;  // attention's tail-part counter (4 bytes)
   int num_pages;  // 128-key pages of the K/V arrays (contiguous or paged)
   size_t total;
 };
@@ -157,6 +158,8 @@ int make_plan(const XattnShape* sh, const XattnParams* pr, Plan* p) {
     off = align_up(off + (size_t)p->num_pages * p->hkv * p->d * XATTN_BLOCK * 2);
   p->off_lists = off;
   off = align_up(off + B * p->hkv * (size_t)p->max_qb * (p->max_kb + 1) * sizeof(int32_t));
+  p->off_ctr = off;
+  off = align_up(off + sizeof(int32_t));
   p->total = off;
   return XATTN_OK;
 }
@@ -304,6 +307,7 @@ hipError_t plan_attention(const XattnShape* sh, const Plan& p, const AttnArgs& a
     pa.jb0 = aa.jb0;
     pa.jb1 = aa.jb1;
     pa.lists = ws_at<int32_t>(ws, p.off_lists);
+    pa.tail_ctr = ws_at<int>(ws, p.off_ctr);
     return launch_plan(pa, p.batch, st);
   }
   return hipSuccess;
@@ -335,12 +339,17 @@ int device_cu_count() {
 // CUs at once (one round) and the longest row exceeds the share by at least
 // 4 blocks and 2%, rows longer than the share keep a head of `share` blocks
 // and move the rest into a tail part; longest first, the tails start on the
-// CUs whose short rows finish first, which evens out the CUs' totals.  One
-// sequence without splits keeps the kernel's default order, which is the
-// same order.
+// CUs whose short rows finish first, which evens out the CUs' totals.  When
+// the ping-pong kernel runs the launch, the tails are not given workgroups
+// of their own: every workgroup draws them from a counter after its head or
+// unsplit row, so CUs that run faster (the XCDs differ by a few percent)
+// take more of them.  One sequence without splits keeps the kernel's default
+// order, which is the same order.
 void set_order(const XattnShape* sh, const Plan& p, AttnArgs& aa, void* ws, SplitMergeArgs* sm) {
   sm->n = 0;
   aa.n_order = 0;
+  aa.n_static = 0;
+  aa.tail_ctr = nullptr;
   struct Row {
     int len, b, i;
   };
@@ -408,7 +417,26 @@ void set_order(const XattnShape* sh, const Plan& p, AttnArgs& aa, void* ws, Spli
     nsplit = 0;
   }
   if (p.batch == 1 && nsplit == 0) return;
-  std::stable_sort(items.begin(), items.end(), [](const Item& x, const Item& y) { return x.neg_len < y.neg_len; });
+  // dynamic tails: heads and unsplit rows first, then the tails, each run
+  // longest first
+  const bool dyn = head > 0 && attention_uses_pp(aa, p.d);
+  std::stable_sort(items.begin(), items.end(), [dyn](const Item& x, const Item& y) {
+    if (dyn) {
+      const bool tx = ((x.entry >> 28) & 3u) != 0, ty = ((y.entry >> 28) & 3u) != 0;
+      if (tx != ty) return !tx;
+    }
+    return x.neg_len < y.neg_len;
+  });
+  aa.n_static = 0;
+  aa.tail_ctr = nullptr;
+  if (dyn) {
+    int ns = 0;
+    while (ns < (int)items.size() && ((items[ns].entry >> 28) & 3u) == 0) ++ns;
+    if (ns < (int)items.size()) {
+      aa.n_static = ns;
+      aa.tail_ctr = ws_at<int>(ws, p.off_ctr);
+    }
+  }
   aa.n_order = (int)items.size();
   for (size_t r = 0; r < items.size(); ++r) {
     aa.order[r] = (int)items[r].entry;

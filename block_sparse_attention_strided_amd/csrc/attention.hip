@@ -156,6 +156,19 @@ __device__ __forceinline__ void wait_vmcnt() {
 struct WorkUnit {
   int b, g, pair, i, s, ns, cut;
 };
+// Unit of order entry r in kv slot `slot` (slot = pair * hkv + g).
+__device__ __forceinline__ WorkUnit entry_unit(const AttnArgs& a, int hkv, int r, int slot) {
+  WorkUnit u;
+  const uint32_t e = (uint32_t)a.order[r];
+  u.b = (int)((e >> 16) & 0xfffu);
+  u.i = (int)(e & 0xffffu);
+  u.s = (int)((e >> 28) & 3u);
+  u.ns = (int)(e >> 30) + 1;
+  u.cut = a.order_cut[r];
+  u.g = slot % hkv;
+  u.pair = slot / hkv;
+  return u;
+}
 __device__ __forceinline__ WorkUnit work_unit(const AttnArgs& a, int hkv, int npair, int id, int nwg) {
   WorkUnit u;
   const int ns = hkv * npair;
@@ -169,15 +182,7 @@ __device__ __forceinline__ WorkUnit work_unit(const AttnArgs& a, int hkv, int np
       slot = id % ns;
       r = id / ns;
     }
-    const uint32_t e = (uint32_t)a.order[r];
-    u.b = (int)((e >> 16) & 0xfffu);
-    u.i = (int)(e & 0xffffu);
-    u.s = (int)((e >> 28) & 3u);
-    u.ns = (int)(e >> 30) + 1;
-    u.cut = a.order_cut[r];
-    u.g = slot % hkv;
-    u.pair = slot / hkv;
-    return u;
+    return entry_unit(a, hkv, r, slot);
   }
   const int full = (nwg / 8) * 8;
   const int logical = id < full ? (id % 8) * (nwg / 8) + id / 8 : id;
@@ -260,6 +265,7 @@ __global__ __launch_bounds__(64) void plan_kernel(PlanArgs a) {
   const int lk = a.cu_k[b + 1] - a.cu_k[b];
   const int qb = lq / kBlock, kh = (lk - lq) / kBlock;
   int32_t* out = a.lists + (((long long)b * a.hkv + g) * a.max_qb + i) * (a.max_kb + 1);
+  if (a.tail_ctr && i == 0 && g == 0 && b == 0 && lane == 0) *a.tail_ctr = 0;
   if (i >= qb) {
     if (lane == 0) out[0] = 0;
     return;
@@ -579,447 +585,471 @@ __global__ __launch_bounds__(512) void attn_pp(AttnArgs a, int hkv) {
   __shared__ __align__(1024) char tiles[2 * ST * TILE];  // K stages, then V stages
   extern __shared__ int32_t list[];
 
-  // ---- work unit (XCD-aware: the 8 XCDs take consecutive ids round-robin)
+  // ---- work units.  Unit of workgroup id: XCD-aware (the 8 XCDs take
+  // consecutive ids round-robin).  With dynamic tails, every workgroup then
+  // draws further units from the launch's counter until they run out.
   const int npair = a.group / 2;
-  const WorkUnit wk = work_unit(a, hkv, npair, blockIdx.x, gridDim.x);
-  const int pair = wk.pair, g = wk.g, b = wk.b, i = wk.i;
-  const int q0 = a.cu_q[b];
-  const int lq = a.cu_q[b + 1] - q0;
-  if (i >= lq / kBlock) return;
+  const int slots = hkv * npair;
+  const bool dyn = a.n_static > 0 && a.n_static < a.n_order && a.tail_ctr != nullptr;
+  __shared__ int next_unit;
+  auto run_unit = [&](const WorkUnit wk) __attribute__((always_inline)) {
+    const int pair = wk.pair, g = wk.g, b = wk.b, i = wk.i;
+    const int q0 = a.cu_q[b];
+    const int lq = a.cu_q[b + 1] - q0;
+    if (i >= lq / kBlock) return;
 
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-  const int l32 = lane & 31, hh = lane >> 5;
-  const int grp = __builtin_amdgcn_readfirstlane(w >> 2), qs = w & 3;
-  const int h = g * a.group + pair * 2 + grp;
-  const int xq = qs * 32 + l32;  // query within the block
-  const int x = i * kBlock + xq;
+    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    const int l32 = lane & 31, hh = lane >> 5;
+    const int grp = __builtin_amdgcn_readfirstlane(w >> 2), qs = w & 3;
+    const int h = g * a.group + pair * 2 + grp;
+    const int xq = qs * 32 + l32;  // query within the block
+    const int x = i * kBlock + xq;
 
-  // Block list of this row, copied to LDS.
-  const int32_t* glist = a.lists + (((long long)b * hkv + g) * a.max_qb + i) * (a.max_kb + 1);
-  const int nblk = __builtin_amdgcn_readfirstlane(load_row_list(glist, list, wk.s, wk.ns, wk.cut, tid, 64 * NW));
-  __syncthreads();
-  const int ntile = 2 * nblk;
-  // The diagonal block, if present, is the last entry: only its two tiles
-  // need the causal mask.
-  const int first_diag = __builtin_amdgcn_readfirstlane((nblk > 0 && (list[nblk] & 1)) ? ntile - 2 : ntile);
-  const uint32_t list_lds = (uint32_t)(uintptr_t)(lds_ptr_t)list;
+    // Block list of this row, copied to LDS.
+    const int32_t* glist = a.lists + (((long long)b * hkv + g) * a.max_qb + i) * (a.max_kb + 1);
+    const int nblk = __builtin_amdgcn_readfirstlane(load_row_list(glist, list, wk.s, wk.ns, wk.cut, tid, 64 * NW));
+    __syncthreads();
+    const int ntile = 2 * nblk;
+    // The diagonal block, if present, is the last entry: only its two tiles
+    // need the causal mask.
+    const int first_diag = __builtin_amdgcn_readfirstlane((nblk > 0 && (list[nblk] & 1)) ? ntile - 2 : ntile);
+    const uint32_t list_lds = (uint32_t)(uintptr_t)(lds_ptr_t)list;
 
-  // Q fragments: B operand of S^T (query col = lane%32, d slots 8*hh .. +8).
-  bf16x8 qf[D / 16];
-  {
-    const char* qrow = a.q + ((long long)(q0 + x) * a.hq + h) * D * 2;
-#pragma unroll
-    for (int kk = 0; kk < D / 16; ++kk) qf[kk] = *(const bf16x8*)(qrow + (kk * 16 + hh * 8) * 2);
-  }
-
-  // Per-thread constant parts of the direct-load addresses.
-  const long long k_page_bytes = (long long)kBlock * hkv * D * 2;
-  const long long k_row_bytes = (long long)hkv * D * 2;
-  // V row swizzle of the transposing reads: the rows one read instruction
-  // touches (4hh + c/4 plus a multiple of 8) spread over all 64 banks, two
-  // lanes per bank (the minimum for 512 bytes)
-  auto vn_swz = [](int row) { return (KCPR == 16) ? 4 * (row & 3) : 4 * ((row >> 1) & 1); };
-  int koff[LPW], voff[LPW];
-#pragma unroll
-  for (int n = 0; n < LPW; ++n) {
-    const int idx = (w * LPW + n) * 64 + lane;
-    const int krow = idx / KCPR, kpch = idx % KCPR;
-    const int kc = (KCPR == 16) ? (kpch ^ (krow & 15)) : (kpch ^ ((krow >> 1) & 7));
-    koff[n] = (int)(krow * k_row_bytes + kc * 16);
-    // V in its own layout, 16-byte chunks of a row XOR-swizzled for the
-    // transposing reads
-    voff[n] = (int)(krow * k_row_bytes + (kpch ^ vn_swz(krow)) * 16);
-  }
-  const char* kbase = a.k.base + (long long)g * D * 2;
-  const char* vbase = a.v.base + (long long)g * D * 2;
-
-  // Tile copies: one raw buffer descriptor per operand for the whole launch
-  // (its K and V spans are below 2^31 bytes, checked by the launcher); a
-  // tile is a 32-bit byte offset in soffset plus the constant per-lane
-  // offsets, its LDS destination goes to m0.  Copy group gi copies K of
-  // tile gi+3 into K stage (gi+3)%4 and V of tile gi+2 into V stage
-  // (gi+2)%4.  Those stages last held K of tile gi-1 and V of tile gi-2,
-  // both last read in the MFMA phases of tile gi-1, which both groups have
-  // finished before group gi is issued.  Every group issues all its loads:
-  // a tile past the end (or before the start) re-reads an existing tile
-  // into its own stage, which no later phase reads, so the number of
-  // loads in flight -- and every vmcnt below -- is the same for each group.
-  const int wu = __builtin_amdgcn_readfirstlane(w);
-  const __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc(
-      (void*)kbase, (short)0, (int)(a.num_pages * k_page_bytes - (long long)g * D * 2), kBufFlags);
-  const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc(
-      (void*)vbase, (short)0, (int)(a.num_pages * k_page_bytes - (long long)g * D * 2), kBufFlags);
-  const int kpb = (int)k_page_bytes, khalf = (int)(KT * k_row_bytes);
-  char* const kl0 = tiles + wu * LPW * 1024;  // this wave's part of K stage 0 (V stage 0 at + ST * TILE)
-  // Copy sources.  Lane j of `eb` holds the byte offset of the page of block
-  // eb0 + j (the last block's for lanes past the end), read from the list in
-  // LDS by one read that waits for its own result (a read left in flight in
-  // an asm output could be copied by the compiler before it lands) and
-  // refilled once per 64 blocks; a group takes its offsets with v_readlane.
-  // Tile t is half t & 1 of block t >> 1.  A group past the last tile copies
-  // a tile of the last block into a stage that no later phase reads.
-  int eb = 0, eb0 = 0;
-  auto refill = [&](int base) __attribute__((always_inline)) {
-    eb0 = base;
-    const int z = base + lane < nblk ? base + lane : nblk - 1;
-    eb = (lds_read4_sync(list_lds + 4 * (1 + z)) >> 1) * kpb;
-  };
-  int soff_k = 0, soff_v = 0;
-  // The loads of one copy group: K into stage KS, V into stage VS.
-  auto issue = [&](int ks, int vs) __attribute__((always_inline)) {
-    const uint32_t lk = (uint32_t)(uintptr_t)(lds_ptr_t)kl0 + ks * TILE;
-    const uint32_t lv = (uint32_t)(uintptr_t)(lds_ptr_t)kl0 + (ST + vs) * TILE;
-    [&]<int... N>(std::integer_sequence<int, N...>) {
-      (__builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (lds_ptr_t)(uintptr_t)(lk + N * 1024), 16, (uint32_t)koff[N],
-                                                soff_k, 0, 0),
-       ...);
-      (__builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (lds_ptr_t)(uintptr_t)(lv + N * 1024), 16, (uint32_t)voff[N],
-                                                soff_v, 0, 0),
-       ...);
-    }(std::make_integer_sequence<int, LPW>{});
-  };
-  // Groups -3..-1 (G = gi + 3 = 0..2): K of tile G into stage G, V of tile
-  // max(G - 1, 0) into stage max(G - 1, 0), tiles clamped to the last one.
-  auto copy_prologue = [&](auto g_tag) __attribute__((always_inline)) {
-    constexpr int G = decltype(g_tag)::value, GV = G > 1 ? G - 1 : 0;
-    const int tk = G < ntile ? G : ntile - 1;
-    const int tv = GV < ntile ? GV : ntile - 1;
-    soff_k = __builtin_amdgcn_readlane(eb, tk >> 1) + (tk & 1) * khalf;
-    soff_v = __builtin_amdgcn_readlane(eb, tv >> 1) + (tv & 1) * khalf;
-    issue(G, GV);
-  };
-  // Group gi >= 0 (P = gi % 2): K of tile gi + 3 into stage (gi + 3) % 4, V
-  // of tile gi + 2 into stage (gi + 2) % 4.  For even gi both tiles are the
-  // halves of block (gi + 3) >> 1, whose offset the previous group took
-  // (e_last); for odd gi the K tile opens the next block and the V tile is
-  // the second half of e_last's.  li = ((gi + 3) >> 1) - eb0.
-  int e_last = 0, li = 1;
-  auto copy_group = [&](auto p_tag, int gi) __attribute__((always_inline)) {
-    if constexpr (decltype(p_tag)::value) {
-      if (++li == 64) {
-        refill(eb0 + 64);
-        li = 0;
-      }
-      const int e = __builtin_amdgcn_readlane(eb, li);
-      soff_k = e;
-      soff_v = e_last + khalf;
-      e_last = e;
-    } else {
-      soff_k = e_last + khalf;
-      soff_v = e_last;
+    // Q fragments: B operand of S^T (query col = lane%32, d slots 8*hh .. +8).
+    bf16x8 qf[D / 16];
+    {
+      const char* qrow = a.q + ((long long)(q0 + x) * a.hq + h) * D * 2;
+  #pragma unroll
+      for (int kk = 0; kk < D / 16; ++kk) qf[kk] = *(const bf16x8*)(qrow + (kk * 16 + hh * 8) * 2);
     }
-    issue((gi + 3) & (ST - 1), (gi + 2) & (ST - 1));
-  };
-  // Per-lane LDS addresses of the MFMA A fragments in stage 0.
-  const uint32_t lds0 = (uint32_t)(uintptr_t)(lds_ptr_t)tiles;
-  const int kswz = (KCPR == 16) ? (l32 & 15) : ((l32 >> 1) & 7);
-  uint32_t kaddr[D / 16], vaddr[4] = {0u, 0u, 0u, 0u};
-#pragma unroll
-  for (int kk = 0; kk < D / 16; ++kk) kaddr[kk] = lds0 + l32 * KROW + (((2 * kk + hh) ^ kswz) * 16);
-  {
-    // Transposing reads of V rows: for d block n and read r of key chunk m,
-    // lane c of 16-lane group G (c = lane % 16) addresses key row
-    // 16m + 8r + 4hh + c/4 at d = 32n + 16 (G % 2) + 4 (c % 4); lane l then
-    // holds V[16m + 8r + 4hh + e][32n + l % 32], e = 0..3, in k-slots
-    // 8hh + 4r + e: the keys P^T's k-slots hold (see vperm).  The row part
-    // 16m + 8r is an immediate offset; vaddr[n] carries the rest.
-    const int c = lane & 15, row0 = 4 * hh + (c >> 2);
-#pragma unroll
-    for (int n = 0; n < D / 32; ++n) {
-      const int d = 32 * n + 16 * ((lane >> 4) & 1) + 4 * (c & 3);
-      vaddr[n] = lds0 + ST * TILE + row0 * KROW + (((d >> 3) ^ vn_swz(row0)) * 16) + ((d >> 2) & 1) * 8;
-    }
-  }
 
-  f32x16 oacc[D / 32];
-#pragma unroll
-  for (int n = 0; n < D / 32; ++n)
-#pragma unroll
-    for (int e = 0; e < 16; ++e) oacc[n][e] = 0.f;
-  f32x16 s0, s1;
-  bf16x8 pb[4];
-  float m_run = kNegInf, l_run = 0.f;
-  float mneg = 0.f, m_thr = kNegInf;  // -m_run (0 while it is -inf); (m_run + 8) / c2
-  const float c2 = a.scale2;
+    // Per-thread constant parts of the direct-load addresses.
+    const long long k_page_bytes = (long long)kBlock * hkv * D * 2;
+    const long long k_row_bytes = (long long)hkv * D * 2;
+    // V row swizzle of the transposing reads: the rows one read instruction
+    // touches (4hh + c/4 plus a multiple of 8) spread over all 64 banks, two
+    // lanes per bank (the minimum for 512 bytes)
+    auto vn_swz = [](int row) { return (KCPR == 16) ? 4 * (row & 3) : 4 * ((row >> 1) & 1); };
+    int koff[LPW], voff[LPW];
+  #pragma unroll
+    for (int n = 0; n < LPW; ++n) {
+      const int idx = (w * LPW + n) * 64 + lane;
+      const int krow = idx / KCPR, kpch = idx % KCPR;
+      const int kc = (KCPR == 16) ? (kpch ^ (krow & 15)) : (kpch ^ ((krow >> 1) & 7));
+      koff[n] = (int)(krow * k_row_bytes + kc * 16);
+      // V in its own layout, 16-byte chunks of a row XOR-swizzled for the
+      // transposing reads
+      voff[n] = (int)(krow * k_row_bytes + (kpch ^ vn_swz(krow)) * 16);
+    }
+    const char* kbase = a.k.base + (long long)g * D * 2;
+    const char* vbase = a.v.base + (long long)g * D * 2;
 
-  // ---- MFMA phase of tile u: O^T += V^T(u-1) P^T(u-1) if PV, S^T(u) = K(u) Q^T
-  // if SS.  The two MFMA streams alternate; LDS fragments are read two ahead.
-  auto mma = [&](auto pv_tag, auto ss_tag, int u) __attribute__((always_inline)) {
-    constexpr bool PV = decltype(pv_tag)::value, SS = decltype(ss_tag)::value;
-    constexpr int NOPS = (PV ? NPV : 0) + (SS ? NS : 0);
-    // K(u) in stage u % 4, V(u - 1) in stage (u - 1) % 4
-    const uint32_t kst = (uint32_t)((u & (ST - 1)) * TILE);
-    const uint32_t vst = (uint32_t)(((u + ST - 1) & (ST - 1)) * TILE);
-    uint32_t ka[D / 16], va4[4];
-    if constexpr (SS) {
-#pragma unroll
-      for (int kk = 0; kk < D / 16; ++kk) ka[kk] = kaddr[kk] + kst;
-#pragma unroll
-      for (int z = 0; z < 16; ++z) {
-        s0[z] = 0.f;
-        s1[z] = 0.f;
-      }
-    }
-    if constexpr (PV) {
-#pragma unroll
-      for (int m = 0; m < 4; ++m) va4[m] = vaddr[m] + vst;
-    }
-    // op J: a PV step when PV and (J even or !SS), else an S step
-    auto is_pv = [](int j) constexpr { return PV && (!SS || (j % 2 == 0)); };
-    auto sub_idx = [](int j) constexpr { return (PV && SS) ? j / 2 : j; };
-    // LDS read instructions of op j (a PV step reads two halves when V is
-    // read transposed), and those of ops J+1 .. J+PF (issued before op J's
-    // wait)
-    auto after = [=](int j) constexpr {
-      int c = 0;
-      for (int x = j + 1; x < NOPS && x <= j + PF; ++x) c += is_pv(x) ? 2 : 1;
-      return c < 15 ? c : 15;  // lgkmcnt field limit; a smaller count only waits longer
+    // Tile copies: one raw buffer descriptor per operand for the whole launch
+    // (its K and V spans are below 2^31 bytes, checked by the launcher); a
+    // tile is a 32-bit byte offset in soffset plus the constant per-lane
+    // offsets, its LDS destination goes to m0.  Copy group gi copies K of
+    // tile gi+3 into K stage (gi+3)%4 and V of tile gi+2 into V stage
+    // (gi+2)%4.  Those stages last held K of tile gi-1 and V of tile gi-2,
+    // both last read in the MFMA phases of tile gi-1, which both groups have
+    // finished before group gi is issued.  Every group issues all its loads:
+    // a tile past the end (or before the start) re-reads an existing tile
+    // into its own stage, which no later phase reads, so the number of
+    // loads in flight -- and every vmcnt below -- is the same for each group.
+    const int wu = __builtin_amdgcn_readfirstlane(w);
+    const __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)kbase, (short)0, (int)(a.num_pages * k_page_bytes - (long long)g * D * 2), kBufFlags);
+    const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)vbase, (short)0, (int)(a.num_pages * k_page_bytes - (long long)g * D * 2), kBufFlags);
+    const int kpb = (int)k_page_bytes, khalf = (int)(KT * k_row_bytes);
+    char* const kl0 = tiles + wu * LPW * 1024;  // this wave's part of K stage 0 (V stage 0 at + ST * TILE)
+    // Copy sources.  Lane j of `eb` holds the byte offset of the page of block
+    // eb0 + j (the last block's for lanes past the end), read from the list in
+    // LDS by one read that waits for its own result (a read left in flight in
+    // an asm output could be copied by the compiler before it lands) and
+    // refilled once per 64 blocks; a group takes its offsets with v_readlane.
+    // Tile t is half t & 1 of block t >> 1.  A group past the last tile copies
+    // a tile of the last block into a stage that no later phase reads.
+    int eb = 0, eb0 = 0;
+    auto refill = [&](int base) __attribute__((always_inline)) {
+      eb0 = base;
+      const int z = base + lane < nblk ? base + lane : nblk - 1;
+      eb = (lds_read4_sync(list_lds + 4 * (1 + z)) >> 1) * kpb;
     };
-    // fragment of op J: fr[J] (16-byte read) or fl[J], fh[J] (transposing
-    // halves); reads run PF ops ahead of the MFMAs
-    u32x4 fr[NOPS];
-    u32x2 fl[NOPS], fh[NOPS];
-    auto frag = [&](auto j_tag) {
-      constexpr int J = decltype(j_tag)::value;
-      constexpr int I = sub_idx(J);
-      if constexpr (is_pv(J)) {
-        constexpr int M = I / (D / 32), N = I % (D / 32);
-        fl[J] = lds_read8_tr_at<(16 * M) * KROW>(va4[N]);
-        fh[J] = lds_read8_tr_at<(16 * M + 8) * KROW>(va4[N]);
+    int soff_k = 0, soff_v = 0;
+    // The loads of one copy group: K into stage KS, V into stage VS.
+    auto issue = [&](int ks, int vs) __attribute__((always_inline)) {
+      const uint32_t lk = (uint32_t)(uintptr_t)(lds_ptr_t)kl0 + ks * TILE;
+      const uint32_t lv = (uint32_t)(uintptr_t)(lds_ptr_t)kl0 + (ST + vs) * TILE;
+      [&]<int... N>(std::integer_sequence<int, N...>) {
+        (__builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (lds_ptr_t)(uintptr_t)(lk + N * 1024), 16, (uint32_t)koff[N],
+                                                  soff_k, 0, 0),
+         ...);
+        (__builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (lds_ptr_t)(uintptr_t)(lv + N * 1024), 16, (uint32_t)voff[N],
+                                                  soff_v, 0, 0),
+         ...);
+      }(std::make_integer_sequence<int, LPW>{});
+    };
+    // Groups -3..-1 (G = gi + 3 = 0..2): K of tile G into stage G, V of tile
+    // max(G - 1, 0) into stage max(G - 1, 0), tiles clamped to the last one.
+    auto copy_prologue = [&](auto g_tag) __attribute__((always_inline)) {
+      constexpr int G = decltype(g_tag)::value, GV = G > 1 ? G - 1 : 0;
+      const int tk = G < ntile ? G : ntile - 1;
+      const int tv = GV < ntile ? GV : ntile - 1;
+      soff_k = __builtin_amdgcn_readlane(eb, tk >> 1) + (tk & 1) * khalf;
+      soff_v = __builtin_amdgcn_readlane(eb, tv >> 1) + (tv & 1) * khalf;
+      issue(G, GV);
+    };
+    // Group gi >= 0 (P = gi % 2): K of tile gi + 3 into stage (gi + 3) % 4, V
+    // of tile gi + 2 into stage (gi + 2) % 4.  For even gi both tiles are the
+    // halves of block (gi + 3) >> 1, whose offset the previous group took
+    // (e_last); for odd gi the K tile opens the next block and the V tile is
+    // the second half of e_last's.  li = ((gi + 3) >> 1) - eb0.
+    int e_last = 0, li = 1;
+    auto copy_group = [&](auto p_tag, int gi) __attribute__((always_inline)) {
+      if constexpr (decltype(p_tag)::value) {
+        if (++li == 64) {
+          refill(eb0 + 64);
+          li = 0;
+        }
+        const int e = __builtin_amdgcn_readlane(eb, li);
+        soff_k = e;
+        soff_v = e_last + khalf;
+        e_last = e;
       } else {
-        constexpr int KK = I >> 1, HALF = I & 1;
-        fr[J] = lds_read16_at<HALF * 32 * KROW>(ka[KK]);
+        soff_k = e_last + khalf;
+        soff_v = e_last;
       }
+      issue((gi + 3) & (ST - 1), (gi + 2) & (ST - 1));
     };
-    [&]<int... J>(std::integer_sequence<int, J...>) {
-      (frag(std::integral_constant<int, J>{}), ...);
-    }(std::make_integer_sequence<int, (PF < NOPS ? PF : NOPS)>{});
-    auto op = [&](auto j_tag) {
-      constexpr int J = decltype(j_tag)::value;
-      constexpr int I = sub_idx(J);
-      if constexpr (J + PF < NOPS) frag(std::integral_constant<int, J + PF>{});
-      u32x4 fa;
-      if constexpr (is_pv(J)) {
-        lgkm_wait<after(J)>(fl[J], fh[J]);
-        fa = u32x4{fl[J][0], fl[J][1], fh[J][0], fh[J][1]};
-      } else {
-        lgkm_wait<after(J)>(fr[J]);
-        fa = fr[J];
+    // Per-lane LDS addresses of the MFMA A fragments in stage 0.
+    const uint32_t lds0 = (uint32_t)(uintptr_t)(lds_ptr_t)tiles;
+    const int kswz = (KCPR == 16) ? (l32 & 15) : ((l32 >> 1) & 7);
+    uint32_t kaddr[D / 16], vaddr[4] = {0u, 0u, 0u, 0u};
+  #pragma unroll
+    for (int kk = 0; kk < D / 16; ++kk) kaddr[kk] = lds0 + l32 * KROW + (((2 * kk + hh) ^ kswz) * 16);
+    {
+      // Transposing reads of V rows: for d block n and read r of key chunk m,
+      // lane c of 16-lane group G (c = lane % 16) addresses key row
+      // 16m + 8r + 4hh + c/4 at d = 32n + 16 (G % 2) + 4 (c % 4); lane l then
+      // holds V[16m + 8r + 4hh + e][32n + l % 32], e = 0..3, in k-slots
+      // 8hh + 4r + e: the keys P^T's k-slots hold (see vperm).  The row part
+      // 16m + 8r is an immediate offset; vaddr[n] carries the rest.
+      const int c = lane & 15, row0 = 4 * hh + (c >> 2);
+  #pragma unroll
+      for (int n = 0; n < D / 32; ++n) {
+        const int d = 32 * n + 16 * ((lane >> 4) & 1) + 4 * (c & 3);
+        vaddr[n] = lds0 + ST * TILE + row0 * KROW + (((d >> 3) ^ vn_swz(row0)) * 16) + ((d >> 2) & 1) * 8;
       }
-      if constexpr (is_pv(J)) {
-        constexpr int M = I / (D / 32), N = I % (D / 32);
-        oacc[N] = mfma32(__builtin_bit_cast(bf16x8, fa), pb[M], oacc[N]);
-      } else {
-        constexpr int KK = I >> 1, HALF = I & 1;
-        if constexpr (HALF == 0) s0 = mfma32(__builtin_bit_cast(bf16x8, fa), qf[KK], s0);
-        else s1 = mfma32(__builtin_bit_cast(bf16x8, fa), qf[KK], s1);
-      }
-    };
-    [&]<int... J>(std::integer_sequence<int, J...>) {
-      (op(std::integral_constant<int, J>{}), ...);
-    }(std::make_integer_sequence<int, NOPS>{});
-  };
+    }
 
-  // ---- softmax of tile u (P = u % 2): S^T registers -> P^T (bf16) in pb
-  auto smax = [&](auto p_tag, int u) __attribute__((always_inline)) {
-    constexpr int sub = decltype(p_tag)::value;
-    const bool diag = u >= first_diag;
-    if (diag) {
-      // key = kc + 4 hh > xq with kc a constant: compare kc with xq - 4 hh,
-      // which passes through an empty asm so that neither the keys nor the
-      // compares are hoisted out of the loop into 64 registers or lane masks
-      int xt = xq - 4 * hh;
-      asm volatile("" : "+v"(xt)::"memory");
-#pragma unroll
-      for (int z = 0; z < 16; ++z) {
-        const int kc = sub * KT + 8 * (z >> 2) + (z & 3);
-        if (kc > xt) s0[z] = kNegInf;
-        if (kc + 32 > xt) s1[z] = kNegInf;
-      }
-    }
-    // Row max as a tree of three-input maxima (IEEE maximum lowers to
-    // v_maximum3_f32 without operand canonicalisation): 17 instructions for
-    // the 32 values of a lane.
-    auto mx3 = [](float p, float q, float r) {
-      return __builtin_elementwise_maximum(__builtin_elementwise_maximum(p, q), r);
-    };
-    float t[11];
-#pragma unroll
-    for (int k = 0; k < 5; ++k) {
-      t[k] = mx3(s0[3 * k], s0[3 * k + 1], s0[3 * k + 2]);
-      t[5 + k] = mx3(s1[3 * k], s1[3 * k + 1], s1[3 * k + 2]);
-    }
-    t[10] = __builtin_elementwise_maximum(s0[15], s1[15]);
-    float mx = __builtin_elementwise_maximum(mx3(mx3(t[0], t[1], t[2]), mx3(t[3], t[4], t[5]), mx3(t[6], t[7], t[8])),
-                                             __builtin_elementwise_maximum(t[9], t[10]));
-    mx = half_max(mx);
-    // Lazy rescale: the running max moves only when the tile's exceeds it by
-    // more than 8 (weights stay below 2^8); m_thr is that bound on the
-    // unscaled scores.
-    if (__ballot(mx > m_thr) != 0ull) {
-      const float m_new = fmaxf(m_run, mx * c2);
-      const float alpha = fast_exp2(m_run - m_new);
-      l_run *= alpha;
-#pragma unroll
-      for (int n = 0; n < D / 32; ++n)
-#pragma unroll
-        for (int z = 0; z < 16; ++z) oacc[n][z] *= alpha;
-      m_run = m_new;
-      mneg = (m_new == kNegInf) ? 0.f : -m_new;
-      m_thr = (m_new + 8.0f) / c2;
-    }
-    // Row sum of the fp32 probabilities (rounding them to bf16 first would
-    // move the LSE of short rows by up to half a bf16 ulp), four chains.
-    float ps[4];
-    auto chunk = [&](auto c_tag) {
-      constexpr int C = decltype(c_tag)::value;
-#pragma unroll
-      for (int z = 4 * C; z < 4 * C + 4; ++z) {
-        s0[z] = fast_exp2(fmaf(s0[z], c2, mneg));
-        s1[z] = fast_exp2(fmaf(s1[z], c2, mneg));
-        if constexpr (C == 0) ps[z & 3] = s0[z] + s1[z];
-        else ps[z & 3] += s0[z] + s1[z];
-      }
-    };
-    chunk(std::integral_constant<int, 0>{});
-    chunk(std::integral_constant<int, 1>{});
-    chunk(std::integral_constant<int, 2>{});
-    chunk(std::integral_constant<int, 3>{});
-#pragma unroll
-    for (int m = 0; m < 4; ++m) {
-      const int i0 = 2 * (m & 1);
-#pragma unroll
-      for (int z = 0; z < 8; ++z) pb[m][z] = (__bf16)((m < 2) ? s0[4 * i0 + z] : s1[4 * i0 + z]);
-    }
-    l_run += (ps[0] + ps[1]) + (ps[2] + ps[3]);
-  };
+    f32x16 oacc[D / 32];
+  #pragma unroll
+    for (int n = 0; n < D / 32; ++n)
+  #pragma unroll
+      for (int e = 0; e < 16; ++e) oacc[n][e] = 0.f;
+    f32x16 s0, s1;
+    bf16x8 pb[4];
+    float m_run = kNegInf, l_run = 0.f;
+    float mneg = 0.f, m_thr = kNegInf;  // -m_run (0 while it is -inf); (m_run + 8) / c2
+    const float c2 = a.scale2;
 
-  // Register fences: the compiler would otherwise move the tail of a phase
-  // (e.g. the exponentials, whose only consumer is the next MFMA phase)
-  // across the barrier into the other phase of the same wave, where it runs
-  // serially with that wave's MFMAs instead of beside the other group's.
-  auto fence_mma = [&]() __attribute__((always_inline)) {
-    reg_fence(s0);
-    reg_fence(s1);
-#pragma unroll
-    for (int n = 0; n < D / 32; ++n) reg_fence(oacc[n]);
-  };
-  auto fence_smax = [&]() __attribute__((always_inline)) {
-#pragma unroll
-    for (int m = 0; m < 4; ++m) reg_fence(pb[m]);
-    reg_fence(l_run);
-    reg_fence(m_run);
-#pragma unroll
-    for (int n = 0; n < D / 32; ++n) reg_fence(oacc[n]);
-  };
-  using T_ = std::integral_constant<bool, true>;
-  using F_ = std::integral_constant<bool, false>;
-  // Schedule.  Per tile u, group A (waves 0-3) runs the MFMA phase of u
-  // (O += V^T(u-1) P(u-1) and S(u)) and then the softmax phase of u (copy
-  // group u, P(u) from S(u)); group B runs the softmax phase of u - 1 and
-  // then the MFMA phase of u; one workgroup barrier ends the tile.  On each
-  // SIMD the A wave's MFMAs thus run beside the B wave's softmax and vice
-  // versa; the barrier realigns the two halves once per tile.
-  // Copies: before barrier u, every wave has its copy group u - 2 done (A
-  // has issued up to group u and waits for all but two groups, B up to
-  // u - 1 and waits for all but one), so after it both operands of MFMA
-  // phase u + 1 (K(u + 1), V(u), from group u - 2) are in LDS.  Group g
-  // overwrites K(g - 1) and V(g - 2), which only MFMA phase g - 1 reads:
-  // A issues it after barrier g - 1, B after barrier g, and every wave's
-  // MFMA phase g - 1 precedes barrier g - 1.
-  // Prologue: copy groups -3..-1 (K of tiles 0..2, V of tiles 0..1); the
-  // barrier after it makes group -3 (K(0)) visible.
-  if (ntile > 0) {
-    refill(0);
-    e_last = __builtin_amdgcn_readlane(eb, 1);  // block 1 (or the last)
-    copy_prologue(std::integral_constant<int, 0>{});  // V part: tile 0, the same bytes as group -2's
-    copy_prologue(std::integral_constant<int, 1>{});
-    copy_prologue(std::integral_constant<int, 2>{});
-    wait_vmcnt<4 * LPW>();
-  }
-  __builtin_amdgcn_s_barrier();
-  // Tile 0 has no PV part; the loops are unrolled by two so that the tile
-  // parity (the copy sources' bookkeeping and the diagonal mask) is a
-  // constant.
-  auto softmax_phase = [&](auto p_tag, int u) __attribute__((always_inline)) {
-    copy_group(p_tag, u);
-    smax(p_tag, u);
-    fence_smax();
-  };
-  auto mma_phase = [&](auto pv_tag, int u) __attribute__((always_inline)) {
-    __builtin_amdgcn_s_setprio(1);
-    mma(pv_tag, T_{}, u);
-    fence_mma();
-    __builtin_amdgcn_s_setprio(0);
-  };
-  using Even = std::integral_constant<int, 0>;
-  using Odd = std::integral_constant<int, 1>;
-  if (ntile > 0) {
-    if (grp == 0) {
-      auto step = [&](auto pv_tag, auto p_tag, int u) __attribute__((always_inline)) {
-        mma_phase(pv_tag, u);
-        softmax_phase(p_tag, u);
-        wait_vmcnt<4 * LPW>();
-        __builtin_amdgcn_s_barrier();
+    // ---- MFMA phase of tile u: O^T += V^T(u-1) P^T(u-1) if PV, S^T(u) = K(u) Q^T
+    // if SS.  The two MFMA streams alternate; LDS fragments are read two ahead.
+    auto mma = [&](auto pv_tag, auto ss_tag, int u) __attribute__((always_inline)) {
+      constexpr bool PV = decltype(pv_tag)::value, SS = decltype(ss_tag)::value;
+      constexpr int NOPS = (PV ? NPV : 0) + (SS ? NS : 0);
+      // K(u) in stage u % 4, V(u - 1) in stage (u - 1) % 4
+      const uint32_t kst = (uint32_t)((u & (ST - 1)) * TILE);
+      const uint32_t vst = (uint32_t)(((u + ST - 1) & (ST - 1)) * TILE);
+      uint32_t ka[D / 16], va4[4];
+      if constexpr (SS) {
+  #pragma unroll
+        for (int kk = 0; kk < D / 16; ++kk) ka[kk] = kaddr[kk] + kst;
+  #pragma unroll
+        for (int z = 0; z < 16; ++z) {
+          s0[z] = 0.f;
+          s1[z] = 0.f;
+        }
+      }
+      if constexpr (PV) {
+  #pragma unroll
+        for (int m = 0; m < 4; ++m) va4[m] = vaddr[m] + vst;
+      }
+      // op J: a PV step when PV and (J even or !SS), else an S step
+      auto is_pv = [](int j) constexpr { return PV && (!SS || (j % 2 == 0)); };
+      auto sub_idx = [](int j) constexpr { return (PV && SS) ? j / 2 : j; };
+      // LDS read instructions of op j (a PV step reads two halves when V is
+      // read transposed), and those of ops J+1 .. J+PF (issued before op J's
+      // wait)
+      auto after = [=](int j) constexpr {
+        int c = 0;
+        for (int x = j + 1; x < NOPS && x <= j + PF; ++x) c += is_pv(x) ? 2 : 1;
+        return c < 15 ? c : 15;  // lgkmcnt field limit; a smaller count only waits longer
       };
-      step(F_{}, Even{}, 0);
-      int u = 1;
-      for (; u + 1 < ntile; u += 2) {
-        step(T_{}, Odd{}, u);
-        step(T_{}, Even{}, u + 1);
+      // fragment of op J: fr[J] (16-byte read) or fl[J], fh[J] (transposing
+      // halves); reads run PF ops ahead of the MFMAs
+      u32x4 fr[NOPS];
+      u32x2 fl[NOPS], fh[NOPS];
+      auto frag = [&](auto j_tag) {
+        constexpr int J = decltype(j_tag)::value;
+        constexpr int I = sub_idx(J);
+        if constexpr (is_pv(J)) {
+          constexpr int M = I / (D / 32), N = I % (D / 32);
+          fl[J] = lds_read8_tr_at<(16 * M) * KROW>(va4[N]);
+          fh[J] = lds_read8_tr_at<(16 * M + 8) * KROW>(va4[N]);
+        } else {
+          constexpr int KK = I >> 1, HALF = I & 1;
+          fr[J] = lds_read16_at<HALF * 32 * KROW>(ka[KK]);
+        }
+      };
+      [&]<int... J>(std::integer_sequence<int, J...>) {
+        (frag(std::integral_constant<int, J>{}), ...);
+      }(std::make_integer_sequence<int, (PF < NOPS ? PF : NOPS)>{});
+      auto op = [&](auto j_tag) {
+        constexpr int J = decltype(j_tag)::value;
+        constexpr int I = sub_idx(J);
+        if constexpr (J + PF < NOPS) frag(std::integral_constant<int, J + PF>{});
+        u32x4 fa;
+        if constexpr (is_pv(J)) {
+          lgkm_wait<after(J)>(fl[J], fh[J]);
+          fa = u32x4{fl[J][0], fl[J][1], fh[J][0], fh[J][1]};
+        } else {
+          lgkm_wait<after(J)>(fr[J]);
+          fa = fr[J];
+        }
+        if constexpr (is_pv(J)) {
+          constexpr int M = I / (D / 32), N = I % (D / 32);
+          oacc[N] = mfma32(__builtin_bit_cast(bf16x8, fa), pb[M], oacc[N]);
+        } else {
+          constexpr int KK = I >> 1, HALF = I & 1;
+          if constexpr (HALF == 0) s0 = mfma32(__builtin_bit_cast(bf16x8, fa), qf[KK], s0);
+          else s1 = mfma32(__builtin_bit_cast(bf16x8, fa), qf[KK], s1);
+        }
+      };
+      [&]<int... J>(std::integer_sequence<int, J...>) {
+        (op(std::integral_constant<int, J>{}), ...);
+      }(std::make_integer_sequence<int, NOPS>{});
+    };
+
+    // ---- softmax of tile u (P = u % 2): S^T registers -> P^T (bf16) in pb
+    auto smax = [&](auto p_tag, int u) __attribute__((always_inline)) {
+      constexpr int sub = decltype(p_tag)::value;
+      const bool diag = u >= first_diag;
+      if (diag) {
+        // key = kc + 4 hh > xq with kc a constant: compare kc with xq - 4 hh,
+        // which passes through an empty asm so that neither the keys nor the
+        // compares are hoisted out of the loop into 64 registers or lane masks
+        int xt = xq - 4 * hh;
+        asm volatile("" : "+v"(xt)::"memory");
+  #pragma unroll
+        for (int z = 0; z < 16; ++z) {
+          const int kc = sub * KT + 8 * (z >> 2) + (z & 3);
+          if (kc > xt) s0[z] = kNegInf;
+          if (kc + 32 > xt) s1[z] = kNegInf;
+        }
       }
-      if (u < ntile) step(T_{}, Odd{}, u);
-    } else {
-      mma_phase(F_{}, 0);
-      wait_vmcnt<2 * LPW>();
-      __builtin_amdgcn_s_barrier();
-      auto step = [&](auto p_tag, int u) __attribute__((always_inline)) {
-        softmax_phase(p_tag, u - 1);  // p_tag: parity of u - 1
-        mma_phase(T_{}, u);
+      // Row max as a tree of three-input maxima (IEEE maximum lowers to
+      // v_maximum3_f32 without operand canonicalisation): 17 instructions for
+      // the 32 values of a lane.
+      auto mx3 = [](float p, float q, float r) {
+        return __builtin_elementwise_maximum(__builtin_elementwise_maximum(p, q), r);
+      };
+      float t[11];
+  #pragma unroll
+      for (int k = 0; k < 5; ++k) {
+        t[k] = mx3(s0[3 * k], s0[3 * k + 1], s0[3 * k + 2]);
+        t[5 + k] = mx3(s1[3 * k], s1[3 * k + 1], s1[3 * k + 2]);
+      }
+      t[10] = __builtin_elementwise_maximum(s0[15], s1[15]);
+      float mx = __builtin_elementwise_maximum(mx3(mx3(t[0], t[1], t[2]), mx3(t[3], t[4], t[5]), mx3(t[6], t[7], t[8])),
+                                               __builtin_elementwise_maximum(t[9], t[10]));
+      mx = half_max(mx);
+      // Lazy rescale: the running max moves only when the tile's exceeds it by
+      // more than 8 (weights stay below 2^8); m_thr is that bound on the
+      // unscaled scores.
+      if (__ballot(mx > m_thr) != 0ull) {
+        const float m_new = fmaxf(m_run, mx * c2);
+        const float alpha = fast_exp2(m_run - m_new);
+        l_run *= alpha;
+  #pragma unroll
+        for (int n = 0; n < D / 32; ++n)
+  #pragma unroll
+          for (int z = 0; z < 16; ++z) oacc[n][z] *= alpha;
+        m_run = m_new;
+        mneg = (m_new == kNegInf) ? 0.f : -m_new;
+        m_thr = (m_new + 8.0f) / c2;
+      }
+      // Row sum of the fp32 probabilities (rounding them to bf16 first would
+      // move the LSE of short rows by up to half a bf16 ulp), four chains.
+      float ps[4];
+      auto chunk = [&](auto c_tag) {
+        constexpr int C = decltype(c_tag)::value;
+  #pragma unroll
+        for (int z = 4 * C; z < 4 * C + 4; ++z) {
+          s0[z] = fast_exp2(fmaf(s0[z], c2, mneg));
+          s1[z] = fast_exp2(fmaf(s1[z], c2, mneg));
+          if constexpr (C == 0) ps[z & 3] = s0[z] + s1[z];
+          else ps[z & 3] += s0[z] + s1[z];
+        }
+      };
+      chunk(std::integral_constant<int, 0>{});
+      chunk(std::integral_constant<int, 1>{});
+      chunk(std::integral_constant<int, 2>{});
+      chunk(std::integral_constant<int, 3>{});
+  #pragma unroll
+      for (int m = 0; m < 4; ++m) {
+        const int i0 = 2 * (m & 1);
+  #pragma unroll
+        for (int z = 0; z < 8; ++z) pb[m][z] = (__bf16)((m < 2) ? s0[4 * i0 + z] : s1[4 * i0 + z]);
+      }
+      l_run += (ps[0] + ps[1]) + (ps[2] + ps[3]);
+    };
+
+    // Register fences: the compiler would otherwise move the tail of a phase
+    // (e.g. the exponentials, whose only consumer is the next MFMA phase)
+    // across the barrier into the other phase of the same wave, where it runs
+    // serially with that wave's MFMAs instead of beside the other group's.
+    auto fence_mma = [&]() __attribute__((always_inline)) {
+      reg_fence(s0);
+      reg_fence(s1);
+  #pragma unroll
+      for (int n = 0; n < D / 32; ++n) reg_fence(oacc[n]);
+    };
+    auto fence_smax = [&]() __attribute__((always_inline)) {
+  #pragma unroll
+      for (int m = 0; m < 4; ++m) reg_fence(pb[m]);
+      reg_fence(l_run);
+      reg_fence(m_run);
+  #pragma unroll
+      for (int n = 0; n < D / 32; ++n) reg_fence(oacc[n]);
+    };
+    using T_ = std::integral_constant<bool, true>;
+    using F_ = std::integral_constant<bool, false>;
+    // Schedule.  Per tile u, group A (waves 0-3) runs the MFMA phase of u
+    // (O += V^T(u-1) P(u-1) and S(u)) and then the softmax phase of u (copy
+    // group u, P(u) from S(u)); group B runs the softmax phase of u - 1 and
+    // then the MFMA phase of u; one workgroup barrier ends the tile.  On each
+    // SIMD the A wave's MFMAs thus run beside the B wave's softmax and vice
+    // versa; the barrier realigns the two halves once per tile.
+    // Copies: before barrier u, every wave has its copy group u - 2 done (A
+    // has issued up to group u and waits for all but two groups, B up to
+    // u - 1 and waits for all but one), so after it both operands of MFMA
+    // phase u + 1 (K(u + 1), V(u), from group u - 2) are in LDS.  Group g
+    // overwrites K(g - 1) and V(g - 2), which only MFMA phase g - 1 reads:
+    // A issues it after barrier g - 1, B after barrier g, and every wave's
+    // MFMA phase g - 1 precedes barrier g - 1.
+    // Prologue: copy groups -3..-1 (K of tiles 0..2, V of tiles 0..1); the
+    // barrier after it makes group -3 (K(0)) visible.
+    if (ntile > 0) {
+      refill(0);
+      e_last = __builtin_amdgcn_readlane(eb, 1);  // block 1 (or the last)
+      copy_prologue(std::integral_constant<int, 0>{});  // V part: tile 0, the same bytes as group -2's
+      copy_prologue(std::integral_constant<int, 1>{});
+      copy_prologue(std::integral_constant<int, 2>{});
+      wait_vmcnt<4 * LPW>();
+    }
+    __builtin_amdgcn_s_barrier();
+    // Tile 0 has no PV part; the loops are unrolled by two so that the tile
+    // parity (the copy sources' bookkeeping and the diagonal mask) is a
+    // constant.
+    auto softmax_phase = [&](auto p_tag, int u) __attribute__((always_inline)) {
+      copy_group(p_tag, u);
+      smax(p_tag, u);
+      fence_smax();
+    };
+    auto mma_phase = [&](auto pv_tag, int u) __attribute__((always_inline)) {
+      __builtin_amdgcn_s_setprio(1);
+      mma(pv_tag, T_{}, u);
+      fence_mma();
+      __builtin_amdgcn_s_setprio(0);
+    };
+    using Even = std::integral_constant<int, 0>;
+    using Odd = std::integral_constant<int, 1>;
+    if (ntile > 0) {
+      if (grp == 0) {
+        auto step = [&](auto pv_tag, auto p_tag, int u) __attribute__((always_inline)) {
+          mma_phase(pv_tag, u);
+          softmax_phase(p_tag, u);
+          wait_vmcnt<4 * LPW>();
+          __builtin_amdgcn_s_barrier();
+        };
+        step(F_{}, Even{}, 0);
+        int u = 1;
+        for (; u + 1 < ntile; u += 2) {
+          step(T_{}, Odd{}, u);
+          step(T_{}, Even{}, u + 1);
+        }
+        if (u < ntile) step(T_{}, Odd{}, u);
+      } else {
+        mma_phase(F_{}, 0);
         wait_vmcnt<2 * LPW>();
         __builtin_amdgcn_s_barrier();
-      };
-      int u = 1;
-      for (; u + 1 < ntile; u += 2) {
-        step(Even{}, u);
-        step(Odd{}, u + 1);
+        auto step = [&](auto p_tag, int u) __attribute__((always_inline)) {
+          softmax_phase(p_tag, u - 1);  // p_tag: parity of u - 1
+          mma_phase(T_{}, u);
+          wait_vmcnt<2 * LPW>();
+          __builtin_amdgcn_s_barrier();
+        };
+        int u = 1;
+        for (; u + 1 < ntile; u += 2) {
+          step(Even{}, u);
+          step(Odd{}, u + 1);
+        }
+        if (u < ntile) step(Even{}, u);
+        if (ntile & 1) softmax_phase(Even{}, ntile - 1);
+        else softmax_phase(Odd{}, ntile - 1);
       }
-      if (u < ntile) step(Even{}, u);
-      if (ntile & 1) softmax_phase(Even{}, ntile - 1);
-      else softmax_phase(Odd{}, ntile - 1);
+      mma(T_{}, F_{}, ntile);  // PV of the last tile
     }
-    mma(T_{}, F_{}, ntile);  // PV of the last tile
-  }
-  wait_vmcnt<0>();  // copies of the groups past the end land in LDS before exit
+    wait_vmcnt<0>();  // copies of the groups past the end land in LDS before exit
 
-  const float l_tot = half_sum(l_run);
-  const float inv = (l_tot > 0.f) ? 1.f / l_tot : 0.f;
-  const long long orow = ((long long)(q0 + x) * a.hq + h) * D;
-  float* const of32 = wk.ns > 1 ? a.split_o[wk.s] : a.out_f32;
-  float* const lsep = wk.ns > 1 ? a.split_l[wk.s] : a.lse;
-#pragma unroll
-  for (int n = 0; n < D / 32; ++n)
-#pragma unroll
-    for (int ii = 0; ii < 4; ++ii) {
-      const int d = n * 32 + 8 * ii + 4 * hh;
-      const float v0 = oacc[n][4 * ii + 0] * inv, v1 = oacc[n][4 * ii + 1] * inv;
-      const float v2 = oacc[n][4 * ii + 2] * inv, v3 = oacc[n][4 * ii + 3] * inv;
-      if (of32) {
-        f32x4 v = {v0, v1, v2, v3};
-        *(f32x4*)(of32 + orow + d) = v;
-      } else {
-        typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
-        bf16x4 o4;
-        o4[0] = (__bf16)v0;
-        o4[1] = (__bf16)v1;
-        o4[2] = (__bf16)v2;
-        o4[3] = (__bf16)v3;
-        *(bf16x4*)((char*)a.out + (orow + d) * 2) = o4;
+    const float l_tot = half_sum(l_run);
+    const float inv = (l_tot > 0.f) ? 1.f / l_tot : 0.f;
+    const long long orow = ((long long)(q0 + x) * a.hq + h) * D;
+    float* const of32 = wk.ns > 1 ? a.split_o[wk.s] : a.out_f32;
+    float* const lsep = wk.ns > 1 ? a.split_l[wk.s] : a.lse;
+  #pragma unroll
+    for (int n = 0; n < D / 32; ++n)
+  #pragma unroll
+      for (int ii = 0; ii < 4; ++ii) {
+        const int d = n * 32 + 8 * ii + 4 * hh;
+        const float v0 = oacc[n][4 * ii + 0] * inv, v1 = oacc[n][4 * ii + 1] * inv;
+        const float v2 = oacc[n][4 * ii + 2] * inv, v3 = oacc[n][4 * ii + 3] * inv;
+        if (of32) {
+          f32x4 v = {v0, v1, v2, v3};
+          *(f32x4*)(of32 + orow + d) = v;
+        } else {
+          typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+          bf16x4 o4;
+          o4[0] = (__bf16)v0;
+          o4[1] = (__bf16)v1;
+          o4[2] = (__bf16)v2;
+          o4[3] = (__bf16)v3;
+          *(bf16x4*)((char*)a.out + (orow + d) * 2) = o4;
+        }
       }
+    if (lsep && hh == 0) {
+      const float lse = (l_tot > 0.f) ? (m_run + log2f(l_tot)) * kLn2 : kNegInf;
+      lsep[(long long)h * a.total_q + q0 + x] = lse;
     }
-  if (lsep && hh == 0) {
-    const float lse = (l_tot > 0.f) ? (m_run + log2f(l_tot)) * kLn2 : kNegInf;
-    lsep[(long long)h * a.total_q + q0 + x] = lse;
+  };
+  WorkUnit wk = work_unit(a, hkv, npair, blockIdx.x, gridDim.x);
+  for (;;) {
+    run_unit(wk);
+    if (!dyn) break;
+    const int nt = (a.n_order - a.n_static) * slots;
+    __syncthreads();  // every wave is done with list[], tiles[] and next_unit
+    if (threadIdx.x == 0) {
+      const int t = atomicAdd(a.tail_ctr, 1);
+      // every workgroup increments once past the last unit, so the launch's
+      // last increment returns nt + gridDim.x - 1: reset for the next launch
+      if (t == nt + (int)gridDim.x - 1) *a.tail_ctr = 0;
+      next_unit = t;
+    }
+    __syncthreads();
+    const int t = __builtin_amdgcn_readfirstlane(next_unit);
+    if (t >= nt) break;
+    wk = entry_unit(a, hkv, a.n_static + t / slots, t % slots);
   }
 }
 
@@ -1219,7 +1249,8 @@ hipError_t attn_dispatch(const AttnArgs& a, int dtype, int batch, hipStream_t s)
   if (dtype == 0) {
     const int hkv = a.hq / a.group;
     const int hpw = (a.group % 2 == 0) ? 2 : 1;
-    const int nwg = (a.n_order > 0 ? a.n_order : batch * a.max_qb) * hkv * (a.group / hpw);
+    const bool dyn = a.n_static > 0 && a.n_static < a.n_order && a.tail_ctr && uses_attn_pp(a, D);
+    const int nwg = (dyn ? a.n_static : a.n_order > 0 ? a.n_order : batch * a.max_qb) * hkv * (a.group / hpw);
     const size_t shm = (size_t)(a.max_kb + 1) * sizeof(int32_t);
     if (uses_attn_pp(a, D)) hipLaunchKernelGGL((attn_pp<D, XATTN_PF>), dim3(nwg), dim3(512), shm, s, a, hkv);
     else if (hpw == 2) hipLaunchKernelGGL((attn_mfma<D, 2>), dim3(nwg), dim3(512), shm, s, a, hkv);
@@ -1236,6 +1267,8 @@ hipError_t attn_dispatch(const AttnArgs& a, int dtype, int batch, hipStream_t s)
 bool attention_reads_vt(const AttnArgs& a, int dtype, int head_dim) {
   return dtype == 0 && !uses_attn_pp(a, head_dim);
 }
+
+bool attention_uses_pp(const AttnArgs& a, int head_dim) { return uses_attn_pp(a, head_dim); }
 
 hipError_t launch_attention(const AttnArgs& a, int dtype, int head_dim, int batch,
                             hipStream_t s) {

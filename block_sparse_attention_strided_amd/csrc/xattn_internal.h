@@ -87,6 +87,7 @@ struct PlanArgs {
   int jb0;
   int jb1;
   int32_t* lists;
+  int* tail_ctr;  // attention's tail-part counter, cleared by the plan
 };
 
 // Attention of one launch.  Keys come from blocks j in [jb0, jb1) whose mask
@@ -108,6 +109,12 @@ struct AttnArgs {
   // For an entry with ns == 2: part 0 takes the first (count * cut) / 256
   // entries of the row's block list and part 1 the rest (cut 0: halves).
   uint8_t order_cut[kMaxOrder];
+  // 0 < n_static < n_order: one workgroup per (entry, kv slot) of the first
+  // n_static entries; after its own unit every workgroup draws units of the
+  // remaining entries (entry-major, longest first) from *tail_ctr, which is
+  // zero at launch and which the launch's last increment sets back to zero.
+  int n_static;
+  int* tail_ctr;
   // Rows split into ns > 1 parts write part s as a normalised fp32 output
   // and its natural-log LSE to split_o[s] / split_l[s] (layouts of out_f32 /
   // lse); a split merge then writes the final output.
@@ -172,6 +179,9 @@ hipError_t launch_attention(const AttnArgs& a, int dtype, int head_dim, int batc
                             hipStream_t s);
 // Whether the attention launch for `a` reads the V^T pages (a.vt).
 bool attention_reads_vt(const AttnArgs& a, int dtype, int head_dim);
+// Whether the bf16 launch runs the ping-pong kernel (the one that draws tail
+// units dynamically).
+bool attention_uses_pp(const AttnArgs& a, int head_dim);
 hipError_t launch_merge(const MergeArgs& a, hipStream_t s);
 hipError_t launch_split_merge(const SplitMergeArgs& a, hipStream_t s);
 // Copies block j of src (host memory mapped into the device address space)
