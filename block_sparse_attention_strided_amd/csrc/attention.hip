@@ -265,7 +265,7 @@ __global__ __launch_bounds__(64) void plan_kernel(PlanArgs a) {
   const int lk = a.cu_k[b + 1] - a.cu_k[b];
   const int qb = lq / kBlock, kh = (lk - lq) / kBlock;
   int32_t* out = a.lists + (((long long)b * a.hkv + g) * a.max_qb + i) * (a.max_kb + 1);
-  if (a.tail_ctr && i == 0 && g == 0 && b == 0 && lane == 0) *a.tail_ctr = 0;
+  if (a.tail_ctr && i == 0 && g == 0 && b == 0 && lane == 0) atomicExch(a.tail_ctr, 0);
   if (i >= qb) {
     if (lane == 0) out[0] = 0;
     return;
@@ -1043,7 +1043,7 @@ __global__ __launch_bounds__(512) void attn_pp(AttnArgs a, int hkv) {
       const int t = atomicAdd(a.tail_ctr, 1);
       // every workgroup increments once past the last unit, so the launch's
       // last increment returns nt + gridDim.x - 1: reset for the next launch
-      if (t == nt + (int)gridDim.x - 1) *a.tail_ctr = 0;
+      if (t == nt + (int)gridDim.x - 1) atomicExch(a.tail_ctr, 0);
       next_unit = t;
     }
     __syncthreads();

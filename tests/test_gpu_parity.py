@@ -229,6 +229,16 @@ def test_attention_head_tail_split(mask_kind):
     out, lse = r.attend(mask_t)
     ref_o, ref_l = r.oracle_attention(mask_t, rows=rows)
     assert_attention_close(out, lse, ref_o, ref_l, w.dtype, rows_idx=idx, label="head/tail " + mask_kind)
+    # the tails are drawn from a counter the plan clears and each launch
+    # resets at its end: three launches on one plan give the same bits
+    md = mask_t.to("cuda", torch.uint8).contiguous()
+    X.xattn_attn_plan(r.shape, r.params, r.v, md, r.ws)
+    for _ in range(3):
+        o2 = torch.full_like(r.q, float("nan"))
+        l2 = torch.full((r.hq, r.shape.total_q), float("nan"), device="cuda")
+        X.xattn_attn_run(r.shape, r.params, r.q, r.k, r.v, md, o2, l2, r.ws)
+        torch.cuda.synchronize()
+        assert torch.equal(o2.cpu(), out.cpu()) and torch.equal(l2.cpu(), lse.cpu()), "repeated launch differs"
 
 
 def test_merge_attention():
