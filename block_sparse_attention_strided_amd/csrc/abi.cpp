@@ -337,8 +337,8 @@ int device_cu_count() {
 // parts whose partial outputs a split merge combines (the merge rule of
 // partial attention results).  Otherwise, when all workgroups fit on the
 // CUs at once (one round) and the longest row exceeds the share by at least
-// 4 blocks and 2%, rows longer than the share keep a head of `share` blocks
-// and move the rest into a tail part; longest first, the tails start on the
+// 4 blocks and 2%, rows longer than 98% of the share keep a head of that
+// many blocks and move the rest into a tail part; longest first, the tails start on the
 // CUs whose short rows finish first, which evens out the CUs' totals.  When
 // the ping-pong kernel runs the launch, the tails are not given workgroups
 // of their own: every workgroup draws them from a counter after its head or
@@ -378,7 +378,9 @@ void set_order(const XattnShape* sh, const Plan& p, AttnArgs& aa, void* ws, Spli
     if (lmax >= 4 && lmax > 1.25 * share) {
       bmax = std::max({(int)std::ceil(share), (lmax + 2) / 3, 2});
     } else if ((long long)rows.size() * per_row <= cus && lmax >= share + 4 && lmax >= 1.02 * share) {
-      head = (int)std::ceil(share);
+      // heads a little below the share leave the faster XCDs tail work to
+      // take over from the slowest one (whose heads set the launch's end)
+      head = (int)std::ceil(0.98 * share);
     }
   }
   struct Item {
