@@ -335,11 +335,11 @@ int device_cu_count() {
 // whose long rows would set the launch time -- rows longer than
 // bmax = max(share, longest / 3) are cut into ns = ceil(length / bmax) <= 3
 // parts whose partial outputs a split merge combines (the merge rule of
-// partial attention results).  Otherwise, when all workgroups fit on the
-// CUs at once (one round) and the longest row exceeds the share by at least
-// 4 blocks and 2%, rows longer than 98% of the share keep a head of that
-// many blocks and move the rest into a tail part; longest first, the tails start on the
-// CUs whose short rows finish first, which evens out the CUs' totals.  When
+// partial attention results).  Otherwise, when the longest row exceeds the
+// share by at least 4 blocks and 2%, rows longer than 98% of the share keep
+// a head of that many blocks and move the rest into a tail part; the tails
+// come after every head and unsplit row, longest first, so they start on
+// the CUs that finish first, which evens out the CUs' totals.  When
 // the ping-pong kernel runs the launch, the tails are not given workgroups
 // of their own: every workgroup draws them from a counter after its head or
 // unsplit row, so CUs that run faster (the XCDs differ by a few percent)
@@ -377,7 +377,7 @@ void set_order(const XattnShape* sh, const Plan& p, AttnArgs& aa, void* ws, Spli
     const double share = (double)total * per_row / cus;
     if (lmax >= 4 && lmax > 1.25 * share) {
       bmax = std::max({(int)std::ceil(share), (lmax + 2) / 3, 2});
-    } else if ((long long)rows.size() * per_row <= cus && lmax >= share + 4 && lmax >= 1.02 * share) {
+    } else if (lmax >= share + 4 && lmax >= 1.02 * share) {
       // heads a little below the share leave the faster XCDs tail work to
       // take over from the slowest one (whose heads set the launch's end)
       head = (int)std::ceil(0.98 * share);
@@ -419,11 +419,11 @@ void set_order(const XattnShape* sh, const Plan& p, AttnArgs& aa, void* ws, Spli
     nsplit = 0;
   }
   if (p.batch == 1 && nsplit == 0) return;
-  // dynamic tails: heads and unsplit rows first, then the tails, each run
-  // longest first
+  // heads and unsplit rows first, then the tails, each run longest first;
+  // the ping-pong kernel draws the tails dynamically
   const bool dyn = head > 0 && attention_uses_pp(aa, p.d);
-  std::stable_sort(items.begin(), items.end(), [dyn](const Item& x, const Item& y) {
-    if (dyn) {
+  std::stable_sort(items.begin(), items.end(), [head](const Item& x, const Item& y) {
+    if (head > 0) {
       const bool tx = ((x.entry >> 28) & 3u) != 0, ty = ((y.entry >> 28) & 3u) != 0;
       if (tx != ty) return !tx;
     }
