@@ -375,7 +375,10 @@ void set_order(const XattnShape* sh, const Plan& p, AttnArgs& aa, void* ws, Spli
   int head = 0;     // > 0: head + tail parts
   if (aa.out && !aa.out_f32 && cus > 0) {
     const double share = (double)total * per_row / cus;
-    if (lmax >= 4 && lmax > 1.25 * share) {
+    // rows more than twice the share: up to three equal parts; else, when
+    // the longest row is over the share, head + tail (the tail at most
+    // about one head long)
+    if (lmax >= 4 && lmax > 2.0 * share) {
       bmax = std::max({(int)std::ceil(share), (lmax + 2) / 3, 2});
     } else if (lmax >= share + 4 && lmax >= 1.02 * share) {
       // heads a little below the share leave the faster XCDs tail work to
