@@ -42,6 +42,12 @@
  *    never uses the null stream unless `stream` is NULL.
  *  - The library never allocates device memory inside these calls except in
  *    xattn_ring_create; scratch space is the caller's workspace `ws`.
+ *  - Calls that use one workspace must not overlap in time: enqueue them on
+ *    one stream or order them with events.  A workspace carries state from
+ *    call to call (the attention plan, and a work counter that the plan
+ *    clears and every attention launch returns to zero as it ends), so two
+ *    concurrent launches on one workspace race.  Different workspaces are
+ *    independent.
  *  - Outputs are owned by the caller; the library keeps no pointer after a
  *    call returns (the ring keeps only its own slots).
  */
