@@ -225,9 +225,13 @@ hipError_t run_block_sums(const XattnShape* sh, const Plan& p, const float* part
   return launch_block_sums(ba, p.batch, st);
 }
 
+// plan_ws (bf16 only, or nullptr): the workspace whose attention block lists
+// the selection should also write, for an attention over the whole key range
+// of `kview`; *lists_done tells whether it did.
 hipError_t run_select(const XattnShape* sh, const XattnParams* pr, const Plan& p, const float* bs,
-                      uint8_t* maskq, uint8_t* maskkv, uint8_t* hist, int32_t* counts, hipStream_t st) {
-  SelectArgs sa;
+                      uint8_t* maskq, uint8_t* maskkv, uint8_t* hist, int32_t* counts, hipStream_t st,
+                      void* plan_ws = nullptr, const KvView* kview = nullptr, bool* lists_done = nullptr) {
+  SelectArgs sa{};
   sa.block_sums = bs;
   sa.cu_q = sh->cu_q;
   sa.cu_k = sh->cu_k;
@@ -243,7 +247,13 @@ hipError_t run_select(const XattnShape* sh, const XattnParams* pr, const Plan& p
   sa.mask_kv = maskkv;
   sa.hist_sel = hist;
   sa.counts = counts;
-  return launch_select(sa, p.batch, st);
+  if (plan_ws && kview && p.dtype == XATTN_DTYPE_BF16) {
+    sa.lists = ws_at<int32_t>(plan_ws, p.off_lists);
+    sa.block_table = kview->block_table;
+    sa.max_blocks = kview->max_blocks;
+    sa.tail_ctr = ws_at<int>(plan_ws, p.off_ctr);
+  }
+  return launch_select(sa, p.batch, st, lists_done);
 }
 
 AttnArgs attn_args(const XattnShape* sh, const Plan& p, const void* q, KvView kv, KvView vv,
@@ -280,7 +290,7 @@ AttnArgs attn_args(const XattnShape* sh, const Plan& p, const void* q, KvView kv
 // bf16 preparation of an attention launch over blocks [jb0, jb1) of
 // aa.mask: V^T pages of `v` (num_pages pages) and the per-row block lists.
 hipError_t plan_attention(const XattnShape* sh, const Plan& p, const AttnArgs& aa, const void* v, int num_pages,
-                          void* ws, bool transpose_v, hipStream_t st) {
+                          void* ws, bool transpose_v, hipStream_t st, bool lists_ready = false) {
   if (p.dtype == XATTN_DTYPE_BF16) {
     char* vt = ws_at<char>(ws, p.off_vt);
     AttnArgs probe = aa;
@@ -295,6 +305,7 @@ hipError_t plan_attention(const XattnShape* sh, const Plan& p, const AttnArgs& a
       hipError_t e = launch_vt_transpose(va, st);
       if (e != hipSuccess) return e;
     }
+    if (lists_ready) return hipSuccess;  // written by the selection
     PlanArgs pa;
     pa.mask = aa.mask;
     pa.cu_q = sh->cu_q;
@@ -475,10 +486,11 @@ hipError_t launch_planned(const XattnShape* sh, const Plan& p, AttnArgs aa, void
 }
 
 // Attention over blocks [jb0, jb1) of `mask`: prepare (bf16), then attend.
+// lists_ready: the block lists are in the workspace already.
 hipError_t run_attention(const XattnShape* sh, const Plan& p, AttnArgs aa, const void* v, int num_pages,
-                         void* ws, bool transpose_v, hipStream_t st) {
+                         void* ws, bool transpose_v, hipStream_t st, bool lists_ready = false) {
   aa.num_pages = num_pages;
-  hipError_t e = plan_attention(sh, p, aa, v, num_pages, ws, transpose_v, st);
+  hipError_t e = plan_attention(sh, p, aa, v, num_pages, ws, transpose_v, st, lists_ready);
   if (e != hipSuccess) return e;
   return launch_planned(sh, p, aa, ws, st);
 }
@@ -1073,6 +1085,7 @@ int xattn_prefill_chunk(XattnRing* ring, const XattnShape* shape, const XattnPar
   int32_t* cnt = counts ? counts : ws_at<int32_t>(ws, p.off_counts);
   const KvView kview = make_view(shape, p, k), vview = make_view(shape, p, v);
   hipError_t e = hipSuccess;
+  bool lists_ready = false;  // block lists written by the selection kernels
   if (params->reuse_selection) {
     if (!aux || !aux->mask_kv) return fail(XATTN_ERR_INVALID, "reuse_selection needs aux->mask_kv");
   } else {
@@ -1080,14 +1093,15 @@ int xattn_prefill_chunk(XattnRing* ring, const XattnShape* shape, const XattnPar
     if (e != hipSuccess) return hip_fail(e, "estimate launch");
     e = run_block_sums(shape, p, part, bs, st);
     if (e != hipSuccess) return hip_fail(e, "block-sum launch");
-    e = run_select(shape, params, p, bs, ws_at<uint8_t>(ws, p.off_maskq), maskkv, hist, cnt, st);
+    e = run_select(shape, params, p, bs, ws_at<uint8_t>(ws, p.off_maskq), maskkv, hist, cnt, st, ws, &kview,
+                   &lists_ready);
     if (e != hipSuccess) return hip_fail(e, "select launch");
   }
   AttnArgs aa = attn_args(shape, p, q, kview, vview, maskkv, 0, p.max_kb);
   if (p.dtype == XATTN_DTYPE_BF16) aa.out = out;
   else aa.out_f32 = (float*)out;
   aa.lse = lse;
-  e = run_attention(shape, p, aa, v, p.num_pages, ws, true, st);
+  e = run_attention(shape, p, aa, v, p.num_pages, ws, true, st, lists_ready);
   if (e != hipSuccess) return hip_fail(e, "attention launch");
   return XATTN_OK;
 }

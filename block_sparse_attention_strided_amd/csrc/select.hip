@@ -114,6 +114,42 @@ __device__ __forceinline__ void wave_lds_sync() {
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
+// Attention block list of row (b, g, i) in the plan kernel's layout: the
+// count, then (page << 1) | (j is the diagonal block i + kh) for every j <
+// jend whose mask byte flag(j) is set and whose page is present, in
+// increasing j (pages from the block table, else contiguous from the
+// sequence's first key).  All threads of the workgroup call it; wcnt holds
+// one int per wave.  Clears the attention's tail-part counter once per
+// launch (workgroup (0, 0, 0)).
+template <typename F>
+__device__ void emit_row_list(const SelectArgs& a, int b, int g, int i, int kh, int jend, F flag, int* wcnt) {
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int nthr = blockDim.x, nw = nthr >> 6;
+  int32_t* out = a.lists + (((long long)b * a.hkv + g) * a.max_qb + i) * (a.max_kb + 1);
+  if (a.tail_ctr && i == 0 && g == 0 && b == 0 && tid == 0) atomicExch(a.tail_ctr, 0);
+  const int page0 = a.cu_k[b] / kBlock;
+  int n = 0;
+  for (int j0 = 0; j0 < jend; j0 += nthr) {
+    const int j = j0 + tid;
+    int page = -1;
+    if (j < jend && flag(j)) page = a.block_table ? a.block_table[(long long)b * a.max_blocks + j] : page0 + j;
+    const bool take = page >= 0;
+    const unsigned long long bal = __ballot(take);
+    if (lane == 0) wcnt[w] = __popcll(bal);
+    __syncthreads();
+    int before = n, total = n;
+    for (int x = 0; x < nw; ++x) {
+      const int c = wcnt[x];
+      before += (x < w) ? c : 0;
+      total += c;
+    }
+    if (take) out[1 + before + __popcll(bal & ((1ull << lane) - 1ull))] = (page << 1) | (j == i + kh ? 1 : 0);
+    n = total;
+    __syncthreads();  // wcnt reused
+  }
+  if (tid == 0) out[0] = n;
+}
+
 // Threshold selection and GQA aggregation fused.  One workgroup per (q block
 // i, kv head g, sequence b) with one wave per q head of the group; wave w
 // works on row (b, h = g*G + w, i) in its own LDS region (the aggregated row
@@ -192,8 +228,11 @@ __global__ __launch_bounds__(64 * kSelMaxWaves) void select_group_kernel(SelectA
   // layout), which chunk_vote_mask_kernel turns into the effective mask_kv
   uint8_t* const dst = a.select_mode == 1 ? a.mask_q : a.mask_kv;
   uint8_t* out = dst + (((long long)b * a.hkv + g) * a.max_qb + i) * a.max_kb;
+  __shared__ int wcnt[kSelMaxWaves];
+  const bool emit = a.lists && a.select_mode == 0;
   if (i >= qb) {
     for (int j = tid; j < a.max_kb; j += nthr) out[j] = 0;
+    if (emit) emit_row_list(a, b, g, i, kh, 0, [](int) { return false; }, wcnt);
     return;
   }
   const int n = i + kh + 1;
@@ -264,6 +303,7 @@ __global__ __launch_bounds__(64 * kSelMaxWaves) void select_group_kernel(SelectA
   }
   __syncthreads();
   const uint8_t* flags = smem + (size_t)G * n2 * 10;
+  uint8_t* rowf = smem + (size_t)G * n2 * 10 + (size_t)G * a.max_kb;  // the row, for the block list
   for (int j = tid; j < a.max_kb; j += nthr) {
     uint8_t val = 0;
     if (j < n) {
@@ -274,6 +314,11 @@ __global__ __launch_bounds__(64 * kSelMaxWaves) void select_group_kernel(SelectA
       val = keep ? 1 : 0;
     }
     out[j] = val;
+    if (emit) rowf[j] = val;
+  }
+  if (emit) {
+    __syncthreads();
+    emit_row_list(a, b, g, i, kh, n, [&](int j) { return rowf[j] != 0; }, wcnt);
   }
 }
 
@@ -412,8 +457,10 @@ __global__ __launch_bounds__(256) void chunk_vote_mask_kernel(SelectArgs a) {
   const int qb = lq / kBlock, kb = lk / kBlock, kh = (lk - lq) / kBlock;
   const bool lead = (i == 0 && g == 0);
   uint8_t* out = a.mask_kv + (((long long)b * a.hkv + g) * a.max_qb + i) * a.max_kb;
+  __shared__ int wcnt[4];
   if (i >= qb && !lead) {
     for (int j = tid; j < a.max_kb; j += 256) out[j] = 0;
+    if (a.lists) emit_row_list(a, b, g, i, kh, 0, [](int) { return false; }, wcnt);
     return;
   }
   const int nrows = a.hkv * qb;
@@ -464,6 +511,8 @@ __global__ __launch_bounds__(256) void chunk_vote_mask_kernel(SelectArgs a) {
   }
   for (int j = tid; j < a.max_kb; j += 256)
     out[j] = (i < qb && j < kb) ? ((j < kh) ? hs[j] : (j <= i + kh ? 1 : 0)) : 0;
+  if (a.lists)
+    emit_row_list(a, b, g, i, kh, i < qb ? i + kh + 1 : 0, [&](int j) { return j >= kh || hs[j] != 0; }, wcnt);
   if (lead && a.counts) {
     for (int off = 32; off > 0; off >>= 1) mine += __shfl_xor(mine, off, 64);
     if ((tid & 63) == 0) nsel[tid >> 6] = mine;
@@ -477,13 +526,16 @@ __global__ __launch_bounds__(256) void chunk_vote_mask_kernel(SelectArgs a) {
 
 }  // namespace
 
-hipError_t launch_select(const SelectArgs& a, int batch, hipStream_t s) {
+hipError_t launch_select(const SelectArgs& a, int batch, hipStream_t s, bool* lists_done) {
+  if (lists_done) *lists_done = false;
   if (a.max_kb <= 0 || batch <= 0) return hipSuccess;
   int n2 = 1;
   while (n2 < a.max_kb) n2 <<= 1;
   const int group = a.hq / a.hkv;
-  const size_t fused_lds = (size_t)group * n2 * 10 + (size_t)group * a.max_kb;
+  const size_t fused_lds = (size_t)group * n2 * 10 + (size_t)(group + (a.lists ? 1 : 0)) * a.max_kb;
   const bool fused = group <= kSelMaxWaves && fused_lds <= kSelMaxLds;
+  // the fused kernels write the attention block lists when asked to
+  if (lists_done) *lists_done = a.lists && fused && a.max_qb > 0;
   hipError_t e = hipSuccess;
   if (a.max_qb > 0) {
     if (fused) {

@@ -59,6 +59,14 @@ struct SelectArgs {
   uint8_t* mask_kv;  // [batch, hkv, max_qb, max_kb]
   uint8_t* hist_sel; // [batch, max_kb]
   int32_t* counts;   // [batch, 2]
+  // lists != nullptr: the kernel that writes a final mask_kv row also writes
+  // that row's attention block list over the whole key range (PlanArgs
+  // layout, pages from block_table or contiguous), and the attention's
+  // tail-part counter is cleared, so that no plan launch is needed
+  int32_t* lists;
+  const int32_t* block_table;  // [batch, max_blocks] or nullptr
+  int max_blocks;
+  int* tail_ctr;
 };
 
 // V re-laid out for the attention kernel: page p (128 keys) of kv head g is a
@@ -172,7 +180,8 @@ struct MergeArgs {
 hipError_t launch_estimate(const EstArgs& a, int dtype, int head_dim, int stride, int batch,
                            hipStream_t s);
 hipError_t launch_block_sums(const BlockSumArgs& a, int batch, hipStream_t s);
-hipError_t launch_select(const SelectArgs& a, int batch, hipStream_t s);
+// *lists_done (if given) tells whether the kernels wrote a.lists.
+hipError_t launch_select(const SelectArgs& a, int batch, hipStream_t s, bool* lists_done = nullptr);
 hipError_t launch_vt_transpose(const VtArgs& a, hipStream_t s);
 hipError_t launch_plan(const PlanArgs& a, int batch, hipStream_t s);
 hipError_t launch_attention(const AttnArgs& a, int dtype, int head_dim, int batch,
