@@ -192,11 +192,13 @@ KvView make_view(const XattnShape* sh, const Plan& p, const void* base) {
 // k_pages: 128-key pages addressable from kview.base.
 hipError_t run_estimate(const XattnShape* sh, const Plan& p, const void* q, KvView kview, int jb0,
                         int jb_count, int k_pages, float* part, hipStream_t st) {
-  EstArgs ea;
+  EstArgs ea{};
   ea.q = (const char*)q;
   ea.k = kview;
   ea.cu_q = sh->cu_q;
   ea.cu_k = sh->cu_k;
+  ea.cu_q_host = sh->cu_q_host;
+  ea.cu_k_host = sh->cu_k_host;
   ea.hq = p.hq;
   ea.group = p.hq / p.hkv;
   ea.jb0 = jb0;

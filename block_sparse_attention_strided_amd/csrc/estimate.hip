@@ -207,7 +207,9 @@ constexpr int kEstBig = 256;
 // rows (part w>>1); XT x YT accumulators.  A stage covers BK reduction
 // elements (LDS rows of 2*BK bytes); NBUF LDS stage buffers: NBUF - 1 stages
 // of copies are in flight while one is computed.
-template <int D, int S, int TT, int NW, int NBUF, int BK>
+// TAB: workgroups numbered over the tiles with work (a.tile_base), else over
+// the whole (sequence, head, row tile, column tile) grid.
+template <int D, int S, int TT, int NW, int NBUF, int BK, bool TAB>
 __global__ __launch_bounds__(64 * NW) void est_gemm_bf16(EstArgs a) {
   constexpr int RB = kBlock / S;
   constexpr int TILEB = TT * BK * 2; // bytes of one operand tile
@@ -237,8 +239,43 @@ __global__ __launch_bounds__(64 * NW) void est_gemm_bf16(EstArgs a) {
   const int nwg = gridDim.x, id = blockIdx.x;
   const int full = (nwg / 8) * 8;
   const int logical = id < full ? (id % 8) * (nwg / 8) + id / 8 : id;
-  const int bx = logical % ntx, by = (logical / ntx) % nty, bh = logical / (ntx * nty);
-  const int b = bh / a.hq, h = bh % a.hq, g = h / a.group;
+  int bx, by, b, h;
+  if (TAB) {
+    // the logical-th tile with work: its sequence by binary search of
+    // tile_base, then head, row tile and column tile (est_active_tiles)
+    int lo = 0, hi = a.n_tab - 1;  // tile_base[lo] <= logical < tile_base[hi]
+    while (hi - lo > 1) {
+      const int mid = (lo + hi) >> 1;
+      if (a.tile_base[mid] <= logical) lo = mid;
+      else hi = mid;
+    }
+    b = lo;
+    const int per_head = (a.tile_base[b + 1] - a.tile_base[b]) / a.hq;
+    int rem = logical - a.tile_base[b];
+    h = rem / per_head;
+    rem -= h * per_head;
+    const int lq_ = a.cu_q[b + 1] - a.cu_q[b], lk_ = a.cu_k[b + 1] - a.cu_k[b];
+    const int R_ = lq_ / S, C_ = lk_ / S, os_ = (lk_ - lq_) / S;
+    const int cbase = a.jb0 * RB, cend = min((a.jb0 + a.jb_count) * RB, C_);
+    by = 0;
+    bx = 0;
+    for (int r0 = 0; r0 < R_; r0 += TT, ++by) {
+      const int lim = min(cend, min(r0 + TT, R_) + os_);
+      const int nbx = lim > cbase ? (lim - cbase + TT - 1) / TT : 0;
+      if (rem < nbx) {
+        bx = rem;
+        break;
+      }
+      rem -= nbx;
+    }
+  } else {
+    bx = logical % ntx;
+    by = (logical / ntx) % nty;
+    const int bh = logical / (ntx * nty);
+    b = bh / a.hq;
+    h = bh % a.hq;
+  }
+  const int g = h / a.group, bh = b * a.hq + h;
   const int q0 = a.cu_q[b];
   const int lq = a.cu_q[b + 1] - q0;
   const int lk = a.cu_k[b + 1] - a.cu_k[b];
@@ -603,6 +640,40 @@ __global__ __launch_bounds__(1024) void block_sums_reg_kernel(BlockSumArgs a) {
   }
 }
 
+// Tiles of a sequence's head that have work for tile size tt over the
+// launch's key blocks [jb0, jb0 + jb_count): row tile r0 keeps the column
+// tiles whose first column c0 lies before both the key range's end and the
+// causal bound of its last row (c0 <= r_last + (Lk - Lq)/s), the same rules
+// by which est_gemm_bf16 skips a tile.
+int est_active_tiles(int lq, int lk, int S, int tt, int jb0, int jb_count) {
+  const int RB = kBlock / S;
+  const int R = lq / S, C = lk / S, o_s = (lk - lq) / S;
+  const int cbase = jb0 * RB, cend = std::min((jb0 + jb_count) * RB, C);
+  int n = 0;
+  for (int r0 = 0; r0 < R; r0 += tt) {
+    const int lim = std::min(cend, std::min(r0 + tt, R) + o_s);
+    if (lim > cbase) n += (lim - cbase + tt - 1) / tt;
+  }
+  return n;
+}
+
+// Fills a.tile_base / a.n_tab for tile size tt; false (and n_tab 0) when the
+// batch is beyond the table or a count overflows.
+bool est_tile_table(EstArgs& a, int S, int tt, int batch) {
+  a.n_tab = 0;
+  if (!a.cu_q_host || !a.cu_k_host || batch > kEstMaxSeq) return false;
+  long long acc = 0;
+  for (int b = 0; b < batch; ++b) {
+    a.tile_base[b] = (int)acc;
+    const int lq = a.cu_q_host[b + 1] - a.cu_q_host[b], lk = a.cu_k_host[b + 1] - a.cu_k_host[b];
+    acc += (long long)a.hq * est_active_tiles(lq, lk, S, tt, a.jb0, a.jb_count);
+    if (acc >= (1ll << 31)) return false;
+  }
+  a.tile_base[batch] = (int)acc;
+  a.n_tab = batch + 1;
+  return true;
+}
+
 template <int D, int S>
 hipError_t est_dispatch(const EstArgs& a, int dtype, int batch, hipStream_t st) {
   constexpr int RB = kBlock / S;
@@ -610,19 +681,35 @@ hipError_t est_dispatch(const EstArgs& a, int dtype, int batch, hipStream_t st) 
     // 256 x 256 tiles (8 waves) when they still fill the chip, else 128 x 128
     // tiles (4 waves); both need Q and K spans within 31-bit buffer offsets.
     if (a.q_bytes < (1ll << 31) && a.k_bytes < (1ll << 31)) {
+      // several sequences: one workgroup per tile with work when the batch
+      // fits the table, so that every XCD gets the same number of tiles
+      // whatever the sequences' lengths (one per grid tile otherwise: for a
+      // single sequence that measured 1-2 us faster)
       dim3 big((a.jb_count * RB + kEstBig - 1) / kEstBig, (a.max_r + kEstBig - 1) / kEstBig, batch * a.hq);
-      const long long nbig = (long long)big.x * big.y * big.z;
       EstArgs a2 = a;
+      long long nbig = (long long)big.x * big.y * big.z;
+      if (batch > 1 && est_tile_table(a2, S, kEstBig, batch)) nbig = a2.tile_base[batch];
       if (nbig >= 256) {
         a2.tiles_c = (int)big.x;
         a2.tiles_r = (int)big.y;
-        hipLaunchKernelGGL((est_gemm_bf16<D, S, kEstBig, 8, XATTN_EST_BIG_NBUF, XATTN_EST_BIG_BK>), dim3((unsigned)nbig),
-                           dim3(512), 0, st, a2);
+        if (a2.n_tab > 0)
+          hipLaunchKernelGGL((est_gemm_bf16<D, S, kEstBig, 8, XATTN_EST_BIG_NBUF, XATTN_EST_BIG_BK, true>),
+                             dim3((unsigned)nbig), dim3(512), 0, st, a2);
+        else
+          hipLaunchKernelGGL((est_gemm_bf16<D, S, kEstBig, 8, XATTN_EST_BIG_NBUF, XATTN_EST_BIG_BK, false>),
+                             dim3((unsigned)nbig), dim3(512), 0, st, a2);
       } else {
         a2.tiles_c = (a.jb_count * RB + kEstTile - 1) / kEstTile;
         a2.tiles_r = (a.max_r + kEstTile - 1) / kEstTile;
-        const long long n = (long long)a2.tiles_c * a2.tiles_r * batch * a.hq;
-        hipLaunchKernelGGL((est_gemm_bf16<D, S, kEstTile, 4, XATTN_EST_NBUF, 64>), dim3((unsigned)n), dim3(256), 0, st, a2);
+        long long n = (long long)a2.tiles_c * a2.tiles_r * batch * a.hq;
+        if (batch > 1 && est_tile_table(a2, S, kEstTile, batch)) n = a2.tile_base[batch];
+        else a2.n_tab = 0;
+        if (n > 0 && a2.n_tab > 0)
+          hipLaunchKernelGGL((est_gemm_bf16<D, S, kEstTile, 4, XATTN_EST_NBUF, 64, true>), dim3((unsigned)n), dim3(256), 0,
+                             st, a2);
+        else if (n > 0)
+          hipLaunchKernelGGL((est_gemm_bf16<D, S, kEstTile, 4, XATTN_EST_NBUF, 64, false>), dim3((unsigned)n), dim3(256),
+                             0, st, a2);
       }
       return hipGetLastError();
     }

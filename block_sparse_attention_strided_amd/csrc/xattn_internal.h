@@ -12,6 +12,8 @@ namespace xattn {
 // in [jb0, jb0 + jb_count), reshaped query row r) the base-2 log-sum-exp of
 // est_scale*log2(e)*S over the allowed columns of block j.  Stored at
 // part[((b*hq + h)*max_kb + j)*max_r + r].
+constexpr int kEstMaxSeq = 64;  // sequences of the tile GEMM's active-tile table
+
 struct EstArgs {
   const char* q;
   KvView k;
@@ -29,6 +31,15 @@ struct EstArgs {
   long long k_bytes;  // bytes addressable from k.base
   int tiles_c;        // big-tile GEMM: column tiles per head (set by the launcher)
   int tiles_r;        // big-tile GEMM: row tiles per head
+  // Host copies of cu_q / cu_k (launcher only).  With them the launcher
+  // gives the tile GEMM one workgroup per tile that has work, numbered
+  // (sequence, head, row tile, column tile) with tile_base[b] the number of
+  // such tiles before sequence b (n_tab = batch + 1 entries; 0: one
+  // workgroup per grid tile, the empty ones exit).
+  const int32_t* cu_q_host;
+  const int32_t* cu_k_host;
+  int n_tab;
+  int tile_base[kEstMaxSeq + 1];
 };
 
 struct BlockSumArgs {

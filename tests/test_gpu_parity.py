@@ -25,6 +25,12 @@ EST_CASES = {
                             paged=True),
     "bf16_empty_seqs": dict(hq=2, hkv=1, d=128, lq=[256, 0, 128, 0], lk=[512, 256, 128, 0], stride=8),
     "f32_s8_d64": dict(hq=2, hkv=1, d=64, lq=[512], lk=[1024], stride=8, dtype=torch.float32),
+    # the launcher's table of tiles with work holds up to 64 sequences; 65
+    # and more use one workgroup per grid tile
+    "bf16_64_seqs": dict(hq=2, hkv=1, d=64, lq=[128 * (1 + i % 2) for i in range(64)],
+                         lk=[128 * (2 + i % 3) for i in range(64)], stride=8),
+    "bf16_65_seqs": dict(hq=2, hkv=1, d=64, lq=[128 * (1 + i % 2) for i in range(65)],
+                         lk=[128 * (2 + i % 3) for i in range(65)], stride=8),
     # large enough (>= 256 tiles of 256 x 256) for the big-tile GEMM path:
     # ragged rows/columns, causal tiles, two sequences
     "bf16_big_s8_varlen": dict(hq=16, hkv=4, d=128, lq=[2432, 640], lk=[8192, 1024], stride=8),
