@@ -263,28 +263,27 @@ __global__ __launch_bounds__(64 * kSelMaxWaves) void select_group_kernel(SelectA
     wave_lds_sync();
     double total = 0.0;
     if (lane == 0) {
-      // blocks of 8 values, the next block's loads issued before the
-      // current block's additions (the additions are the serial chain)
+      // blocks of 16 values, the next block's loads issued before the
+      // current block's additions (the additions are the serial chain);
+      // each value's slot takes the sum before it as soon as it is read
+      constexpr int SB = 16;
       double acc = 0.0;
-      const int nfull = n & ~7;
-      double cur[8] = {}, nxt[8] = {};
+      const int nfull = n & ~(SB - 1);
+      double cur[SB] = {}, nxt[SB] = {};
       if (nfull > 0)
 #pragma unroll
-        for (int k = 0; k < 8; ++k) cur[k] = vals[k];
-      for (int x0 = 0; x0 < nfull; x0 += 8) {
-        if (x0 + 8 < nfull)
+        for (int k = 0; k < SB; ++k) cur[k] = vals[k];
+      for (int x0 = 0; x0 < nfull; x0 += SB) {
+        if (x0 + SB < nfull)
 #pragma unroll
-          for (int k = 0; k < 8; ++k) nxt[k] = vals[x0 + 8 + k];
-        double bef[8];
+          for (int k = 0; k < SB; ++k) nxt[k] = vals[x0 + SB + k];
 #pragma unroll
-        for (int k = 0; k < 8; ++k) {
-          bef[k] = acc;
+        for (int k = 0; k < SB; ++k) {
+          vals[x0 + k] = acc;
           acc += cur[k];
         }
 #pragma unroll
-        for (int k = 0; k < 8; ++k) vals[x0 + k] = bef[k];
-#pragma unroll
-        for (int k = 0; k < 8; ++k) cur[k] = nxt[k];
+        for (int k = 0; k < SB; ++k) cur[k] = nxt[k];
       }
       for (int x = nfull; x < n; ++x) {
         const double v0 = vals[x];
