@@ -167,11 +167,74 @@ __device__ void emit_row_list(const SelectArgs& a, int b, int g, int i, int kh, 
 // and writes the mask_kv row.  In per-KV-head mode workgroup (0, 0, b) also
 // clears hist_sel[b].  Dynamic LDS per wave: n2 8-byte keys (then values)
 // and n2 16-bit indices; then G * max_kb flag bytes.
+__device__ __forceinline__ uint64_t shfl_xor_u64(uint64_t v, int m) {
+  const int lo = __shfl_xor((int)(uint32_t)v, m, 64);
+  const int hi = __shfl_xor((int)(uint32_t)(v >> 32), m, 64);
+  return ((uint64_t)(uint32_t)hi << 32) | (uint32_t)lo;
+}
+
+// The same bitonic network on KPL keys per lane held in registers (key x =
+// p * 64 + lane in k[p]): compare-exchange partners 64 or more apart sit in
+// the same lane, closer ones in lane ^ js of the same register, swapped with
+// lane shuffles.  64 * KPL >= n2 keys are sorted (the extra ones are zero
+// padding and end up last); keys[0 .. n2) receive the result.
+template <int KPL>
+__device__ __forceinline__ void sort_keys_in_registers(uint64_t* keys, const float* row, int n, int n2, int lane) {
+  constexpr int N = 64 * KPL;
+  uint64_t k[KPL];
+#pragma unroll
+  for (int p = 0; p < KPL; ++p) {
+    const int x = lane + 64 * p;
+    k[p] = (x < n) ? (((uint64_t)orderable(row[x]) << 32) | (uint64_t)(0xffffffffu - (uint32_t)x)) : 0ull;
+  }
+#pragma unroll
+  for (int size = 2; size <= N; size <<= 1) {
+#pragma unroll
+    for (int js = size >> 1; js > 0; js >>= 1) {
+      if (js >= 64) {
+        const int pj = js >> 6;
+#pragma unroll
+        for (int p = 0; p < KPL; ++p) {
+          if ((p & pj) == 0) {
+            const int q = p | pj;
+            const bool desc = (((p << 6) | lane) & size) == 0;
+            const uint64_t lo = k[p], hi = k[q];
+            const bool sw = (lo < hi) == desc;
+            k[p] = sw ? hi : lo;
+            k[q] = sw ? lo : hi;
+          }
+        }
+      } else {
+#pragma unroll
+        for (int p = 0; p < KPL; ++p) {
+          const uint64_t o = shfl_xor_u64(k[p], js);
+          const bool desc = (((p << 6) | lane) & size) == 0, lower = (lane & js) == 0;
+          // the lower position of a pair keeps the larger key in a
+          // descending run, the smaller in an ascending one
+          const bool keep_larger = lower == desc;
+          k[p] = ((k[p] < o) == keep_larger) ? o : k[p];
+        }
+      }
+    }
+  }
+#pragma unroll
+  for (int p = 0; p < KPL; ++p) {
+    const int x = lane + 64 * p;
+    if (x < n2) keys[x] = k[p];
+  }
+  wave_lds_sync();
+}
+
 // Wave-synchronous bitonic sort of one row's keys in LDS: key x < n is
 // (orderable(row[x]) << 32) | ~x, keys n..n2-1 are 0; descending order =
-// value desc, index asc, padding last.
+// value desc, index asc, padding last.  Rows of up to 512 keys are sorted in
+// registers (sort_keys_in_registers), longer ones in LDS.
 template <int PPL>
 __device__ __forceinline__ void sort_row_keys(uint64_t* keys, const float* row, int n, int n2, int lane) {
+  if constexpr (PPL <= 4) {
+    sort_keys_in_registers<2 * PPL>(keys, row, n, n2, lane);
+    return;
+  }
   // all of a lane's row loads in flight at once
 #pragma unroll
   for (int p = 0; p < 2 * PPL; ++p) {
