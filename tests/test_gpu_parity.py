@@ -365,3 +365,25 @@ def test_well_separated_masks_bit_exact(seed, mode):
     w = make_well_separated("ws", seed=seed, hq=8, hkv=4, d=128, lq=[1024, 512], lk=[2048, 512],
                             select_mode=mode)
     _prefill_and_check(w, max_mismatch=0.0, label="well-separated %d %s" % (seed, mode))
+
+
+@pytest.mark.parametrize("mode", ["per_kvhead", "chunk_vote"])
+@pytest.mark.parametrize("case", [
+    dict(name="paged_3seq", hq=4, hkv=2, d=128, lq=[512, 256, 128], lk=[2048, 256, 1536], paged=True),
+    dict(name="varlen_with_empty", hq=4, hkv=2, d=128, lq=[384, 0, 256], lk=[1024, 128, 256]),
+    dict(name="causal_2k_gqa2", hq=16, hkv=8, d=128, lq=[2048], lk=[2048]),
+], ids=lambda c: c["name"])
+def test_prefill_block_lists_match_the_plan_path(case, mode):
+    """In the resident prefill the selection kernels write the attention's
+    block lists themselves (no plan launch); attending over the same
+    effective mask through xattn_sparse_attn (plan kernel) must give the same
+    bits, split rows and dynamically drawn tail parts included."""
+    c = dict(case)
+    name = c.pop("name")
+    w = make_random(name, seed=71, select_mode=mode, **c)
+    r = Run(w)
+    say("block lists %s %s" % (name, mode))
+    out, lse, counts, aux = r.prefill()
+    out2, lse2 = r.attend(aux["mask_kv"])
+    assert torch.equal(out.cpu(), out2.cpu()), "output differs from the plan path"
+    assert torch.equal(lse.cpu(), lse2.cpu()), "LSE differs from the plan path"
