@@ -387,3 +387,33 @@ def test_prefill_block_lists_match_the_plan_path(case, mode):
     out2, lse2 = r.attend(aux["mask_kv"])
     assert torch.equal(out.cpu(), out2.cpu()), "output differs from the plan path"
     assert torch.equal(lse.cpu(), lse2.cpu()), "LSE differs from the plan path"
+
+
+@pytest.mark.parametrize("case", [
+    # every sequence alone still takes the 256 x 256 tiles (>= 256 of them)
+    dict(name="big_tiles", hq=32, hkv=8, d=128, lq=[2048, 2432, 512], lk=[16384, 8192, 16384]),
+    dict(name="small_tiles", hq=4, hkv=2, d=128, lq=[512, 0, 256, 128], lk=[2048, 256, 256, 1536]),
+], ids=lambda c: c["name"])
+def test_estimate_batch_matches_per_sequence_launches(case):
+    """A launch over several sequences numbers its workgroups over the tiles
+    that have work (a per-sequence table of them); a single sequence's launch
+    numbers them over its whole tile grid.  Each sequence's block sums must
+    come out bit-identical either way."""
+    import dataclasses
+
+    c = dict(case)
+    name = c.pop("name")
+    w = make_random(name, seed=81, **c)
+    say("estimate batch vs singles " + name)
+    bs = Run(w).estimate().cpu()
+    for b in range(w.batch):
+        lq, lk = w.lens(b)
+        if lq == 0:
+            continue
+        q0, k0 = w.cu_q[b], w.cu_k[b]
+        one = dataclasses.replace(w, q=w.q[q0:q0 + lq].contiguous(), k=w.k[k0:k0 + lk].contiguous(),
+                                  v=w.v[k0:k0 + lk].contiguous(), cu_q=[0, lq], cu_k=[0, lk],
+                                  block_table=None, k_cache=None, v_cache=None)
+        bs1 = Run(one).estimate().cpu()
+        qb, kb = lq // 128, lk // 128
+        assert torch.equal(bs[b, :, :qb, :kb], bs1[0, :, :qb, :kb]), "sequence %d differs" % b
