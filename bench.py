@@ -41,7 +41,7 @@ def parse():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="chunked_prefill_32k")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-sample-rows", type=int, default=1536,
+    ap.add_argument("--cpu-sample-rows", type=int, default=3072,
                     help="query rows of the oracle attention sample (scaled to the chunk)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 512 MiB device copy kernel (reference for PMC byte counters)")
