@@ -200,14 +200,19 @@ class Ring:
             pass
 
 
+def _aux(aux):
+    if aux is None:
+        return None
+    a = XattnAux()
+    a.block_sums = aux.get("block_sums").data_ptr() if aux.get("block_sums") is not None else None
+    a.mask_kv = aux.get("mask_kv").data_ptr() if aux.get("mask_kv") is not None else None
+    a.hist_sel = aux.get("hist_sel").data_ptr() if aux.get("hist_sel") is not None else None
+    return a
+
+
 def xattn_prefill_chunk(shape, params, q, k, v, out, lse, counts, ws, *, aux=None, ring=None,
                         k_hist=None, v_hist=None, hist_blocks=0, stream=None):
-    a = None
-    if aux is not None:
-        a = XattnAux()
-        a.block_sums = aux.get("block_sums").data_ptr() if aux.get("block_sums") is not None else None
-        a.mask_kv = aux.get("mask_kv").data_ptr() if aux.get("mask_kv") is not None else None
-        a.hist_sel = aux.get("hist_sel").data_ptr() if aux.get("hist_sel") is not None else None
+    a = _aux(aux)
     _check(_lib.load().xattn_prefill_chunk(
         ring.handle if ring is not None else None, ctypes.byref(shape.c), ctypes.byref(params),
         _ptr(q), _ptr(k), _ptr(v), _ptr(k_hist), _ptr(v_hist), int(hist_blocks), _ptr(out), _ptr(lse),

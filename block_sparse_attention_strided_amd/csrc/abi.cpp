@@ -9,6 +9,8 @@
 #include <cstring>
 #include <unistd.h>
 
+#include <cstdlib>
+
 #include <algorithm>
 #include <utility>
 #include <string>
@@ -37,6 +39,22 @@ int hip_fail(hipError_t e, const char* what) {
   return fail(XATTN_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
 }
 
+}  // namespace
+
+namespace xattn {
+int fail_message(int code, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return code;
+}
+}  // namespace xattn
+
+namespace {
+
 constexpr int kMaxKb = 4096;  // select sorts up to this many blocks per row in LDS
 constexpr int kStageChunk = 128;  // history blocks per pipeline step of a staged ring
 
@@ -54,6 +72,7 @@ struct Plan {
   size_t off_vt, off_lists;
   size_t off_ctr;  // attention's tail-part counter (4 bytes)
   int num_pages;  // 128-key pages of the K/V arrays (contiguous or paged)
+  bool reads_vt;  // some attention launch reads V^T pages (off_vt holds them)
   size_t total;
 };
 
@@ -154,8 +173,13 @@ int make_plan(const XattnShape* sh, const XattnParams* pr, Plan* p) {
   off = align_up(off + (size_t)(p->max_kb + 1) * sizeof(int32_t));
   p->num_pages = sh->block_table ? sh->num_phys_blocks : p->total_k / XATTN_BLOCK;
   p->off_vt = off;
-  if (p->dtype == XATTN_DTYPE_BF16)
-    off = align_up(off + (size_t)p->num_pages * p->hkv * p->d * XATTN_BLOCK * 2);
+  // V^T pages are read only by the single-phase bf16 attention kernel (odd
+  // GQA groups, or K/V spans beyond 31-bit buffer offsets); every attention
+  // launch of a call addresses at most num_pages pages, so the ping-pong
+  // kernel serves all of them when the whole span fits
+  const size_t span = (size_t)p->num_pages * p->hkv * p->d * XATTN_BLOCK * 2;
+  p->reads_vt = p->dtype == XATTN_DTYPE_BF16 && ((p->hq / p->hkv) % 2 != 0 || span >= ((size_t)1 << 31));
+  if (p->reads_vt) off = align_up(off + span);
   p->off_lists = off;
   off = align_up(off + B * p->hkv * (size_t)p->max_qb * (p->max_kb + 1) * sizeof(int32_t));
   p->off_ctr = off;
@@ -182,6 +206,7 @@ KvView make_view(const XattnShape* sh, const Plan& p, const void* base) {
   v.block_table = sh->block_table;
   v.cu_k = sh->cu_k;
   v.max_blocks = sh->max_blocks_per_seq;
+  v.num_pages = p.num_pages;
   v.kv_heads = p.hkv;
   v.head_dim = p.d;
   v.elem_bytes = p.elem;
@@ -253,6 +278,7 @@ hipError_t run_select(const XattnShape* sh, const XattnParams* pr, const Plan& p
     sa.lists = ws_at<int32_t>(plan_ws, p.off_lists);
     sa.block_table = kview->block_table;
     sa.max_blocks = kview->max_blocks;
+    sa.num_pages = kview->num_pages;
     sa.tail_ctr = ws_at<int>(plan_ws, p.off_ctr);
   }
   return launch_select(sa, p.batch, st, lists_done);
@@ -290,18 +316,24 @@ AttnArgs attn_args(const XattnShape* sh, const Plan& p, const void* q, KvView kv
 }
 
 // bf16 preparation of an attention launch over blocks [jb0, jb1) of
-// aa.mask: V^T pages of `v` (num_pages pages) and the per-row block lists.
+// aa.mask: V^T pages of `v` (num_pages pages; with transpose_v only pages
+// [vt_first, vt_first + vt_count), all from vt_first when vt_count < 0) and
+// the per-row block lists.
 hipError_t plan_attention(const XattnShape* sh, const Plan& p, const AttnArgs& aa, const void* v, int num_pages,
-                          void* ws, bool transpose_v, hipStream_t st, bool lists_ready = false) {
+                          void* ws, bool transpose_v, hipStream_t st, bool lists_ready = false, int vt_first = 0,
+                          int vt_count = -1) {
   if (p.dtype == XATTN_DTYPE_BF16) {
-    char* vt = ws_at<char>(ws, p.off_vt);
     AttnArgs probe = aa;
     probe.num_pages = num_pages;
-    if (transpose_v && attention_reads_vt(probe, 0, p.d)) {
+    if (vt_count < 0) vt_count = num_pages - vt_first;
+    // make_plan reserves V^T pages whenever a launch of the call can read them
+    if (attention_reads_vt(probe, 0, p.d) && !p.reads_vt) return hipErrorInvalidValue;
+    if (transpose_v && vt_count > 0 && attention_reads_vt(probe, 0, p.d)) {
+      const size_t page_v = (size_t)XATTN_BLOCK * p.hkv * p.d * 2;  // bytes of one page of V (= of V^T)
       VtArgs va;
-      va.v = (const char*)v;
-      va.vt = vt;
-      va.num_pages = num_pages;
+      va.v = (const char*)v + (size_t)vt_first * page_v;
+      va.vt = ws_at<char>(ws, p.off_vt) + (size_t)vt_first * page_v;
+      va.num_pages = vt_count;
       va.hkv = p.hkv;
       va.head_dim = p.d;
       hipError_t e = launch_vt_transpose(va, st);
@@ -314,6 +346,7 @@ hipError_t plan_attention(const XattnShape* sh, const Plan& p, const AttnArgs& a
     pa.cu_k = sh->cu_k;
     pa.block_table = aa.k.block_table;
     pa.max_blocks = aa.k.max_blocks;
+    pa.num_pages = num_pages;
     pa.hkv = p.hkv;
     pa.max_qb = p.max_qb;
     pa.max_kb = p.max_kb;
@@ -490,9 +523,10 @@ hipError_t launch_planned(const XattnShape* sh, const Plan& p, AttnArgs aa, void
 // Attention over blocks [jb0, jb1) of `mask`: prepare (bf16), then attend.
 // lists_ready: the block lists are in the workspace already.
 hipError_t run_attention(const XattnShape* sh, const Plan& p, AttnArgs aa, const void* v, int num_pages,
-                         void* ws, bool transpose_v, hipStream_t st, bool lists_ready = false) {
+                         void* ws, bool transpose_v, hipStream_t st, bool lists_ready = false, int vt_first = 0,
+                         int vt_count = -1) {
   aa.num_pages = num_pages;
-  hipError_t e = plan_attention(sh, p, aa, v, num_pages, ws, transpose_v, st, lists_ready);
+  hipError_t e = plan_attention(sh, p, aa, v, num_pages, ws, transpose_v, st, lists_ready, vt_first, vt_count);
   if (e != hipSuccess) return e;
   return launch_planned(sh, p, aa, ws, st);
 }
@@ -656,10 +690,12 @@ int prefill_ring(XattnRing* r, const XattnShape* sh, const XattnParams* pr, cons
   if ((e = hipMemcpyAsync(table, r->host_table, (size_t)kb * sizeof(int32_t), hipMemcpyHostToDevice, st)) != hipSuccess)
     return hip_fail(e, "table copy");
 
-  auto paged_view = [&](const void* base) {
+  // the current chunk (qb pages at k / v) or one slot (slot_blocks pages)
+  auto paged_view = [&](const void* base, int pages) {
     KvView kv = make_view(sh, p, base);
     kv.block_table = table;
     kv.max_blocks = kb;
+    kv.num_pages = pages;
     return kv;
   };
   float* o_acc = ws_at<float>(ws, p.off_o[0]);
@@ -672,7 +708,7 @@ int prefill_ring(XattnRing* r, const XattnShape* sh, const XattnParams* pr, cons
 
   // ---- current chunk (causal), overlapping the first history copies
   {
-    AttnArgs aa = attn_args(sh, p, q, paged_view(k), paged_view(v), maskkv, kh, kb);
+    AttnArgs aa = attn_args(sh, p, q, paged_view(k, qb), paged_view(v, qb), maskkv, kh, kb);
     if (sel.empty()) {
       if (bf16) aa.out = out;
       else aa.out_f32 = (float*)out;
@@ -697,7 +733,8 @@ int prefill_ring(XattnRing* r, const XattnShape* sh, const XattnParams* pr, cons
     if ((e = ring_fill(r, s, kh_ptr, vh_ptr, runs, true)) != hipSuccess) return hip_fail(e, "ring copy");
     if ((e = hipStreamWaitEvent(st, r->ready[s], 0)) != hipSuccess) return hip_fail(e, "ring wait");
     const bool first = (x0 == 0);
-    AttnArgs aa = attn_args(sh, p, q, paged_view(r->k_slots + s * slot_bytes), paged_view(r->v_slots + s * slot_bytes),
+    AttnArgs aa = attn_args(sh, p, q, paged_view(r->k_slots + s * slot_bytes, r->slot_blocks),
+                            paged_view(r->v_slots + s * slot_bytes, r->slot_blocks),
                             maskkv, sel[x0], sel[x1 - 1] + 1);
     aa.out_f32 = first ? o_acc : o_tmp;
     aa.lse = first ? l_acc : l_tmp;
@@ -848,7 +885,8 @@ int prefill_staged(XattnRing* r, const XattnShape* sh, const XattnParams* pr, co
       aa.out_f32 = o_cur;
       aa.lse = l_cur;
     }
-    if ((e = run_attention(sh, p, aa, sv, kb, ws, true, st)) != hipSuccess) return hip_fail(e, "attention launch");
+    if ((e = run_attention(sh, p, aa, sv, kb, ws, true, st, false, kh, qb)) != hipSuccess)
+      return hip_fail(e, "attention launch");
   }
   MergeArgs ma;
   ma.rows = p.total_q;
@@ -860,7 +898,8 @@ int prefill_staged(XattnRing* r, const XattnShape* sh, const XattnParams* pr, co
     AttnArgs aa = attn_args(sh, p, q, kview, vview, maskkv, j0, j1);
     aa.out_f32 = c == 0 ? o_acc : o_tmp;
     aa.lse = c == 0 ? l_acc : l_tmp;
-    if ((e = run_attention(sh, p, aa, sv, kb, ws, true, st)) != hipSuccess) return hip_fail(e, "attention launch");
+    if ((e = run_attention(sh, p, aa, sv, kb, ws, true, st, false, j0, j1 - j0)) != hipSuccess)
+      return hip_fail(e, "attention launch");
     if (c > 0) {
       ma.o_a = o_acc;
       ma.lse_a = l_acc;
@@ -941,7 +980,80 @@ int ring_create(int num_slots, int slot_blocks, int num_kv_heads, int head_dim, 
 }
 
 
+
+// XATTN_DEBUG set to anything but "" or "0": calls with a block table first
+// copy it to the host (after the caller's stream has drained) and reject an
+// entry that a sequence uses (key block j < Lk/128) but that names no page of
+// the cache.  Without it such entries are treated as absent pages by every
+// kernel (keys read as missing), which is memory-safe but silently changes
+// the result.
+bool debug_mode() {
+  const char* e = getenv("XATTN_DEBUG");
+  return e && *e && strcmp(e, "0") != 0;
+}
+
+int validate_block_table(const XattnShape* sh, const Plan& p, hipStream_t st) {
+  if (!sh->block_table || !debug_mode()) return XATTN_OK;
+  std::vector<int32_t> t((size_t)sh->batch * sh->max_blocks_per_seq);
+  hipError_t e = hipMemcpyAsync(t.data(), sh->block_table, t.size() * sizeof(int32_t), hipMemcpyDeviceToHost, st);
+  if (e == hipSuccess) e = hipStreamSynchronize(st);
+  if (e != hipSuccess) return hip_fail(e, "block table copy (XATTN_DEBUG)");
+  for (int b = 0; b < sh->batch; ++b) {
+    const int nb = (sh->cu_k_host[b + 1] - sh->cu_k_host[b]) / XATTN_BLOCK;
+    for (int j = 0; j < nb; ++j) {
+      const int page = t[(size_t)b * sh->max_blocks_per_seq + j];
+      if (page < 0 || page >= p.num_pages)
+        return fail(XATTN_ERR_INVALID,
+                    "sequence %d: block_table entry %d is %d, not a page of the cache [0, %d) (XATTN_DEBUG)", b, j,
+                    page, p.num_pages);
+    }
+  }
+  return XATTN_OK;
+}
+
+// The resident-K/V path of xattn_prefill_chunk on workspace `ws` (validated).
+int prefill_resident(const XattnShape* shape, const XattnParams* params, const Plan& p, const void* q,
+                     const void* k, const void* v, void* out, float* lse, int32_t* counts, const XattnAux* aux,
+                     void* ws, hipStream_t st) {
+  g_last_error.clear();
+  float* part = ws_at<float>(ws, p.off_part);
+  float* bs = (aux && aux->block_sums) ? aux->block_sums : ws_at<float>(ws, p.off_bs);
+  uint8_t* maskkv = (aux && aux->mask_kv) ? aux->mask_kv : ws_at<uint8_t>(ws, p.off_maskkv);
+  uint8_t* hist = (aux && aux->hist_sel) ? aux->hist_sel : ws_at<uint8_t>(ws, p.off_hist);
+  int32_t* cnt = counts ? counts : ws_at<int32_t>(ws, p.off_counts);
+  const KvView kview = make_view(shape, p, k), vview = make_view(shape, p, v);
+  hipError_t e = hipSuccess;
+  bool lists_ready = false;  // block lists written by the selection kernels
+  if (params->reuse_selection) {
+    if (!aux || !aux->mask_kv) return fail(XATTN_ERR_INVALID, "reuse_selection needs aux->mask_kv");
+  } else {
+    e = run_estimate(shape, p, q, kview, 0, p.max_kb, p.num_pages, part, st);
+    if (e != hipSuccess) return hip_fail(e, "estimate launch");
+    e = run_block_sums(shape, p, part, bs, st);
+    if (e != hipSuccess) return hip_fail(e, "block-sum launch");
+    e = run_select(shape, params, p, bs, ws_at<uint8_t>(ws, p.off_maskq), maskkv, hist, cnt, st, ws, &kview,
+                   &lists_ready);
+    if (e != hipSuccess) return hip_fail(e, "select launch");
+  }
+  AttnArgs aa = attn_args(shape, p, q, kview, vview, maskkv, 0, p.max_kb);
+  if (p.dtype == XATTN_DTYPE_BF16) aa.out = out;
+  else aa.out_f32 = (float*)out;
+  aa.lse = lse;
+  e = run_attention(shape, p, aa, v, p.num_pages, ws, true, st, lists_ready);
+  if (e != hipSuccess) return hip_fail(e, "attention launch");
+  return XATTN_OK;
+}
+
 }  // namespace
+
+namespace xattn {
+int workspace_bytes(const XattnShape* shape, const XattnParams* params, size_t* bytes) {
+  Plan p;
+  const int rc = make_plan(shape, params, &p);
+  *bytes = rc ? 0 : p.total;
+  return rc;
+}
+}  // namespace xattn
 
 extern "C" {
 
@@ -960,6 +1072,7 @@ int xattn_estimate(const XattnShape* shape, const XattnParams* params, const voi
   if (rc) return rc;
   if (!q || !k || !block_sums) return fail(XATTN_ERR_INVALID, "q, k and block_sums must not be NULL");
   if ((rc = check_ws(p, ws, ws_bytes))) return rc;
+  if ((rc = validate_block_table(shape, p, (hipStream_t)stream))) return rc;
   g_last_error.clear();
   hipStream_t st = (hipStream_t)stream;
   float* part = ws_at<float>(ws, p.off_part);
@@ -996,6 +1109,7 @@ int xattn_sparse_attn(const XattnShape* shape, const XattnParams* params, const 
   if (!q || !k || !v || !mask_kv || !out)
     return fail(XATTN_ERR_INVALID, "q, k, v, mask_kv and out must not be NULL");
   if ((rc = check_ws(p, ws, ws_bytes))) return rc;
+  if ((rc = validate_block_table(shape, p, (hipStream_t)stream))) return rc;
   g_last_error.clear();
   AttnArgs aa = attn_args(shape, p, q, make_view(shape, p, k), make_view(shape, p, v), mask_kv, 0, p.max_kb);
   if (p.dtype == XATTN_DTYPE_BF16) aa.out = out;
@@ -1013,6 +1127,7 @@ int xattn_attn_plan(const XattnShape* shape, const XattnParams* params, const vo
   if (rc) return rc;
   if (!v || !mask_kv) return fail(XATTN_ERR_INVALID, "v and mask_kv must not be NULL");
   if ((rc = check_ws(p, ws, ws_bytes))) return rc;
+  if ((rc = validate_block_table(shape, p, (hipStream_t)stream))) return rc;
   g_last_error.clear();
   AttnArgs aa = attn_args(shape, p, nullptr, make_view(shape, p, v), make_view(shape, p, v), mask_kv, 0, p.max_kb);
   hipError_t e = plan_attention(shape, p, aa, v, p.num_pages, ws, true, (hipStream_t)stream);
@@ -1028,6 +1143,7 @@ int xattn_attn_run(const XattnShape* shape, const XattnParams* params, const voi
   if (!q || !k || !v || !mask_kv || !out)
     return fail(XATTN_ERR_INVALID, "q, k, v, mask_kv and out must not be NULL");
   if ((rc = check_ws(p, ws, ws_bytes))) return rc;
+  if ((rc = validate_block_table(shape, p, (hipStream_t)stream))) return rc;
   g_last_error.clear();
   AttnArgs aa = attn_args(shape, p, q, make_view(shape, p, k), make_view(shape, p, v), mask_kv, 0, p.max_kb);
   if (p.dtype == XATTN_DTYPE_BF16) aa.out = out;
@@ -1078,34 +1194,8 @@ int xattn_prefill_chunk(XattnRing* ring, const XattnShape* shape, const XattnPar
   if (ring)
     return prefill_ring(ring, shape, params, p, q, k, v, k_hist_host, v_hist_host, hist_blocks, out, lse, counts,
                         aux, ws, (hipStream_t)stream);
-  g_last_error.clear();
-  hipStream_t st = (hipStream_t)stream;
-  float* part = ws_at<float>(ws, p.off_part);
-  float* bs = (aux && aux->block_sums) ? aux->block_sums : ws_at<float>(ws, p.off_bs);
-  uint8_t* maskkv = (aux && aux->mask_kv) ? aux->mask_kv : ws_at<uint8_t>(ws, p.off_maskkv);
-  uint8_t* hist = (aux && aux->hist_sel) ? aux->hist_sel : ws_at<uint8_t>(ws, p.off_hist);
-  int32_t* cnt = counts ? counts : ws_at<int32_t>(ws, p.off_counts);
-  const KvView kview = make_view(shape, p, k), vview = make_view(shape, p, v);
-  hipError_t e = hipSuccess;
-  bool lists_ready = false;  // block lists written by the selection kernels
-  if (params->reuse_selection) {
-    if (!aux || !aux->mask_kv) return fail(XATTN_ERR_INVALID, "reuse_selection needs aux->mask_kv");
-  } else {
-    e = run_estimate(shape, p, q, kview, 0, p.max_kb, p.num_pages, part, st);
-    if (e != hipSuccess) return hip_fail(e, "estimate launch");
-    e = run_block_sums(shape, p, part, bs, st);
-    if (e != hipSuccess) return hip_fail(e, "block-sum launch");
-    e = run_select(shape, params, p, bs, ws_at<uint8_t>(ws, p.off_maskq), maskkv, hist, cnt, st, ws, &kview,
-                   &lists_ready);
-    if (e != hipSuccess) return hip_fail(e, "select launch");
-  }
-  AttnArgs aa = attn_args(shape, p, q, kview, vview, maskkv, 0, p.max_kb);
-  if (p.dtype == XATTN_DTYPE_BF16) aa.out = out;
-  else aa.out_f32 = (float*)out;
-  aa.lse = lse;
-  e = run_attention(shape, p, aa, v, p.num_pages, ws, true, st, lists_ready);
-  if (e != hipSuccess) return hip_fail(e, "attention launch");
-  return XATTN_OK;
+  if ((rc = validate_block_table(shape, p, (hipStream_t)stream))) return rc;
+  return prefill_resident(shape, params, p, q, k, v, out, lse, counts, aux, ws, (hipStream_t)stream);
 }
 
 int xattn_ring_create(int num_slots, int slot_blocks, int num_kv_heads, int head_dim, int dtype,

@@ -278,7 +278,7 @@ __global__ __launch_bounds__(64) void plan_kernel(PlanArgs a) {
     const int j = j0 + lane;
     int page = -1;
     if (j < jend && mrow[j]) page = a.block_table ? a.block_table[(long long)b * a.max_blocks + j] : page0 + j;
-    const bool take = page >= 0;
+    const bool take = page >= 0 && page < a.num_pages;
     const unsigned long long bal = __ballot(take);
     const int before = __popcll(bal & ((1ull << lane) - 1ull));
     if (take) out[1 + n + before] = (page << 1) | (j == i + kh ? 1 : 0);
@@ -1056,12 +1056,13 @@ __global__ __launch_bounds__(512) void attn_pp(AttnArgs a, int hkv) {
 struct BlockIter {
   const uint8_t* mrow;
   const int32_t* table;  // block table row (paged) or nullptr
+  int num_pages;         // table entries outside [0, num_pages) are absent
   int jend;
   // First selected block >= j (page present), or jend.
   __device__ __forceinline__ int next(int j) const {
     for (; j < jend; ++j) {
       if (!mrow[j]) continue;
-      if (table && table[j] < 0) continue;
+      if (table && (table[j] < 0 || table[j] >= num_pages)) continue;
       return j;
     }
     return jend;
@@ -1091,6 +1092,7 @@ __global__ __launch_bounds__(128) void attn_f32(AttnArgs a) {
   BlockIter it;
   it.mrow = a.mask + (((long long)b * (a.hq / a.group) + g) * a.max_qb + i) * a.max_kb;
   it.table = a.k.block_table ? a.k.block_table + (long long)b * a.k.max_blocks : nullptr;
+  it.num_pages = a.k.num_pages;
   it.jend = min(a.jb1, i + kh + 1);
 
   float qv[D];

@@ -133,7 +133,7 @@ __device__ void emit_row_list(const SelectArgs& a, int b, int g, int i, int kh, 
     const int j = j0 + tid;
     int page = -1;
     if (j < jend && flag(j)) page = a.block_table ? a.block_table[(long long)b * a.max_blocks + j] : page0 + j;
-    const bool take = page >= 0;
+    const bool take = page >= 0 && page < a.num_pages;
     const unsigned long long bal = __ballot(take);
     if (lane == 0) wcnt[w] = __popcll(bal);
     __syncthreads();

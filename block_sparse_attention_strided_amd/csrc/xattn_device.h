@@ -46,18 +46,20 @@ struct KvView {
   const int32_t* block_table;  // [batch, max_blocks] or nullptr
   const int32_t* cu_k;         // [batch+1] (contiguous layout)
   int max_blocks;
+  int num_pages;  // paged: pages addressable from base; an entry outside [0, num_pages) is absent
   int kv_heads;
   int head_dim;
   int elem_bytes;
   int y_offset;  // contiguous layout: the array starts at key y_offset of the sequence
 
   // Byte address of key `y` (sequence-relative), kv head `g`, element 0.
-  // Paged: returns nullptr when the page is unallocated (-1).
+  // Paged: returns nullptr when the page is unallocated (-1) or outside the
+  // cache (an entry >= num_pages is never dereferenced).
   __device__ __forceinline__ const char* row(int b, int y, int g) const {
     const long long row_bytes = (long long)kv_heads * head_dim * elem_bytes;
     if (block_table) {
       const int page = block_table[(long long)b * max_blocks + (y >> 7)];
-      if (page < 0) return nullptr;
+      if (page < 0 || page >= num_pages) return nullptr;
       return base + ((long long)page * kBlock + (y & (kBlock - 1))) * row_bytes +
              (long long)g * head_dim * elem_bytes;
     }

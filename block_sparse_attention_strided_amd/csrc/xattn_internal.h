@@ -5,6 +5,7 @@
 #include <stdint.h>
 
 #include "xattn_device.h"
+#include "../../include/xattn.h"
 
 namespace xattn {
 
@@ -77,6 +78,7 @@ struct SelectArgs {
   int32_t* lists;
   const int32_t* block_table;  // [batch, max_blocks] or nullptr
   int max_blocks;
+  int num_pages;  // pages of the K/V arrays; table entries outside [0, num_pages) are absent
   int* tail_ctr;
 };
 
@@ -100,6 +102,7 @@ struct PlanArgs {
   const int32_t* cu_k;
   const int32_t* block_table;  // [batch, max_blocks] or nullptr (contiguous)
   int max_blocks;
+  int num_pages;  // pages of the K/V arrays; table entries outside [0, num_pages) are absent
   int hkv;
   int max_qb;
   int max_kb;
@@ -187,6 +190,12 @@ struct MergeArgs {
   void* o_bf16;    // bf16 out (or nullptr)
   float* lse;      // may be nullptr
 };
+
+// Sets the calling thread's xattn_last_error message (printf format) and
+// returns `code`.
+int fail_message(int code, const char* fmt, ...);
+// Workspace bytes of a call (xattn_workspace_size) with make_plan's status.
+int workspace_bytes(const XattnShape* shape, const XattnParams* params, size_t* bytes);
 
 hipError_t launch_estimate(const EstArgs& a, int dtype, int head_dim, int stride, int batch,
                            hipStream_t s);

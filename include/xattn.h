@@ -31,6 +31,14 @@
  *    paged-attention page, "Caminho Varlen").  With a block table, key y of
  *    sequence b lives in page block_table[b*max_blocks_per_seq + y/128] at row
  *    y%128; -1 marks an unallocated page ("Caminho de decodificação").
+ *    Every entry a sequence uses (key block j < Lk/128) must name a page in
+ *    [0, num_phys_blocks).  An entry that does not is treated as an absent
+ *    page by every kernel (the estimate reads its keys as zero vectors and
+ *    the attention skips the block; nothing outside the cache is read),
+ *    which silently changes the result.  With the environment variable XATTN_DEBUG set (to anything
+ *    but "" or "0") the calls that take a block table first wait for `stream`
+ *    to drain, copy the table to the host and return XATTN_ERR_INVALID for
+ *    such an entry, before enqueuing anything.
  *  - The queries of a sequence are its LAST Lq = cu_q[b+1]-cu_q[b] positions:
  *    query x sits at absolute position (Lk - Lq) + x and sees keys y <= that.
  *  - Every length must be a multiple of 128 and Lk >= Lq (the design doc's

@@ -14,3 +14,12 @@ def pytest_configure(config):
 
 
 GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
+
+
+def pytest_terminal_summary(terminalreporter, exitstatus, config):
+    from tests import metrics
+
+    if metrics.LINES:
+        terminalreporter.section("parity figures")
+        for line in metrics.LINES:
+            terminalreporter.write_line(line)

@@ -100,3 +100,26 @@ def test_block_table_too_short_is_rejected():
     p = X.make_params()
     assert _lib.load().xattn_workspace_size(ctypes.byref(s.c), ctypes.byref(p)) == 0
     assert "max_blocks_per_seq" in _lib.last_error()
+
+
+def test_vt_pages_reserved_only_for_the_single_phase_kernel():
+    """The V^T pages (read only by the single-phase bf16 attention: odd GQA
+    groups, or K/V spans beyond 31-bit offsets) are reserved only when some
+    launch can run that kernel: with an even group the workspace does not
+    grow with the paged cache; with an odd group it grows by one V page per
+    cache page; fp32 never reserves them."""
+    p = X.make_params()
+    t = torch.zeros((1, 4), dtype=torch.int32)
+    page = 128 * 2 * 128 * 2  # one bf16 page of V at 2 kv heads, d = 128
+    lib = _lib.load()
+
+    def size(hq, phys, dtype=torch.bfloat16):
+        s = _shape(lq=(128,), lk=(512,), hq=hq, hkv=2, table=t, phys=phys, dtype=dtype)
+        return lib.xattn_workspace_size(ctypes.byref(s.c), ctypes.byref(p))
+
+    assert size(4, 16) == size(4, 4096)                      # group 2
+    assert size(6, 4096) - size(6, 16) == (4096 - 16) * page  # group 3
+    assert size(6, 4096, torch.float32) == size(6, 16, torch.float32)
+    # an even group whose cache spans 2 GiB or more reserves them too
+    big = (1 << 31) // page
+    assert size(4, big) - size(4, big - 1) == big * page

@@ -5,6 +5,12 @@ Checks: agreement with the resident-KV path and with the oracle; bit-equal
 results when every slot copy is delayed on the host (a missing wait would
 let a kernel read a stale slot); slot reuse with 2 slots; a pageable history
 is rejected before any work; the 128K-context workload on sampled rows.
+
+Unless a test says otherwise the inputs are well separated with block ranks
+shared by the kv heads, so the chunk vote keeps a scattered tenth of the
+history: the slot packing (several runs per slot, block j in slot position
+x != j), the gather's skipping of unvoted blocks and the per-slot key windows
+all run on gaps.  Each such test asserts that the vote left gaps.
 """
 
 import numpy as np
@@ -12,8 +18,9 @@ import pytest
 import torch
 
 import block_sparse_attention_strided_amd as X
-from tests.gpu_util import Run, assert_attention_close, assert_block_sums_close, sample_rows, say
-from workloads import make_random, make_workload
+from tests.gpu_util import (Run, assert_attention_close, assert_block_sums_close, assert_gapped, check_selection,
+                            sample_rows, say)
+from workloads import make_random, make_well_separated, make_workload
 
 pytestmark = [pytest.mark.gpu,
               pytest.mark.skipif(not torch.cuda.is_available(), reason="needs a GPU")]
@@ -52,21 +59,40 @@ def _run_ring(r, w, ring, k_hist, v_hist, k_cur, v_cur, kh):
     return out, lse, counts, aux
 
 
-def _small():
-    return make_random("ring_small", seed=41, hq=8, hkv=2, d=128, lq=[1024], lk=[16384],
-                       stride=16, threshold=0.95, select_mode="chunk_vote", kv_chunk_tokens=1024)
+SMALL = dict(d=128, lq=[1024], lk=[16384], stride=16, threshold=0.95, select_mode="chunk_vote",
+             kv_chunk_tokens=1024)
 
 
-def test_ring_matches_resident_path_and_oracle():
-    w = _small()
+def _small(kind="sparse", hq=8, hkv=2, seed=41, lk=None):
+    """1024 queries over 16K keys (120 history blocks), s=16, tau=0.95.
+    sparse: well-separated shared ranks, step 0.3 (the vote keeps 12 of 120
+    history blocks in 11 runs); gaussian: planted Gaussian inputs (the vote
+    keeps every block)."""
+    kw = dict(SMALL, hq=hq, hkv=hkv)
+    if lk is not None:
+        kw["lk"] = [lk]
+    if kind == "gaussian":
+        return make_random("ring_small_gauss", seed=seed, **kw)
+    return make_well_separated("ring_small_sparse", seed=seed, shared_ranks=True, rank_step=0.3, **kw)
+
+
+@pytest.mark.parametrize("kind,hq,slots", [
+    ("sparse", 8, 4), ("sparse", 8, 2), ("sparse", 6, 4), ("gaussian", 8, 4)],
+    ids=["sparse-g4-4slots", "sparse-g4-2slots", "sparse-g3-4slots", "gaussian-g4-4slots"])
+def test_ring_matches_resident_path_and_oracle(kind, hq, slots):
+    """Group 3 (hq=6, hkv=2) runs the single-phase attention kernel, which
+    reads V^T pages of each slot."""
+    w = _small(kind, hq=hq)
     r = Run(w)
     k_hist, v_hist, k_cur, v_cur, kh = _ring_inputs(w)
-    ring = X.Ring(4, 8, w.num_kv_heads, w.head_dim, w.dtype)
-    say("ring small: resident path")
+    ring = X.Ring(slots, 8, w.num_kv_heads, w.head_dim, w.dtype)
+    say("ring small %s hq=%d slots=%d: resident path" % (kind, hq, slots))
     o_res, l_res, c_res, aux_res = r.prefill()
     say("ring small: ring path")
     o_ring, l_ring, c_ring, aux_ring = _run_ring(r, w, ring, k_hist, v_hist, k_cur, v_cur, kh)
     ring.close()
+    if kind == "sparse":
+        assert_gapped(aux_ring["hist_sel"][0], kh, "ring %s hq=%d slots=%d" % (kind, hq, slots))
     # the estimate and the selection see bit-identical inputs either way
     assert torch.equal(aux_res["block_sums"], aux_ring["block_sums"])
     assert torch.equal(aux_res["mask_kv"], aux_ring["mask_kv"])
@@ -74,6 +100,10 @@ def test_ring_matches_resident_path_and_oracle():
     assert (o_res.float() - o_ring.float()).abs().max().item() <= 2e-2
     ref = r.oracle(attention=False)
     assert_block_sums_close(aux_ring["block_sums"], ref["block_sums"], w.stride, "ring small")
+    check_selection(r, ref, aux_ring["block_sums"], aux_ring["mask_kv"], aux_ring["hist_sel"],
+                    "ring small %s hq=%d" % (kind, hq))
+    if kind == "sparse":
+        assert torch.equal(aux_ring["hist_sel"][0, :kh].cpu(), torch.from_numpy(ref["hist_sel"][0, :kh]).to(torch.uint8))
     ref_o, ref_l = r.oracle_attention(aux_ring["mask_kv"])
     assert_attention_close(o_ring, l_ring, ref_o, ref_l, w.dtype, label="ring small")
 
@@ -88,6 +118,7 @@ def test_ring_delayed_copies_give_identical_results(slots):
     ring = X.Ring(slots, 8, w.num_kv_heads, w.head_dim, w.dtype)
     say("ring delay test slots=%d: no delay" % slots)
     o0, l0, c0, a0 = _run_ring(r, w, ring, k_hist, v_hist, k_cur, v_cur, kh)
+    assert_gapped(a0["hist_sel"][0], kh, "ring delay slots=%d" % slots)
     ring.set_copy_delay_us(2000)
     say("ring delay test slots=%d: 2 ms delay per copy" % slots)
     o1, l1, c1, a1 = _run_ring(r, w, ring, k_hist, v_hist, k_cur, v_cur, kh)
@@ -103,17 +134,25 @@ def test_ring_delayed_copies_give_identical_results(slots):
         assert torch.equal(l_, l0)
 
 
+def _write_back_pair(seed_chunk2, seed_chunk1, L=16384, lq=1024):
+    """Chunk 2 (the last lq of L keys) and chunk 1 (the lq before it) of one
+    well-separated sequence: chunk 1's keys are chunk 2's first L - lq."""
+    kw = dict(hq=8, hkv=2, d=128, stride=16, threshold=0.95, select_mode="chunk_vote", kv_chunk_tokens=1024,
+              shared_ranks=True, rank_step=0.3)
+    w2 = make_well_separated("wb2", seed=seed_chunk2, lq=[lq], lk=[L], **kw)
+    w1 = make_well_separated("wb1", seed=seed_chunk1, lq=[lq], lk=[L - lq], **kw)
+    w1.k = w2.k[: L - lq].clone()
+    w1.v = w2.v[: L - lq].clone()
+    return w1, w2
+
+
 def test_ring_write_back_feeds_the_next_chunk():
     """Chunk 1's K/V, written back into the pinned history on the ring's
     offload stream (every copy delayed 2 ms by a host callback), are read by
     chunk 2's ring prefill: its estimate, selection and output equal chunk 2
     with all K/V resident, and the host history holds chunk 1's K/V."""
     L, lq = 16384, 1024
-    kw = dict(hq=8, hkv=2, d=128, stride=16, threshold=0.95, select_mode="chunk_vote", kv_chunk_tokens=1024)
-    w2 = make_random("wb2", seed=43, lq=[lq], lk=[L], **kw)
-    w1 = make_random("wb1", seed=44, lq=[lq], lk=[L - lq], **kw)
-    w1.k = w2.k[: L - lq].clone()  # chunk 1 sees the first L - lq keys of the same sequence
-    w1.v = w2.v[: L - lq].clone()
+    w1, w2 = _write_back_pair(43, 43)
     r1, r2 = Run(w1), Run(w2)
     hkv, d = w2.num_kv_heads, w2.head_dim
     nh, h1 = (L - lq) // 128, (L - 2 * lq) // 128
@@ -125,7 +164,8 @@ def test_ring_write_back_feeds_the_next_chunk():
     ring.set_copy_delay_us(2000)
     k1, v1 = w2.k[L - 2 * lq: L - lq].cuda(), w2.v[L - 2 * lq: L - lq].cuda()
     say("write-back: chunk 1 through the ring")
-    _run_ring(r1, w1, ring, k_host[:h1], v_host[:h1], k1, v1, h1)
+    _, _, _, a1 = _run_ring(r1, w1, ring, k_host[:h1], v_host[:h1], k1, v1, h1)
+    assert_gapped(a1["hist_sel"][0], h1, "write-back chunk 1")
     say("write-back: chunk 1 K/V to host blocks %d..%d" % (h1, nh))
     ring.offload_chunk(k1, v1, k_host[h1:], v_host[h1:], lq // 128)
     k2, v2 = w2.k[L - lq:].cuda(), w2.v[L - lq:].cuda()
@@ -134,6 +174,7 @@ def test_ring_write_back_feeds_the_next_chunk():
     ring.offload_wait()
     torch.cuda.synchronize()
     ring.close()
+    assert_gapped(a2["hist_sel"][0], nh, "write-back chunk 2")
     assert torch.equal(k_host.reshape(-1, hkv, d), w2.k[: L - lq])
     assert torch.equal(v_host.reshape(-1, hkv, d), w2.v[: L - lq])
     say("write-back: chunk 2 resident")
@@ -154,6 +195,7 @@ def test_ring_reusing_a_selection_skips_the_estimate():
     ring = X.Ring(4, 8, w.num_kv_heads, w.head_dim, w.dtype)
     say("ring reuse: full path")
     o0, l0, c0, a0 = _run_ring(r, w, ring, k_hist, v_hist, k_cur, v_cur, kh)
+    assert_gapped(a0["hist_sel"][0], kh, "ring reuse")
     params = X.make_params(stride=w.stride, threshold=r.tau, est_scale=r.est_scale, softmax_scale=r.softmax_scale,
                            kv_chunk_tokens=w.kv_chunk_tokens, select_mode=w.select_mode, reuse_selection=1)
     out = torch.full_like(r.q, float("nan"))
@@ -170,21 +212,26 @@ def test_ring_reusing_a_selection_skips_the_estimate():
     assert torch.equal(lse, l0)
 
 
-def test_staged_ring_matches_resident_path():
+@pytest.mark.parametrize("hq", [8, 6], ids=["g4", "g3"])
+def test_staged_ring_matches_resident_path(hq):
     """Staged ring (history K in chunks, device-driven gather of the voted V
     blocks from mapped pinned memory, chunked attention with merges):
     estimate and selection bit-identical to the resident path, output within
     the bf16 tolerance of it and of the oracle; bit-identical to itself with
-    every copy delayed 2 ms and with a reused selection."""
-    w = _small()
+    every copy delayed 2 ms and with a reused selection.  hq=6 (group 3) runs
+    the single-phase kernel, which reads V^T pages transposed per launch.
+    The 20K history spans two staging chunks of 128 blocks."""
+    w = _small(hq=hq, lk=20480)
     r = Run(w)
     k_hist, v_hist, k_cur, v_cur, kh = _ring_inputs(w)
     lq, lk = w.lens(0)
     ring = X.Ring(1, lk // 128, w.num_kv_heads, w.head_dim, w.dtype, staged=True)
-    say("staged ring: resident path")
+    say("staged ring hq=%d: resident path" % hq)
     o_res, l_res, c_res, a_res = r.prefill()
     say("staged ring: staged path")
     o_st, l_st, c_st, a_st = _run_ring(r, w, ring, k_hist, v_hist, k_cur, v_cur, kh)
+    runs = assert_gapped(a_st["hist_sel"][0], kh, "staged hq=%d" % hq)
+    assert any(j < 128 for j, _ in runs) and any(j + n > 128 for j, n in runs), runs
     for a in ("block_sums", "mask_kv", "hist_sel"):
         assert torch.equal(a_st[a], a_res[a]), a
     assert torch.equal(c_st, c_res)
@@ -218,11 +265,7 @@ def test_staged_ring_write_back_feeds_the_next_chunk():
     copy) into the pinned history, chunk 2 through the staged ring: equal to
     chunk 2 with all K/V resident."""
     L, lq = 16384, 1024
-    kw = dict(hq=8, hkv=2, d=128, stride=16, threshold=0.95, select_mode="chunk_vote", kv_chunk_tokens=1024)
-    w2 = make_random("swb2", seed=45, lq=[lq], lk=[L], **kw)
-    w1 = make_random("swb1", seed=46, lq=[lq], lk=[L - lq], **kw)
-    w1.k = w2.k[: L - lq].clone()
-    w1.v = w2.v[: L - lq].clone()
+    w1, w2 = _write_back_pair(45, 45)
     r1, r2 = Run(w1), Run(w2)
     hkv, d = w2.num_kv_heads, w2.head_dim
     nh, h1 = (L - lq) // 128, (L - 2 * lq) // 128
@@ -242,6 +285,7 @@ def test_staged_ring_write_back_feeds_the_next_chunk():
     ring.offload_wait()
     torch.cuda.synchronize()
     ring.close()
+    assert_gapped(a2["hist_sel"][0], nh, "staged write-back chunk 2")
     o_res, l_res, c_res, a_res = r2.prefill()
     assert torch.equal(a2["block_sums"], a_res["block_sums"])
     assert torch.equal(a2["mask_kv"], a_res["mask_kv"])
@@ -272,23 +316,45 @@ def test_ring_rejects_pageable_history():
     ring.close()
 
 
-def test_ring_qwen3_4b_128k_sampled():
-    w = make_workload("qwen3_4b_128k_ring")
+def _ring_128k_check(w, staged=False):
     r = Run(w)
     k_hist, v_hist, k_cur, v_cur, kh = _ring_inputs(w)
-    ring = X.Ring(w.ring_slots, w.ring_slot_blocks, w.num_kv_heads, w.head_dim, w.dtype)
-    say("ring 128K: ring path")
+    if staged:
+        ring = X.Ring(1, w.lens(0)[1] // 128, w.num_kv_heads, w.head_dim, w.dtype, staged=True)
+    else:
+        ring = X.Ring(w.ring_slots, w.ring_slot_blocks, w.num_kv_heads, w.head_dim, w.dtype)
+    say("ring 128K %s: %s path" % (w.name, "staged" if staged else "slot"))
     out, lse, counts, aux = _run_ring(r, w, ring, k_hist, v_hist, k_cur, v_cur, kh)
     ring.close()
     ref = r.oracle(attention=False)
     assert_block_sums_close(aux["block_sums"], ref["block_sums"], w.stride, "128K")
-    gm = aux["mask_kv"].cpu().numpy().astype(bool)
-    mism = float((gm != ref["mask_kv"]).mean())
-    say("  mask mismatch %.4g counts %s vs %s" % (mism, counts.tolist(), ref["counts"].tolist()))
-    assert mism <= 0.01
+    mism, soft, firm = check_selection(r, ref, aux["block_sums"], aux["mask_kv"], aux["hist_sel"],
+                                       "128K %s %s" % (w.name, "staged" if staged else "slots"))
+    say("  mask mismatch %.4g (%d soft / %d firm rows) counts %s vs %s" % (
+        mism, soft, firm, counts.tolist(), ref["counts"].tolist()))
     rng = np.random.default_rng(3)
     blocks = sorted(rng.choice(32, size=3, replace=False).tolist())
     rows = {0: sorted({b * 128 + int(x) for b in blocks for x in rng.choice(128, 16, replace=False)} |
                       {b * 128 for b in blocks} | {b * 128 + 127 for b in blocks})}
     ref_o, ref_l = r.oracle_attention(aux["mask_kv"], rows=rows)
     assert_attention_close(out, lse, ref_o, ref_l, w.dtype, rows_idx=np.asarray(rows[0]), label="128K")
+    return aux, ref, kh
+
+
+def test_ring_qwen3_4b_128k_sampled():
+    _ring_128k_check(make_workload("qwen3_4b_128k_ring"))
+
+
+@pytest.mark.parametrize("staged", [False, True], ids=["slots", "staged"])
+def test_ring_128k_sparse_vote(staged):
+    """The 128K ring shape (32 q / 8 kv heads, s=16, tau=0.95, 4 slots of 32
+    blocks) on well-separated inputs with shared ranks, step 0.05: the vote
+    keeps about 6% of the 992 history blocks in about 50 runs, which the
+    slot ring packs several runs to a slot and the staged ring gathers."""
+    w = make_well_separated("ring128k_sparse", seed=202, hq=32, hkv=8, d=128, lq=[4096], lk=[131072], stride=16,
+                            threshold=0.95, select_mode="chunk_vote", kv_chunk_tokens=4096, shared_ranks=True,
+                            rank_step=0.05, ring=True)
+    aux, ref, kh = _ring_128k_check(w, staged=staged)
+    runs = assert_gapped(aux["hist_sel"][0], kh, "128K sparse %s" % ("staged" if staged else "slots"))
+    assert len(runs) >= 10
+    assert torch.equal(aux["hist_sel"][0, :kh].cpu(), torch.from_numpy(ref["hist_sel"][0, :kh]).to(torch.uint8))

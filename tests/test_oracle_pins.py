@@ -488,3 +488,60 @@ def test_well_separated_family_has_wide_margins():
     # most rows clear the 5e-3 margin; none is within fp32 rounding of a flip
     assert np.mean(np.array(margins) >= 5e-3) >= 0.7
     assert min(margins) >= 1e-3
+
+
+def test_selection_margin_hand_computed():
+    """selection_margin against values worked out by hand.  v = (1/8, 1/2,
+    1/8, 1/4) sorts to 1/2, 1/4, 1/8, 1/8 (indices 1, 3, 0, 2) with
+    cumulative sums C = 0, 1/2, 3/4, 7/8, 1 and T = 1."""
+    v = [0.125, 0.5, 0.125, 0.25]
+    # tau = 0.7: keeps 2 (C1 = 1/2 < 0.7 <= C2 = 3/4); margins 0.2, 0.05 and
+    # the gap 1/4 - 1/8 at the cut -> 0.05
+    assert O.selection_margin(v, 0.7) == pytest.approx(0.05, abs=1e-12)
+    # tau = 0.5: keeps 1; C1 = 1/2 sits exactly on tau*T -> 0
+    assert O.selection_margin(v, 0.5) == 0.0
+    # tau = 0.3: keeps 1; margins 0.3, 0.2, gap 1/4 -> 0.2
+    assert O.selection_margin(v, 0.3) == pytest.approx(0.2, abs=1e-12)
+    # equal values at the cut: the order there is a tie -> 0
+    assert O.selection_margin([0.25] * 4, 0.6) == 0.0
+    # everything kept: only the distance below the threshold counts
+    assert O.selection_margin([1.0], 0.9) == pytest.approx(0.9)
+    assert O.selection_margin(v, 1.0) == np.inf
+    # relative: scaling the row leaves it unchanged
+    assert O.selection_margin([8 * x for x in v], 0.7) == pytest.approx(0.05, abs=1e-12)
+
+
+def test_selection_margin_bounds_every_flip():
+    """Any perturbation whose total size sum|dv| stays below half the margin
+    times T leaves the kept set unchanged (the property the GPU mask checks
+    rely on); moving just over the margin times T from one item to another
+    (total size 2.1 m T) changes it, so the bound is tight up to a factor 4."""
+    rng = np.random.default_rng(17)
+    for trial in range(300):
+        n = int(rng.integers(2, 14))
+        v = rng.exponential(1.0, size=n)
+        tau = float(rng.choice([0.3, 0.5, 0.7, 0.9, 0.95]))
+        m = O.selection_margin(v, tau)
+        keep = O.threshold_select_row(v, tau)
+        t = v.sum()
+        for _ in range(20):
+            d = rng.standard_normal(n)
+            d *= 0.49 * m * t / np.abs(d).sum()
+            d = np.maximum(d, -v)  # values stay >= 0
+            assert (O.threshold_select_row(v + d, tau) == keep).all(), (v, tau, m)
+        if 0 < m < np.inf:
+            k = int(keep.sum())
+            flipped = False
+            for a in range(n):
+                for b in range(n):
+                    if a == b or v[b] < 1.05 * m * t:
+                        continue
+                    w = v.copy()
+                    w[a] += 1.05 * m * t
+                    w[b] -= 1.05 * m * t
+                    if not (O.threshold_select_row(w, tau) == keep).all():
+                        flipped = True
+                        break
+                if flipped:
+                    break
+            assert flipped, (v, tau, m, k)

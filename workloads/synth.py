@@ -194,11 +194,18 @@ def make_well_separated(
     kv_chunk_tokens: int = 4096,
     noise: float = 0.05,
     paged: bool = False,
+    shared_ranks: bool = False,
+    rank_step: float = 1.0,
+    ring: bool = False,
 ) -> Workload:
-    """Q[x,h] = sqrt(d) u_g + noise; K[y,g] = pi_g(y // 128) u_g + noise.
+    """Q[x,h] = sqrt(d) u_g + noise; K[y,g] = rank_step * pi_g(y // 128) u_g + noise.
 
     With est_scale = 1/(stride*sqrt(d)) the estimated logit of key block j is
-    close to the integer pi_g(j), so block masses are spaced by factors of e.
+    close to rank_step * pi_g(j), so sorted block masses fall by a factor of
+    e^rank_step from one to the next.  ``shared_ranks`` draws one permutation
+    per sequence for all KV heads (instead of one per head), so the heads
+    agree on the important blocks and a chunk vote keeps them: the voted
+    history is then a scattered subset whose size falls as rank_step grows.
     """
     lq = list(lq)
     lk = list(lk)
@@ -215,13 +222,16 @@ def make_well_separated(
     k = np.empty((cu_k[-1], hkv, d))
     for b in range(len(lq)):
         kb = lk[b] // BLOCK
-        perms = [rng.permutation(kb) for _ in range(hkv)]
+        if shared_ranks:
+            perms = [rng.permutation(kb)] * hkv
+        else:
+            perms = [rng.permutation(kb) for _ in range(hkv)]
         for g in range(hkv):
             for hh in range(group):
                 h = g * group + hh
                 q[cu_q[b]:cu_q[b + 1], h, :] = math.sqrt(d) * u[g]
             ranks = np.repeat(perms[g], BLOCK)[: lk[b]].astype(np.float64)
-            k[cu_k[b]:cu_k[b + 1], g, :] = ranks[:, None] * u[g][None, :]
+            k[cu_k[b]:cu_k[b + 1], g, :] = rank_step * ranks[:, None] * u[g][None, :]
     q += noise * rng.standard_normal(q.shape)
     k += noise * rng.standard_normal(k.shape)
     v = rng.standard_normal((cu_k[-1], hkv, d))
@@ -241,7 +251,8 @@ def make_well_separated(
         threshold=threshold,
         kv_chunk_tokens=kv_chunk_tokens,
         select_mode=select_mode,
-        description="well-separated block ranks",
+        ring=ring,
+        description="well-separated block ranks (step %g%s)" % (rank_step, ", shared by the kv heads" if shared_ranks else ""),
     )
     if paged:
         to_paged(w, rng)
