@@ -210,6 +210,15 @@ def _aux(aux):
     return a
 
 
+def xattn_prefill_chunk_static(shape, params, q, k, v, out, lse, counts, *, aux=None, stream=None):
+    """Resident-K/V prefill on the library's static per-device scratch (no
+    workspace, no device allocation)."""
+    a = _aux(aux)
+    _check(_lib.load().xattn_prefill_chunk_static(
+        ctypes.byref(shape.c), ctypes.byref(params), _ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse),
+        _ptr(counts), ctypes.byref(a) if a is not None else None, _stream(stream)))
+
+
 def xattn_prefill_chunk(shape, params, q, k, v, out, lse, counts, ws, *, aux=None, ring=None,
                         k_hist=None, v_hist=None, hist_blocks=0, stream=None):
     a = _aux(aux)

@@ -33,6 +33,7 @@ EXPORTED = (
     "xattn_attn_run",
     "xattn_merge_attn",
     "xattn_prefill_chunk",
+    "xattn_prefill_chunk_static",
     "xattn_ring_create",
     "xattn_ring_destroy",
     "xattn_ring_create_staged",
@@ -117,6 +118,8 @@ def load():
     lib.xattn_prefill_chunk.argtypes = [vp, sp, pp, vp, vp, vp, vp, vp, ctypes.c_int, vp, vp, vp,
                                         ctypes.POINTER(XattnAux), vp, ctypes.c_size_t, vp]
     lib.xattn_prefill_chunk.restype = ctypes.c_int
+    lib.xattn_prefill_chunk_static.argtypes = [sp, pp, vp, vp, vp, vp, vp, vp, ctypes.POINTER(XattnAux), vp]
+    lib.xattn_prefill_chunk_static.restype = ctypes.c_int
     lib.xattn_ring_create.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
                                       ctypes.POINTER(vp)]
     lib.xattn_ring_create.restype = ctypes.c_int

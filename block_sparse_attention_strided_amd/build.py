@@ -12,7 +12,7 @@ import sys
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
-SOURCES = ["csrc/estimate.hip", "csrc/select.hip", "csrc/attention.hip", "csrc/abi.cpp"]
+SOURCES = ["csrc/estimate.hip", "csrc/select.hip", "csrc/attention.hip", "csrc/abi.cpp", "csrc/prefill_static.hip"]
 LIB = os.path.join(HERE, "libxattn.so")
 BUILD_DIR = os.path.join(ROOT, "_build")
 

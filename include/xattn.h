@@ -226,6 +226,24 @@ int xattn_prefill_chunk(XattnRing *ring, const XattnShape *shape, const XattnPar
                         void *out, float *lse, int32_t *counts, const XattnAux *aux,
                         void *ws, size_t ws_bytes, void *stream);
 
+/* Allocation-free variant of xattn_prefill_chunk with resident K/V (ring ==
+ * NULL), for callers that cannot allocate device memory: code under HIP
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc.  The
+ * library's scratch comes from a fixed per-device array of
+ * XATTN_STATIC_SCRATCH_BYTES instead of a caller workspace; each GPU the
+ * library runs on holds its own copy until the process ends.  The call makes
+ * no device allocation; the caller passes inputs and outputs as for
+ * xattn_prefill_chunk.  Every call on one GPU shares that GPU's array and
+ * leaves its contents behind: calls that overlap in time on one GPU race
+ * (enqueue them on one stream or order them with events).  Errors: as
+ * xattn_prefill_chunk; a shape and params whose xattn_workspace_size exceeds
+ * XATTN_STATIC_SCRATCH_BYTES return XATTN_ERR_UNSUPPORTED (nothing
+ * enqueued). */
+#define XATTN_STATIC_SCRATCH_BYTES (256u << 20)
+int xattn_prefill_chunk_static(const XattnShape *shape, const XattnParams *params, const void *q,
+                               const void *k, const void *v, void *out, float *lse,
+                               int32_t *counts, const XattnAux *aux, void *stream);
+
 /* Device ring of `num_slots` slots of `slot_blocks` 128-token K and V blocks
  * (the design doc's ring-buffer pipeline; 4 slots as in the layerwise
  * offload plan, 1.1).  Owns its slots, one transfer stream (default
