@@ -306,12 +306,35 @@ def _paged3(seed=5):
     )
 
 
+def _chunk32k_sparse_vote(seed=203):
+    w = make_well_separated(
+        "chunked_prefill_32k_sparse_vote",
+        seed=seed, hq=16, hkv=8, d=128, lq=[4096], lk=[32768], stride=8, threshold=0.9,
+        select_mode="chunk_vote", kv_chunk_tokens=4096, shared_ranks=True, rank_step=0.04)
+    w.description = ("the 32K chunk's shape on well-separated inputs whose block ranks the kv heads share "
+                     "(step 0.04): the vote keeps about a quarter of the history")
+    return w
+
+
+def _chunk32k_sparse_kvhead(seed=204):
+    w = make_well_separated(
+        "chunked_prefill_32k_sparse_kvhead",
+        seed=seed, hq=16, hkv=8, d=128, lq=[4096], lk=[32768], stride=8, threshold=0.9,
+        select_mode="per_kvhead", kv_chunk_tokens=4096, shared_ranks=True, rank_step=0.1)
+    w.description = ("the 32K chunk's shape on well-separated inputs (shared ranks, step 0.1), per-KV-head "
+                     "selection: about a tenth of each row's blocks")
+    return w
+
+
 WORKLOADS = {
     "tiny_causal_fp32_1k": _tiny,
     "qwen3_0p6b_4k": _qwen06_4k,
     "chunked_prefill_32k": _chunk32k,
     "qwen3_4b_128k_ring": _ring128k,
     "paged_varlen_3seq": _paged3,
+    # sparse regimes at the 32K shape (measurement stages, not configs)
+    "chunked_prefill_32k_sparse_vote": _chunk32k_sparse_vote,
+    "chunked_prefill_32k_sparse_kvhead": _chunk32k_sparse_kvhead,
 }
 
 
