@@ -375,6 +375,46 @@ def sparse_regime(name, steps, warmup, dev, stream):
     }
 
 
+def reuse_accuracy(dev, mixes=(0.0, 0.2, 0.5, 1.0)):
+    """Selection reuse across layers measured against the layer's own
+    selection: synthetic layer pairs at the 32K shape whose block ranks
+    partly agree (a fraction `mix` of the blocks trade ranks), layer B run
+    once on its own estimate and once on layer A's mask."""
+    import torch
+
+    from workloads import make_layer_pair
+
+    kw = dict(hq=16, hkv=8, d=128, lq=[4096], lk=[32768], stride=8, threshold=0.9, select_mode="chunk_vote",
+              kv_chunk_tokens=4096, rank_step=0.04)
+    rows = []
+    for mix in mixes:
+        wa, wb = make_layer_pair(203, mix, **kw)
+        ca, cb = Case(wa, dev), Case(wb, dev)
+        ca.step()
+        cb.step()
+        torch.cuda.synchronize()
+        own_out, own_lse, own_mask = cb.out.float().clone(), cb.lse.clone(), cb.mask.clone()
+        reuse = cb.X.make_params(stride=wb.stride, threshold=wb.threshold, kv_chunk_tokens=wb.kv_chunk_tokens,
+                                 select_mode=wb.select_mode, reuse_selection=1)
+        cb.step(reuse, {"mask_kv": ca.mask, "hist_sel": ca.hist}, None)
+        torch.cuda.synchronize()
+        err = cb.out.float() - own_out
+        rows.append({
+            "mix": mix,
+            "mask_mismatch": float((ca.mask != own_mask).float().mean()),
+            "density_own": cb.density()[0],
+            "density_reused": ca.density()[0],
+            "out_max_abs_err": float(err.abs().max()),
+            "out_rel_err": float(err.norm() / own_out.norm()),
+            "lse_max_abs_err": float((cb.lse - own_lse).abs().max()),
+        })
+        ca.close()
+        cb.close()
+        del ca, cb
+    return {"workload": "layer pairs at the 32K chunk's shape (well-separated, shared ranks, step 0.04; "
+                        "chunk vote); layer B on its own selection vs on layer A's", "pairs": rows}
+
+
 def main():
     args = parse()
     if args.summarize_profile:
@@ -485,6 +525,7 @@ def main():
     if w.name == "chunked_prefill_32k" and not args.no_sparse_stages:
         res["sparse_regimes"] = [sparse_regime(n, min(args.steps, 50), min(args.warmup, 10), dev, stream)
                                  for n in SPARSE_STAGES]
+        res["reuse_accuracy"] = reuse_accuracy(dev)
     if not args.no_achievable:
         res["achievable"] = achievable_rates(dev)
     if not args.no_cpu_baseline:

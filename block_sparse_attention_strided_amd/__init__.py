@@ -17,13 +17,15 @@ from ._lib import (  # noqa: F401
     GQA_ANY,
     GQA_MAJORITY,
     SELECT_CHUNK_VOTE,
+    SELECT_CHUNK_VOTE_SPARSE,
     SELECT_PER_KVHEAD,
     XattnAux,
     XattnParams,
     XattnShape,
 )
 
-_MODES = {"per_kvhead": SELECT_PER_KVHEAD, "chunk_vote": SELECT_CHUNK_VOTE}
+_MODES = {"per_kvhead": SELECT_PER_KVHEAD, "chunk_vote": SELECT_CHUNK_VOTE,
+          "chunk_vote_sparse": SELECT_CHUNK_VOTE_SPARSE}
 _AGGS = {"any": GQA_ANY, "majority": GQA_MAJORITY}
 
 

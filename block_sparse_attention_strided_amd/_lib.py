@@ -21,6 +21,7 @@ DTYPE_BF16 = 0
 DTYPE_F32 = 1
 SELECT_PER_KVHEAD = 0
 SELECT_CHUNK_VOTE = 1
+SELECT_CHUNK_VOTE_SPARSE = 2
 GQA_ANY = 0
 GQA_MAJORITY = 1
 

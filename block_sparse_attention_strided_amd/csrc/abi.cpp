@@ -108,7 +108,8 @@ int make_plan(const XattnShape* sh, const XattnParams* pr, Plan* p) {
     return fail(XATTN_ERR_INVALID, "softmax_scale must be finite and >= 0 (0 = default)");
   if (pr->kv_chunk_tokens < 0 || pr->kv_chunk_tokens % XATTN_BLOCK != 0)
     return fail(XATTN_ERR_INVALID, "kv_chunk_tokens must be a non-negative multiple of 128");
-  if (pr->select_mode != XATTN_SELECT_PER_KVHEAD && pr->select_mode != XATTN_SELECT_CHUNK_VOTE)
+  if (pr->select_mode != XATTN_SELECT_PER_KVHEAD && pr->select_mode != XATTN_SELECT_CHUNK_VOTE &&
+      pr->select_mode != XATTN_SELECT_CHUNK_VOTE_SPARSE)
     return fail(XATTN_ERR_INVALID, "unknown select_mode %d", pr->select_mode);
   if (pr->group_agg != XATTN_GQA_ANY && pr->group_agg != XATTN_GQA_MAJORITY)
     return fail(XATTN_ERR_INVALID, "unknown group_agg %d", pr->group_agg);
@@ -620,8 +621,8 @@ int prefill_ring(XattnRing* r, const XattnShape* sh, const XattnParams* pr, cons
   if (r->hkv != p.hkv || r->d != p.d || r->dtype != p.dtype)
     return fail(XATTN_ERR_INVALID, "ring geometry (kv heads %d, head_dim %d, dtype %d) does not match the shape",
                 r->hkv, r->d, r->dtype);
-  if (pr->select_mode != XATTN_SELECT_CHUNK_VOTE)
-    return fail(XATTN_ERR_UNSUPPORTED, "ring mode streams the voted history blocks: select_mode must be CHUNK_VOTE");
+  if (pr->select_mode == XATTN_SELECT_PER_KVHEAD)
+    return fail(XATTN_ERR_UNSUPPORTED, "ring mode streams the voted history blocks: select_mode must be a chunk vote");
   const bool reuse = pr->reuse_selection == 1;
   if (reuse && (!aux || !aux->mask_kv || !aux->hist_sel))
     return fail(XATTN_ERR_INVALID, "reuse_selection in ring mode needs aux->mask_kv and aux->hist_sel");
@@ -789,8 +790,8 @@ int prefill_staged(XattnRing* r, const XattnShape* sh, const XattnParams* pr, co
   if (r->hkv != p.hkv || r->d != p.d || r->dtype != p.dtype)
     return fail(XATTN_ERR_INVALID, "ring geometry (kv heads %d, head_dim %d, dtype %d) does not match the shape",
                 r->hkv, r->d, r->dtype);
-  if (pr->select_mode != XATTN_SELECT_CHUNK_VOTE)
-    return fail(XATTN_ERR_UNSUPPORTED, "ring mode streams the voted history blocks: select_mode must be CHUNK_VOTE");
+  if (pr->select_mode == XATTN_SELECT_PER_KVHEAD)
+    return fail(XATTN_ERR_UNSUPPORTED, "ring mode streams the voted history blocks: select_mode must be a chunk vote");
   if (kb > r->slot_blocks)
     return fail(XATTN_ERR_INVALID, "the sequence has %d blocks; the staged ring holds %d", kb, r->slot_blocks);
   const bool reuse = pr->reuse_selection == 1;

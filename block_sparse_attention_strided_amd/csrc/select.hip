@@ -287,9 +287,9 @@ __global__ __launch_bounds__(64 * kSelMaxWaves) void select_group_kernel(SelectA
   const int nthr = 64 * G;
   if (a.select_mode == 0 && i == 0 && g == 0)
     for (int j = tid; j < a.max_kb; j += nthr) a.hist_sel[(long long)b * a.max_kb + j] = 0;
-  // chunk-vote mode: the per-KV-head rows go to the mask_q scratch (same
+  // chunk-vote modes: the per-KV-head rows go to the mask_q scratch (same
   // layout), which chunk_vote_mask_kernel turns into the effective mask_kv
-  uint8_t* const dst = a.select_mode == 1 ? a.mask_q : a.mask_kv;
+  uint8_t* const dst = a.select_mode != 0 ? a.mask_q : a.mask_kv;
   uint8_t* out = dst + (((long long)b * a.hkv + g) * a.max_qb + i) * a.max_kb;
   __shared__ int wcnt[kSelMaxWaves];
   const bool emit = a.lists && a.select_mode == 0;
@@ -418,7 +418,7 @@ __global__ __launch_bounds__(1024) void vote_kernel(SelectArgs a) {
   const int lk = a.cu_k[b + 1] - a.cu_k[b];
   const int qb = lq / kBlock, kh = (lk - lq) / kBlock;
   int votes = 0;
-  if (a.select_mode == 1 && j < kh) {
+  if (a.select_mode != 0 && j < kh) {
     const int nrows = a.hkv * qb;
 #pragma unroll 8
     for (int r = rl; r < nrows; r += 16) {
@@ -430,7 +430,7 @@ __global__ __launch_bounds__(1024) void vote_kernel(SelectArgs a) {
   __syncthreads();
   if (rl == 0 && j < a.max_kb) {
     uint8_t sel = 0;
-    if (a.select_mode == 1 && qb > 0 && j < kh) {
+    if (a.select_mode != 0 && qb > 0 && j < kh) {
       int v = 0;
 #pragma unroll
       for (int x = 0; x < 16; ++x) v += part[x][c];
@@ -440,8 +440,10 @@ __global__ __launch_bounds__(1024) void vote_kernel(SelectArgs a) {
   }
 }
 
-// Chunk-vote mode: effective mask row (g, i): voted history, dense causal
-// current chunk.  One workgroup per (i, g, b).
+// Chunk-vote modes: effective mask row (g, i): voted history; current chunk
+// dense causal (mode 1) or the row's own per-KV-head selection with the sink
+// and the diagonal forced (mode 2, read in place from the aggregated row).
+// One workgroup per (i, g, b).
 __global__ __launch_bounds__(256) void effective_mask_kernel(SelectArgs a) {
   const int i = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
   const int lq = a.cu_q[b + 1] - a.cu_q[b];
@@ -451,7 +453,10 @@ __global__ __launch_bounds__(256) void effective_mask_kernel(SelectArgs a) {
   const uint8_t* hs = a.hist_sel + (long long)b * a.max_kb;
   for (int j = threadIdx.x; j < a.max_kb; j += 256) {
     uint8_t v = 0;
-    if (i < qb && j < kb) v = (j < kh) ? hs[j] : (j <= i + kh ? 1 : 0);
+    if (i < qb && j < kb) {
+      if (j < kh) v = hs[j];
+      else if (j <= i + kh) v = (a.select_mode == 1 || row[j] || j == i + kh || j == 0) ? 1 : 0;
+    }
     row[j] = v;
   }
 }
@@ -500,15 +505,17 @@ __global__ __launch_bounds__(1024) void counts_kernel(SelectArgs a) {
   }
 }
 
-// Chunk-vote mode after select_group_kernel, which left the per-KV-head
+// Chunk-vote modes after select_group_kernel, which left the per-KV-head
 // rows in the mask_q scratch: one workgroup per (q block i, kv head g,
 // sequence b) counts the votes of every history column over the sequence's
 // Hkv*Qb rows itself (16 row lanes x 16 chunks of 16 columns per pass,
 // partial counts met in LDS; the rows are 57 KiB at 32K, read from L2 by
-// every workgroup), then writes its effective mask_kv row (voted history,
-// dense causal current chunk; zeros past the sequence).  Workgroup (0, 0, b)
-// also writes hist_sel and counts = {selected history blocks, history
-// blocks}.  One launch instead of vote + effective mask + counts.
+// every workgroup), then writes its effective mask_kv row (voted history;
+// current chunk dense causal in mode 1, the row's own per-KV-head selection
+// with sink and diagonal forced in mode 2; zeros past the sequence).
+// Workgroup (0, 0, b) also writes hist_sel, and in mode 1 counts =
+// {selected history blocks, history blocks}.  One launch instead of vote +
+// effective mask (+ counts).
 __global__ __launch_bounds__(256) void chunk_vote_mask_kernel(SelectArgs a) {
   extern __shared__ uint8_t hs[];  // max_kb voted history flags
   __shared__ int part[16][256];
@@ -571,11 +578,16 @@ __global__ __launch_bounds__(256) void chunk_vote_mask_kernel(SelectArgs a) {
     }
     __syncthreads();  // part[] reused; hs[] complete after the last pass
   }
-  for (int j = tid; j < a.max_kb; j += 256)
-    out[j] = (i < qb && j < kb) ? ((j < kh) ? hs[j] : (j <= i + kh ? 1 : 0)) : 0;
-  if (a.lists)
-    emit_row_list(a, b, g, i, kh, i < qb ? i + kh + 1 : 0, [&](int j) { return j >= kh || hs[j] != 0; }, wcnt);
-  if (lead && a.counts) {
+  // mode 2: this row's per-KV-head selection (un-forced) for the current chunk
+  const uint8_t* own = a.mask_q + (((long long)b * a.hkv + g) * a.max_qb + i) * a.max_kb;
+  const bool dense_cur = a.select_mode == 1;
+  auto keep = [&](int j) -> bool {
+    if (j < kh) return hs[j] != 0;
+    return j <= i + kh && (dense_cur || own[j] != 0 || j == i + kh || j == 0);
+  };
+  for (int j = tid; j < a.max_kb; j += 256) out[j] = (i < qb && j < kb && keep(j)) ? 1 : 0;
+  if (a.lists) emit_row_list(a, b, g, i, kh, i < qb ? i + kh + 1 : 0, keep, wcnt);
+  if (lead && a.counts && dense_cur) {
     for (int off = 32; off > 0; off >>= 1) mine += __shfl_xor(mine, off, 64);
     if ((tid & 63) == 0) nsel[tid >> 6] = mine;
     __syncthreads();
@@ -611,8 +623,11 @@ hipError_t launch_select(const SelectArgs& a, int batch, hipStream_t s, bool* li
         default: hipLaunchKernelGGL(select_group_kernel<32>, grid, block, fused_lds, s, a, n2); break;
       }
       if ((e = hipGetLastError()) != hipSuccess) return e;
-      if (a.select_mode == 1) {
+      if (a.select_mode != 0) {
         hipLaunchKernelGGL(chunk_vote_mask_kernel, dim3(a.max_qb, a.hkv, batch), dim3(256), (size_t)a.max_kb, s, a);
+        if ((e = hipGetLastError()) != hipSuccess || a.select_mode == 1 || !a.counts) return e;
+        // mode 2: counts over the effective mask (per-KV-head statistics)
+        hipLaunchKernelGGL(counts_kernel, dim3(batch), dim3(1024), 0, s, a);
         return hipGetLastError();
       }
     } else {
@@ -624,11 +639,11 @@ hipError_t launch_select(const SelectArgs& a, int batch, hipStream_t s, bool* li
     }
   }
   // the fused kernel clears hist_sel itself in per-KV-head mode
-  if (a.select_mode == 1 || !fused || a.max_qb == 0) {
+  if (a.select_mode != 0 || !fused || a.max_qb == 0) {
     hipLaunchKernelGGL(vote_kernel, dim3((a.max_kb + 63) / 64, batch), dim3(1024), 0, s, a);
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
-  if (a.select_mode == 1 && a.max_qb > 0) {
+  if (a.select_mode != 0 && a.max_qb > 0) {
     hipLaunchKernelGGL(effective_mask_kernel, dim3(a.max_qb, a.hkv, batch), dim3(256), 0, s, a);
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }

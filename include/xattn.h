@@ -83,6 +83,8 @@ extern "C" {
 /* select_mode */
 #define XATTN_SELECT_PER_KVHEAD 0 /* per (kv head, q block) masks + sink/diagonal */
 #define XATTN_SELECT_CHUNK_VOTE 1 /* history majority vote, dense causal current  */
+#define XATTN_SELECT_CHUNK_VOTE_SPARSE 2 /* history majority vote, current chunk
+                                            per KV head (sink and diagonal kept) */
 /* group_agg: how the q heads of one KV group combine their masks */
 #define XATTN_GQA_ANY 0      /* any head keeps the block (design doc Step 4)   */
 #define XATTN_GQA_MAJORITY 1 /* more than half of the group's heads keep it    */
@@ -165,11 +167,17 @@ int xattn_estimate(const XattnShape *shape, const XattnParams *params, const voi
  *  CHUNK_VOTE: history block j < Kh is kept iff more than half of the Hkv*Qb
  *    (kv head, q block) rows keep it; blocks 0 and Kh-1 are always kept; the
  *    current chunk (j >= Kh) stays dense causal.
+ *  CHUNK_VOTE_SPARSE: history as CHUNK_VOTE; the current chunk as
+ *    PER_KVHEAD (each row keeps its group's selected blocks, the sink and its
+ *    diagonal), the per-KV-head selection the GPU-only mode makes over the
+ *    whole key range ("XAttention Offload Stream Synchronization Fix",
+ *    测试结果).  With no history it equals PER_KVHEAD.
  * Out: mask_kv [batch, Hkv, maxQb, maxKb] uint8 effective attention mask;
  *      hist_sel [batch, maxKb] uint8 (may be NULL; zero in PER_KVHEAD mode);
  *      counts [batch, 2] int32 = {selected, available} (design doc, Density
- *      统计 API): CHUNK_VOTE {sum hist_sel, Kh}; PER_KVHEAD {sum mask_kv,
- *      number of allowed (kv head, q block, block) triples}. */
+ *      统计 API): CHUNK_VOTE {sum hist_sel, Kh}; PER_KVHEAD and
+ *      CHUNK_VOTE_SPARSE {sum mask_kv, number of allowed (kv head, q block,
+ *      block) triples}. */
 int xattn_select(const XattnShape *shape, const XattnParams *params,
                  const float *block_sums, uint8_t *mask_kv, uint8_t *hist_sel,
                  int32_t *counts, void *ws, size_t ws_bytes, void *stream);

@@ -46,6 +46,12 @@ R6  forced blocks: chunk-vote mode forces the first and last history block
 R7  GQA aggregation ANY (default) or MAJORITY (2*count > G).
 R9  the vote runs over history columns only, per sequence.
 R10 chunk-vote mode keeps the current chunk dense causal.
+R23 sparse-current chunk-vote mode (the current chunk selected per KV head,
+    as the GPU-only mode selects over all KV): history columns follow the
+    chunk vote exactly as in R9; current-chunk columns follow the per-KV-head
+    rule (GQA aggregate of the threshold selection, sink and diagonal
+    forced); counts are the per-KV-head statistics over every allowed
+    (kv head, q block, block).  With no history it is per-KV-head mode.
 """
 
 from __future__ import annotations
@@ -60,6 +66,7 @@ BLOCK = 128
 
 PER_KVHEAD = "per_kvhead"
 CHUNK_VOTE = "chunk_vote"
+CHUNK_VOTE_SPARSE = "chunk_vote_sparse"
 AGG_ANY = "any"
 AGG_MAJORITY = "majority"
 
@@ -305,7 +312,7 @@ def select_blocks(bs, *, kh, tau, group, mode, agg=AGG_ANY, num_to_choose=0):
             eff[:, i, i + kh] = True
         eff &= allowed[None]
         counts = (int(eff.sum()), int(hkv * allowed.sum()))
-    elif mode == CHUNK_VOTE:
+    elif mode in (CHUNK_VOTE, CHUNK_VOTE_SPARSE):
         if kh > 0:
             votes = per_kv[:, :, :kh].sum(axis=(0, 1))  # [Kh]
             hist_sel[:kh] = 2 * votes > hkv * qb  # strictly more than half
@@ -313,8 +320,17 @@ def select_blocks(bs, *, kh, tau, group, mode, agg=AGG_ANY, num_to_choose=0):
             hist_sel[kh - 1] = True
         eff = np.zeros((hkv, qb, kb), dtype=bool)
         eff[:, :, :kh] = hist_sel[None, None, :kh]
-        eff[:, :, kh:] = allowed[None, :, kh:]
-        counts = (int(hist_sel.sum()), int(kh))
+        if mode == CHUNK_VOTE:
+            eff[:, :, kh:] = allowed[None, :, kh:]
+            counts = (int(hist_sel.sum()), int(kh))
+        else:
+            # R23: the current chunk per KV head, sink and diagonal forced
+            cur = per_kv.copy()
+            for i in range(qb):
+                cur[:, i, 0] = True
+                cur[:, i, i + kh] = True
+            eff[:, :, kh:] = cur[:, :, kh:] & allowed[None, :, kh:]
+            counts = (int(eff.sum()), int(hkv * allowed.sum()))
     else:
         raise ValueError(mode)
     return {"mask_q": mask_q, "mask_kv": eff, "hist_sel": hist_sel, "counts": counts}
@@ -449,7 +465,8 @@ def prefill(q, k, v, cu_q, cu_k, *, num_kv_heads, stride, block=BLOCK, threshold
     q: [total_q, Hq, d]; k, v: [total_k, Hkv, d] (or paged caches via
     ``block_table``).  ``rows``: optional dict b -> query indices to attend.
     ``pages_order`` evaluates chunk-vote attention as history-then-current
-    with a merge (identical up to rounding to one masked pass).
+    with a merge (identical up to rounding to one masked pass; chunk_vote
+    mode only).
     Returns a dict with block_sums [B,Hq,maxQb,maxKb], mask_q, mask_kv
     [B,Hkv,maxQb,maxKb], hist_sel [B,maxKb], counts [B,2], out
     [total_q,Hq,d], lse [Hq,total_q].

@@ -207,10 +207,11 @@ def check_selection(r, ref, gpu_bs, gpu_mask, gpu_hist=None, label=""):
     under the rule above; returns (mismatch fraction, soft rows, firm rows).
 
     Per-KV-head mode: a (kv head, q block) row must match when all q-head
-    rows of its group are firm.  Chunk-vote mode: with U kv rows holding a
+    rows of its group are firm.  Chunk-vote modes: with U kv rows holding a
     soft q-head row, history block j's vote can move by at most U, so
     hist_sel[j] must match unless that can cross the strict majority; the
-    current chunk is dense causal and must always match."""
+    current chunk must always match when dense causal (chunk_vote) and on
+    firm rows when selected per KV head (chunk_vote_sparse)."""
     w = r.w
     group = w.num_q_heads // w.num_kv_heads
     hkv = w.num_kv_heads
@@ -245,8 +246,13 @@ def check_selection(r, ref, gpu_bs, gpu_mask, gpu_hist=None, label=""):
             bad = (gm != om).any(axis=2) & kv_firm
             assert not bad.any(), "%s: seq %d: %d firm (kv head, q block) rows differ" % (label, b, int(bad.sum()))
         else:
-            # current chunk: dense causal on both sides
-            assert (gm[:, :, kh:] == om[:, :, kh:]).all(), "%s: seq %d: current-chunk mask differs" % (label, b)
+            if r.mode == "chunk_vote":
+                # current chunk: dense causal on both sides
+                assert (gm[:, :, kh:] == om[:, :, kh:]).all(), "%s: seq %d: current-chunk mask differs" % (label, b)
+            else:
+                # current chunk per KV head: firm rows must match
+                bad = (gm[:, :, kh:] != om[:, :, kh:]).any(axis=2) & kv_firm
+                assert not bad.any(), "%s: seq %d: %d firm current-chunk rows differ" % (label, b, int(bad.sum()))
             if kh > 0:
                 u = int((~kv_firm).sum())
                 votes = ref["mask_q"][b, :, :qb, :kh].reshape(hkv, group, qb, kh)

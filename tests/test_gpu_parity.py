@@ -69,7 +69,7 @@ def test_estimate_tiny_fp32_workload():
     assert_block_sums_close(bs, ref, w.stride, "tiny")
 
 
-@pytest.mark.parametrize("mode", ["per_kvhead", "chunk_vote"])
+@pytest.mark.parametrize("mode", ["per_kvhead", "chunk_vote", "chunk_vote_sparse"])
 @pytest.mark.parametrize("agg", ["any", "majority"])
 @pytest.mark.parametrize("tau", [0.0, 0.5, 0.9, 0.95, 1.0])
 def test_select_matches_oracle_bit_exact(mode, agg, tau):
@@ -105,7 +105,7 @@ def test_select_matches_oracle_bit_exact(mode, agg, tau):
     dict(hq=32, hkv=1, lq=[256], lk=[16384]),       # 32 q heads per group: two-kernel path (group size)
     dict(hq=1, hkv=1, lq=[128, 256], lk=[384000, 1024]),  # 3000-block rows: 4096-key sort
 ])
-@pytest.mark.parametrize("mode", ["per_kvhead", "chunk_vote"])
+@pytest.mark.parametrize("mode", ["per_kvhead", "chunk_vote", "chunk_vote_sparse"])
 def test_select_wide_rows_and_groups(case, mode):
     """Selection on seeded block sums (exponential, with ties) for row widths
     and group sizes on both sides of the fused kernel's limits."""
@@ -133,7 +133,7 @@ def test_select_wide_rows_and_groups(case, mode):
     dict(hq=8, hkv=2, lq=[512, 256], lk=[2048, 256]),  # fused kernel
     dict(hq=32, hkv=1, lq=[256], lk=[16384]),           # two-kernel path (group size)
 ])
-@pytest.mark.parametrize("mode", ["per_kvhead", "chunk_vote"])
+@pytest.mark.parametrize("mode", ["per_kvhead", "chunk_vote", "chunk_vote_sparse"])
 def test_select_topk(k, case, mode):
     """Top-k rule (num_to_choose) on seeded block sums with ties, both
     kernel paths, k below, inside and above the row widths."""
@@ -383,6 +383,8 @@ def test_well_separated_masks_bit_exact(seed, mode):
     # per-KV-head rows of about 21 of up to 256 blocks: the attention's row
     # order and splits on short, uneven rows
     dict(name="kvhead_step0.1", mode="per_kvhead", step=0.1),
+    # history by the vote, the current chunk per KV head
+    dict(name="vote_sparse_cur_step0.1", mode="chunk_vote_sparse", step=0.1),
 ], ids=lambda c: c["name"])
 def test_prefill_32k_sparse_selection(case):
     """The 32K chunk (16 q / 8 kv heads, 4096 queries over 32768 keys, s=8,
@@ -396,11 +398,15 @@ def test_prefill_32k_sparse_selection(case):
     mism, counts, aux = _prefill_and_check(w, rows=rows, rows_idx=idx, exact=True, label=w.name)
     dens = O.density(counts.cpu().tolist())
     assert 0.0 < dens < 0.5, "%s: density %.3g is not sparse" % (w.name, dens)
-    if case["mode"] == "chunk_vote":
+    if case["mode"] != "per_kvhead":
         assert_gapped(aux["hist_sel"][0], 224, w.name)
+    if case["mode"] == "chunk_vote_sparse":
+        # the current chunk really is sparse: fewer blocks than dense causal
+        cur = aux["mask_kv"][0, :, :, 224:].cpu().numpy().astype(bool)
+        assert cur.sum() < 8 * sum(i + 1 for i in range(32))
 
 
-@pytest.mark.parametrize("mode", ["per_kvhead", "chunk_vote"])
+@pytest.mark.parametrize("mode", ["per_kvhead", "chunk_vote", "chunk_vote_sparse"])
 @pytest.mark.parametrize("case", [
     dict(name="paged_3seq", hq=4, hkv=2, d=128, lq=[512, 256, 128], lk=[2048, 256, 1536], paged=True),
     dict(name="varlen_with_empty", hq=4, hkv=2, d=128, lq=[384, 0, 256], lk=[1024, 128, 256]),

@@ -63,12 +63,12 @@ SMALL = dict(d=128, lq=[1024], lk=[16384], stride=16, threshold=0.95, select_mod
              kv_chunk_tokens=1024)
 
 
-def _small(kind="sparse", hq=8, hkv=2, seed=41, lk=None):
+def _small(kind="sparse", hq=8, hkv=2, seed=41, lk=None, mode="chunk_vote"):
     """1024 queries over 16K keys (120 history blocks), s=16, tau=0.95.
     sparse: well-separated shared ranks, step 0.3 (the vote keeps 12 of 120
     history blocks in 11 runs); gaussian: planted Gaussian inputs (the vote
     keeps every block)."""
-    kw = dict(SMALL, hq=hq, hkv=hkv)
+    kw = dict(SMALL, hq=hq, hkv=hkv, select_mode=mode)
     if lk is not None:
         kw["lk"] = [lk]
     if kind == "gaussian":
@@ -76,13 +76,15 @@ def _small(kind="sparse", hq=8, hkv=2, seed=41, lk=None):
     return make_well_separated("ring_small_sparse", seed=seed, shared_ranks=True, rank_step=0.3, **kw)
 
 
-@pytest.mark.parametrize("kind,hq,slots", [
-    ("sparse", 8, 4), ("sparse", 8, 2), ("sparse", 6, 4), ("gaussian", 8, 4)],
-    ids=["sparse-g4-4slots", "sparse-g4-2slots", "sparse-g3-4slots", "gaussian-g4-4slots"])
-def test_ring_matches_resident_path_and_oracle(kind, hq, slots):
+@pytest.mark.parametrize("kind,hq,slots,mode", [
+    ("sparse", 8, 4, "chunk_vote"), ("sparse", 8, 2, "chunk_vote"), ("sparse", 6, 4, "chunk_vote"),
+    ("gaussian", 8, 4, "chunk_vote"), ("sparse", 8, 4, "chunk_vote_sparse")],
+    ids=["sparse-g4-4slots", "sparse-g4-2slots", "sparse-g3-4slots", "gaussian-g4-4slots", "sparse-cur-g4-4slots"])
+def test_ring_matches_resident_path_and_oracle(kind, hq, slots, mode):
     """Group 3 (hq=6, hkv=2) runs the single-phase attention kernel, which
-    reads V^T pages of each slot."""
-    w = _small(kind, hq=hq)
+    reads V^T pages of each slot; chunk_vote_sparse also selects inside the
+    resident current chunk."""
+    w = _small(kind, hq=hq, mode=mode)
     r = Run(w)
     k_hist, v_hist, k_cur, v_cur, kh = _ring_inputs(w)
     ring = X.Ring(slots, 8, w.num_kv_heads, w.head_dim, w.dtype)

@@ -342,6 +342,49 @@ def test_per_kvhead_forces_sink_and_diagonal():
     assert sel["counts"] == (6, 3 + 4)
 
 
+def test_sparse_current_chunk_vote_hand_worked():
+    """Sparse-current chunk vote (R23) on a toy worked by hand: Hkv = G = 1,
+    Qb = 2, Kh = 4, tau = 0.5.  Row 0 (blocks 0..4) = .05 .6 .05 .05 .25
+    keeps block 1 only (the sum before the second-largest is .6 >= .5); row
+    1 (blocks 0..5) = .05 .55 .05 .05 .1 .2 keeps block 1 only.  Votes: block
+    1 has 2 of 2 (> 1), block 2 has 0; blocks 0 and Kh-1 = 3 are forced ->
+    history 1 1 0 1.  Current chunk: row 0 sees block 4, its diagonal
+    (forced); row 1 sees blocks 4 and 5: block 4 was not selected (the
+    chunk-vote mode would keep it), block 5 is its diagonal."""
+    kh, qb, kb = 4, 2, 6
+    bs = np.zeros((1, qb, kb))
+    bs[0, 0, :5] = [0.05, 0.6, 0.05, 0.05, 0.25]
+    bs[0, 1, :6] = [0.05, 0.55, 0.05, 0.05, 0.1, 0.2]
+    sel = O.select_blocks(bs, kh=kh, tau=0.5, group=1, mode=O.CHUNK_VOTE_SPARSE)
+    assert sel["hist_sel"][:kh].tolist() == [True, True, False, True]
+    assert sel["mask_kv"][0, 0].tolist() == [True, True, False, True, True, False]
+    assert sel["mask_kv"][0, 1].tolist() == [True, True, False, True, False, True]
+    assert sel["counts"] == (8, 11)
+    dense = O.select_blocks(bs, kh=kh, tau=0.5, group=1, mode=O.CHUNK_VOTE)
+    assert dense["mask_kv"][0, 1].tolist() == [True, True, False, True, True, True]
+
+
+@pytest.mark.parametrize("agg", [O.AGG_ANY, O.AGG_MAJORITY])
+def test_sparse_current_chunk_vote_is_vote_history_plus_kvhead_current(agg):
+    """On random block sums: history columns and hist_sel equal the chunk
+    vote's, current-chunk columns equal per-KV-head mode's; with no history
+    the whole result (mask and counts) is per-KV-head mode's."""
+    rng = np.random.default_rng(31)
+    for kh, qb, hq, g in ((5, 3, 4, 2), (0, 4, 6, 3), (1, 2, 2, 1), (12, 2, 8, 4)):
+        kb = kh + qb
+        bs = rng.exponential(1.0, size=(hq, qb, kb))
+        for tau in (0.3, 0.8):
+            sp = O.select_blocks(bs, kh=kh, tau=tau, group=g, mode=O.CHUNK_VOTE_SPARSE, agg=agg)
+            cv = O.select_blocks(bs, kh=kh, tau=tau, group=g, mode=O.CHUNK_VOTE, agg=agg)
+            pk = O.select_blocks(bs, kh=kh, tau=tau, group=g, mode=O.PER_KVHEAD, agg=agg)
+            assert (sp["hist_sel"] == cv["hist_sel"]).all()
+            assert (sp["mask_kv"][:, :, :kh] == cv["mask_kv"][:, :, :kh]).all()
+            assert (sp["mask_kv"][:, :, kh:] == pk["mask_kv"][:, :, kh:]).all()
+            if kh == 0:
+                assert (sp["mask_kv"] == pk["mask_kv"]).all() and sp["counts"] == pk["counts"]
+            assert sp["counts"] == (int(sp["mask_kv"].sum()), pk["counts"][1])
+
+
 # ------------------------------------------------------------ O7 / O8
 
 def _sdpa_causal(q, k, v, scale):
@@ -359,7 +402,7 @@ def _sdpa_causal(q, k, v, scale):
     return out.permute(1, 0, 2).numpy(), lse.numpy()
 
 
-@pytest.mark.parametrize("mode", [O.PER_KVHEAD, O.CHUNK_VOTE])
+@pytest.mark.parametrize("mode", [O.PER_KVHEAD, O.CHUNK_VOTE, O.CHUNK_VOTE_SPARSE])
 def test_tau_one_is_full_causal_attention(mode):
     lq, lk, hq, hkv, d = 256, 640, 4, 2, 32
     q = _rand((lq, hq, d), 20)

@@ -9,6 +9,7 @@ the same tensors without sharing any code that computes a result.
 from .synth import (  # noqa: F401
     WORKLOADS,
     Workload,
+    make_layer_pair,
     make_workload,
     make_random,
     make_well_separated,

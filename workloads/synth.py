@@ -197,6 +197,7 @@ def make_well_separated(
     shared_ranks: bool = False,
     rank_step: float = 1.0,
     ring: bool = False,
+    perms: Optional[list] = None,
 ) -> Workload:
     """Q[x,h] = sqrt(d) u_g + noise; K[y,g] = rank_step * pi_g(y // 128) u_g + noise.
 
@@ -223,14 +224,16 @@ def make_well_separated(
     for b in range(len(lq)):
         kb = lk[b] // BLOCK
         if shared_ranks:
-            perms = [rng.permutation(kb)] * hkv
+            seq_perms = [rng.permutation(kb)] * hkv
         else:
-            perms = [rng.permutation(kb) for _ in range(hkv)]
+            seq_perms = [rng.permutation(kb) for _ in range(hkv)]
+        if perms is not None:  # given ranks (the draws above keep the stream aligned)
+            seq_perms = [np.asarray(perms[b])] * hkv
         for g in range(hkv):
             for hh in range(group):
                 h = g * group + hh
                 q[cu_q[b]:cu_q[b + 1], h, :] = math.sqrt(d) * u[g]
-            ranks = np.repeat(perms[g], BLOCK)[: lk[b]].astype(np.float64)
+            ranks = np.repeat(seq_perms[g], BLOCK)[: lk[b]].astype(np.float64)
             k[cu_k[b]:cu_k[b + 1], g, :] = rank_step * ranks[:, None] * u[g][None, :]
     q += noise * rng.standard_normal(q.shape)
     k += noise * rng.standard_normal(k.shape)
@@ -257,6 +260,26 @@ def make_well_separated(
     if paged:
         to_paged(w, rng)
     return w
+
+
+def make_layer_pair(seed: int, mix: float, **kw):
+    """Two layers of one sequence whose important blocks partly agree: layer
+    A is make_well_separated with shared ranks; layer B draws its own Q/K/V
+    (seed + 1) with A's block ranks, except that a fraction ``mix`` of the
+    blocks trade their ranks among themselves (0: the same ranks, 1: ranks
+    unrelated to A's).  Single sequence; kw as make_well_separated."""
+    wa = make_well_separated("layer_a", seed=seed, shared_ranks=True, **kw)
+    lk = list(kw["lk"])[0]
+    kb = lk // BLOCK
+    ra = np.random.default_rng(seed)
+    ra.standard_normal((kw["hkv"], kw["d"]))  # the draw of A's directions
+    pa = ra.permutation(kb)  # A's shared ranks (first permutation drawn)
+    rng = np.random.default_rng(seed + 1000)
+    moved = rng.choice(kb, size=int(round(mix * kb)), replace=False)
+    pb = pa.copy()
+    pb[moved] = pa[rng.permutation(moved)]
+    wb = make_well_separated("layer_b", seed=seed + 1, shared_ranks=True, perms=[pb], **kw)
+    return wa, wb
 
 
 def _tiny(seed=1):
