@@ -73,6 +73,8 @@ struct Plan {
   size_t off_ctr;  // attention's tail-part counter (4 bytes)
   int num_pages;  // 128-key pages of the K/V arrays (contiguous or paged)
   bool reads_vt;  // some attention launch reads V^T pages (off_vt holds them)
+  int f32_splits;           // fp32 attention: key-block parts per row (1: none)
+  size_t off_f32o, off_f32l;  // their partial outputs and LSEs
   size_t total;
 };
 
@@ -185,6 +187,15 @@ int make_plan(const XattnShape* sh, const XattnParams* pr, Plan* p) {
   off = align_up(off + B * p->hkv * (size_t)p->max_qb * (p->max_kb + 1) * sizeof(int32_t));
   p->off_ctr = off;
   off = align_up(off + sizeof(int32_t));
+  // fp32 attention: partials of the rows' key-block splits
+  p->f32_splits = p->dtype == XATTN_DTYPE_F32 ? f32_attention_splits((long long)p->max_qb * p->hq * p->batch) : 1;
+  p->off_f32o = p->off_f32l = off;
+  if (p->f32_splits > 1) {
+    p->off_f32o = off;
+    off = align_up(off + (size_t)p->f32_splits * p->total_q * p->hq * p->d * sizeof(float));
+    p->off_f32l = off;
+    off = align_up(off + (size_t)p->f32_splits * p->hq * p->total_q * sizeof(float));
+  }
   p->total = off;
   return XATTN_OK;
 }
@@ -309,6 +320,9 @@ AttnArgs attn_args(const XattnShape* sh, const Plan& p, const void* q, KvView kv
   aa.lists = nullptr;
   aa.num_pages = p.num_pages;
   aa.n_order = 0;
+  aa.f32_splits = 1;
+  aa.f32_o = nullptr;
+  aa.f32_l = nullptr;
   for (int x = 0; x < 3; ++x) {
     aa.split_o[x] = nullptr;
     aa.split_l[x] = nullptr;
@@ -513,6 +527,9 @@ void set_order(const XattnShape* sh, const Plan& p, AttnArgs& aa, void* ws, Spli
 hipError_t launch_planned(const XattnShape* sh, const Plan& p, AttnArgs aa, void* ws, hipStream_t st) {
   aa.vt = ws_at<char>(ws, p.off_vt);
   aa.lists = ws_at<int32_t>(ws, p.off_lists);
+  aa.f32_splits = p.f32_splits;
+  aa.f32_o = ws_at<float>(ws, p.off_f32o);
+  aa.f32_l = ws_at<float>(ws, p.off_f32l);
   SplitMergeArgs sm;
   sm.n = 0;
   if (p.dtype == XATTN_DTYPE_BF16) set_order(sh, p, aa, ws, &sm);

@@ -1070,7 +1070,10 @@ struct BlockIter {
 };
 
 // ---------------------------------------------------------------------------
-// fp32 inputs: one thread per query, key tiles of 32 staged in LDS.
+// fp32 inputs: one thread per query, key tiles of 32 staged in LDS.  With
+// f32_splits = S > 1, blockIdx.z = b * S + s and the workgroup takes the
+// s-th contiguous part of the row's candidate key blocks, writing a partial
+// (normalised output, LSE) for merge_f32_kernel.
 // ---------------------------------------------------------------------------
 template <int D>
 __global__ __launch_bounds__(128) void attn_f32(AttnArgs a) {
@@ -1078,7 +1081,8 @@ __global__ __launch_bounds__(128) void attn_f32(AttnArgs a) {
   __shared__ __align__(16) float ks[KT * D];
   __shared__ __align__(16) float vs[KT * D];
   const int i = a.max_qb - 1 - blockIdx.x;
-  const int h = blockIdx.y, b = blockIdx.z;
+  const int ns = a.f32_splits;
+  const int h = blockIdx.y, b = blockIdx.z / ns, sp = blockIdx.z % ns;
   const int g = h / a.group;
   const int q0 = a.cu_q[b];
   const int lq = a.cu_q[b + 1] - q0;
@@ -1093,7 +1097,14 @@ __global__ __launch_bounds__(128) void attn_f32(AttnArgs a) {
   it.mrow = a.mask + (((long long)b * (a.hq / a.group) + g) * a.max_qb + i) * a.max_kb;
   it.table = a.k.block_table ? a.k.block_table + (long long)b * a.k.max_blocks : nullptr;
   it.num_pages = a.k.num_pages;
-  it.jend = min(a.jb1, i + kh + 1);
+  const int jend = min(a.jb1, i + kh + 1);
+  int jb0 = a.jb0;
+  it.jend = jend;
+  if (ns > 1) {
+    const int n = max(0, jend - a.jb0);
+    jb0 = a.jb0 + (int)(((long long)sp * n) / ns);
+    it.jend = a.jb0 + (int)(((long long)(sp + 1) * n) / ns);
+  }
 
   float qv[D];
   const float* qrow = (const float*)a.q + ((long long)(q0 + x) * a.hq + h) * D;
@@ -1104,7 +1115,7 @@ __global__ __launch_bounds__(128) void attn_f32(AttnArgs a) {
   for (int e = 0; e < D; ++e) acc[e] = 0.f;
   float m_run = kNegInf, l_run = 0.f;
 
-  for (int j = it.next(a.jb0); j < it.jend; j = it.next(j + 1)) {
+  for (int j = it.next(jb0); j < it.jend; j = it.next(j + 1)) {
     const bool diag = (j == i + kh);
     for (int t0 = 0; t0 < kBlock; t0 += KT) {
       __syncthreads();
@@ -1140,10 +1151,51 @@ __global__ __launch_bounds__(128) void attn_f32(AttnArgs a) {
   }
   const float inv = (l_run > 0.f) ? 1.f / l_run : 0.f;
   const long long orow = ((long long)(q0 + x) * a.hq + h) * D;
-  float* out = a.out_f32 ? a.out_f32 : (float*)a.out;
+  float* out = ns > 1 ? a.f32_o + (long long)sp * a.total_q * a.hq * D : (a.out_f32 ? a.out_f32 : (float*)a.out);
+  float* lse = ns > 1 ? a.f32_l + (long long)sp * a.hq * a.total_q : a.lse;
 #pragma unroll
   for (int e = 0; e < D; ++e) out[orow + e] = acc[e] * inv;
-  if (a.lse) a.lse[(long long)h * a.total_q + q0 + x] = (l_run > 0.f) ? (m_run + log2f(l_run)) * kLn2 : kNegInf;
+  if (lse) lse[(long long)h * a.total_q + q0 + x] = (l_run > 0.f) ? (m_run + log2f(l_run)) * kLn2 : kNegInf;
+}
+
+// Merge of the f32_splits partials of the fp32 attention: one thread per
+// (query, head) row, over the query rows of every q block the launch
+// covered (rows of sequences' q blocks only; others are never written).
+// lse = M + log(sum_s e^(lse_s - M)), out = sum_s e^(lse_s - lse) o_s; a row
+// whose parts all saw no key gets out 0 and lse -inf, as unsplit.
+template <int D>
+__global__ __launch_bounds__(256) void merge_f32_kernel(AttnArgs a) {
+  const long long t = (long long)blockIdx.x * 256 + threadIdx.x;
+  if (t >= (long long)a.total_q * a.hq) return;
+  const int h = (int)(t % a.hq);
+  const long long xq = t / a.hq;
+  const int ns = a.f32_splits;
+  const long long plane_o = (long long)a.total_q * a.hq * D, plane_l = (long long)a.hq * a.total_q;
+  float l[8];
+  float mx = kNegInf;
+  for (int s = 0; s < ns; ++s) {
+    l[s] = a.f32_l[s * plane_l + (long long)h * a.total_q + xq];
+    mx = fmaxf(mx, l[s]);
+  }
+  float w[8];
+  float tot = 0.f;
+  for (int s = 0; s < ns; ++s) {
+    w[s] = (mx == kNegInf || l[s] == kNegInf) ? 0.f : expf(l[s] - mx);
+    tot += w[s];
+  }
+  const float inv = tot > 0.f ? 1.f / tot : 0.f;
+  float* out = a.out_f32 ? a.out_f32 : (float*)a.out;
+  const long long orow = xq * a.hq * D + (long long)h * D;
+  for (int e = 0; e < D; e += 4) {
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    for (int s = 0; s < ns; ++s) {
+      if (w[s] == 0.f) continue;
+      const f32x4 o = *(const f32x4*)(a.f32_o + s * plane_o + orow + e);
+      acc += o * (w[s] * inv);
+    }
+    *(f32x4*)(out + orow + e) = acc;
+  }
+  if (a.lse) a.lse[(long long)h * a.total_q + xq] = tot > 0.f ? mx + logf(tot) : kNegInf;
 }
 
 // ---------------------------------------------------------------------------
@@ -1264,8 +1316,12 @@ hipError_t attn_dispatch(const AttnArgs& a, int dtype, int batch, hipStream_t s)
     else if (hpw == 2) hipLaunchKernelGGL((attn_mfma<D, 2>), dim3(nwg), dim3(512), shm, s, a, hkv);
     else hipLaunchKernelGGL((attn_mfma<D, 1>), dim3(nwg), dim3(256), shm, s, a, hkv);
   } else {
-    dim3 grid(a.max_qb, a.hq, batch);
+    dim3 grid(a.max_qb, a.hq, batch * max(1, a.f32_splits));
     hipLaunchKernelGGL((attn_f32<D>), grid, dim3(128), 0, s, a);
+    if (a.f32_splits > 1) {
+      const long long n = (long long)a.total_q * a.hq;
+      hipLaunchKernelGGL((merge_f32_kernel<D>), dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, a);
+    }
   }
   return hipGetLastError();
 }

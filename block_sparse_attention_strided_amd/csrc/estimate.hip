@@ -190,6 +190,20 @@ __device__ __forceinline__ void est_copy_rows(__amdgpu_buffer_rsrc_t r, char* ld
     __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_ptr)(lds + n * 1024), 16, voff[n], soff, 0, 0);
 }
 
+// Maximum and sum of v over the lane pair (l, l ^ 32) -- the two halves of a
+// 32-column MFMA accumulator row.  v_permlane32_swap of v with itself leaves
+// one lane's own value and its partner's in the two results (which is which
+// depends on the half); max and sum treat them alike, and a + b == b + a
+// exactly, so both lanes get identical bits.
+__device__ __forceinline__ float pair_max(float v) {
+  const auto p = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __builtin_elementwise_maximum(__uint_as_float(p[0]), __uint_as_float(p[1]));
+}
+__device__ __forceinline__ float pair_sum(float v) {
+  const auto p = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(p[0]) + __uint_as_float(p[1]);
+}
+
 constexpr int kEstBig = 256;
 #ifndef XATTN_EST_NBUF
 #define XATTN_EST_NBUF 4  // stage buffers of the 128 x 128 tile kernel
@@ -402,10 +416,13 @@ __global__ __launch_bounds__(64 * NW) void est_gemm_bf16(EstArgs a) {
   }
 
   // ---- epilogue: per (query row, key block) base-2 log-sum-exp over the
-  // block's allowed columns; a block's columns are split between lanes l
-  // and l ^ 32, combined with one swap of the (max, sum) pair
+  // block's allowed columns.  A block's columns are split between lanes l and
+  // l ^ 32: the pair first agrees on the block's maximum (one swap of the two
+  // halves' maxima), each lane sums 2^(z - max) over its half, and one more
+  // swap adds the two sums, so lse = max + log2(sum of both halves).
   constexpr int NBLK = 32 / RB;  // key blocks per 32-column accumulator
   constexpr int EPB = 16 / NBLK; // accumulator values per lane and block
+  static_assert(EPB % 2 == 0, "max tree pairs");
   const int j_end = a.jb0 + a.jb_count;
   // Whole tile inside the rows, the launch's columns and the causal bound
   // (the common case): no per-element masks.  Exponentials and logarithm
@@ -414,6 +431,9 @@ __global__ __launch_bounds__(64 * NW) void est_gemm_bf16(EstArgs a) {
   // to zero changes nothing at fp32 resolution.
   const bool unmasked = (r0 + TT <= R) && (c0 + TT <= c_end) && (c0 + TT - 1 <= r0 + o_s);
   const float sc = a.scale2;
+  auto mx3 = [](float p, float q, float r) {
+    return __builtin_elementwise_maximum(__builtin_elementwise_maximum(p, q), r);
+  };
 #pragma unroll
   for (int y = 0; y < YT; ++y) {
     const int r = r0 + wr * (YT * 32) + y * 32 + l32;
@@ -422,16 +442,23 @@ __global__ __launch_bounds__(64 * NW) void est_gemm_bf16(EstArgs a) {
       const int cblk = c0 + wc * (TT / 2) + x * 32;
 #pragma unroll
       for (int m = 0; m < NBLK; ++m) {
-        float mx = kNegInf, sm = 0.f;
+        float lse = kNegInf;
         if (unmasked) {
+          // max of the lane's EPB raw scores (sc > 0 keeps the order), then of the pair
           float am = acc[x][y][m * EPB];
+          int q = 1;
 #pragma unroll
-          for (int q = 1; q < EPB; ++q) am = fmaxf(am, acc[x][y][m * EPB + q]);
-          mx = am * sc;
+          for (; q + 1 < EPB; q += 2) am = mx3(am, acc[x][y][m * EPB + q], acc[x][y][m * EPB + q + 1]);
 #pragma unroll
-          for (int q = 0; q < EPB; ++q) sm += __builtin_amdgcn_exp2f(fmaf(acc[x][y][m * EPB + q], sc, -mx));
+          for (; q < EPB; ++q) am = __builtin_elementwise_maximum(am, acc[x][y][m * EPB + q]);
+          const float mxs = pair_max(am) * sc;
+          float sm = 0.f;
+#pragma unroll
+          for (int e = 0; e < EPB; ++e) sm += __builtin_amdgcn_exp2f(fmaf(acc[x][y][m * EPB + e], sc, -mxs));
+          lse = mxs + __builtin_amdgcn_logf(pair_sum(sm));
         } else {
           float z[EPB];
+          float mx = kNegInf;
 #pragma unroll
           for (int q = 0; q < EPB; ++q) {
             const int e = m * EPB + q;
@@ -440,21 +467,14 @@ __global__ __launch_bounds__(64 * NW) void est_gemm_bf16(EstArgs a) {
             z[q] = ok ? acc[x][y][e] * sc : kNegInf;
             mx = fmaxf(mx, z[q]);
           }
-          if (mx != kNegInf) {
+          const float M = pair_max(mx);
+          float sm = 0.f;
+          if (M != kNegInf) {
 #pragma unroll
-            for (int q = 0; q < EPB; ++q) sm += __builtin_amdgcn_exp2f(z[q] - mx);
+            for (int q = 0; q < EPB; ++q) sm += __builtin_amdgcn_exp2f(z[q] - M);
           }
-        }
-        const auto pm = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx), false, false);
-        const auto ps = __builtin_amdgcn_permlane32_swap(__float_as_uint(sm), __float_as_uint(sm), false, false);
-        const float m0 = __uint_as_float(pm[0]), m1 = __uint_as_float(pm[1]);
-        const float s0 = __uint_as_float(ps[0]), s1 = __uint_as_float(ps[1]);
-        const float M = fmaxf(m0, m1);
-        float lse = kNegInf;
-        if (M != kNegInf) {
-          const float tot = (m0 == kNegInf ? 0.f : s0 * __builtin_amdgcn_exp2f(m0 - M)) +
-                            (m1 == kNegInf ? 0.f : s1 * __builtin_amdgcn_exp2f(m1 - M));
-          lse = M + __builtin_amdgcn_logf(tot);
+          const float tot = pair_sum(sm);
+          if (M != kNegInf) lse = M + __builtin_amdgcn_logf(tot);
         }
         const int j = cblk / RB + m;
         if (hh == 0 && r < R && j < j_end && j * RB < C)

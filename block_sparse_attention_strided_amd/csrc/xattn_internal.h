@@ -157,7 +157,20 @@ struct AttnArgs {
   void* out;          // [total_q, hq, d] dtype   (nullptr if partial)
   float* out_f32;     // [total_q, hq, d] fp32    (nullptr if final)
   float* lse;         // [hq, total_q] natural log (may be nullptr)
+  // fp32 path: f32_splits > 1 workgroups share each (q block, head) row,
+  // part s taking a contiguous s-th of the row's key blocks; part s writes
+  // its normalised output and natural-log LSE to f32_o + s*total_q*hq*d and
+  // f32_l + s*hq*total_q, and a merge writes the result.
+  int f32_splits;
+  float* f32_o;
+  float* f32_l;
 };
+
+// Key-block splits of the fp32 attention for a launch of `rows` (q block,
+// head, sequence) rows: enough workgroups for a 256-CU chip (at most 8).
+constexpr int f32_attention_splits(long long rows) {
+  return rows <= 0 ? 1 : (rows >= 512 ? 1 : (int)(512 / rows < 8 ? 512 / rows : 8));
+}
 
 constexpr uint32_t order_entry(int b, int i, int s, int ns) {
   return (uint32_t)i | ((uint32_t)b << 16) | ((uint32_t)s << 28) | ((uint32_t)(ns - 1) << 30);
