@@ -321,6 +321,7 @@ AttnArgs attn_args(const XattnShape* sh, const Plan& p, const void* q, KvView kv
   aa.num_pages = p.num_pages;
   aa.n_order = 0;
   aa.f32_splits = 1;
+  aa.split_whole = 0;
   aa.f32_o = nullptr;
   aa.f32_l = nullptr;
   for (int x = 0; x < 3; ++x) {
@@ -409,6 +410,7 @@ int device_cu_count() {
 void set_order(const XattnShape* sh, const Plan& p, AttnArgs& aa, void* ws, SplitMergeArgs* sm) {
   sm->n = 0;
   aa.n_order = 0;
+  aa.split_whole = 0;
   aa.n_static = 0;
   aa.tail_ctr = nullptr;
   struct Row {
@@ -471,7 +473,10 @@ void set_order(const XattnShape* sh, const Plan& p, AttnArgs& aa, void* ws, Spli
       items.push_back({-r.len, order_entry(r.b, r.i, 0, 1), 0});
     }
     if (ns > 1) {
-      if (nsplit < kMaxOrder) sm->rows[nsplit] = (sh->cu_q_host[r.b] / XATTN_BLOCK + r.i) | ((ns - 1) << 28);
+      if (nsplit < kMaxOrder) {
+        sm->rows[nsplit] = (sh->cu_q_host[r.b] / XATTN_BLOCK + r.i) | ((ns - 1) << 28);
+        sm->row_bi[nsplit] = (r.b << 16) | r.i;
+      }
       ++nsplit;
     }
   }
@@ -516,6 +521,12 @@ void set_order(const XattnShape* sh, const Plan& p, AttnArgs& aa, void* ws, Spli
       sm->l[x] = aa.split_l[x];
     }
     sm->n = nsplit;
+    sm->lists = ws_at<int32_t>(ws, p.off_lists);
+    sm->group = p.hq / p.hkv;
+    sm->max_qb = p.max_qb;
+    sm->max_kb = p.max_kb;
+    // rows whose selection kept no more than a part's share are done whole
+    sm->whole = aa.split_whole = bmax > 0 ? bmax : head;
     sm->heads = p.hq;
     sm->head_dim = p.d;
     sm->total_q = p.total_q;

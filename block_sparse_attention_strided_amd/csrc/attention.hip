@@ -205,11 +205,20 @@ __device__ __forceinline__ WorkUnit work_unit(const AttnArgs& a, int hkv, int np
 // (count * cut) / 256 entries and the rest; the diagonal block (the last
 // entry) falls in the last part.  The caller synchronises before reading
 // `list`.
+// A row cut into ns > 1 parts whose list holds at most `whole` entries (the
+// selection kept few of its blocks) is done whole by part 0, which writes the
+// final output; its other parts are empty and the split merge skips the row
+// (split_row_whole).
+__device__ __forceinline__ bool split_row_whole(int nall, int ns, int whole) { return ns > 1 && nall <= whole; }
+
 __device__ __forceinline__ int load_row_list(const int32_t* glist, int32_t* list, int s, int ns, int cut, int tid,
-                                             int nthreads) {
+                                             int nthreads, int whole) {
   const int nall = glist[0];
   int z0, n;
-  if (ns == 2 && cut > 0) {
+  if (split_row_whole(nall, ns, whole)) {
+    z0 = 0;
+    n = s == 0 ? nall : 0;
+  } else if (ns == 2 && cut > 0) {
     const int c = (nall * cut) >> 8;
     z0 = s ? c : 0;
     n = s ? nall - c : c;
@@ -323,8 +332,10 @@ __global__ __launch_bounds__(256 * HPW) void attn_mfma(AttnArgs a, int hkv) {
 
   // Block list of this row, copied to LDS.
   const int32_t* glist = a.lists + (((long long)b * hkv + g) * a.max_qb + i) * (a.max_kb + 1);
-  const int nblk = load_row_list(glist, list, wk.s, wk.ns, wk.cut, tid, 64 * NW);
+  const int nblk = load_row_list(glist, list, wk.s, wk.ns, wk.cut, tid, 64 * NW, a.split_whole);
+  const bool whole = split_row_whole(glist[0], wk.ns, a.split_whole);
   __syncthreads();
+  if (whole && wk.s > 0) return;  // part 0 does the whole row
   const int ntile = 2 * nblk;
   // The diagonal block, if present, is the last entry: only its two tiles
   // need the causal mask.
@@ -520,8 +531,8 @@ __global__ __launch_bounds__(256 * HPW) void attn_mfma(AttnArgs a, int hkv) {
   const float l_tot = l_run + __shfl_xor(l_run, 32, 64);
   const float inv = (l_tot > 0.f) ? 1.f / l_tot : 0.f;
   const long long orow = ((long long)(q0 + x) * a.hq + h) * D;
-  float* const of32 = wk.ns > 1 ? a.split_o[wk.s] : a.out_f32;
-  float* const lsep = wk.ns > 1 ? a.split_l[wk.s] : a.lse;
+  float* const of32 = (wk.ns > 1 && !whole) ? a.split_o[wk.s] : a.out_f32;
+  float* const lsep = (wk.ns > 1 && !whole) ? a.split_l[wk.s] : a.lse;
 #pragma unroll
   for (int n = 0; n < D / 32; ++n)
 #pragma unroll
@@ -607,8 +618,11 @@ __global__ __launch_bounds__(512) void attn_pp(AttnArgs a, int hkv) {
 
     // Block list of this row, copied to LDS.
     const int32_t* glist = a.lists + (((long long)b * hkv + g) * a.max_qb + i) * (a.max_kb + 1);
-    const int nblk = __builtin_amdgcn_readfirstlane(load_row_list(glist, list, wk.s, wk.ns, wk.cut, tid, 64 * NW));
+    const int nblk =
+        __builtin_amdgcn_readfirstlane(load_row_list(glist, list, wk.s, wk.ns, wk.cut, tid, 64 * NW, a.split_whole));
+    const bool whole = split_row_whole(__builtin_amdgcn_readfirstlane(glist[0]), wk.ns, a.split_whole);
     __syncthreads();
+    if (whole && wk.s > 0) return;  // part 0 does the whole row
     const int ntile = 2 * nblk;
     // The diagonal block, if present, is the last entry: only its two tiles
     // need the causal mask.
@@ -1006,8 +1020,8 @@ __global__ __launch_bounds__(512) void attn_pp(AttnArgs a, int hkv) {
     const float l_tot = half_sum(l_run);
     const float inv = (l_tot > 0.f) ? 1.f / l_tot : 0.f;
     const long long orow = ((long long)(q0 + x) * a.hq + h) * D;
-    float* const of32 = wk.ns > 1 ? a.split_o[wk.s] : a.out_f32;
-    float* const lsep = wk.ns > 1 ? a.split_l[wk.s] : a.lse;
+    float* const of32 = (wk.ns > 1 && !whole) ? a.split_o[wk.s] : a.out_f32;
+    float* const lsep = (wk.ns > 1 && !whole) ? a.split_l[wk.s] : a.lse;
   #pragma unroll
     for (int n = 0; n < D / 32; ++n)
   #pragma unroll
@@ -1257,6 +1271,13 @@ __global__ __launch_bounds__(256) void split_merge_kernel(SplitMergeArgs a) {
   const int h = qh % a.heads, xq = qh / a.heads;
   const uint32_t e = (uint32_t)a.rows[r];
   const int ns = (int)(e >> 28) + 1;
+  {
+    // a row the attention did whole (few selected blocks) already holds its output
+    const int rb = a.row_bi[r], g = h / a.group;
+    const int nall = a.lists[(((long long)(rb >> 16) * (a.heads / a.group) + g) * a.max_qb + (rb & 0xffff)) *
+                             (a.max_kb + 1)];
+    if (split_row_whole(nall, ns, a.whole)) return;
+  }
   const long long tok = (long long)(e & 0x0fffffffu) * kBlock + xq;
   const long long li = (long long)h * a.total_q + tok;
   const long long off = (tok * a.heads + h) * a.head_dim + dv * V;

@@ -142,6 +142,9 @@ struct AttnArgs {
   // lse); a split merge then writes the final output.
   float* split_o[3];
   float* split_l[3];
+  // A split row whose block list holds at most split_whole entries is done
+  // whole by its part 0, which writes the final output (0: never).
+  int split_whole;
   const uint8_t* mask;  // [batch, hkv, max_qb, max_kb]
   const int32_t* cu_q;
   const int32_t* cu_k;
@@ -189,6 +192,10 @@ struct SplitMergeArgs {
   void* out;   // bf16 [total_q, heads, d]
   float* lse;  // [heads, total_q] or nullptr
   int rows[kMaxOrder];  // q block (global) | (ns - 1) << 28
+  // rows the attention did whole (list count <= whole) are skipped
+  int row_bi[kMaxOrder];  // sequence << 16 | q block of rows[r]
+  const int32_t* lists;   // the attention's block lists (PlanArgs layout)
+  int group, max_qb, max_kb, whole;
 };
 
 struct MergeArgs {

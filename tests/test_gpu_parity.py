@@ -211,13 +211,15 @@ def test_sparse_attention(name, mask_kind):
     assert_attention_close(out, lse, ref_o, ref_l, w.dtype, label=name)
 
 
-@pytest.mark.parametrize("mask_kind", ["dense", "random"])
+@pytest.mark.parametrize("mask_kind", ["dense", "random", "mixed"])
 def test_attention_head_tail_split(mask_kind):
     """Two sequences whose 32 q blocks x 8 kv heads = 256 workgroups fill a
     256-CU launch in one round, rows of 61..86 key blocks: rows longer than
     98% of the per-CU share (73.5 blocks) keep a 73-block head and queue the
     rest as a tail part (uneven two-part split), which the split merge
-    combines.
+    combines.  A split row whose mask keeps at most 73 blocks is done whole
+    by its head part ("random" keeps 70%: every row; "mixed": dense rows
+    split, rows keeping 20% whole, in one launch).
     Sampled rows (first and last of every q block) against the oracle."""
     w = make_random("head_tail", seed=41, hq=16, hkv=8, d=128, lq=[2048, 2048],
                     lk=[2048 + 128 * 60, 2048 + 128 * 70])
@@ -229,7 +231,10 @@ def test_attention_head_tail_split(mask_kind):
         kh = (lk - lq) // 128
         for i in range(lq // 128):
             n = i + kh + 1
-            row = np.ones((r.hkv, n), bool) if mask_kind == "dense" else rng.random((r.hkv, n)) < 0.7
+            if mask_kind == "dense" or (mask_kind == "mixed" and i % 2 == 0):
+                row = np.ones((r.hkv, n), bool)
+            else:
+                row = rng.random((r.hkv, n)) < (0.7 if mask_kind == "random" else 0.2)
             row[:, i + kh] = True
             mask[b, :, i, :n] = row
     mask_t = torch.from_numpy(mask)
