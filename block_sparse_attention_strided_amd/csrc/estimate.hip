@@ -173,6 +173,8 @@ template <int N, int M>
 __device__ __forceinline__ void est_lgkm_wait_arr(u32x4* f) {
   if constexpr (M == 2) {
     asm volatile("s_waitcnt lgkmcnt(%2)" : "+v"(f[0]), "+v"(f[1]) : "n"(N));
+  } else if constexpr (M == 3) {
+    asm volatile("s_waitcnt lgkmcnt(%3)" : "+v"(f[0]), "+v"(f[1]), "+v"(f[2]) : "n"(N));
   } else if constexpr (M == 4) {
     asm volatile("s_waitcnt lgkmcnt(%4)" : "+v"(f[0]), "+v"(f[1]), "+v"(f[2]), "+v"(f[3]) : "n"(N));
   } else {
@@ -205,9 +207,17 @@ __device__ __forceinline__ float pair_sum(float v) {
 }
 
 constexpr int kEstBig = 256;
+// 128 x 128 tiles: 8 waves (two per SIMD, each 64 x 32), 4 stage buffers of
+// 32 reduction elements (64 KiB of LDS).  Measured on the 4K layer: 4 waves
+// with 4 buffers of 64 19.5 us; 8 waves with 4 x 64 17.5, 2 x 64 17.5,
+// 2 x 32 18.0, 4 x 32 17.0 us (same bits).
 #ifndef XATTN_EST_NBUF
-#define XATTN_EST_NBUF 4  // stage buffers of the 128 x 128 tile kernel
+#define XATTN_EST_NBUF 4
 #endif
+#ifndef XATTN_EST_BK
+#define XATTN_EST_BK 32
+#endif
+constexpr int kEstSmallWaves = 8;
 // 256 x 256 tiles: 2 stage buffers of 64 reduction elements (measured at
 // 32K: 4 buffers of 32 elements 0.082 ms, 2 of 32 0.088, 2 of 64 0.078)
 #ifndef XATTN_EST_BIG_NBUF
@@ -699,7 +709,7 @@ hipError_t est_dispatch(const EstArgs& a, int dtype, int batch, hipStream_t st) 
   constexpr int RB = kBlock / S;
   if (dtype == 0) {
     // 256 x 256 tiles (8 waves) when they still fill the chip, else 128 x 128
-    // tiles (4 waves); both need Q and K spans within 31-bit buffer offsets.
+    // tiles (8 waves); both need Q and K spans within 31-bit buffer offsets.
     if (a.q_bytes < (1ll << 31) && a.k_bytes < (1ll << 31)) {
       // several sequences: one workgroup per tile with work when the batch
       // fits the table, so that every XCD gets the same number of tiles
@@ -725,10 +735,10 @@ hipError_t est_dispatch(const EstArgs& a, int dtype, int batch, hipStream_t st) 
         if (batch > 1 && est_tile_table(a2, S, kEstTile, batch)) n = a2.tile_base[batch];
         else a2.n_tab = 0;
         if (n > 0 && a2.n_tab > 0)
-          hipLaunchKernelGGL((est_gemm_bf16<D, S, kEstTile, 4, XATTN_EST_NBUF, 64, true>), dim3((unsigned)n), dim3(256), 0,
+          hipLaunchKernelGGL((est_gemm_bf16<D, S, kEstTile, kEstSmallWaves, XATTN_EST_NBUF, XATTN_EST_BK, true>), dim3((unsigned)n), dim3(64 * kEstSmallWaves), 0,
                              st, a2);
         else if (n > 0)
-          hipLaunchKernelGGL((est_gemm_bf16<D, S, kEstTile, 4, XATTN_EST_NBUF, 64, false>), dim3((unsigned)n), dim3(256),
+          hipLaunchKernelGGL((est_gemm_bf16<D, S, kEstTile, kEstSmallWaves, XATTN_EST_NBUF, XATTN_EST_BK, false>), dim3((unsigned)n), dim3(64 * kEstSmallWaves),
                              0, st, a2);
       }
       return hipGetLastError();

@@ -546,3 +546,27 @@ def test_block_table_entries_outside_the_cache(monkeypatch):
     monkeypatch.setenv("XATTN_DEBUG", "1")
     out, lse, counts, aux = r.prefill()  # a valid table passes the check
     assert torch.isfinite(out.float()).all()
+
+
+@pytest.mark.parametrize("case", [
+    dict(name="s8_g2", hq=16, hkv=8, d=128, lq=[2048], lk=[8192], stride=8),
+    dict(name="s16_g4", hq=32, hkv=8, d=128, lq=[1024], lk=[16384], stride=16),
+    dict(name="s4_g2_d64", hq=4, hkv=2, d=64, lq=[512], lk=[2048], stride=4),
+    dict(name="paged_varlen", hq=8, hkv=4, d=128, lq=[512, 0, 256], lk=[2048, 128, 1024], stride=8, paged=True),
+    dict(name="g16", hq=16, hkv=1, d=64, lq=[256], lk=[8192], stride=8),
+    dict(name="wide_rows", hq=4, hkv=1, d=64, lq=[128], lk=[131072], stride=8),
+], ids=lambda c: c["name"])
+@pytest.mark.parametrize("mode", ["per_kvhead", "chunk_vote"])
+def test_prefill_block_sums_equal_the_estimate_kernel(case, mode):
+    """The whole path's block sums (the aux output of xattn_prefill_chunk)
+    are bit-identical to xattn_estimate's on the same inputs, for the three
+    reshaped block sizes, GQA groups up to 16, paged varlen batches and rows
+    too wide for the fused selection kernel."""
+    c = dict(case)
+    name = c.pop("name")
+    w = make_random(name, seed=99, select_mode=mode, **c)
+    r = Run(w)
+    say("block sums, prefill vs estimate: %s %s" % (name, mode))
+    bs_est = r.estimate()
+    _, _, _, aux = r.prefill()
+    assert torch.equal(aux["block_sums"].cpu(), bs_est.cpu()), "prefill block sums differ from xattn_estimate's"
