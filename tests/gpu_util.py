@@ -107,7 +107,7 @@ class Run:
         kw = dict(num_kv_heads=w.num_kv_heads, stride=w.stride, threshold=self.tau,
                   est_scale=self.est_scale, softmax_scale=self.softmax_scale,
                   kv_chunk_tokens=w.kv_chunk_tokens, mode=self.mode, agg=self.agg,
-                  attention=attention, rows=rows)
+                  attention=attention, rows=rows, num_to_choose=self.num_to_choose)
         if self.paged:
             return O.prefill(w.q, None, None, w.cu_q, w.cu_k, block_table=w.block_table.numpy(),
                              k_cache=w.k_cache, v_cache=w.v_cache, **kw)

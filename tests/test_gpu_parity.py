@@ -570,3 +570,24 @@ def test_prefill_block_sums_equal_the_estimate_kernel(case, mode):
     bs_est = r.estimate()
     _, _, _, aux = r.prefill()
     assert torch.equal(aux["block_sums"].cpu(), bs_est.cpu()), "prefill block sums differ from xattn_estimate's"
+
+
+@pytest.mark.parametrize("k", [3, 9])
+@pytest.mark.parametrize("mode", ["per_kvhead", "chunk_vote", "chunk_vote_sparse"])
+def test_prefill_topk_end_to_end(k, mode):
+    """The top-k rule (num_to_choose) through the whole path on
+    well-separated inputs (large value gaps at every row's k-th block):
+    masks and counts bit-exact, attention against the oracle on the GPU's
+    mask."""
+    w = make_well_separated("topk_e2e", seed=105, hq=8, hkv=4, d=128, lq=[1024, 512], lk=[4096, 512],
+                            select_mode=mode)
+    r = Run(w, num_to_choose=k)
+    say("top-%d end to end %s" % (k, mode))
+    out, lse, counts, aux = r.prefill()
+    ref = r.oracle(attention=False)
+    assert_block_sums_close(aux["block_sums"], ref["block_sums"], w.stride, "top-k")
+    gm = aux["mask_kv"].cpu().numpy().astype(bool)
+    assert (gm == ref["mask_kv"]).all(), "top-%d mask differs from the oracle" % k
+    assert (counts.cpu().numpy() == ref["counts"]).all()
+    ref_o, ref_l = r.oracle_attention(aux["mask_kv"])
+    assert_attention_close(out, lse, ref_o, ref_l, w.dtype, label="top-k e2e")

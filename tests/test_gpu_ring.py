@@ -214,8 +214,9 @@ def test_ring_reusing_a_selection_skips_the_estimate():
     assert torch.equal(lse, l0)
 
 
-@pytest.mark.parametrize("hq", [8, 6], ids=["g4", "g3"])
-def test_staged_ring_matches_resident_path(hq):
+@pytest.mark.parametrize("hq,mode", [(8, "chunk_vote"), (6, "chunk_vote"), (8, "chunk_vote_sparse")],
+                         ids=["g4", "g3", "g4-sparse-cur"])
+def test_staged_ring_matches_resident_path(hq, mode):
     """Staged ring (history K in chunks, device-driven gather of the voted V
     blocks from mapped pinned memory, chunked attention with merges):
     estimate and selection bit-identical to the resident path, output within
@@ -223,12 +224,12 @@ def test_staged_ring_matches_resident_path(hq):
     every copy delayed 2 ms and with a reused selection.  hq=6 (group 3) runs
     the single-phase kernel, which reads V^T pages transposed per launch.
     The 20K history spans two staging chunks of 128 blocks."""
-    w = _small(hq=hq, lk=20480)
+    w = _small(hq=hq, lk=20480, mode=mode)
     r = Run(w)
     k_hist, v_hist, k_cur, v_cur, kh = _ring_inputs(w)
     lq, lk = w.lens(0)
     ring = X.Ring(1, lk // 128, w.num_kv_heads, w.head_dim, w.dtype, staged=True)
-    say("staged ring hq=%d: resident path" % hq)
+    say("staged ring hq=%d %s: resident path" % (hq, mode))
     o_res, l_res, c_res, a_res = r.prefill()
     say("staged ring: staged path")
     o_st, l_st, c_st, a_st = _run_ring(r, w, ring, k_hist, v_hist, k_cur, v_cur, kh)
@@ -360,3 +361,26 @@ def test_ring_128k_sparse_vote(staged):
     runs = assert_gapped(aux["hist_sel"][0], kh, "128K sparse %s" % ("staged" if staged else "slots"))
     assert len(runs) >= 10
     assert torch.equal(aux["hist_sel"][0, :kh].cpu(), torch.from_numpy(ref["hist_sel"][0, :kh]).to(torch.uint8))
+
+
+def test_ring_fp32_matches_resident_path_and_oracle():
+    """fp32 K/V through the slot ring (4 slots of 2 blocks) on a gapped vote:
+    selection bit-identical to the resident path, outputs within the fp32
+    tolerance of it and of the oracle."""
+    w = make_well_separated("ring_f32", seed=47, hq=2, hkv=1, d=64, lq=[256], lk=[4096], dtype=torch.float32,
+                            stride=8, threshold=0.9, select_mode="chunk_vote", kv_chunk_tokens=512,
+                            shared_ranks=True, rank_step=0.3)
+    r = Run(w)
+    k_hist, v_hist, k_cur, v_cur, kh = _ring_inputs(w)
+    ring = X.Ring(4, 2, w.num_kv_heads, w.head_dim, w.dtype)
+    say("ring fp32: resident path")
+    o_res, l_res, c_res, a_res = r.prefill()
+    say("ring fp32: ring path")
+    o_ring, l_ring, c_ring, a_ring = _run_ring(r, w, ring, k_hist, v_hist, k_cur, v_cur, kh)
+    ring.close()
+    assert_gapped(a_ring["hist_sel"][0], kh, "ring fp32")
+    assert torch.equal(a_res["block_sums"], a_ring["block_sums"])
+    assert torch.equal(a_res["mask_kv"], a_ring["mask_kv"])
+    assert (o_res - o_ring).abs().max().item() <= 1e-4
+    ref_o, ref_l = r.oracle_attention(a_ring["mask_kv"])
+    assert_attention_close(o_ring, l_ring, ref_o, ref_l, w.dtype, label="ring fp32")
