@@ -317,15 +317,56 @@ __global__ __launch_bounds__(64 * kSelMaxWaves) void select_group_kernel(SelectA
     }
   } else {
     sort_row_keys<PPL>(keys, row, n, n2, lane);
+    // exponent range of the row's nonzero values: 2^me <= v < 2^(me+1), and v
+    // a multiple of 2^qe (its fp32 ulp; denormals 2^-149)
+    int me_max = -1000, qe_min = 1000;
     for (int x = lane; x < n; x += 64) {
       const uint64_t key = keys[x];
       idx[x] = (uint16_t)(0xffffffffu - (uint32_t)(key & 0xffffffffu));
-      vals[x] = (double)from_orderable((uint32_t)(key >> 32));
+      const float v = from_orderable((uint32_t)(key >> 32));
+      vals[x] = (double)v;
+      const uint32_t vb = __float_as_uint(v);
+      if ((vb & 0x7fffffffu) != 0u) {
+        const int ef = (int)((vb >> 23) & 0xffu);
+        me_max = max(me_max, ef - 127);
+        qe_min = min(qe_min, max(ef, 1) - 150);
+      }
     }
     for (int j = n + lane; j < a.max_kb; j += 64) fl[j] = 0;
+    for (int o = 32; o > 0; o >>= 1) {
+      me_max = max(me_max, __shfl_xor(me_max, o, 64));
+      qe_min = min(qe_min, __shfl_xor(qe_min, o, 64));
+    }
+    // Every partial sum of these values is a multiple of 2^qe_min below
+    // n * 2^(me_max+1); when that bound is at most 2^(qe_min+53) every
+    // float64 addition is exact, so any order of the additions -- here a
+    // wave-parallel scan -- gives the bits of the left-to-right sum.
+    const int lg_n = n > 1 ? 32 - __clz(n - 1) : 0;
+    const bool exact = me_max + 1 + lg_n <= qe_min + 53;
     wave_lds_sync();
     double total = 0.0;
-    if (lane == 0) {
+    if (exact) {
+      const int c = (n + 63) / 64;  // values per lane, contiguous in sorted order
+      const int x0 = lane * c;
+      double loc = 0.0;
+      for (int k = 0; k < c; ++k)
+        if (x0 + k < n) loc += vals[x0 + k];
+      double inc = loc;
+      for (int o = 1; o < 64; o <<= 1) {
+        const double y = __shfl_up(inc, o, 64);
+        if (lane >= o) inc += y;
+      }
+      double run = __shfl_up(inc, 1, 64);
+      if (lane == 0) run = 0.0;
+      for (int k = 0; k < c; ++k) {
+        if (x0 + k < n) {
+          const double v0 = vals[x0 + k];
+          vals[x0 + k] = run;
+          run += v0;
+        }
+      }
+      total = __shfl(inc, 63, 64);
+    } else if (lane == 0) {
       // blocks of 16 values, the next block's loads issued before the
       // current block's additions (the additions are the serial chain);
       // each value's slot takes the sum before it as soon as it is read
@@ -355,7 +396,7 @@ __global__ __launch_bounds__(64 * kSelMaxWaves) void select_group_kernel(SelectA
       }
       total = acc;
     }
-    // lane 0's total to every lane
+    // lane 0's total to every lane (every lane holds it already when exact)
     const uint64_t tb = (uint64_t)__double_as_longlong(total);
     const uint32_t t_lo = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)tb);
     const uint32_t t_hi = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(tb >> 32));

@@ -591,3 +591,33 @@ def test_prefill_topk_end_to_end(k, mode):
     assert (counts.cpu().numpy() == ref["counts"]).all()
     ref_o, ref_l = r.oracle_attention(aux["mask_kv"])
     assert_attention_close(out, lse, ref_o, ref_l, w.dtype, label="top-k e2e")
+
+
+@pytest.mark.parametrize("spread", ["narrow", "wide"])
+@pytest.mark.parametrize("width", [40, 256, 3000])
+def test_select_exact_and_serial_scans(spread, width):
+    """The selection adds a row's sorted values in float64 with a wave-wide
+    scan when every partial sum is exact (values within a narrow exponent
+    range: any order gives the same bits), else serially in sorted order.
+    narrow: values in [0.5, 1) (exact scan); wide: values 2^-60 .. 1
+    (serial scan, where the rounding order matters).  Both bit-exact
+    against the oracle's left-to-right cumulative sum."""
+    lk = 128 * width
+    w = make_random("scan", seed=27, hq=4, hkv=2, d=64, lq=[256], lk=[lk], dtype=torch.float32, stride=8,
+                    select_mode="per_kvhead")
+    r = Run(w, threshold=0.9)
+    rng = np.random.default_rng(28)
+    shape = (r.B, r.hq, r.max_qb, r.max_kb)
+    if spread == "narrow":
+        bs32 = (0.5 + 0.5 * rng.random(shape)).astype(np.float32)
+    else:
+        bs32 = np.exp2(-60.0 * rng.random(shape)).astype(np.float32)
+    say("select scan %s %d" % (spread, width))
+    mask, hist, counts = r.select(torch.from_numpy(bs32))
+    lq, lk_ = w.lens(0)
+    qb, kb = lq // 128, lk_ // 128
+    sel = O.select_blocks(bs32[0, :, :qb, :kb].astype(np.float64), kh=(lk_ - lq) // 128, tau=r.tau,
+                          group=2, mode="per_kvhead")
+    m = mask[0].cpu().numpy().astype(bool)
+    assert (m[:, :qb, :kb] == sel["mask_kv"]).all()
+    assert tuple(counts[0].tolist()) == sel["counts"]
