@@ -28,6 +28,10 @@ namespace xattn {
 namespace {
 
 constexpr float kNegInf = -__builtin_huge_valf();
+constexpr float kPosInf = __builtin_huge_valf();
+// Bound on a lane's sum of the probabilities of one tile (32 per lane) taken
+// at a running max that has not moved; a larger sum moves the max.
+constexpr float kLazySum = 1024.f;
 #ifndef XATTN_GATHER_WGS
 #define XATTN_GATHER_WGS 16
 #endif
@@ -211,10 +215,8 @@ __device__ __forceinline__ WorkUnit work_unit(const AttnArgs& a, int hkv, int np
 // (split_row_whole).
 __device__ __forceinline__ bool split_row_whole(int nall, int ns, int whole) { return ns > 1 && nall <= whole; }
 
-__device__ __forceinline__ int load_row_list(const int32_t* glist, int32_t* list, int s, int ns, int cut, int tid,
-                                             int nthreads, int whole) {
-  const int nall = glist[0];
-  int z0, n;
+// Entries [z0, z0 + n) of a row list of nall entries that part s of ns takes.
+__device__ __forceinline__ void row_part(int nall, int s, int ns, int cut, int whole, int& z0, int& n) {
   if (split_row_whole(nall, ns, whole)) {
     z0 = 0;
     n = s == 0 ? nall : 0;
@@ -226,6 +228,13 @@ __device__ __forceinline__ int load_row_list(const int32_t* glist, int32_t* list
     z0 = (s * nall) / ns;
     n = ((s + 1) * nall) / ns - z0;
   }
+}
+
+__device__ __forceinline__ int load_row_list(const int32_t* glist, int32_t* list, int s, int ns, int cut, int tid,
+                                             int nthreads, int whole) {
+  const int nall = glist[0];
+  int z0, n;
+  row_part(nall, s, ns, cut, whole, z0, n);
   for (int z = tid; z <= n; z += nthreads) list[z] = (z == 0) ? n : glist[z0 + z];
   return n;
 }
@@ -764,7 +773,7 @@ __global__ __launch_bounds__(512) void attn_pp(AttnArgs a, int hkv) {
     f32x16 s0, s1;
     bf16x8 pb[4];
     float m_run = kNegInf, l_run = 0.f;
-    float mneg = 0.f, m_thr = kNegInf;  // -m_run (0 while it is -inf); (m_run + 8) / c2
+    float mneg = kPosInf;  // -m_run; +inf while m_run is -inf
     const float c2 = a.scale2;
 
     // ---- MFMA phase of tile u: O^T += V^T(u-1) P^T(u-1) if PV, S^T(u) = K(u) Q^T
@@ -862,61 +871,70 @@ __global__ __launch_bounds__(512) void attn_pp(AttnArgs a, int hkv) {
           if (kc + 32 > xt) s1[z] = kNegInf;
         }
       }
-      // Row max as a tree of three-input maxima (IEEE maximum lowers to
-      // v_maximum3_f32 without operand canonicalisation): 17 instructions for
-      // the 32 values of a lane.
-      auto mx3 = [](float p, float q, float r) {
-        return __builtin_elementwise_maximum(__builtin_elementwise_maximum(p, q), r);
-      };
-      float t[11];
+      // Probabilities at the running max, packed to bf16 into pb; returns the
+      // lane's fp32 sum of them (rounding them to bf16 first would move the
+      // LSE of short rows by up to half a bf16 ulp), four chains.
+      auto probs = [&](float mc) __attribute__((always_inline)) {
+        float ps[4], p0[16], p1[16];
   #pragma unroll
-      for (int k = 0; k < 5; ++k) {
-        t[k] = mx3(s0[3 * k], s0[3 * k + 1], s0[3 * k + 2]);
-        t[5 + k] = mx3(s1[3 * k], s1[3 * k + 1], s1[3 * k + 2]);
+        for (int z = 0; z < 16; ++z) {
+          p0[z] = fast_exp2(fmaf(s0[z], c2, mc));
+          p1[z] = fast_exp2(fmaf(s1[z], c2, mc));
+          if (z < 4) ps[z & 3] = p0[z] + p1[z];
+          else ps[z & 3] += p0[z] + p1[z];
+        }
+  #pragma unroll
+        for (int m = 0; m < 4; ++m) {
+          const int i0 = 2 * (m & 1);
+  #pragma unroll
+          for (int z = 0; z < 8; ++z) pb[m][z] = (__bf16)((m < 2) ? p0[4 * i0 + z] : p1[4 * i0 + z]);
+        }
+        return (ps[0] + ps[1]) + (ps[2] + ps[3]);
+      };
+      // Lazy rescale.  The probabilities are first taken at the running max
+      // as it stands; that stands when every lane's tile sum is at most
+      // kLazySum (so is every probability).  Otherwise -- a score well above
+      // the running max, or a row with no max yet (mneg = +inf makes the sum
+      // infinite or NaN) -- the tile's max moves the running max and the
+      // probabilities are taken again.  The first tile of a unit goes
+      // straight to the second path.
+      float tsum = 0.f;
+      bool moved = u == 0;
+      if (!moved) {
+        tsum = probs(mneg);
+        moved = __ballot(!(tsum <= kLazySum)) != 0ull;
       }
-      t[10] = __builtin_elementwise_maximum(s0[15], s1[15]);
-      float mx = __builtin_elementwise_maximum(mx3(mx3(t[0], t[1], t[2]), mx3(t[3], t[4], t[5]), mx3(t[6], t[7], t[8])),
-                                               __builtin_elementwise_maximum(t[9], t[10]));
-      mx = half_max(mx);
-      // Lazy rescale: the running max moves only when the tile's exceeds it by
-      // more than 8 (weights stay below 2^8); m_thr is that bound on the
-      // unscaled scores.
-      if (__ballot(mx > m_thr) != 0ull) {
+      if (moved) {
+        // Row max as a tree of three-input maxima (IEEE maximum lowers to
+        // v_maximum3_f32 without operand canonicalisation): 17 instructions
+        // for the 32 values of a lane.
+        auto mx3 = [](float p, float q, float r) {
+          return __builtin_elementwise_maximum(__builtin_elementwise_maximum(p, q), r);
+        };
+        float t[11];
+  #pragma unroll
+        for (int k = 0; k < 5; ++k) {
+          t[k] = mx3(s0[3 * k], s0[3 * k + 1], s0[3 * k + 2]);
+          t[5 + k] = mx3(s1[3 * k], s1[3 * k + 1], s1[3 * k + 2]);
+        }
+        t[10] = __builtin_elementwise_maximum(s0[15], s1[15]);
+        float mx = __builtin_elementwise_maximum(
+            mx3(mx3(t[0], t[1], t[2]), mx3(t[3], t[4], t[5]), mx3(t[6], t[7], t[8])),
+            __builtin_elementwise_maximum(t[9], t[10]));
+        mx = half_max(mx);
         const float m_new = fmaxf(m_run, mx * c2);
-        const float alpha = fast_exp2(m_run - m_new);
+        const float alpha = (m_new == m_run) ? 1.f : fast_exp2(m_run - m_new);
         l_run *= alpha;
   #pragma unroll
         for (int n = 0; n < D / 32; ++n)
   #pragma unroll
           for (int z = 0; z < 16; ++z) oacc[n][z] *= alpha;
         m_run = m_new;
-        mneg = (m_new == kNegInf) ? 0.f : -m_new;
-        m_thr = (m_new + 8.0f) / c2;
+        const float mc = (m_new == kNegInf) ? 0.f : -m_new;
+        mneg = (m_new == kNegInf) ? kPosInf : mc;
+        tsum = probs(mc);
       }
-      // Row sum of the fp32 probabilities (rounding them to bf16 first would
-      // move the LSE of short rows by up to half a bf16 ulp), four chains.
-      float ps[4];
-      auto chunk = [&](auto c_tag) {
-        constexpr int C = decltype(c_tag)::value;
-  #pragma unroll
-        for (int z = 4 * C; z < 4 * C + 4; ++z) {
-          s0[z] = fast_exp2(fmaf(s0[z], c2, mneg));
-          s1[z] = fast_exp2(fmaf(s1[z], c2, mneg));
-          if constexpr (C == 0) ps[z & 3] = s0[z] + s1[z];
-          else ps[z & 3] += s0[z] + s1[z];
-        }
-      };
-      chunk(std::integral_constant<int, 0>{});
-      chunk(std::integral_constant<int, 1>{});
-      chunk(std::integral_constant<int, 2>{});
-      chunk(std::integral_constant<int, 3>{});
-  #pragma unroll
-      for (int m = 0; m < 4; ++m) {
-        const int i0 = 2 * (m & 1);
-  #pragma unroll
-        for (int z = 0; z < 8; ++z) pb[m][z] = (__bf16)((m < 2) ? s0[4 * i0 + z] : s1[4 * i0 + z]);
-      }
-      l_run += (ps[0] + ps[1]) + (ps[2] + ps[3]);
+      l_run += tsum;
     };
 
     // Register fences: the compiler would otherwise move the tail of a phase
@@ -1019,29 +1037,84 @@ __global__ __launch_bounds__(512) void attn_pp(AttnArgs a, int hkv) {
 
     const float l_tot = half_sum(l_run);
     const float inv = (l_tot > 0.f) ? 1.f / l_tot : 0.f;
-    const long long orow = ((long long)(q0 + x) * a.hq + h) * D;
     float* const of32 = (wk.ns > 1 && !whole) ? a.split_o[wk.s] : a.out_f32;
     float* const lsep = (wk.ns > 1 && !whole) ? a.split_l[wk.s] : a.lse;
+    // Output rows through LDS.  A lane holds one query (16-byte pieces at
+    // d = 32n + 8ii + 4hh), so a store straight from the registers would
+    // touch 32 rows, one partial cache line each; instead every wave writes
+    // its 32 rows into its own slice of the tile ring (idle once every wave
+    // has passed the barrier below: all fragment reads and copies are done),
+    // 16-byte pieces XOR-swizzled by the row, and reads them back row-major,
+    // so that each store instruction writes whole rows.  The slice is read
+    // only by the wave that wrote it (a wave's LDS operations run in order).
+    __syncthreads();
+    char* const ow = tiles + w * (32 * D * 4);
+    // first query row of this wave and the distance between rows, in elements
+    const long long obase = ((long long)(q0 + i * kBlock + qs * 32) * a.hq + h) * D;
+    int ostride = a.hq * D;
+    // The stride and the lane index pass through empty asm statements so that
+    // the offsets and LDS addresses below are formed here: hoisted out of the
+    // unit loop they would hold registers through the whole kernel.
+    int ql = l32, ln = lane;
+    asm volatile("" : "+s"(ostride), "+v"(ql), "+v"(ln));
+    if (of32) {
+      constexpr int CPR = D / 4;            // 16-byte pieces per fp32 row
+      constexpr int NR = 32 * CPR / 64;     // reads (and stores) per lane
   #pragma unroll
-    for (int n = 0; n < D / 32; ++n)
+      for (int n = 0; n < D / 32; ++n)
   #pragma unroll
-      for (int ii = 0; ii < 4; ++ii) {
-        const int d = n * 32 + 8 * ii + 4 * hh;
-        const float v0 = oacc[n][4 * ii + 0] * inv, v1 = oacc[n][4 * ii + 1] * inv;
-        const float v2 = oacc[n][4 * ii + 2] * inv, v3 = oacc[n][4 * ii + 3] * inv;
-        if (of32) {
-          f32x4 v = {v0, v1, v2, v3};
-          *(f32x4*)(of32 + orow + d) = v;
-        } else {
-          typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
-          bf16x4 o4;
-          o4[0] = (__bf16)v0;
-          o4[1] = (__bf16)v1;
-          o4[2] = (__bf16)v2;
-          o4[3] = (__bf16)v3;
-          *(bf16x4*)((char*)a.out + (orow + d) * 2) = o4;
+        for (int ii = 0; ii < 4; ++ii) {
+          const int c = 8 * n + 2 * ii + hh;
+          const f32x4 v = {oacc[n][4 * ii + 0] * inv, oacc[n][4 * ii + 1] * inv, oacc[n][4 * ii + 2] * inv,
+                           oacc[n][4 * ii + 3] * inv};
+          *(f32x4*)(ow + ql * (D * 4) + ((c ^ (ql & (CPR - 1))) * 16)) = v;
         }
+      asm volatile("" ::: "memory");
+      // every piece in its own registers before the first store, so that no
+      // store's data registers are rewritten while it is in flight
+      constexpr int RPI = 64 / CPR;  // rows per store instruction
+      const int r0 = ln / CPR, c = ln % CPR;
+      f32x4 rv[NR];
+  #pragma unroll
+      for (int j = 0; j < NR; ++j) {
+        const int r = j * RPI + r0;
+        rv[j] = *(const f32x4*)(ow + r * (D * 4) + ((c ^ (r & (CPR - 1))) * 16));
       }
+      const __amdgpu_buffer_rsrc_t ro =
+          __builtin_amdgcn_make_buffer_rsrc((void*)(of32 + obase), (short)0, 32 * ostride * 4, kBufFlags);
+      const int voff = (r0 * ostride + c * 4) * 4;
+  #pragma unroll
+      for (int j = 0; j < NR; ++j)
+        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, rv[j]), ro, voff, j * RPI * ostride * 4, 0);
+    } else {
+      typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+      constexpr int GPR = D / 8;            // 16-byte pieces per bf16 row
+      constexpr int NR = 32 * GPR / 64;
+  #pragma unroll
+      for (int n = 0; n < D / 32; ++n)
+  #pragma unroll
+        for (int ii = 0; ii < 4; ++ii) {
+          const int c8 = 8 * n + 2 * ii + hh;  // 8-byte piece of the row
+          bf16x4 o4;
+  #pragma unroll
+          for (int e = 0; e < 4; ++e) o4[e] = (__bf16)(oacc[n][4 * ii + e] * inv);
+          *(bf16x4*)(ow + ql * (D * 2) + (((c8 >> 1) ^ (ql & (GPR - 1))) * 16) + (c8 & 1) * 8) = o4;
+        }
+      asm volatile("" ::: "memory");
+      constexpr int RPI = 64 / GPR;
+      const int r0 = ln / GPR, gch = ln % GPR;
+      u32x4 rv[NR];
+  #pragma unroll
+      for (int j = 0; j < NR; ++j) {
+        const int r = j * RPI + r0;
+        rv[j] = *(const u32x4*)(ow + r * (D * 2) + ((gch ^ (r & (GPR - 1))) * 16));
+      }
+      const __amdgpu_buffer_rsrc_t ro =
+          __builtin_amdgcn_make_buffer_rsrc((void*)((char*)a.out + obase * 2), (short)0, 32 * ostride * 2, kBufFlags);
+      const int voff = (r0 * ostride + gch * 8) * 2;
+  #pragma unroll
+      for (int j = 0; j < NR; ++j) __builtin_amdgcn_raw_buffer_store_b128(rv[j], ro, voff, j * RPI * ostride * 2, 0);
+    }
     if (lsep && hh == 0) {
       const float lse = (l_tot > 0.f) ? (m_run + log2f(l_tot)) * kLn2 : kNegInf;
       lsep[(long long)h * a.total_q + q0 + x] = lse;

@@ -173,6 +173,46 @@ __device__ __forceinline__ uint64_t shfl_xor_u64(uint64_t v, int m) {
   return ((uint64_t)(uint32_t)hi << 32) | (uint32_t)lo;
 }
 
+// The 32-bit value of lane ^ JS without an LDS round trip where the
+// hardware has a direct lane exchange: DPP quad permutes for 1 and 2,
+// ds_swizzle's xor mode (within 32 lanes, no address register) for 4, 8 and
+// 16, v_permlane32_swap for 32.  permlane32_swap of v with itself returns the
+// lane's own value and its partner's in an order that depends on the half;
+// the one that differs from the own value is the partner's (when both are
+// equal either is).
+template <int JS>
+__device__ __forceinline__ uint32_t xor_lane_u32(uint32_t v) {
+  if constexpr (JS == 1) {
+    return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0xB1, 0xF, 0xF, true);  // quad_perm [1,0,3,2]
+  } else if constexpr (JS == 2) {
+    return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x4E, 0xF, 0xF, true);  // quad_perm [2,3,0,1]
+  } else if constexpr (JS == 4 || JS == 8 || JS == 16) {
+    return (uint32_t)__builtin_amdgcn_ds_swizzle((int)v, 0x1F | (JS << 10));  // and 0x1f, or 0, xor JS
+  } else if constexpr (JS == 32) {
+    const auto p = __builtin_amdgcn_permlane32_swap(v, v, false, false);
+    return (uint32_t)p[0] == v ? (uint32_t)p[1] : (uint32_t)p[0];
+  } else {
+    return (uint32_t)__shfl_xor((int)v, JS, 64);
+  }
+}
+template <int JS>
+__device__ __forceinline__ uint64_t xor_lane_u64(uint64_t v) {
+  const uint32_t lo = xor_lane_u32<JS>((uint32_t)v);
+  const uint32_t hi = xor_lane_u32<JS>((uint32_t)(v >> 32));
+  return ((uint64_t)hi << 32) | lo;
+}
+__device__ __forceinline__ uint64_t xor_lane_u64(uint64_t v, int js) {
+  switch (js) {
+    case 1: return xor_lane_u64<1>(v);
+    case 2: return xor_lane_u64<2>(v);
+    case 4: return xor_lane_u64<4>(v);
+    case 8: return xor_lane_u64<8>(v);
+    case 16: return xor_lane_u64<16>(v);
+    case 32: return xor_lane_u64<32>(v);
+    default: return shfl_xor_u64(v, js);
+  }
+}
+
 // The same bitonic network on KPL keys per lane held in registers (key x =
 // p * 64 + lane in k[p]): compare-exchange partners 64 or more apart sit in
 // the same lane, closer ones in lane ^ js of the same register, swapped with
@@ -207,7 +247,7 @@ __device__ __forceinline__ void sort_keys_in_registers(uint64_t* keys, const flo
       } else {
 #pragma unroll
         for (int p = 0; p < KPL; ++p) {
-          const uint64_t o = shfl_xor_u64(k[p], js);
+          const uint64_t o = xor_lane_u64(k[p], js);
           const bool desc = (((p << 6) | lane) & size) == 0, lower = (lane & js) == 0;
           // the lower position of a pair keeps the larger key in a
           // descending run, the smaller in an ascending one
