@@ -1157,14 +1157,17 @@ struct BlockIter {
 };
 
 // ---------------------------------------------------------------------------
-// fp32 inputs: one thread per query, key tiles of 32 staged in LDS.  With
+// fp32 inputs: one thread per query, key tiles of 32 staged in LDS.  A tile's
+// 32 scores are formed first (independent chains), then one running-max
+// update and rescale per tile, then the PV accumulation.  With
 // f32_splits = S > 1, blockIdx.z = b * S + s and the workgroup takes the
-// s-th contiguous part of the row's candidate key blocks, writing a partial
+// s-th contiguous part of the row's candidate key tiles, writing a partial
 // (normalised output, LSE) for merge_f32_kernel.
 // ---------------------------------------------------------------------------
 template <int D>
 __global__ __launch_bounds__(128) void attn_f32(AttnArgs a) {
   constexpr int KT = 32;
+  constexpr int TPB = kBlock / KT;  // tiles per key block
   __shared__ __align__(16) float ks[KT * D];
   __shared__ __align__(16) float vs[KT * D];
   const int i = a.max_qb - 1 - blockIdx.x;
@@ -1185,12 +1188,13 @@ __global__ __launch_bounds__(128) void attn_f32(AttnArgs a) {
   it.table = a.k.block_table ? a.k.block_table + (long long)b * a.k.max_blocks : nullptr;
   it.num_pages = a.k.num_pages;
   const int jend = min(a.jb1, i + kh + 1);
-  int jb0 = a.jb0;
   it.jend = jend;
+  // this part's candidate tiles [ta, tb), numbered from block jb0
+  const int nt = TPB * max(0, jend - a.jb0);
+  int ta = 0, tb = nt;
   if (ns > 1) {
-    const int n = max(0, jend - a.jb0);
-    jb0 = a.jb0 + (int)(((long long)sp * n) / ns);
-    it.jend = a.jb0 + (int)(((long long)(sp + 1) * n) / ns);
+    ta = (int)(((long long)sp * nt) / ns);
+    tb = (int)(((long long)(sp + 1) * nt) / ns);
   }
 
   float qv[D];
@@ -1202,37 +1206,67 @@ __global__ __launch_bounds__(128) void attn_f32(AttnArgs a) {
   for (int e = 0; e < D; ++e) acc[e] = 0.f;
   float m_run = kNegInf, l_run = 0.f;
 
-  for (int j = it.next(jb0); j < it.jend; j = it.next(j + 1)) {
-    const bool diag = (j == i + kh);
-    for (int t0 = 0; t0 < kBlock; t0 += KT) {
-      __syncthreads();
-      for (int c = tid; c < KT * D / 4; c += 128) {
-        const int key = c / (D / 4), part = c % (D / 4);
-        *(f32x4*)(&ks[key * D + part * 4]) =
-            *(const f32x4*)((const float*)a.k.row(b, j * kBlock + t0 + key, g) + part * 4);
-        *(f32x4*)(&vs[key * D + part * 4]) =
-            *(const f32x4*)((const float*)a.v.row(b, j * kBlock + t0 + key, g) + part * 4);
+  for (int tt = ta; tt < tb; ++tt) {
+    // skip to the first selected block at or after the tile's block
+    const int jc = a.jb0 + tt / TPB;
+    const int j = it.next(jc);
+    if (j >= jend) break;
+    if (j != jc) {
+      tt = (j - a.jb0) * TPB;
+      if (tt >= tb) break;
+    }
+    const int t0 = (tt % TPB) * KT;
+    __syncthreads();
+    for (int c = tid; c < KT * D / 4; c += 128) {
+      const int key = c / (D / 4), part = c % (D / 4);
+      *(f32x4*)(&ks[key * D + part * 4]) =
+          *(const f32x4*)((const float*)a.k.row(b, j * kBlock + t0 + key, g) + part * 4);
+      *(f32x4*)(&vs[key * D + part * 4]) =
+          *(const f32x4*)((const float*)a.v.row(b, j * kBlock + t0 + key, g) + part * 4);
+    }
+    __syncthreads();
+    float sc[KT];
+#pragma unroll
+    for (int kk = 0; kk < KT; ++kk) {
+      float d0 = 0.f, d1 = 0.f;
+#pragma unroll
+      for (int e = 0; e < D; e += 4) {
+        const f32x4 kv = *(const f32x4*)(&ks[kk * D + e]);
+        d0 = fmaf(qv[e], kv[0], d0);
+        d1 = fmaf(qv[e + 1], kv[1], d1);
+        d0 = fmaf(qv[e + 2], kv[2], d0);
+        d1 = fmaf(qv[e + 3], kv[3], d1);
       }
-      __syncthreads();
-      for (int kk = 0; kk < KT; ++kk) {
-        const int key = j * kBlock + t0 + kk;
-        if (diag && key > qpos) continue;
-        float sdot = 0.f;
+      sc[kk] = (d0 + d1) * a.scale2;
+    }
+    if (j == i + kh) {  // diagonal block: keys after the query are masked
 #pragma unroll
-        for (int e = 0; e < D; ++e) sdot = fmaf(qv[e], ks[kk * D + e], sdot);
-        const float z = sdot * a.scale2;
-        if (z > m_run) {
-          const float alpha = exp2f(m_run - z);
-          l_run = l_run * alpha + 1.f;
+      for (int kk = 0; kk < KT; ++kk)
+        if (j * kBlock + t0 + kk > qpos) sc[kk] = kNegInf;
+    }
+    float mx = sc[0];
 #pragma unroll
-          for (int e = 0; e < D; ++e) acc[e] = acc[e] * alpha + vs[kk * D + e];
-          m_run = z;
-        } else {
-          const float p = exp2f(z - m_run);
-          l_run += p;
+    for (int kk = 1; kk < KT; ++kk) mx = fmaxf(mx, sc[kk]);
+    const float m_new = fmaxf(m_run, mx);
+    // reference for this tile's weights: 0 while every score so far is -inf
+    // (weights 0), else the running max; alpha rescales what came before
+    const float mc = (m_new == kNegInf) ? 0.f : m_new;
+    const float alpha = exp2f(m_run - mc);
+    l_run *= alpha;
 #pragma unroll
-          for (int e = 0; e < D; ++e) acc[e] = fmaf(p, vs[kk * D + e], acc[e]);
-        }
+    for (int e = 0; e < D; ++e) acc[e] *= alpha;
+    m_run = m_new;
+#pragma unroll
+    for (int kk = 0; kk < KT; ++kk) {
+      const float p = exp2f(sc[kk] - mc);
+      l_run += p;
+#pragma unroll
+      for (int e = 0; e < D; e += 4) {
+        const f32x4 vv = *(const f32x4*)(&vs[kk * D + e]);
+        acc[e] = fmaf(p, vv[0], acc[e]);
+        acc[e + 1] = fmaf(p, vv[1], acc[e + 1]);
+        acc[e + 2] = fmaf(p, vv[2], acc[e + 2]);
+        acc[e + 3] = fmaf(p, vv[3], acc[e + 3]);
       }
     }
   }
@@ -1241,48 +1275,57 @@ __global__ __launch_bounds__(128) void attn_f32(AttnArgs a) {
   float* out = ns > 1 ? a.f32_o + (long long)sp * a.total_q * a.hq * D : (a.out_f32 ? a.out_f32 : (float*)a.out);
   float* lse = ns > 1 ? a.f32_l + (long long)sp * a.hq * a.total_q : a.lse;
 #pragma unroll
-  for (int e = 0; e < D; ++e) out[orow + e] = acc[e] * inv;
+  for (int e = 0; e < D; e += 4) {
+    const f32x4 v = {acc[e] * inv, acc[e + 1] * inv, acc[e + 2] * inv, acc[e + 3] * inv};
+    *(f32x4*)(out + orow + e) = v;
+  }
   if (lse) lse[(long long)h * a.total_q + q0 + x] = (l_run > 0.f) ? (m_run + log2f(l_run)) * kLn2 : kNegInf;
 }
 
-// Merge of the f32_splits partials of the fp32 attention: one thread per
-// (query, head) row, over the query rows of every q block the launch
-// covered (rows of sequences' q blocks only; others are never written).
-// lse = M + log(sum_s e^(lse_s - M)), out = sum_s e^(lse_s - lse) o_s; a row
-// whose parts all saw no key gets out 0 and lse -inf, as unsplit.
+// Merge of the f32_splits partials of the fp32 attention: one thread per 4
+// consecutive d of one (query, head) row, over the query rows of every q
+// block the launch covered (rows of sequences' q blocks only; others are
+// never written).  lse = M + log(sum_s e^(lse_s - M)),
+// out = sum_s e^(lse_s - lse) o_s; a row whose parts all saw no key gets out
+// 0 and lse -inf, as unsplit.  The part loops have a fixed trip count
+// (kMaxF32Splits, predicated on the launch's count) so that nothing is
+// indexed by a run-time part number.
 template <int D>
 __global__ __launch_bounds__(256) void merge_f32_kernel(AttnArgs a) {
+  constexpr int DV = D / 4;
   const long long t = (long long)blockIdx.x * 256 + threadIdx.x;
-  if (t >= (long long)a.total_q * a.hq) return;
-  const int h = (int)(t % a.hq);
-  const long long xq = t / a.hq;
+  if (t >= (long long)a.total_q * a.hq * DV) return;
+  const int dv = (int)(t % DV);
+  const long long row = t / DV;
+  const int h = (int)(row % a.hq);
+  const long long xq = row / a.hq;
   const int ns = a.f32_splits;
   const long long plane_o = (long long)a.total_q * a.hq * D, plane_l = (long long)a.hq * a.total_q;
-  float l[8];
+  const float* lp = a.f32_l + (long long)h * a.total_q + xq;
   float mx = kNegInf;
-  for (int s = 0; s < ns; ++s) {
-    l[s] = a.f32_l[s * plane_l + (long long)h * a.total_q + xq];
-    mx = fmaxf(mx, l[s]);
-  }
-  float w[8];
+#pragma unroll
+  for (int s = 0; s < kMaxF32Splits; ++s)
+    if (s < ns) mx = fmaxf(mx, lp[s * plane_l]);
+  const long long off = xq * a.hq * D + (long long)h * D + 4 * dv;
   float tot = 0.f;
-  for (int s = 0; s < ns; ++s) {
-    w[s] = (mx == kNegInf || l[s] == kNegInf) ? 0.f : expf(l[s] - mx);
-    tot += w[s];
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  if (mx != kNegInf) {
+#pragma unroll
+    for (int s = 0; s < kMaxF32Splits; ++s) {
+      if (s < ns) {
+        const float ls = lp[s * plane_l];
+        if (ls != kNegInf) {
+          const float w = expf(ls - mx);
+          tot += w;
+          acc += *(const f32x4*)(a.f32_o + s * plane_o + off) * w;
+        }
+      }
+    }
   }
   const float inv = tot > 0.f ? 1.f / tot : 0.f;
   float* out = a.out_f32 ? a.out_f32 : (float*)a.out;
-  const long long orow = xq * a.hq * D + (long long)h * D;
-  for (int e = 0; e < D; e += 4) {
-    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-    for (int s = 0; s < ns; ++s) {
-      if (w[s] == 0.f) continue;
-      const f32x4 o = *(const f32x4*)(a.f32_o + s * plane_o + orow + e);
-      acc += o * (w[s] * inv);
-    }
-    *(f32x4*)(out + orow + e) = acc;
-  }
-  if (a.lse) a.lse[(long long)h * a.total_q + xq] = tot > 0.f ? mx + logf(tot) : kNegInf;
+  *(f32x4*)(out + off) = acc * inv;
+  if (a.lse && dv == 0) a.lse[(long long)h * a.total_q + xq] = tot > 0.f ? mx + logf(tot) : kNegInf;
 }
 
 // ---------------------------------------------------------------------------
@@ -1413,7 +1456,7 @@ hipError_t attn_dispatch(const AttnArgs& a, int dtype, int batch, hipStream_t s)
     dim3 grid(a.max_qb, a.hq, batch * max(1, a.f32_splits));
     hipLaunchKernelGGL((attn_f32<D>), grid, dim3(128), 0, s, a);
     if (a.f32_splits > 1) {
-      const long long n = (long long)a.total_q * a.hq;
+      const long long n = (long long)a.total_q * a.hq * (D / 4);
       hipLaunchKernelGGL((merge_f32_kernel<D>), dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, a);
     }
   }

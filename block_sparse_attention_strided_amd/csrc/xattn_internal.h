@@ -161,18 +161,22 @@ struct AttnArgs {
   float* out_f32;     // [total_q, hq, d] fp32    (nullptr if final)
   float* lse;         // [hq, total_q] natural log (may be nullptr)
   // fp32 path: f32_splits > 1 workgroups share each (q block, head) row,
-  // part s taking a contiguous s-th of the row's key blocks; part s writes
-  // its normalised output and natural-log LSE to f32_o + s*total_q*hq*d and
-  // f32_l + s*hq*total_q, and a merge writes the result.
+  // part s taking a contiguous s-th of the row's candidate key tiles (32
+  // keys each); part s writes its normalised output and natural-log LSE to
+  // f32_o + s*total_q*hq*d and f32_l + s*hq*total_q, and a merge writes the
+  // result.
   int f32_splits;
   float* f32_o;
   float* f32_l;
 };
 
-// Key-block splits of the fp32 attention for a launch of `rows` (q block,
-// head, sequence) rows: enough workgroups for a 256-CU chip (at most 8).
+// Key-tile splits of the fp32 attention for a launch of `rows` (q block,
+// head, sequence) rows: about 1024 workgroups' worth of parts for a 256-CU
+// chip, at most kMaxF32Splits.
+constexpr int kMaxF32Splits = 32;
 constexpr int f32_attention_splits(long long rows) {
-  return rows <= 0 ? 1 : (rows >= 512 ? 1 : (int)(512 / rows < 8 ? 512 / rows : 8));
+  return rows <= 0 ? 1
+                   : (rows >= 512 ? 1 : (int)(1024 / rows < kMaxF32Splits ? 1024 / rows : kMaxF32Splits));
 }
 
 constexpr uint32_t order_entry(int b, int i, int s, int ns) {
