@@ -496,14 +496,21 @@ __global__ __launch_bounds__(64 * NW) void est_gemm_bf16(EstArgs a) {
 
 // ---------------------------------------------------------------------------
 // fp32 inputs: plain VALU dot products (tiny workloads; fp32 accuracy).
-// Workgroup = one key block j x (256 / RB) reshaped rows; lane group of RB
-// lanes = one row's RB columns, reduced with cross-lane shuffles.
+// Workgroup = one key block j x 4 reshaped rows, one wave per row; within a
+// wave, lane = cx * PT + pt: PT = 64 / RB lanes share column cx, each summing
+// S / PT of the S token offsets (two chains), and the parts are added with
+// cross-lane shuffles (fixed order, so every launch of the same cell gives
+// the same bits); the RB columns of the row are then reduced to the block's
+// log-sum-exp with shuffles as well.
 // ---------------------------------------------------------------------------
 template <int D, int S>
 __global__ __launch_bounds__(256) void est_partial_f32(EstArgs a) {
   constexpr int RB = kBlock / S;
-  constexpr int RT = 256 / RB;
-  const int cx = threadIdx.x % RB, ry = threadIdx.x / RB;
+  constexpr int PT = 64 / RB;  // lanes per column
+  constexpr int TP = S / PT;   // token offsets per lane
+  static_assert(PT >= 1 && S % PT == 0, "stride / lane split");
+  const int lane = threadIdx.x & 63;
+  const int cx = lane / PT, pt = lane % PT;
   const int bh = blockIdx.z;
   const int b = bh / a.hq, h = bh % a.hq, g = h / a.group;
   const int q0 = a.cu_q[b];
@@ -511,13 +518,15 @@ __global__ __launch_bounds__(256) void est_partial_f32(EstArgs a) {
   const int lk = a.cu_k[b + 1] - a.cu_k[b];
   const int R = lq / S, C = lk / S, o_s = (lk - lq) / S;
   const int j = a.jb0 + blockIdx.x;
-  if ((int)blockIdx.y * RT >= R || j * RB >= C) return;
-  const int r = blockIdx.y * RT + ry;
+  const int r = blockIdx.y * 4 + (int)(threadIdx.x >> 6);
+  if (r >= R || j * RB >= C) return;  // whole waves: r is uniform in a wave
   const int c = j * RB + cx;
-  float z = kNegInf;
-  if (r < R && c <= r + o_s) {
-    float s = 0.f;
-    for (int t = 0; t < S; ++t) {
+  const bool allowed = c <= r + o_s;
+  float s0 = 0.f, s1 = 0.f;
+  if (allowed) {
+#pragma unroll
+    for (int u = 0; u < TP; ++u) {
+      const int t = pt * TP + u;
       const float* qp = (const float*)(a.q) + ((long long)(q0 + r * S + S - 1 - t) * a.hq + h) * D;
       const float* kp = (const float*)a.k.row(b, c * S + t, g);
       if (!kp) continue;
@@ -525,21 +534,25 @@ __global__ __launch_bounds__(256) void est_partial_f32(EstArgs a) {
       for (int e = 0; e < D; e += 4) {
         const f32x4 qv = *(const f32x4*)(qp + e);
         const f32x4 kv = *(const f32x4*)(kp + e);
-        s = fmaf(qv[0], kv[0], s);
-        s = fmaf(qv[1], kv[1], s);
-        s = fmaf(qv[2], kv[2], s);
-        s = fmaf(qv[3], kv[3], s);
+        s0 = fmaf(qv[0], kv[0], s0);
+        s1 = fmaf(qv[1], kv[1], s1);
+        s0 = fmaf(qv[2], kv[2], s0);
+        s1 = fmaf(qv[3], kv[3], s1);
       }
     }
-    z = s * a.scale2;
   }
+  float sd = s0 + s1;
+#pragma unroll
+  for (int off = 1; off < PT; off <<= 1) sd += __shfl_xor(sd, off, 64);
+  const float z = allowed ? sd * a.scale2 : kNegInf;
   float mx = z;
 #pragma unroll
-  for (int off = RB / 2; off > 0; off >>= 1) mx = fmaxf(mx, __shfl_xor(mx, off, 64));
-  float e = (mx == kNegInf) ? 0.f : exp2f(z - mx);
+  for (int off = PT; off < 64; off <<= 1) mx = fmaxf(mx, __shfl_xor(mx, off, 64));
+  // each column is held by PT lanes: count it once
+  float e = (mx == kNegInf || pt != 0) ? 0.f : exp2f(z - mx);
 #pragma unroll
-  for (int off = RB / 2; off > 0; off >>= 1) e += __shfl_xor(e, off, 64);
-  if (cx == 0 && r < R)
+  for (int off = 1; off < 64; off <<= 1) e += __shfl_xor(e, off, 64);
+  if (lane == 0)
     a.part[((long long)bh * a.max_kb + j) * a.max_r + r] = (mx == kNegInf) ? kNegInf : mx + log2f(e);
 }
 
@@ -747,8 +760,7 @@ hipError_t est_dispatch(const EstArgs& a, int dtype, int batch, hipStream_t st) 
               batch * a.hq);
     hipLaunchKernelGGL((est_partial_bf16<D, S>), grid, dim3(256), 0, st, a);
   } else {
-    constexpr int RT = 256 / RB;
-    dim3 grid(a.jb_count, (a.max_r + RT - 1) / RT, batch * a.hq);
+    dim3 grid(a.jb_count, (a.max_r + 3) / 4, batch * a.hq);
     hipLaunchKernelGGL((est_partial_f32<D, S>), grid, dim3(256), 0, st, a);
   }
   return hipGetLastError();
