@@ -1197,6 +1197,12 @@ __global__ __launch_bounds__(128) void attn_f32(AttnArgs a) {
     tb = (int)(((long long)(sp + 1) * nt) / ns);
   }
 
+  if (ns > 1 && ta >= tb) {
+    // an empty part: LSE -inf marks it for the merge, which then reads none
+    // of its output
+    a.f32_l[(long long)sp * a.hq * a.total_q + (long long)h * a.total_q + q0 + x] = kNegInf;
+    return;
+  }
   float qv[D];
   const float* qrow = (const float*)a.q + ((long long)(q0 + x) * a.hq + h) * D;
 #pragma unroll
@@ -1287,9 +1293,10 @@ __global__ __launch_bounds__(128) void attn_f32(AttnArgs a) {
 // block the launch covered (rows of sequences' q blocks only; others are
 // never written).  lse = M + log(sum_s e^(lse_s - M)),
 // out = sum_s e^(lse_s - lse) o_s; a row whose parts all saw no key gets out
-// 0 and lse -inf, as unsplit.  The part loops have a fixed trip count
-// (kMaxF32Splits, predicated on the launch's count) so that nothing is
-// indexed by a run-time part number.
+// 0 and lse -inf, as unsplit.  Every part's LSE and output are loaded before
+// any is used (fixed trip counts, part indices clamped to the launch's
+// count), so the loads overlap; a part with LSE -inf (empty parts write no
+// output) is excluded by a select, whatever its output memory holds.
 template <int D>
 __global__ __launch_bounds__(256) void merge_f32_kernel(AttnArgs a) {
   constexpr int DV = D / 4;
@@ -1302,25 +1309,27 @@ __global__ __launch_bounds__(256) void merge_f32_kernel(AttnArgs a) {
   const int ns = a.f32_splits;
   const long long plane_o = (long long)a.total_q * a.hq * D, plane_l = (long long)a.hq * a.total_q;
   const float* lp = a.f32_l + (long long)h * a.total_q + xq;
+  const long long off = xq * a.hq * D + (long long)h * D + 4 * dv;
+  float ls[kMaxF32Splits];
+  f32x4 os[kMaxF32Splits];
+#pragma unroll
+  for (int s = 0; s < kMaxF32Splits; ++s) {
+    const int sc = s < ns ? s : ns - 1;
+    ls[s] = lp[sc * plane_l];
+    os[s] = *(const f32x4*)(a.f32_o + sc * plane_o + off);
+  }
   float mx = kNegInf;
 #pragma unroll
-  for (int s = 0; s < kMaxF32Splits; ++s)
-    if (s < ns) mx = fmaxf(mx, lp[s * plane_l]);
-  const long long off = xq * a.hq * D + (long long)h * D + 4 * dv;
+  for (int s = 0; s < kMaxF32Splits; ++s) mx = fmaxf(mx, ls[s]);
   float tot = 0.f;
   f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-  if (mx != kNegInf) {
 #pragma unroll
-    for (int s = 0; s < kMaxF32Splits; ++s) {
-      if (s < ns) {
-        const float ls = lp[s * plane_l];
-        if (ls != kNegInf) {
-          const float w = expf(ls - mx);
-          tot += w;
-          acc += *(const f32x4*)(a.f32_o + s * plane_o + off) * w;
-        }
-      }
-    }
+  for (int s = 0; s < kMaxF32Splits; ++s) {
+    const bool use = s < ns && ls[s] != kNegInf;
+    const float w = use ? expf(ls[s] - mx) : 0.f;
+    tot += w;
+    const f32x4 z = {0.f, 0.f, 0.f, 0.f};
+    acc += use ? os[s] * w : z;
   }
   const float inv = tot > 0.f ? 1.f / tot : 0.f;
   float* out = a.out_f32 ? a.out_f32 : (float*)a.out;
