@@ -1396,21 +1396,38 @@ __global__ __launch_bounds__(256) void split_merge_kernel(SplitMergeArgs a) {
   const int h = qh % a.heads, xq = qh / a.heads;
   const uint32_t e = (uint32_t)a.rows[r];
   const int ns = (int)(e >> 28) + 1;
-  {
-    // a row the attention did whole (few selected blocks) already holds its output
-    const int rb = a.row_bi[r], g = h / a.group;
-    const int nall = a.lists[(((long long)(rb >> 16) * (a.heads / a.group) + g) * a.max_qb + (rb & 0xffff)) *
-                             (a.max_kb + 1)];
-    if (split_row_whole(nall, ns, a.whole)) return;
-  }
   const long long tok = (long long)(e & 0x0fffffffu) * kBlock + xq;
   const long long li = (long long)h * a.total_q + tok;
   const long long off = (tok * a.heads + h) * a.head_dim + dv * V;
+  // The row's list count and the parts' LSEs are loaded together, then (for
+  // a row not done whole) every part's output at once: two rounds of loads
+  // instead of four.  Part indices are clamped to the row's count; the
+  // clamped copies are not used.
+  const int rb = a.row_bi[r], g = h / a.group;
+  const int nall =
+      a.lists[(((long long)(rb >> 16) * (a.heads / a.group) + g) * a.max_qb + (rb & 0xffff)) * (a.max_kb + 1)];
   float l[3], w[3];
+#pragma unroll
+  for (int s = 0; s < 3; ++s) l[s] = a.l[s < ns ? s : ns - 1][li];
+  // (empty asm statements that take the loaded values keep the compiler from
+  // sinking the loads past the branch, which would make them a round of
+  // their own)
+  asm volatile("" : "+v"(l[0]), "+v"(l[1]), "+v"(l[2]));
+  // a row the attention did whole (few selected blocks) already holds its output
+  if (split_row_whole(nall, ns, a.whole)) return;
+  f32x4 ov[3][V / 4];
+#pragma unroll
+  for (int s = 0; s < 3; ++s)
+#pragma unroll
+    for (int u = 0; u < V / 4; ++u) ov[s][u] = *(const f32x4*)(a.o[s < ns ? s : ns - 1] + off + 4 * u);
+#pragma unroll
+  for (int s = 0; s < 3; ++s)
+#pragma unroll
+    for (int u = 0; u < V / 4; ++u) asm volatile("" : "+v"(ov[s][u]));
   float mx = kNegInf;
 #pragma unroll
   for (int s = 0; s < 3; ++s) {
-    l[s] = (s < ns) ? a.l[s][li] : kNegInf;
+    if (s >= ns) l[s] = kNegInf;
     mx = fmaxf(mx, l[s]);
   }
   float lse = kNegInf;
@@ -1428,11 +1445,9 @@ __global__ __launch_bounds__(256) void split_merge_kernel(SplitMergeArgs a) {
     for (int s = 0; s < 3; ++s) {
       if (w[s] != 0.f) {
 #pragma unroll
-        for (int u = 0; u < V / 4; ++u) {
-          const f32x4 o = *(const f32x4*)(a.o[s] + off + 4 * u);
+        for (int u = 0; u < V / 4; ++u)
 #pragma unroll
-          for (int c = 0; c < 4; ++c) res[4 * u + c] = fmaf(w[s], o[c], res[4 * u + c]);
-        }
+          for (int c = 0; c < 4; ++c) res[4 * u + c] = fmaf(w[s], ov[s][u][c], res[4 * u + c]);
       }
     }
   }
