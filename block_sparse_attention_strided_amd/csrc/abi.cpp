@@ -398,8 +398,9 @@ int device_cu_count() {
 // bmax = max(share, longest / 3) are cut into ns = ceil(length / bmax) <= 3
 // parts whose partial outputs a split merge combines (the merge rule of
 // partial attention results).  Otherwise, when the longest row exceeds the
-// share by at least 4 blocks and 2%, rows longer than 98% of the share keep
-// a head of that many blocks and move the rest into a tail part; the tails
+// share by at least 4 blocks and 2%, rows longer than 98% of the share plus
+// two blocks keep a head of that many blocks and move the rest into a tail
+// part; the tails
 // come after every head and unsplit row, longest first, so they start on
 // the CUs that finish first, which evens out the CUs' totals.  When
 // the ping-pong kernel runs the launch, the tails are not given workgroups
@@ -445,8 +446,11 @@ void set_order(const XattnShape* sh, const Plan& p, AttnArgs& aa, void* ws, Spli
       bmax = std::max({(int)std::ceil(share), (lmax + 2) / 3, 2});
     } else if (lmax >= share + 4 && lmax >= 1.02 * share) {
       // heads a little below the share leave the faster XCDs tail work to
-      // take over from the slowest one (whose heads set the launch's end)
-      head = (int)std::ceil(0.98 * share);
+      // take over from the slowest one (whose heads set the launch's end);
+      // two blocks more pay for the second unit's fixed cost (block list,
+      // first copies, output: about 8 us against about 3 us per block) on
+      // the CUs that run a short row and then a tail
+      head = (int)std::ceil(0.98 * share) + 2;
     }
   }
   struct Item {

@@ -215,11 +215,11 @@ def test_sparse_attention(name, mask_kind):
 def test_attention_head_tail_split(mask_kind):
     """Two sequences whose 32 q blocks x 8 kv heads = 256 workgroups fill a
     256-CU launch in one round, rows of 61..86 key blocks: rows longer than
-    98% of the per-CU share (73.5 blocks) keep a 73-block head and queue the
-    rest as a tail part (uneven two-part split), which the split merge
-    combines.  A split row whose mask keeps at most 73 blocks is done whole
-    by its head part ("random" keeps 70%: every row; "mixed": dense rows
-    split, rows keeping 20% whole, in one launch).
+    98% of the per-CU share (73.5 blocks) plus two keep a 75-block head and
+    queue the rest as a tail part (uneven two-part split), which the split
+    merge combines.  A split row whose mask keeps at most 75 blocks is done
+    whole by its head part ("random" keeps 70%: every row; "mixed": dense
+    rows split, rows keeping 20% whole, in one launch).
     Sampled rows (first and last of every q block) against the oracle."""
     w = make_random("head_tail", seed=41, hq=16, hkv=8, d=128, lq=[2048, 2048],
                     lk=[2048 + 128 * 60, 2048 + 128 * 70])
