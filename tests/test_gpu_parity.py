@@ -178,6 +178,9 @@ ATTN_CASES = {
     "bf16_d64_gqa2_varlen": dict(hq=4, hkv=2, d=64, lq=[640, 128], lk=[1408, 384]),
     "bf16_paged": dict(hq=4, hkv=1, d=128, lq=[256, 128], lk=[768, 640], paged=True),
     "f32_d64": dict(hq=2, hkv=1, d=64, lq=[256], lk=[512], dtype=torch.float32),
+    # 192 (q block, head) rows: each row's key tiles in 5 parts of up to 16
+    # tiles (a count that is not a power of two, several tiles per part)
+    "f32_d64_gqa3_5parts": dict(hq=6, hkv=2, d=64, lq=[2048, 1024], lk=[2560, 1024], dtype=torch.float32),
 }
 
 
