@@ -158,6 +158,21 @@ def xattn_attn_run(shape, params, q, k, v, mask_kv, out, lse, ws, stream=None):
                                       _ptr(mask_kv), _ptr(out), _ptr(lse), _ptr(ws), ws.numel(), _stream(stream)))
 
 
+def xattn_kernel_timing(on):
+    """Enable (True) or disable the library's event pairs around every
+    attention kernel launch (the measurement hook of include/xattn.h)."""
+    _check(_lib.load().xattn_kernel_timing(1 if on else 0))
+
+
+def xattn_kernel_timing_read():
+    """(total ms, launches) of the attention kernels recorded since the last
+    read or switch; forgets them."""
+    total = ctypes.c_double(0.0)
+    n = ctypes.c_int(0)
+    _check(_lib.load().xattn_kernel_timing_read(ctypes.byref(total), ctypes.byref(n)))
+    return total.value, n.value
+
+
 def xattn_merge_attn(o_a, lse_a, o_b, lse_b, o, lse, stream=None):
     rows, heads, hd = o_a.shape
     _check(_lib.load().xattn_merge_attn(rows, heads, hd, _ptr(o_a), _ptr(lse_a), _ptr(o_b), _ptr(lse_b),

@@ -41,6 +41,8 @@ EXPORTED = (
     "xattn_ring_set_copy_delay_us",
     "xattn_ring_offload_chunk",
     "xattn_ring_offload_wait",
+    "xattn_kernel_timing",
+    "xattn_kernel_timing_read",
     "xattn_last_error",
 )
 
@@ -133,6 +135,10 @@ def load():
     lib.xattn_ring_offload_chunk.argtypes = [vp, vp, vp, vp, vp, ctypes.c_int, vp]
     lib.xattn_ring_offload_chunk.restype = ctypes.c_int
     lib.xattn_ring_offload_wait.argtypes = [vp, vp]
+    lib.xattn_kernel_timing.argtypes = [ctypes.c_int]
+    lib.xattn_kernel_timing.restype = ctypes.c_int
+    lib.xattn_kernel_timing_read.argtypes = [ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_int)]
+    lib.xattn_kernel_timing_read.restype = ctypes.c_int
     lib.xattn_ring_offload_wait.restype = ctypes.c_int
     lib.xattn_ring_set_copy_delay_us.restype = ctypes.c_int
     lib.xattn_last_error.argtypes = []

@@ -12,6 +12,7 @@
 #include <cstdlib>
 
 #include <algorithm>
+#include <mutex>
 #include <utility>
 #include <string>
 #include <vector>
@@ -539,6 +540,39 @@ void set_order(const XattnShape* sh, const Plan& p, AttnArgs& aa, void* ws, Spli
   }
 }
 
+// Measurement hook (xattn_kernel_timing): while enabled, every attention
+// launch records a pair of events around its block-sparse attention kernel
+// on the launch's stream (pairs pooled, never destroyed while the process
+// runs).
+struct KernelTiming {
+  std::mutex mu;
+  bool on = false;
+  std::vector<std::pair<hipEvent_t, hipEvent_t>> used, pool;
+};
+KernelTiming& kernel_timing() {
+  static KernelTiming t;
+  return t;
+}
+// The event pair for the next launch, or {nullptr, nullptr} when timing is off.
+std::pair<hipEvent_t, hipEvent_t> timing_pair() {
+  KernelTiming& t = kernel_timing();
+  std::lock_guard<std::mutex> lock(t.mu);
+  if (!t.on) return {nullptr, nullptr};
+  if (t.pool.empty()) {
+    hipEvent_t a = nullptr, b = nullptr;
+    if (hipEventCreate(&a) != hipSuccess) return {nullptr, nullptr};
+    if (hipEventCreate(&b) != hipSuccess) {
+      (void)hipEventDestroy(a);
+      return {nullptr, nullptr};
+    }
+    t.pool.push_back({a, b});
+  }
+  const auto pr = t.pool.back();
+  t.pool.pop_back();
+  t.used.push_back(pr);
+  return pr;
+}
+
 hipError_t launch_planned(const XattnShape* sh, const Plan& p, AttnArgs aa, void* ws, hipStream_t st) {
   aa.vt = ws_at<char>(ws, p.off_vt);
   aa.lists = ws_at<int32_t>(ws, p.off_lists);
@@ -548,8 +582,16 @@ hipError_t launch_planned(const XattnShape* sh, const Plan& p, AttnArgs aa, void
   SplitMergeArgs sm;
   sm.n = 0;
   if (p.dtype == XATTN_DTYPE_BF16) set_order(sh, p, aa, ws, &sm);
+  const auto tp = timing_pair();
+  if (tp.first) (void)hipEventRecord(tp.first, st);
   hipError_t e = launch_attention(aa, p.dtype == XATTN_DTYPE_BF16 ? 0 : 1, p.d, p.batch, st);
-  if (e != hipSuccess || sm.n == 0) return e;
+  if (tp.second) (void)hipEventRecord(tp.second, st);
+  if (e != hipSuccess) return e;
+  if (p.dtype != XATTN_DTYPE_BF16) {
+    e = launch_f32_merge(aa, p.d, st);
+    if (e != hipSuccess) return e;
+  }
+  if (sm.n == 0) return hipSuccess;
   return launch_split_merge(sm, st);
 }
 
@@ -1091,6 +1133,40 @@ int workspace_bytes(const XattnShape* shape, const XattnParams* params, size_t* 
 extern "C" {
 
 const char* xattn_last_error(void) { return g_last_error.c_str(); }
+
+int xattn_kernel_timing(int on) {
+  KernelTiming& t = kernel_timing();
+  std::lock_guard<std::mutex> lock(t.mu);
+  t.on = on != 0;
+  for (const auto& pr : t.used) t.pool.push_back(pr);
+  t.used.clear();
+  return XATTN_OK;
+}
+
+int xattn_kernel_timing_read(double* total_ms, int* launches) {
+  if (!total_ms || !launches) return fail(XATTN_ERR_INVALID, "xattn_kernel_timing_read: NULL output");
+  KernelTiming& t = kernel_timing();
+  std::lock_guard<std::mutex> lock(t.mu);
+  double sum = 0.0;
+  int n = 0;
+  int rc = XATTN_OK;
+  for (const auto& pr : t.used) {
+    float ms = 0.f;
+    hipError_t e = hipEventSynchronize(pr.second);
+    if (e == hipSuccess) e = hipEventElapsedTime(&ms, pr.first, pr.second);
+    if (e != hipSuccess) {
+      rc = fail(XATTN_ERR_HIP, "xattn_kernel_timing_read: %s", hipGetErrorString(e));
+      break;
+    }
+    sum += ms;
+    ++n;
+  }
+  for (const auto& pr : t.used) t.pool.push_back(pr);
+  t.used.clear();
+  *total_ms = sum;
+  *launches = n;
+  return rc;
+}
 
 size_t xattn_workspace_size(const XattnShape* shape, const XattnParams* params) {
   Plan p;

@@ -1479,10 +1479,6 @@ hipError_t attn_dispatch(const AttnArgs& a, int dtype, int batch, hipStream_t s)
   } else {
     dim3 grid(a.max_qb, a.hq, batch * max(1, a.f32_splits));
     hipLaunchKernelGGL((attn_f32<D>), grid, dim3(128), 0, s, a);
-    if (a.f32_splits > 1) {
-      const long long n = (long long)a.total_q * a.hq * (D / 4);
-      hipLaunchKernelGGL((merge_f32_kernel<D>), dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, a);
-    }
   }
   return hipGetLastError();
 }
@@ -1501,6 +1497,16 @@ hipError_t launch_attention(const AttnArgs& a, int dtype, int head_dim, int batc
   if (head_dim == 128) return attn_dispatch<128>(a, dtype, batch, s);
   if (head_dim == 64) return attn_dispatch<64>(a, dtype, batch, s);
   return hipErrorInvalidValue;
+}
+
+hipError_t launch_f32_merge(const AttnArgs& a, int head_dim, hipStream_t s) {
+  if (a.f32_splits <= 1 || a.total_q <= 0) return hipSuccess;
+  const long long n = (long long)a.total_q * a.hq * (head_dim / 4);
+  const dim3 grid((unsigned)((n + 255) / 256));
+  if (head_dim == 128) hipLaunchKernelGGL((merge_f32_kernel<128>), grid, dim3(256), 0, s, a);
+  else if (head_dim == 64) hipLaunchKernelGGL((merge_f32_kernel<64>), grid, dim3(256), 0, s, a);
+  else return hipErrorInvalidValue;
+  return hipGetLastError();
 }
 
 hipError_t launch_vt_transpose(const VtArgs& a, hipStream_t s) {

@@ -237,6 +237,9 @@ bool attention_reads_vt(const AttnArgs& a, int dtype, int head_dim);
 bool attention_uses_pp(const AttnArgs& a, int head_dim);
 hipError_t launch_merge(const MergeArgs& a, hipStream_t s);
 hipError_t launch_split_merge(const SplitMergeArgs& a, hipStream_t s);
+// fp32 attention with f32_splits > 1: the merge of the parts (after
+// launch_attention)
+hipError_t launch_f32_merge(const AttnArgs& a, int head_dim, hipStream_t s);
 // Copies block j of src (host memory mapped into the device address space)
 // to block j of dst for every j < nblocks with sel[j] != 0.
 hipError_t launch_gather_blocks(const uint8_t* sel, int nblocks, const void* src, void* dst, size_t block_bytes,

@@ -300,6 +300,20 @@ int xattn_ring_offload_chunk(XattnRing *ring, const void *k, const void *v, void
 /* Makes `stream` wait for the ring's last write-back. */
 int xattn_ring_offload_wait(XattnRing *ring, void *stream);
 
+/* Measurement hook, for callers that time the attention kernel alone (the
+ * roofline of the block-sparse attention, a7).  While enabled (on != 0),
+ * every attention launch of the library records a pair of events on its
+ * stream around the block-sparse attention kernel itself -- not the plan,
+ * nor the merges of split rows or fp32 parts that follow it.
+ * xattn_kernel_timing_read waits for the recorded events, writes the sum of
+ * their elapsed times (ms) and their number, and forgets them.  Off by
+ * default; switching it on or off also forgets them.  The library keeps the
+ * events (created on first use) until the process ends.  Not for use while a
+ * stream is being captured into a graph.  Errors: NULL outputs (INVALID); a
+ * HIP error while reading (HIP; the pairs are forgotten). */
+int xattn_kernel_timing(int on);
+int xattn_kernel_timing_read(double *total_ms, int *launches);
+
 /* Message of the last error on the calling thread ("" if none). */
 const char *xattn_last_error(void);
 

@@ -123,3 +123,14 @@ def test_vt_pages_reserved_only_for_the_single_phase_kernel():
     # an even group whose cache spans 2 GiB or more reserves them too
     big = (1 << 31) // page
     assert size(4, big) - size(4, big - 1) == big * page
+
+
+def test_kernel_timing_hook_host_side():
+    """The measurement hook checks its outputs and, with nothing recorded,
+    reads zero launches without touching a device."""
+    lib = _lib.load()
+    assert lib.xattn_kernel_timing_read(None, None) == -1
+    assert lib.xattn_kernel_timing(1) == 0
+    assert X.xattn_kernel_timing_read() == (0.0, 0)
+    assert lib.xattn_kernel_timing(0) == 0
+    assert X.xattn_kernel_timing_read() == (0.0, 0)

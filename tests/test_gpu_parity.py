@@ -258,6 +258,35 @@ def test_attention_head_tail_split(mask_kind):
         assert torch.equal(o2.cpu(), out.cpu()) and torch.equal(l2.cpu(), lse.cpu()), "repeated launch differs"
 
 
+@pytest.mark.parametrize("name", ["bf16_d128_gqa2_varlen", "f32_d64"])
+def test_kernel_timing_hook(name):
+    """While the hook is on, each attention call records one event pair around
+    its attention kernel (not the merges after it); off, nothing is recorded;
+    the outputs are those of an untimed call."""
+    import block_sparse_attention_strided_amd as X
+    w = make_random(name, seed=33, **ATTN_CASES[name])
+    r = Run(w)
+    mask_t = torch.ones((r.B, r.hkv, r.max_qb, r.max_kb), dtype=torch.uint8)
+    out, lse = r.attend(mask_t)
+    md = mask_t.to("cuda").contiguous()
+    o2 = torch.full_like(r.q, float("nan"))
+    l2 = torch.full((r.hq, r.shape.total_q), float("nan"), device="cuda")
+    X.xattn_attn_plan(r.shape, r.params, r.v, md, r.ws)
+    X.xattn_kernel_timing(True)
+    try:
+        for _ in range(3):
+            X.xattn_attn_run(r.shape, r.params, r.q, r.k, r.v, md, o2, l2, r.ws)
+        total, n = X.xattn_kernel_timing_read()
+        assert n == 3 and total > 0.0, (total, n)
+        assert X.xattn_kernel_timing_read() == (0.0, 0)
+    finally:
+        X.xattn_kernel_timing(False)
+    assert torch.equal(o2.cpu(), out.cpu()) and torch.equal(l2.cpu(), lse.cpu())
+    X.xattn_attn_run(r.shape, r.params, r.q, r.k, r.v, md, o2, l2, r.ws)
+    torch.cuda.synchronize()
+    assert X.xattn_kernel_timing_read() == (0.0, 0)
+
+
 def test_merge_attention():
     import block_sparse_attention_strided_amd as X
     rng = np.random.default_rng(7)
