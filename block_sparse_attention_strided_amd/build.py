@@ -17,6 +17,7 @@ LIB = os.path.join(HERE, "libxattn.so")
 BUILD_DIR = os.path.join(ROOT, "_build")
 
 ARCH = "gfx950"
+ROCM = os.environ.get("ROCM_PATH", "/opt/rocm")
 FLAGS = [
     "--offload-arch=" + ARCH,
     "-O3",
@@ -52,7 +53,8 @@ def build(verbose=False):
     with concurrent.futures.ThreadPoolExecutor(max_workers=4) as ex:
         objs = list(ex.map(_compile, SOURCES))
     tmp = LIB + ".tmp"
-    cmd = [_hipcc(), "-shared", "-fPIC", "--offload-arch=" + ARCH, "-o", tmp] + objs
+    cmd = [_hipcc(), "-shared", "-fPIC", "--offload-arch=" + ARCH, "-o", tmp] + objs + [
+        "-L" + os.path.join(ROCM, "lib"), "-lrocprofiler-sdk-roctx", "-Wl,-rpath," + os.path.join(ROCM, "lib")]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError("link failed: %s\n%s\n%s" % (" ".join(cmd), r.stdout, r.stderr))

@@ -17,6 +17,8 @@
 #include <string>
 #include <vector>
 
+#include <rocprofiler-sdk-roctx/roctx.h>
+
 #include "../../include/xattn.h"
 #include "xattn_internal.h"
 
@@ -228,8 +230,18 @@ KvView make_view(const XattnShape* sh, const Plan& p, const void* base) {
 }
 
 // k_pages: 128-key pages addressable from kview.base.
+// Host-side roctx range around one stage's enqueue (visible in a
+// rocprofv3 --marker-trace next to the kernels it launches).
+struct StageRange {
+  explicit StageRange(const char* name) { roctxRangePushA(name); }
+  ~StageRange() { roctxRangePop(); }
+  StageRange(const StageRange&) = delete;
+  StageRange& operator=(const StageRange&) = delete;
+};
+
 hipError_t run_estimate(const XattnShape* sh, const Plan& p, const void* q, KvView kview, int jb0,
                         int jb_count, int k_pages, float* part, hipStream_t st) {
+  const StageRange range("xattn:estimate");
   EstArgs ea{};
   ea.q = (const char*)q;
   ea.k = kview;
@@ -252,6 +264,7 @@ hipError_t run_estimate(const XattnShape* sh, const Plan& p, const void* q, KvVi
 
 hipError_t run_block_sums(const XattnShape* sh, const Plan& p, const float* part, float* bs,
                           hipStream_t st) {
+  const StageRange range("xattn:block_sums");
   BlockSumArgs ba;
   ba.part = part;
   ba.cu_q = sh->cu_q;
@@ -271,6 +284,7 @@ hipError_t run_block_sums(const XattnShape* sh, const Plan& p, const float* part
 hipError_t run_select(const XattnShape* sh, const XattnParams* pr, const Plan& p, const float* bs,
                       uint8_t* maskq, uint8_t* maskkv, uint8_t* hist, int32_t* counts, hipStream_t st,
                       void* plan_ws = nullptr, const KvView* kview = nullptr, bool* lists_done = nullptr) {
+  const StageRange range("xattn:select");
   SelectArgs sa{};
   sa.block_sums = bs;
   sa.cu_q = sh->cu_q;
@@ -600,6 +614,7 @@ hipError_t launch_planned(const XattnShape* sh, const Plan& p, AttnArgs aa, void
 hipError_t run_attention(const XattnShape* sh, const Plan& p, AttnArgs aa, const void* v, int num_pages,
                          void* ws, bool transpose_v, hipStream_t st, bool lists_ready = false, int vt_first = 0,
                          int vt_count = -1) {
+  const StageRange range("xattn:attention");
   aa.num_pages = num_pages;
   hipError_t e = plan_attention(sh, p, aa, v, num_pages, ws, transpose_v, st, lists_ready, vt_first, vt_count);
   if (e != hipSuccess) return e;
@@ -1292,6 +1307,7 @@ int xattn_prefill_chunk(XattnRing* ring, const XattnShape* shape, const XattnPar
                         const void* v_hist_host, int hist_blocks, void* out, float* lse,
                         int32_t* counts, const XattnAux* aux, void* ws, size_t ws_bytes,
                         void* stream) {
+  const StageRange range("xattn_prefill_chunk");
   Plan p;
   int rc = make_plan(shape, params, &p);
   if (rc) return rc;
