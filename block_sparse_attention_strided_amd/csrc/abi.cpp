@@ -73,7 +73,7 @@ struct Plan {
   size_t off_o[3], off_l[3];
   size_t off_table;
   size_t off_vt, off_lists;
-  size_t off_ctr;  // attention's tail-part counter (4 bytes)
+  size_t off_ctr;  // attention's tail-part counter (4 bytes), then the device head length (4 bytes)
   int num_pages;  // 128-key pages of the K/V arrays (contiguous or paged)
   bool reads_vt;  // some attention launch reads V^T pages (off_vt holds them)
   int f32_splits;           // fp32 attention: key-block parts per row (1: none)
@@ -337,6 +337,10 @@ AttnArgs attn_args(const XattnShape* sh, const Plan& p, const void* q, KvView kv
   aa.n_order = 0;
   aa.f32_splits = 1;
   aa.split_whole = 0;
+  aa.cut_rows = 0;
+  aa.cut_cus = 0;
+  aa.cut_head = nullptr;
+  aa.device_cut = 0;
   aa.f32_o = nullptr;
   aa.f32_l = nullptr;
   for (int x = 0; x < 3; ++x) {
@@ -401,6 +405,16 @@ int device_cu_count() {
   }
   return cache[dev];
 }
+
+// Whether a final-output launch takes its head length from the block lists
+// on the device (set_order): in the chunk-vote modes, where the vote makes
+// every row's history the same and rows differ by their causal part, so
+// that the rows the host splits are the longest ones whatever the
+// selection kept (every launch's lists are written before it starts, by the
+// plan kernel or by the selection).  Per-KV-head rows keep the host's head:
+// measured, the per-workgroup sum of the list counts cost the 4K layer 2%
+// and gave the sparse per-KV-head regime nothing.
+bool device_heads(const XattnParams* pr) { return pr->select_mode != XATTN_SELECT_PER_KVHEAD; }
 
 // Launch order of the bf16 attention's rows and the split of long rows.
 // A row's length is the number of key blocks it may see in [jb0, jb1) (the
@@ -468,6 +482,12 @@ void set_order(const XattnShape* sh, const Plan& p, AttnArgs& aa, void* ws, Spli
       head = (int)std::ceil(0.98 * share) + 2;
     }
   }
+  // With the ping-pong kernel the same rule is applied again on the device,
+  // to the block lists' lengths (which a sparse selection makes much shorter
+  // than the causal bounds): the rows cut here get a head of that length and
+  // the rest as their tail, a row that fits it being done whole.
+  const bool dev_head = head > 0 && aa.device_cut && attention_uses_pp(aa, p.d) &&
+                        (long long)p.batch * p.hkv * p.max_qb <= 8192;
   struct Item {
     int neg_len;
     uint32_t entry;
@@ -546,6 +566,15 @@ void set_order(const XattnShape* sh, const Plan& p, AttnArgs& aa, void* ws, Spli
     sm->max_kb = p.max_kb;
     // rows whose selection kept no more than a part's share are done whole
     sm->whole = aa.split_whole = bmax > 0 ? bmax : head;
+    sm->cut_head = nullptr;
+    if (dev_head) {
+      sm->whole = aa.split_whole = -1;
+      aa.cut_rows = p.batch * p.hkv * p.max_qb;
+      aa.cut_cus = cus;
+      aa.cut_head = ws_at<int>(ws, p.off_ctr) + 1;
+      sm->cut_head = aa.cut_head;
+      for (int r = 0; r < aa.n_order; ++r) aa.order_cut[r] = 0;
+    }
     sm->heads = p.hq;
     sm->head_dim = p.d;
     sm->total_q = p.total_q;
@@ -1126,6 +1155,7 @@ int prefill_resident(const XattnShape* shape, const XattnParams* params, const P
     if (e != hipSuccess) return hip_fail(e, "select launch");
   }
   AttnArgs aa = attn_args(shape, p, q, kview, vview, maskkv, 0, p.max_kb);
+  aa.device_cut = device_heads(params);
   if (p.dtype == XATTN_DTYPE_BF16) aa.out = out;
   else aa.out_f32 = (float*)out;
   aa.lse = lse;
@@ -1236,6 +1266,7 @@ int xattn_sparse_attn(const XattnShape* shape, const XattnParams* params, const 
   if ((rc = validate_block_table(shape, p, (hipStream_t)stream))) return rc;
   g_last_error.clear();
   AttnArgs aa = attn_args(shape, p, q, make_view(shape, p, k), make_view(shape, p, v), mask_kv, 0, p.max_kb);
+  aa.device_cut = device_heads(params);
   if (p.dtype == XATTN_DTYPE_BF16) aa.out = out;
   else aa.out_f32 = (float*)out;
   aa.lse = lse;
@@ -1270,6 +1301,7 @@ int xattn_attn_run(const XattnShape* shape, const XattnParams* params, const voi
   if ((rc = validate_block_table(shape, p, (hipStream_t)stream))) return rc;
   g_last_error.clear();
   AttnArgs aa = attn_args(shape, p, q, make_view(shape, p, k), make_view(shape, p, v), mask_kv, 0, p.max_kb);
+  aa.device_cut = device_heads(params);
   if (p.dtype == XATTN_DTYPE_BF16) aa.out = out;
   else aa.out_f32 = (float*)out;
   aa.lse = lse;

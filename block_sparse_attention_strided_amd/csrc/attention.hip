@@ -216,10 +216,15 @@ __device__ __forceinline__ WorkUnit work_unit(const AttnArgs& a, int hkv, int np
 __device__ __forceinline__ bool split_row_whole(int nall, int ns, int whole) { return ns > 1 && nall <= whole; }
 
 // Entries [z0, z0 + n) of a row list of nall entries that part s of ns takes.
-__device__ __forceinline__ void row_part(int nall, int s, int ns, int cut, int whole, int& z0, int& n) {
+// head > 0 (heads from the device): part 0 of two takes the first `head`
+// entries, part 1 the rest.
+__device__ __forceinline__ void row_part(int nall, int s, int ns, int cut, int whole, int head, int& z0, int& n) {
   if (split_row_whole(nall, ns, whole)) {
     z0 = 0;
     n = s == 0 ? nall : 0;
+  } else if (ns == 2 && head > 0) {
+    z0 = s ? head : 0;
+    n = s ? nall - head : head;
   } else if (ns == 2 && cut > 0) {
     const int c = (nall * cut) >> 8;
     z0 = s ? c : 0;
@@ -231,10 +236,10 @@ __device__ __forceinline__ void row_part(int nall, int s, int ns, int cut, int w
 }
 
 __device__ __forceinline__ int load_row_list(const int32_t* glist, int32_t* list, int s, int ns, int cut, int tid,
-                                             int nthreads, int whole) {
-  const int nall = glist[0];
+                                             int nthreads, int whole, int head = 0, int nall = -1) {
+  if (nall < 0) nall = glist[0];
   int z0, n;
-  row_part(nall, s, ns, cut, whole, z0, n);
+  row_part(nall, s, ns, cut, whole, head, z0, n);
   for (int z = tid; z <= n; z += nthreads) list[z] = (z == 0) ? n : glist[z0 + z];
   return n;
 }
@@ -612,6 +617,9 @@ __global__ __launch_bounds__(512) void attn_pp(AttnArgs a, int hkv) {
   const int slots = hkv * npair;
   const bool dyn = a.n_static > 0 && a.n_static < a.n_order && a.tail_ctr != nullptr;
   __shared__ int next_unit;
+  // Heads from the device (formed before the first unit, below).
+  // nall_pre: the first unit's list count, loaded with them.
+  int whole_lim = a.split_whole, dev_head = 0, nall_pre = -1;
   auto run_unit = [&](const WorkUnit wk) __attribute__((always_inline)) {
     const int pair = wk.pair, g = wk.g, b = wk.b, i = wk.i;
     const int q0 = a.cu_q[b];
@@ -627,9 +635,11 @@ __global__ __launch_bounds__(512) void attn_pp(AttnArgs a, int hkv) {
 
     // Block list of this row, copied to LDS.
     const int32_t* glist = a.lists + (((long long)b * hkv + g) * a.max_qb + i) * (a.max_kb + 1);
-    const int nblk =
-        __builtin_amdgcn_readfirstlane(load_row_list(glist, list, wk.s, wk.ns, wk.cut, tid, 64 * NW, a.split_whole));
-    const bool whole = split_row_whole(__builtin_amdgcn_readfirstlane(glist[0]), wk.ns, a.split_whole);
+    const int nall = nall_pre >= 0 ? nall_pre : glist[0];
+    nall_pre = -1;
+    const int nblk = __builtin_amdgcn_readfirstlane(
+        load_row_list(glist, list, wk.s, wk.ns, wk.cut, tid, 64 * NW, whole_lim, dev_head, nall));
+    const bool whole = split_row_whole(__builtin_amdgcn_readfirstlane(nall), wk.ns, whole_lim);
     __syncthreads();
     if (whole && wk.s > 0) return;  // part 0 does the whole row
     const int ntile = 2 * nblk;
@@ -1121,6 +1131,33 @@ __global__ __launch_bounds__(512) void attn_pp(AttnArgs a, int hkv) {
     }
   };
   WorkUnit wk = work_unit(a, hkv, npair, blockIdx.x, gridDim.x);
+  if (a.split_whole < 0) {
+    // Heads from the device: the launch's row blocks are the list counts of
+    // its (sequence, kv head, q block) rows (those of q blocks past a
+    // sequence's end are never written and not read); the head length is
+    // the host rule's, 98% of the per-CU share plus two blocks.  The first
+    // unit's list count is loaded in the same round.  Workgroup 0 stores the
+    // head length for the split merge whatever its own units are.
+    __shared__ int head_red[NW];
+    if (wk.i < (a.cu_q[wk.b + 1] - a.cu_q[wk.b]) / kBlock)
+      nall_pre = a.lists[(((long long)wk.b * hkv + wk.g) * a.max_qb + wk.i) * (a.max_kb + 1)];
+    int part = 0;
+    for (int r = threadIdx.x; r < a.cut_rows; r += 64 * NW) {
+      const int i = r % a.max_qb, b = r / (hkv * a.max_qb);
+      const int cnt = a.lists[(long long)r * (a.max_kb + 1)];
+      if (i < (a.cu_q[b + 1] - a.cu_q[b]) / kBlock) part += cnt;
+    }
+  #pragma unroll
+    for (int off = 32; off > 0; off >>= 1) part += __shfl_xor(part, off, 64);
+    if ((threadIdx.x & 63) == 0) head_red[threadIdx.x >> 6] = part;
+    __syncthreads();
+    int tot = 0;
+  #pragma unroll
+    for (int x = 0; x < NW; ++x) tot += head_red[x];
+    const double share = (double)tot * npair / a.cut_cus;
+    whole_lim = dev_head = __builtin_amdgcn_readfirstlane((int)ceil(0.98 * share) + 2);
+    if (blockIdx.x == 0 && threadIdx.x == 0) *a.cut_head = dev_head;
+  }
   for (;;) {
     run_unit(wk);
     if (!dyn) break;
@@ -1406,15 +1443,16 @@ __global__ __launch_bounds__(256) void split_merge_kernel(SplitMergeArgs a) {
   const int rb = a.row_bi[r], g = h / a.group;
   const int nall =
       a.lists[(((long long)(rb >> 16) * (a.heads / a.group) + g) * a.max_qb + (rb & 0xffff)) * (a.max_kb + 1)];
+  int whole = a.whole >= 0 ? a.whole : *a.cut_head;
   float l[3], w[3];
 #pragma unroll
   for (int s = 0; s < 3; ++s) l[s] = a.l[s < ns ? s : ns - 1][li];
   // (empty asm statements that take the loaded values keep the compiler from
   // sinking the loads past the branch, which would make them a round of
   // their own)
-  asm volatile("" : "+v"(l[0]), "+v"(l[1]), "+v"(l[2]));
+  asm volatile("" : "+v"(l[0]), "+v"(l[1]), "+v"(l[2]), "+v"(whole));
   // a row the attention did whole (few selected blocks) already holds its output
-  if (split_row_whole(nall, ns, a.whole)) return;
+  if (split_row_whole(nall, ns, whole)) return;
   f32x4 ov[3][V / 4];
 #pragma unroll
   for (int s = 0; s < 3; ++s)

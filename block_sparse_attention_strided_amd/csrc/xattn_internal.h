@@ -144,7 +144,20 @@ struct AttnArgs {
   float* split_l[3];
   // A split row whose block list holds at most split_whole entries is done
   // whole by its part 0, which writes the final output (0: never).
+  // split_whole < 0: the head length comes from the device (heads from the
+  // lists): every workgroup sums the list counts of the launch's
+  // cut_rows (sequence, kv head, q block) rows, takes the head length H of
+  // the host rule (98% of the per-CU share over cut_cus CUs, plus two
+  // blocks) from that total, and a two-part row takes H entries in part 0
+  // and the rest in part 1 (whole when it holds at most H); workgroup 0
+  // stores H in *cut_head for the split merge.
   int split_whole;
+  int cut_rows;
+  int cut_cus;
+  int* cut_head;
+  // set by the caller before planning: the launch may take its head length
+  // from the device (its block lists are complete before it starts)
+  int device_cut;
   const uint8_t* mask;  // [batch, hkv, max_qb, max_kb]
   const int32_t* cu_q;
   const int32_t* cu_k;
@@ -200,6 +213,7 @@ struct SplitMergeArgs {
   int row_bi[kMaxOrder];  // sequence << 16 | q block of rows[r]
   const int32_t* lists;   // the attention's block lists (PlanArgs layout)
   int group, max_qb, max_kb, whole;
+  const int* cut_head;    // whole < 0: the head length the attention stored
 };
 
 struct MergeArgs {

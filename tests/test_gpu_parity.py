@@ -217,12 +217,13 @@ def test_sparse_attention(name, mask_kind):
 @pytest.mark.parametrize("mask_kind", ["dense", "random", "mixed"])
 def test_attention_head_tail_split(mask_kind):
     """Two sequences whose 32 q blocks x 8 kv heads = 256 workgroups fill a
-    256-CU launch in one round, rows of 61..86 key blocks: rows longer than
-    98% of the per-CU share (73.5 blocks) plus two keep a 75-block head and
-    queue the rest as a tail part (uneven two-part split), which the split
-    merge combines.  A split row whose mask keeps at most 75 blocks is done
-    whole by its head part ("random" keeps 70%: every row; "mixed": dense
-    rows split, rows keeping 20% whole, in one launch).
+    256-CU launch in one round, rows of 61..86 key blocks.  The head length
+    comes from the rows' block lists: 98% of the per-CU share of the listed
+    blocks plus two ("dense": 73.5 blocks per CU, 75-block heads); longer
+    rows queue the rest as a tail part, which the split merge combines, and
+    rows no longer than the head are done whole by their head part
+    ("random" keeps 70% of every row: shorter rows and shorter heads;
+    "mixed": dense rows beside rows keeping 20%, in one launch).
     Sampled rows (first and last of every q block) against the oracle."""
     w = make_random("head_tail", seed=41, hq=16, hkv=8, d=128, lq=[2048, 2048],
                     lk=[2048 + 128 * 60, 2048 + 128 * 70])
