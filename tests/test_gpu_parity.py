@@ -346,6 +346,21 @@ def test_prefill_chunk32k_sampled():
     _prefill_and_check(w, rows=rows, rows_idx=idx, label="32k")
 
 
+@pytest.mark.parametrize("nseq, mode", [(70, "chunk_vote"), (150, "chunk_vote"), (150, "per_kvhead")])
+def test_prefill_many_sequences(nseq, mode):
+    """Batches past the planners' tables: more sequences than the estimate's
+    per-sequence tile table holds (64; the GEMM then numbers its workgroups
+    over the whole grid) and, at 150 sequences, more (sequence, q block) rows
+    than the attention's order table (256; the kernel's default order, no
+    split rows).  Sequences of 2-3 q blocks over 0-4 history blocks."""
+    rng = np.random.default_rng(nseq)
+    lq = [128 * int(x) for x in rng.integers(2, 4, nseq)]
+    lk = [a + 128 * int(x) for a, x in zip(lq, rng.integers(0, 5, nseq))]
+    w = make_random("many%d" % nseq, seed=61 + nseq, hq=4, hkv=2, d=64, lq=lq, lk=lk, select_mode=mode)
+    rows, idx = sample_rows(w, per_seq=8)
+    _prefill_and_check(w, rows=rows, rows_idx=idx, label="%d sequences %s" % (nseq, mode))
+
+
 def test_prefill_paged_varlen_sampled():
     w = make_workload("paged_varlen_3seq")
     rows, idx = sample_rows(w, per_seq=48)
