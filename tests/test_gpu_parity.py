@@ -214,6 +214,32 @@ def test_sparse_attention(name, mask_kind):
     assert_attention_close(out, lse, ref_o, ref_l, w.dtype, label=name)
 
 
+@pytest.mark.parametrize("profile", ["rising", "falling", "jump"])
+def test_attention_running_max_moves(profile):
+    """Keys whose scale changes along the sequence, so that the running max
+    of a row moves by large steps on many tiles ("rising": 0.25x to 4x),
+    stays at the first tiles' level with later probabilities tiny
+    ("falling"), or jumps once in the middle ("jump": 8x over a few blocks,
+    0.5x elsewhere); dense causal rows of up to 2560 keys."""
+    import dataclasses
+    w = make_random("maxmove_" + profile, seed=37, hq=4, hkv=2, d=128, lq=[512], lk=[2560])
+    n = w.k.shape[0]
+    pos = torch.arange(n, dtype=torch.float32) / n
+    if profile == "rising":
+        sc = 0.25 + 3.75 * pos
+    elif profile == "falling":
+        sc = 4.0 - 3.75 * pos
+    else:
+        sc = torch.where((pos > 0.45) & (pos < 0.5), torch.tensor(8.0), torch.tensor(0.5))
+    w = dataclasses.replace(w, k=(w.k.float() * sc[:, None, None]).to(w.dtype))
+    r = Run(w)
+    mask_t = torch.ones((r.B, r.hkv, r.max_qb, r.max_kb), dtype=torch.uint8)
+    say("attention running max %s" % profile)
+    out, lse = r.attend(mask_t)
+    ref_o, ref_l = r.oracle_attention(mask_t)
+    assert_attention_close(out, lse, ref_o, ref_l, w.dtype, label="running max " + profile)
+
+
 @pytest.mark.parametrize("mask_kind", ["dense", "random", "mixed"])
 def test_attention_head_tail_split(mask_kind):
     """Two sequences whose 32 q blocks x 8 kv heads = 256 workgroups fill a
