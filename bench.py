@@ -20,7 +20,9 @@ xattn_attn_run runs ("attn_call_ms" is the whole call: the kernel, then the
 merge of split rows); algorithmic flops = 4*d per visible selected (query, key) pair
 per q head.  "sparse_regimes" repeats the step and the attention roofline on
 the 32K shape with inputs whose selection is genuinely sparse.
-"achievable" states what this machine reaches on a large bf16 GEMM (hipBLASLt
+"other_configs" gives the step time of the other workloads (the tiny fp32
+layer, the 4K layer, the paged batch, the 128K ring) measured in the same
+run.  "achievable" states what this machine reaches on a large bf16 GEMM (hipBLASLt
 through torch.matmul) and on a device copy, next to the published peaks.
 "cpu_baseline" times the float64 oracle on a bounded sample of the same
 workload on the host cores.
@@ -60,6 +62,8 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-sparse-stages", action="store_true",
                     help="skip the sparse-regime stages measured next to the 32K headline")
+    ap.add_argument("--no-other-configs", action="store_true",
+                    help="skip the step time of the other workloads measured next to the 32K headline")
     ap.add_argument("--cpu-sample-rows", type=int, default=3072,
                     help="query rows of the oracle attention sample (scaled to the chunk)")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -389,6 +393,32 @@ def sparse_regime(name, steps, warmup, dev, stream):
     }
 
 
+# The other workloads, each timed briefly next to the 32K headline.
+OTHER_CONFIGS = ("tiny_causal_fp32_1k", "qwen3_0p6b_4k", "paged_varlen_3seq", "qwen3_4b_128k_ring")
+
+
+def other_config(name, steps, warmup, dev, stream):
+    """Whole-step time of one more workload (its own warmup, then `steps`)."""
+    from workloads import make_workload
+
+    w = make_workload(name)
+    c = Case(w, dev)
+    for _ in range(warmup):
+        c.step()
+    ms, per = time_steps(c.step, steps, stream)
+    dens = c.density()
+    c.close()
+    return {
+        "workload": name,
+        "ms_per_step": ms,
+        "step_ms_median": median(per),
+        "query_tokens_per_s": w.total_q / (ms * 1e-3),
+        "steps": steps,
+        "density": dens,
+        "kv": "ring (pinned host history)" if w.ring else ("paged" if w.block_table is not None else "contiguous"),
+    }
+
+
 def reuse_accuracy(dev, mixes=(0.0, 0.2, 0.5, 1.0)):
     """Selection reuse across layers measured against the layer's own
     selection: synthetic layer pairs at the 32K shape whose block ranks
@@ -540,6 +570,12 @@ def main():
         res["sparse_regimes"] = [sparse_regime(n, min(args.steps, 50), min(args.warmup, 10), dev, stream)
                                  for n in SPARSE_STAGES]
         res["reuse_accuracy"] = reuse_accuracy(dev)
+    if w.name == "chunked_prefill_32k" and not args.no_other_configs:
+        del c
+        res["other_configs"] = [
+            other_config(n, min(args.steps, 5) if "ring" in n else min(args.steps, 50),
+                         min(args.warmup, 2) if "ring" in n else min(args.warmup, 10), dev, stream)
+            for n in OTHER_CONFIGS]
     if not args.no_achievable:
         res["achievable"] = achievable_rates(dev)
     if not args.no_cpu_baseline:
