@@ -387,6 +387,53 @@ def test_prefill_many_sequences(nseq, mode):
     _prefill_and_check(w, rows=rows, rows_idx=idx, label="%d sequences %s" % (nseq, mode))
 
 
+def _random_config(seed):
+    """One seeded draw over the path's parameters: heads and group, head
+    dim, stride, selection mode, group aggregation, dtype, paging, one to
+    three sequences of 1-4 q blocks over 0-8 history blocks, and a threshold
+    in [0.5, 0.99]."""
+    rng = np.random.default_rng(seed)
+    hq, hkv = [(2, 1), (4, 2), (6, 2), (8, 2), (4, 4), (8, 1)][rng.integers(6)]
+    nseq = int(rng.integers(1, 4))
+    lq = [128 * int(x) for x in rng.integers(1, 5, nseq)]
+    lk = [a + 128 * int(x) for a, x in zip(lq, rng.integers(0, 9, nseq))]
+    dtype = torch.float32 if rng.random() < 0.25 else torch.bfloat16
+    return dict(hq=hq, hkv=hkv, d=int(rng.choice([64, 128])), lq=lq, lk=lk, dtype=dtype,
+                stride=int(rng.choice([4, 8, 16])),
+                select_mode=str(rng.choice(["per_kvhead", "chunk_vote", "chunk_vote_sparse"])),
+                group_agg=str(rng.choice(["any", "majority"])), paged=bool(rng.random() < 0.4),
+                threshold=float(np.round(rng.uniform(0.5, 0.99), 3)))
+
+
+@pytest.mark.parametrize("seed", list(range(901, 937)))
+def test_prefill_random_configs(seed):
+    """Whole path against the oracle on seeded random configurations (masks
+    under the margin rule, block sums and attention within tolerance)."""
+    cfg = _random_config(seed)
+    say("random config %d: %s" % (seed, {k: (str(v) if k == "dtype" else v) for k, v in cfg.items()}))
+    w = make_random("rand%d" % seed, seed=seed, **cfg)
+    _prefill_and_check(w, label="random config %d" % seed)
+
+
+@pytest.mark.parametrize("seed", list(range(951, 963)))
+def test_prefill_random_configs_well_separated(seed):
+    """Seeded random configurations on well-separated inputs (block scores
+    far apart, shared ranks in the chunk-vote modes so that the vote keeps a
+    scattered subset): the selection is genuinely sparse and masks and
+    counts must match the oracle exactly."""
+    rng = np.random.default_rng(seed)
+    cfg = _random_config(seed)
+    mode = cfg["select_mode"]
+    kw = dict(hq=cfg["hq"], hkv=cfg["hkv"], d=cfg["d"], lq=cfg["lq"], lk=cfg["lk"], dtype=cfg["dtype"],
+              stride=cfg["stride"], select_mode=mode, paged=cfg["paged"],
+              threshold=float(np.round(rng.uniform(0.8, 0.95), 3)))
+    if mode != "per_kvhead":
+        kw.update(shared_ranks=True, rank_step=0.05)
+    say("well-separated random config %d: %s" % (seed, {k: (str(v) if k == "dtype" else v) for k, v in kw.items()}))
+    w = make_well_separated("wsrand%d" % seed, seed=seed, **kw)
+    _prefill_and_check(w, exact=True, label="well-separated random config %d" % seed)
+
+
 def test_prefill_paged_varlen_sampled():
     w = make_workload("paged_varlen_3seq")
     rows, idx = sample_rows(w, per_seq=48)
