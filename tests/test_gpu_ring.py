@@ -295,6 +295,48 @@ def test_staged_ring_write_back_feeds_the_next_chunk():
     assert (o2.float() - o_res.float()).abs().max().item() <= 2e-2
 
 
+@pytest.mark.parametrize("seed", list(range(1001, 1013)))
+def test_ring_random_configs(seed):
+    """Seeded random ring configurations: slot ring (2 or 4 slots of 4-16
+    blocks) or staged ring, heads and group, d, stride, chunk-vote mode,
+    dtype, well-separated (gapped vote) or Gaussian inputs.  Block sums,
+    masks, history vote and counts bit-identical to the resident path, the
+    output within the dtype's tolerance of it, the selection under the
+    margin rule against the oracle."""
+    rng = np.random.default_rng(seed)
+    hq, hkv = [(2, 1), (4, 2), (6, 2), (8, 2), (4, 4)][rng.integers(5)]
+    lq = 128 * int(rng.integers(2, 9))
+    lk = lq + 128 * int(rng.integers(8, 64))
+    dtype = torch.float32 if rng.random() < 0.25 else torch.bfloat16
+    kw = dict(hq=hq, hkv=hkv, d=int(rng.choice([64, 128])), lq=[lq], lk=[lk], dtype=dtype,
+              stride=int(rng.choice([4, 8, 16])), select_mode=str(rng.choice(["chunk_vote", "chunk_vote_sparse"])),
+              threshold=float(np.round(rng.uniform(0.8, 0.95), 3)), kv_chunk_tokens=int(rng.choice([1024, 4096])))
+    staged = bool(rng.random() < 0.4)
+    slots, slot_blocks = int(rng.choice([2, 4])), int(rng.choice([4, 8, 16]))
+    if rng.random() < 0.7:
+        w = make_well_separated("ring_rand%d" % seed, seed=seed, shared_ranks=True, rank_step=0.3, **kw)
+    else:
+        w = make_random("ring_rand%d" % seed, seed=seed, **kw)
+    say("ring random config %d: staged=%s slots=%d x %d %s" % (seed, staged, slots, slot_blocks,
+                                                             {k: (str(v) if k == "dtype" else v) for k, v in kw.items()}))
+    r = Run(w)
+    k_hist, v_hist, k_cur, v_cur, kh = _ring_inputs(w)
+    ring = (X.Ring(1, lk // 128, hkv, w.head_dim, dtype, staged=True) if staged
+            else X.Ring(slots, slot_blocks, hkv, w.head_dim, dtype))
+    o_res, l_res, c_res, a_res = r.prefill()
+    o_ring, l_ring, c_ring, a_ring = _run_ring(r, w, ring, k_hist, v_hist, k_cur, v_cur, kh)
+    ring.close()
+    for a in ("block_sums", "mask_kv"):
+        assert torch.equal(a_res[a], a_ring[a]), a
+    assert torch.equal(a_res["hist_sel"][:, :kh], a_ring["hist_sel"][:, :kh])
+    assert torch.equal(c_res, c_ring)
+    tol = 2e-2 if dtype == torch.bfloat16 else 1e-4
+    assert (o_res.float() - o_ring.float()).abs().max().item() <= tol
+    ref = r.oracle(attention=False)
+    assert_block_sums_close(a_ring["block_sums"], ref["block_sums"], w.stride, "ring random %d" % seed)
+    check_selection(r, ref, a_ring["block_sums"], a_ring["mask_kv"], a_ring["hist_sel"], "ring random %d" % seed)
+
+
 def test_ring_write_back_rejects_pageable_destination():
     ring = X.Ring(2, 2, 1, 128, torch.bfloat16)
     k = torch.zeros((128, 1, 128), dtype=torch.bfloat16, device="cuda")
