@@ -206,7 +206,6 @@ __device__ __forceinline__ float pair_sum(float v) {
   return __uint_as_float(p[0]) + __uint_as_float(p[1]);
 }
 
-constexpr int kEstBig = 256;
 // 128 x 128 tiles: 8 waves (two per SIMD, each 64 x 32), 4 stage buffers of
 // 32 reduction elements (64 KiB of LDS).  Measured on the 4K layer: 4 waves
 // with 4 buffers of 64 19.5 us; 8 waves with 4 x 64 17.5, 2 x 64 17.5,
@@ -218,41 +217,63 @@ constexpr int kEstBig = 256;
 #define XATTN_EST_BK 32
 #endif
 constexpr int kEstSmallWaves = 8;
-// 256 x 256 tiles: 2 stage buffers of 64 reduction elements (measured at
-// 32K: 4 buffers of 32 elements 0.082 ms, 2 of 32 0.088, 2 of 64 0.078)
+// Big tiles: 256 x 256 over 8 waves, 2 stage buffers of 64 reduction
+// elements (measured at 32K: 4 buffers of 32 elements 0.082 ms, 2 of 32
+// 0.088, 2 of 64 0.078)
+#ifndef XATTN_EST_BIG_TR
+#define XATTN_EST_BIG_TR 256
+#endif
+#ifndef XATTN_EST_BIG_TC
+#define XATTN_EST_BIG_TC 256
+#endif
+#ifndef XATTN_EST_BIG_NW
+#define XATTN_EST_BIG_NW 8
+#endif
 #ifndef XATTN_EST_BIG_NBUF
 #define XATTN_EST_BIG_NBUF 2
 #endif
 #ifndef XATTN_EST_BIG_BK
 #define XATTN_EST_BIG_BK 64
 #endif
+#ifndef XATTN_EST_BIG_WPE
+#define XATTN_EST_BIG_WPE 1
+#endif
+// workgroups of big tiles that share a CU (by their LDS and registers)
+constexpr int kEstBigPerCu =
+    std::min((160 * 1024) / (XATTN_EST_BIG_NBUF * (XATTN_EST_BIG_TR + XATTN_EST_BIG_TC) * XATTN_EST_BIG_BK * 2),
+             std::max(1, 4 * XATTN_EST_BIG_WPE / XATTN_EST_BIG_NW));
 
-// TT x TT tile over NW waves: wave w owns TT/2 columns (half w&1) x 2*TT/NW
-// rows (part w>>1); XT x YT accumulators.  A stage covers BK reduction
-// elements (LDS rows of 2*BK bytes); NBUF LDS stage buffers: NBUF - 1 stages
-// of copies are in flight while one is computed.
+// TR x TC tile (reshaped rows x columns) over NW waves: wave w owns TC/2
+// columns (half w&1) x 2*TR/NW rows (part w>>1); XT x YT accumulators.  A
+// stage covers BK reduction elements (LDS rows of 2*BK bytes); NBUF LDS stage
+// buffers: NBUF - 1 stages of copies are in flight while one is computed.
 // TAB: workgroups numbered over the tiles with work (a.tile_base), else over
-// the whole (sequence, head, row tile, column tile) grid.
-template <int D, int S, int TT, int NW, int NBUF, int BK, bool TAB>
-__global__ __launch_bounds__(64 * NW) void est_gemm_bf16(EstArgs a) {
+// the whole (sequence, head, row tile, column tile) grid.  WPE: waves per SIMD
+// the register allocation must leave room for (2 lets two 4-wave workgroups
+// share a CU, so that one's epilogue runs under the other's MFMAs).
+template <int D, int S, int TR, int TC, int NW, int NBUF, int BK, bool TAB, int WPE>
+__global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(WPE))) void est_gemm_bf16(EstArgs a) {
   constexpr int RB = kBlock / S;
-  constexpr int TILEB = TT * BK * 2; // bytes of one operand tile
+  constexpr int KTB = TC * BK * 2;   // bytes of the K operand tile
+  constexpr int BUFB = (TR + TC) * BK * 2;  // one stage buffer: K tile, then Q tile
   constexpr int CPR = BK / 8;        // 16-byte chunks per LDS row
   constexpr int RPI = 64 / CPR;      // rows per copy instruction (1 KiB)
   constexpr int KS = BK / 16;        // MFMA k-steps per stage
   constexpr int DQ = D / BK;         // stages per token offset
-  constexpr int NST = S * DQ;        // stages (even for every supported S, D)
+  constexpr int NST = S * DQ;        // stages
   constexpr int WR = NW / 2;         // wave rows
-  constexpr int XT = TT / 2 / 32;    // 32-column accumulator tiles per wave
-  constexpr int YT = TT / WR / 32;   // 32-row accumulator tiles per wave
-  constexpr int LPW = TT / (RPI * NW); // copy instructions per wave per operand
+  constexpr int XT = TC / 2 / 32;    // 32-column accumulator tiles per wave
+  constexpr int YT = TR / WR / 32;   // 32-row accumulator tiles per wave
+  constexpr int LPK = TC / (RPI * NW); // K copy instructions per wave and stage
+  constexpr int LPQ = TR / (RPI * NW); // Q copy instructions per wave and stage
   static_assert(BK == 32 || BK == 64, "stage width");
-  static_assert(NST % NBUF == 0, "stage loop is unrolled by NBUF");
-  static_assert(XT >= 1 && YT >= 1 && LPW >= 1 && TT % (RPI * NW) == 0, "tile / wave split");
+  static_assert(NBUF >= 2, "stage ring");
+  static_assert(XT >= 1 && YT >= 1 && LPK >= 1 && LPQ >= 1 && TC % (RPI * NW) == 0 && TR % (RPI * NW) == 0,
+                "tile / wave split");
   // 16-byte chunk swizzle of LDS row `row` (conflict-free fragment reads)
   auto swz = [](int row) { return BK == 64 ? (row & 7) : ((row >> 2) & 3); };
   typedef __attribute__((address_space(3))) void* lds_ptr;
-  __shared__ __align__(1024) char lds[2 * NBUF * TILEB];  // buffer b: K, then Q
+  __shared__ __align__(1024) char lds[NBUF * BUFB];
 
   // XCD-aware work unit: the 8 XCDs take consecutive workgroup ids
   // round-robin, so logical unit (id % 8) * (n / 8) + id / 8 gives each XCD a
@@ -283,9 +304,9 @@ __global__ __launch_bounds__(64 * NW) void est_gemm_bf16(EstArgs a) {
     const int cbase = a.jb0 * RB, cend = min((a.jb0 + a.jb_count) * RB, C_);
     by = 0;
     bx = 0;
-    for (int r0 = 0; r0 < R_; r0 += TT, ++by) {
-      const int lim = min(cend, min(r0 + TT, R_) + os_);
-      const int nbx = lim > cbase ? (lim - cbase + TT - 1) / TT : 0;
+    for (int r0 = 0; r0 < R_; r0 += TR, ++by) {
+      const int lim = min(cend, min(r0 + TR, R_) + os_);
+      const int nbx = lim > cbase ? (lim - cbase + TC - 1) / TC : 0;
       if (rem < nbx) {
         bx = rem;
         break;
@@ -304,12 +325,12 @@ __global__ __launch_bounds__(64 * NW) void est_gemm_bf16(EstArgs a) {
   const int lq = a.cu_q[b + 1] - q0;
   const int lk = a.cu_k[b + 1] - a.cu_k[b];
   const int R = lq / S, C = lk / S, o_s = (lk - lq) / S;
-  const int r0 = by * TT;
+  const int r0 = by * TR;
   if (r0 >= R) return;
-  const int c0 = a.jb0 * RB + bx * TT;
+  const int c0 = a.jb0 * RB + bx * TC;
   const int c_end = min((a.jb0 + a.jb_count) * RB, C);
   if (c0 >= c_end) return;
-  const int r_last = min(r0 + TT, R) - 1;
+  const int r_last = min(r0 + TR, R) - 1;
   if (c0 > r_last + o_s) return;  // whole tile beyond the causal block diagonal
 
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
@@ -317,21 +338,28 @@ __global__ __launch_bounds__(64 * NW) void est_gemm_bf16(EstArgs a) {
   const int wc = w & 1, wr = w >> 1;
   const int l32 = lane & 31, hh = lane >> 5;
 
-  // ---- copies: instruction n of wave w fills tile rows (LPW*w+n)*RPI .. +RPI
+  // ---- copies: instruction n of wave w fills K tile rows (LPK*w+n)*RPI ..
+  // +RPI and Q tile rows (LPQ*w+n)*RPI .. +RPI
   const long long q_tok = (long long)a.hq * D * 2;
   const long long k_row = (long long)a.k.kv_heads * D * 2;
   constexpr uint32_t kOut = 0x80000000u;  // beyond either descriptor's bound
-  uint32_t kvo[LPW], qvo[LPW];
+  uint32_t kvo[LPK], qvo[LPQ];
 #pragma unroll
-  for (int n = 0; n < LPW; ++n) {
-    const int row = (w * LPW + n) * RPI + lane / CPR;
+  for (int n = 0; n < LPK; ++n) {
+    const int row = (w * LPK + n) * RPI + lane / CPR;
     const int lc = (lane % CPR) ^ swz(row);  // logical chunk stored at this lane's position
-    const int c = c0 + row, r = r0 + row;
+    const int c = c0 + row;
     kvo[n] = kOut;
     if (c < c_end) {
       const char* p = a.k.row(b, c * S, g);
       if (p) kvo[n] = (uint32_t)(p - a.k.base) + lc * 16;
     }
+  }
+#pragma unroll
+  for (int n = 0; n < LPQ; ++n) {
+    const int row = (w * LPQ + n) * RPI + lane / CPR;
+    const int lc = (lane % CPR) ^ swz(row);
+    const int r = r0 + row;
     qvo[n] = kOut;
     if (r < R) qvo[n] = (uint32_t)(((long long)(q0 + r * S) * a.hq + h) * D * 2) + lc * 16;
   }
@@ -343,10 +371,10 @@ __global__ __launch_bounds__(64 * NW) void est_gemm_bf16(EstArgs a) {
     const int t = st / DQ, dq = st - (st / DQ) * DQ;
     const int so_k = (int)(t * k_row) + dq * BK * 2;
     const int so_q = (int)((S - 1 - t) * q_tok) + dq * BK * 2;
-    char* kd = lds + bf * 2 * TILEB + wu * LPW * 1024;
-    char* qd = kd + TILEB;
-    est_copy_rows<LPW>(rk, kd, kvo, so_k);
-    est_copy_rows<LPW>(rq, qd, qvo, so_q);
+    char* kd = lds + bf * BUFB + wu * LPK * 1024;
+    char* qd = lds + bf * BUFB + KTB + wu * LPQ * 1024;
+    est_copy_rows<LPK>(rk, kd, kvo, so_k);
+    est_copy_rows<LPQ>(rq, qd, qvo, so_q);
   };
 
   // ---- fragment addresses: every tile row a lane reads has the swizzle of
@@ -358,8 +386,8 @@ __global__ __launch_bounds__(64 * NW) void est_gemm_bf16(EstArgs a) {
 #pragma unroll
     for (int kk = 0; kk < KS; ++kk) {
       const uint32_t ch = (uint32_t)(((2 * kk + hh) ^ swz(l32)) * 16);
-      ka[bf][kk] = lds0 + bf * 2 * TILEB + (wc * (TT / 2) + l32) * (BK * 2) + ch;
-      qa[bf][kk] = lds0 + bf * 2 * TILEB + TILEB + (wr * (YT * 32) + l32) * (BK * 2) + ch;
+      ka[bf][kk] = lds0 + bf * BUFB + (wc * (TC / 2) + l32) * (BK * 2) + ch;
+      qa[bf][kk] = lds0 + bf * BUFB + KTB + (wr * (YT * 32) + l32) * (BK * 2) + ch;
     }
 
   f32x16 acc[XT][YT];
@@ -409,18 +437,20 @@ __global__ __launch_bounds__(64 * NW) void est_gemm_bf16(EstArgs a) {
   // the NBUF - 2 later stages may stay in flight), barrier (every wave's
   // copies of stage st visible; buffer (st - 1) % NBUF, computed in the
   // previous step, free), copy stage st + NBUF - 1 into it, compute st
-  constexpr int PER = 2 * LPW;  // copy instructions per wave and stage
+  constexpr int PER = LPK + LPQ;  // copy instructions per wave and stage
 #pragma unroll
   for (int x = 0; x < NBUF - 1; ++x) issue(x, x);
   for (int st0 = 0; st0 < NST; st0 += NBUF) {
     [&]<int... B>(std::integer_sequence<int, B...>) {
       ([&] {
         const int st = st0 + B;
-        if (st + NBUF - 2 < NST) est_wait_vmcnt<(NBUF - 2) * PER>();
-        else est_wait_vmcnt<0>();
-        __builtin_amdgcn_s_barrier();
-        if (st + NBUF - 1 < NST) issue(st + NBUF - 1, (B + NBUF - 1) % NBUF);
-        compute(std::integral_constant<int, B>{});
+        if (NST % NBUF == 0 || st < NST) {
+          if (st + NBUF - 2 < NST) est_wait_vmcnt<(NBUF - 2) * PER>();
+          else est_wait_vmcnt<0>();
+          __builtin_amdgcn_s_barrier();
+          if (st + NBUF - 1 < NST) issue(st + NBUF - 1, (B + NBUF - 1) % NBUF);
+          compute(std::integral_constant<int, B>{});
+        }
       }(), ...);
     }(std::make_integer_sequence<int, NBUF>{});
   }
@@ -439,7 +469,7 @@ __global__ __launch_bounds__(64 * NW) void est_gemm_bf16(EstArgs a) {
   // are the bare hardware instructions (v_exp_f32 / v_log_f32): every term
   // is 2^(z - max) <= 1 and the sum is >= 1, so flushing terms below 2^-126
   // to zero changes nothing at fp32 resolution.
-  const bool unmasked = (r0 + TT <= R) && (c0 + TT <= c_end) && (c0 + TT - 1 <= r0 + o_s);
+  const bool unmasked = (r0 + TR <= R) && (c0 + TC <= c_end) && (c0 + TC - 1 <= r0 + o_s);
   const float sc = a.scale2;
   auto mx3 = [](float p, float q, float r) {
     return __builtin_elementwise_maximum(__builtin_elementwise_maximum(p, q), r);
@@ -449,7 +479,7 @@ __global__ __launch_bounds__(64 * NW) void est_gemm_bf16(EstArgs a) {
     const int r = r0 + wr * (YT * 32) + y * 32 + l32;
 #pragma unroll
     for (int x = 0; x < XT; ++x) {
-      const int cblk = c0 + wc * (TT / 2) + x * 32;
+      const int cblk = c0 + wc * (TC / 2) + x * 32;
 #pragma unroll
       for (int m = 0; m < NBLK; ++m) {
         float lse = kNegInf;
@@ -688,28 +718,28 @@ __global__ __launch_bounds__(1024) void block_sums_reg_kernel(BlockSumArgs a) {
 // tiles whose first column c0 lies before both the key range's end and the
 // causal bound of its last row (c0 <= r_last + (Lk - Lq)/s), the same rules
 // by which est_gemm_bf16 skips a tile.
-int est_active_tiles(int lq, int lk, int S, int tt, int jb0, int jb_count) {
+int est_active_tiles(int lq, int lk, int S, int tr, int tc, int jb0, int jb_count) {
   const int RB = kBlock / S;
   const int R = lq / S, C = lk / S, o_s = (lk - lq) / S;
   const int cbase = jb0 * RB, cend = std::min((jb0 + jb_count) * RB, C);
   int n = 0;
-  for (int r0 = 0; r0 < R; r0 += tt) {
-    const int lim = std::min(cend, std::min(r0 + tt, R) + o_s);
-    if (lim > cbase) n += (lim - cbase + tt - 1) / tt;
+  for (int r0 = 0; r0 < R; r0 += tr) {
+    const int lim = std::min(cend, std::min(r0 + tr, R) + o_s);
+    if (lim > cbase) n += (lim - cbase + tc - 1) / tc;
   }
   return n;
 }
 
-// Fills a.tile_base / a.n_tab for tile size tt; false (and n_tab 0) when the
-// batch is beyond the table or a count overflows.
-bool est_tile_table(EstArgs& a, int S, int tt, int batch) {
+// Fills a.tile_base / a.n_tab for tr x tc tiles; false (and n_tab 0) when
+// the batch is beyond the table or a count overflows.
+bool est_tile_table(EstArgs& a, int S, int tr, int tc, int batch) {
   a.n_tab = 0;
   if (!a.cu_q_host || !a.cu_k_host || batch > kEstMaxSeq) return false;
   long long acc = 0;
   for (int b = 0; b < batch; ++b) {
     a.tile_base[b] = (int)acc;
     const int lq = a.cu_q_host[b + 1] - a.cu_q_host[b], lk = a.cu_k_host[b + 1] - a.cu_k_host[b];
-    acc += (long long)a.hq * est_active_tiles(lq, lk, S, tt, a.jb0, a.jb_count);
+    acc += (long long)a.hq * est_active_tiles(lq, lk, S, tr, tc, a.jb0, a.jb_count);
     if (acc >= (1ll << 31)) return false;
   }
   a.tile_base[batch] = (int)acc;
@@ -721,38 +751,39 @@ template <int D, int S>
 hipError_t est_dispatch(const EstArgs& a, int dtype, int batch, hipStream_t st) {
   constexpr int RB = kBlock / S;
   if (dtype == 0) {
-    // 256 x 256 tiles (8 waves) when they still fill the chip, else 128 x 128
-    // tiles (8 waves); both need Q and K spans within 31-bit buffer offsets.
+    // big tiles when they still fill the chip, else 128 x 128 tiles (8
+    // waves); both need Q and K spans within 31-bit buffer offsets.
     if (a.q_bytes < (1ll << 31) && a.k_bytes < (1ll << 31)) {
       // several sequences: one workgroup per tile with work when the batch
       // fits the table, so that every XCD gets the same number of tiles
       // whatever the sequences' lengths (one per grid tile otherwise: for a
       // single sequence that measured 1-2 us faster)
-      dim3 big((a.jb_count * RB + kEstBig - 1) / kEstBig, (a.max_r + kEstBig - 1) / kEstBig, batch * a.hq);
+      constexpr int TR = XATTN_EST_BIG_TR, TC = XATTN_EST_BIG_TC, NW = XATTN_EST_BIG_NW;
+      dim3 big((a.jb_count * RB + TC - 1) / TC, (a.max_r + TR - 1) / TR, batch * a.hq);
       EstArgs a2 = a;
       long long nbig = (long long)big.x * big.y * big.z;
-      if (batch > 1 && est_tile_table(a2, S, kEstBig, batch)) nbig = a2.tile_base[batch];
-      if (nbig >= 256) {
+      if (batch > 1 && est_tile_table(a2, S, TR, TC, batch)) nbig = a2.tile_base[batch];
+      if (nbig >= 256 * kEstBigPerCu) {
         a2.tiles_c = (int)big.x;
         a2.tiles_r = (int)big.y;
         if (a2.n_tab > 0)
-          hipLaunchKernelGGL((est_gemm_bf16<D, S, kEstBig, 8, XATTN_EST_BIG_NBUF, XATTN_EST_BIG_BK, true>),
-                             dim3((unsigned)nbig), dim3(512), 0, st, a2);
+          hipLaunchKernelGGL((est_gemm_bf16<D, S, TR, TC, NW, XATTN_EST_BIG_NBUF, XATTN_EST_BIG_BK, true, XATTN_EST_BIG_WPE>),
+                             dim3((unsigned)nbig), dim3(64 * NW), 0, st, a2);
         else
-          hipLaunchKernelGGL((est_gemm_bf16<D, S, kEstBig, 8, XATTN_EST_BIG_NBUF, XATTN_EST_BIG_BK, false>),
-                             dim3((unsigned)nbig), dim3(512), 0, st, a2);
+          hipLaunchKernelGGL((est_gemm_bf16<D, S, TR, TC, NW, XATTN_EST_BIG_NBUF, XATTN_EST_BIG_BK, false, XATTN_EST_BIG_WPE>),
+                             dim3((unsigned)nbig), dim3(64 * NW), 0, st, a2);
       } else {
         a2.tiles_c = (a.jb_count * RB + kEstTile - 1) / kEstTile;
         a2.tiles_r = (a.max_r + kEstTile - 1) / kEstTile;
         long long n = (long long)a2.tiles_c * a2.tiles_r * batch * a.hq;
-        if (batch > 1 && est_tile_table(a2, S, kEstTile, batch)) n = a2.tile_base[batch];
+        if (batch > 1 && est_tile_table(a2, S, kEstTile, kEstTile, batch)) n = a2.tile_base[batch];
         else a2.n_tab = 0;
         if (n > 0 && a2.n_tab > 0)
-          hipLaunchKernelGGL((est_gemm_bf16<D, S, kEstTile, kEstSmallWaves, XATTN_EST_NBUF, XATTN_EST_BK, true>), dim3((unsigned)n), dim3(64 * kEstSmallWaves), 0,
-                             st, a2);
+          hipLaunchKernelGGL((est_gemm_bf16<D, S, kEstTile, kEstTile, kEstSmallWaves, XATTN_EST_NBUF, XATTN_EST_BK, true, 1>),
+                             dim3((unsigned)n), dim3(64 * kEstSmallWaves), 0, st, a2);
         else if (n > 0)
-          hipLaunchKernelGGL((est_gemm_bf16<D, S, kEstTile, kEstSmallWaves, XATTN_EST_NBUF, XATTN_EST_BK, false>), dim3((unsigned)n), dim3(64 * kEstSmallWaves),
-                             0, st, a2);
+          hipLaunchKernelGGL((est_gemm_bf16<D, S, kEstTile, kEstTile, kEstSmallWaves, XATTN_EST_NBUF, XATTN_EST_BK, false, 1>),
+                             dim3((unsigned)n), dim3(64 * kEstSmallWaves), 0, st, a2);
       }
       return hipGetLastError();
     }
