@@ -479,7 +479,7 @@ void set_order(const XattnShape* sh, const Plan& p, AttnArgs& aa, void* ws, Spli
       // two blocks more pay for the second unit's fixed cost (block list,
       // first copies, output: about 8 us against about 3 us per block) on
       // the CUs that run a short row and then a tail
-      head = (int)std::ceil(0.98 * share) + 2;
+      head = (int)std::ceil(0.98 * share) + kHeadPad;
     }
   }
   // With the ping-pong kernel the same rule is applied again on the device,

@@ -1155,7 +1155,7 @@ __global__ __launch_bounds__(512) void attn_pp(AttnArgs a, int hkv) {
   #pragma unroll
     for (int x = 0; x < NW; ++x) tot += head_red[x];
     const double share = (double)tot * npair / a.cut_cus;
-    whole_lim = dev_head = __builtin_amdgcn_readfirstlane((int)ceil(0.98 * share) + 2);
+    whole_lim = dev_head = __builtin_amdgcn_readfirstlane((int)ceil(0.98 * share) + kHeadPad);
     if (blockIdx.x == 0 && threadIdx.x == 0) *a.cut_head = dev_head;
   }
   for (;;) {

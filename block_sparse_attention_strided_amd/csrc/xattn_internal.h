@@ -192,6 +192,13 @@ constexpr int f32_attention_splits(long long rows) {
                    : (rows >= 512 ? 1 : (int)(1024 / rows < kMaxF32Splits ? 1024 / rows : kMaxF32Splits));
 }
 
+// Head length of a split row (host and device rule): ceil(0.98 * share) +
+// kHeadPad blocks, share = the launch's blocks per CU.
+#ifndef XATTN_HEAD_PAD
+#define XATTN_HEAD_PAD 2
+#endif
+constexpr int kHeadPad = XATTN_HEAD_PAD;
+
 constexpr uint32_t order_entry(int b, int i, int s, int ns) {
   return (uint32_t)i | ((uint32_t)b << 16) | ((uint32_t)s << 28) | ((uint32_t)(ns - 1) << 30);
 }
