@@ -589,13 +589,13 @@ def main():
 
 PROFILE_COMMANDS = [
     "rocprofv3 --kernel-trace --stats -f csv -d DIR/prof_{wl} -o trace -- python3 bench.py --workload {wl} "
-    "--steps 100 --warmup 20 --no-cpu-baseline --no-achievable --no-sparse-stages > DIR/prof_{wl}.json",
+    "--steps 100 --warmup 20 --no-cpu-baseline --no-achievable --no-sparse-stages --no-other-configs > DIR/prof_{wl}.json",
     "rocprofv3 --pmc FETCH_SIZE -f csv -d DIR/pmc_fetch_{wl} -o pmc -- python3 bench.py --workload {wl} "
-    "--steps 3 --warmup 1 --no-cpu-baseline --no-achievable --no-sparse-stages --copy-calibration",
+    "--steps 3 --warmup 1 --no-cpu-baseline --no-achievable --no-sparse-stages --no-other-configs --copy-calibration",
     "rocprofv3 --pmc WRITE_SIZE -f csv -d DIR/pmc_write_{wl} -o pmc -- python3 bench.py --workload {wl} "
-    "--steps 3 --warmup 1 --no-cpu-baseline --no-achievable --no-sparse-stages --copy-calibration",
+    "--steps 3 --warmup 1 --no-cpu-baseline --no-achievable --no-sparse-stages --no-other-configs --copy-calibration",
     "rocprofv3 --pmc SQ_INSTS_VALU_MFMA_MOPS_BF16 -f csv -d DIR/pmc_mfma_{wl} -o pmc -- python3 bench.py "
-    "--workload {wl} --steps 3 --warmup 1 --no-cpu-baseline --no-achievable --no-sparse-stages",
+    "--workload {wl} --steps 3 --warmup 1 --no-cpu-baseline --no-achievable --no-sparse-stages --no-other-configs",
     "python3 bench.py --summarize-profile DIR --workload {wl}",
 ]
 
