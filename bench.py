@@ -112,10 +112,10 @@ def estimate_flops(cu_q, cu_k, hq, stride, d):
     return 2.0 * stride * d * tot * hq
 
 
-def profiled_traffic(workload):
+def profiled_traffic(workload, profiles_dir=None):
     """HBM bytes per attention launch from the committed rocprofv3 summary of
     this workload, or None if the attention source changed since then."""
-    path = os.path.join(ROOT, "profiles", "kernels_%s.md" % workload)
+    path = os.path.join(profiles_dir or os.path.join(ROOT, "profiles"), "kernels_%s.md" % workload)
     if not os.path.exists(path):
         return None
     text = open(path).read()
@@ -618,9 +618,10 @@ def _per_kernel(path, counter=None):
     return out
 
 
-def summarize_profile(base, wl):
+def summarize_profile(base, wl, out_dir=None):
     """Kernel durations (trace), copy-calibrated HBM bytes (FETCH_SIZE,
-    WRITE_SIZE) and executed MFMA flops per dispatch for one workload."""
+    WRITE_SIZE) and executed MFMA flops per dispatch for one workload,
+    written to <out_dir or profiles/>/kernels_<wl>.md."""
     stats_csv = _one(base, "prof_%s/**/*kernel_stats.csv" % wl)
     if stats_csv is None:
         sys.exit("no kernel_stats.csv under %s/prof_%s" % (base, wl))
@@ -704,7 +705,7 @@ def summarize_profile(base, wl):
                 "%.3f" % (ex / (t * 1e-6) / 1e12 / PEAK_BF16_TFLOPS) if t else "-"))
     if traffic is not None:
         L += ["", "attention traffic_bytes_per_launch: %d" % int(traffic)]
-    out = os.path.join(ROOT, "profiles", "kernels_%s.md" % wl)
+    out = os.path.join(out_dir or os.path.join(ROOT, "profiles"), "kernels_%s.md" % wl)
     with open(out, "w") as f:
         f.write("\n".join(L) + "\n")
     print(out)
