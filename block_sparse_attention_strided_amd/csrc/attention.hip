@@ -1422,52 +1422,55 @@ __global__ __launch_bounds__(256) void merge_kernel(MergeArgs a) {
 // listed row (grid y: the row; 8 rather than 4 per thread: 4K merge 0.5 us
 // shorter, same bits); the ns partial LSEs give the weights exp(lse_s - lse) with
 // lse = m + log(sum_s exp(lse_s - m)), m the largest partial LSE.
-__global__ __launch_bounds__(256) void split_merge_kernel(SplitMergeArgs a) {
-  constexpr int V = 8;  // d values per thread (head_dim is 64 or 128)
+// d values per thread of the split merge (head_dim is a multiple of it)
+#ifndef XATTN_MERGE_V
+#define XATTN_MERGE_V 8
+#endif
+constexpr int kMergeV = XATTN_MERGE_V;
+
+// One row's merge with its part count NS (2 or 3) fixed, so that no part is
+// loaded twice.  The combine is the same arithmetic for either count: parts
+// past NS would enter as -inf LSEs with zero weight.
+template <int NS>
+__device__ __forceinline__ void split_merge_row(const SplitMergeArgs& a, int r, int rem) {
+  constexpr int V = kMergeV;
   const int dq = a.head_dim / V;
-  const int per_row = kBlock * a.heads * dq;
-  const int r = blockIdx.y;
-  const int rem = blockIdx.x * 256 + threadIdx.x;
-  if (rem >= per_row) return;
   const int dv = rem % dq, qh = rem / dq;
   const int h = qh % a.heads, xq = qh / a.heads;
   const uint32_t e = (uint32_t)a.rows[r];
-  const int ns = (int)(e >> 28) + 1;
   const long long tok = (long long)(e & 0x0fffffffu) * kBlock + xq;
   const long long li = (long long)h * a.total_q + tok;
   const long long off = (tok * a.heads + h) * a.head_dim + dv * V;
   // The row's list count and the parts' LSEs are loaded together, then (for
   // a row not done whole) every part's output at once: two rounds of loads
-  // instead of four.  Part indices are clamped to the row's count; the
-  // clamped copies are not used.
+  // instead of four.
   const int rb = a.row_bi[r], g = h / a.group;
   const int nall =
       a.lists[(((long long)(rb >> 16) * (a.heads / a.group) + g) * a.max_qb + (rb & 0xffff)) * (a.max_kb + 1)];
   int whole = a.whole >= 0 ? a.whole : *a.cut_head;
-  float l[3], w[3];
+  float l[NS], w[NS];
 #pragma unroll
-  for (int s = 0; s < 3; ++s) l[s] = a.l[s < ns ? s : ns - 1][li];
+  for (int s = 0; s < NS; ++s) l[s] = a.l[s][li];
   // (empty asm statements that take the loaded values keep the compiler from
   // sinking the loads past the branch, which would make them a round of
   // their own)
-  asm volatile("" : "+v"(l[0]), "+v"(l[1]), "+v"(l[2]), "+v"(whole));
+#pragma unroll
+  for (int s = 0; s < NS; ++s) asm volatile("" : "+v"(l[s]));
+  asm volatile("" : "+v"(whole));
   // a row the attention did whole (few selected blocks) already holds its output
-  if (split_row_whole(nall, ns, whole)) return;
-  f32x4 ov[3][V / 4];
+  if (split_row_whole(nall, NS, whole)) return;
+  f32x4 ov[NS][V / 4];
 #pragma unroll
-  for (int s = 0; s < 3; ++s)
+  for (int s = 0; s < NS; ++s)
 #pragma unroll
-    for (int u = 0; u < V / 4; ++u) ov[s][u] = *(const f32x4*)(a.o[s < ns ? s : ns - 1] + off + 4 * u);
+    for (int u = 0; u < V / 4; ++u) ov[s][u] = *(const f32x4*)(a.o[s] + off + 4 * u);
 #pragma unroll
-  for (int s = 0; s < 3; ++s)
+  for (int s = 0; s < NS; ++s)
 #pragma unroll
     for (int u = 0; u < V / 4; ++u) asm volatile("" : "+v"(ov[s][u]));
   float mx = kNegInf;
 #pragma unroll
-  for (int s = 0; s < 3; ++s) {
-    if (s >= ns) l[s] = kNegInf;
-    mx = fmaxf(mx, l[s]);
-  }
+  for (int s = 0; s < NS; ++s) mx = fmaxf(mx, l[s]);
   float lse = kNegInf;
   float res[V];
 #pragma unroll
@@ -1475,12 +1478,12 @@ __global__ __launch_bounds__(256) void split_merge_kernel(SplitMergeArgs a) {
   if (mx != kNegInf) {
     float sum = 0.f;
 #pragma unroll
-    for (int s = 0; s < 3; ++s) sum += (l[s] == kNegInf) ? 0.f : expf(l[s] - mx);
+    for (int s = 0; s < NS; ++s) sum += (l[s] == kNegInf) ? 0.f : expf(l[s] - mx);
     lse = mx + logf(sum);
 #pragma unroll
-    for (int s = 0; s < 3; ++s) w[s] = (l[s] == kNegInf) ? 0.f : expf(l[s] - lse);
+    for (int s = 0; s < NS; ++s) w[s] = (l[s] == kNegInf) ? 0.f : expf(l[s] - lse);
 #pragma unroll
-    for (int s = 0; s < 3; ++s) {
+    for (int s = 0; s < NS; ++s) {
       if (w[s] != 0.f) {
 #pragma unroll
         for (int u = 0; u < V / 4; ++u)
@@ -1493,6 +1496,16 @@ __global__ __launch_bounds__(256) void split_merge_kernel(SplitMergeArgs a) {
 #pragma unroll
   for (int c = 0; c < V / 2; ++c) p[c] = pack_bf16x2(res[2 * c], res[2 * c + 1]);
   if (a.lse && dv == 0) a.lse[(long long)h * a.total_q + tok] = lse;
+}
+
+__global__ __launch_bounds__(256) void split_merge_kernel(SplitMergeArgs a) {
+  const int per_row = kBlock * a.heads * (a.head_dim / kMergeV);
+  const int r = blockIdx.y;
+  const int rem = blockIdx.x * 256 + threadIdx.x;
+  if (rem >= per_row) return;
+  const int ns = (int)((uint32_t)a.rows[r] >> 28) + 1;  // uniform per workgroup
+  if (ns == 2) split_merge_row<2>(a, r, rem);
+  else split_merge_row<3>(a, r, rem);
 }
 
 // The ping-pong kernel serves even GQA groups whose K/V spans fit 32-bit
@@ -1606,8 +1619,8 @@ hipError_t launch_gather_blocks(const uint8_t* sel, int nblocks, const void* src
 }
 
 hipError_t launch_split_merge(const SplitMergeArgs& a, hipStream_t s) {
-  const long long per_row = (long long)kBlock * a.heads * (a.head_dim / 8);
-  if (a.head_dim % 8) return hipErrorInvalidValue;
+  const long long per_row = (long long)kBlock * a.heads * (a.head_dim / kMergeV);
+  if (a.head_dim % kMergeV) return hipErrorInvalidValue;
   if (a.n <= 0 || per_row <= 0) return hipSuccess;
   if (per_row >= (1ll << 31)) return hipErrorInvalidValue;
   hipLaunchKernelGGL(split_merge_kernel, dim3((unsigned)((per_row + 255) / 256), a.n), dim3(256), 0, s, a);
