@@ -270,8 +270,13 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(WPE))) 
   static_assert(NBUF >= 2, "stage ring");
   static_assert(XT >= 1 && YT >= 1 && LPK >= 1 && LPQ >= 1 && TC % (RPI * NW) == 0 && TR % (RPI * NW) == 0,
                 "tile / wave split");
-  // 16-byte chunk swizzle of LDS row `row` (conflict-free fragment reads)
-  auto swz = [](int row) { return BK == 64 ? (row & 7) : ((row >> 2) & 3); };
+  // 16-byte chunk swizzle of LDS row `row`.  A ds_read_b128 serves 16 lanes
+  // (256 bytes, all banks) at a time, here 16 consecutive rows at one logical
+  // chunk: the rows sharing a 256-byte bank window position (same parity for
+  // 128-byte rows, same row % 4 for 64-byte rows) need distinct swizzles.
+  // (row & 7 for 128-byte rows gave rows r and r + 8 the same banks: half of
+  // the fragment reads' LDS cycles were bank-conflict stalls.)
+  auto swz = [](int row) { return BK == 64 ? ((row >> 1) & 7) : ((row >> 2) & 3); };
   typedef __attribute__((address_space(3))) void* lds_ptr;
   __shared__ __align__(1024) char lds[NBUF * BUFB];
 
