@@ -596,6 +596,9 @@ PROFILE_COMMANDS = [
     "--steps 3 --warmup 1 --no-cpu-baseline --no-achievable --no-sparse-stages --no-other-configs --copy-calibration",
     "rocprofv3 --pmc SQ_INSTS_VALU_MFMA_MOPS_BF16 -f csv -d DIR/pmc_mfma_{wl} -o pmc -- python3 bench.py "
     "--workload {wl} --steps 3 --warmup 1 --no-cpu-baseline --no-achievable --no-sparse-stages --no-other-configs",
+    "rocprofv3 --pmc SQ_LDS_IDX_ACTIVE SQ_LDS_BANK_CONFLICT SQ_VALU_MFMA_BUSY_CYCLES GRBM_GUI_ACTIVE -f csv "
+    "-d DIR/pmc_lds_{wl} -o pmc -- python3 bench.py --workload {wl} --steps 3 --warmup 1 --no-cpu-baseline "
+    "--no-achievable --no-sparse-stages --no-other-configs",
     "python3 bench.py --summarize-profile DIR --workload {wl}",
 ]
 
@@ -607,6 +610,10 @@ def _one(base, pattern):
 
 def _short(n):
     return n.replace("xattn::(anonymous namespace)::", "").replace("void ", "").split("(")[0]
+
+
+NUM_XCDS = 8      # MI355X: XCDs, each with its own clock domain counter
+NUM_SIMDS = 1024  # 256 CUs x 4 SIMDs
 
 
 def _per_kernel(path, counter=None):
@@ -703,6 +710,36 @@ def summarize_profile(base, wl, out_dir=None):
             L.append("| %s | %.1f | %s | %s | %s |" % (
                 n, ex / 1e9, "%.1f" % (fl / 1e9) if fl else "-", "%.0f" % (ex / (t * 1e-6) / 1e12) if t else "-",
                 "%.3f" % (ex / (t * 1e-6) / 1e12 / PEAK_BF16_TFLOPS) if t else "-"))
+    lds_csv = _one(base, "pmc_lds_%s/**/*counter_collection.csv" % wl)
+    if lds_csv:
+        cnt = {c: _per_kernel(lds_csv, c) for c in ("SQ_LDS_IDX_ACTIVE", "SQ_LDS_BANK_CONFLICT",
+                                                     "SQ_VALU_MFMA_BUSY_CYCLES", "GRBM_GUI_ACTIVE")}
+        L += ["", "## LDS and MFMA busy cycles per dispatch", "",
+              "SQ_VALU_MFMA_BUSY_CYCLES sums the MFMA pipe's busy cycles over all SIMDs (it equals the executed "
+              "MFMA count times each instruction's cycles). GRBM_GUI_ACTIVE sums the GPU's active clock cycles "
+              "over its %d XCDs, so GRBM_GUI_ACTIVE / %d is the dispatch's length in shader clocks (which includes "
+              "launch overhead, so it reads long for dispatches of a few microseconds). The MFMA busy fraction "
+              "divides the first by %d SIMDs times that length; the clock column divides that length by the trace "
+              "duration. Bank-conflict stalls are given as a share of the LDS's active cycles." % (
+                  NUM_XCDS, NUM_XCDS, NUM_SIMDS), "",
+              "| kernel | LDS active cycles | bank-conflict cycles | conflict share | MFMA busy cycles | "
+              "shader clocks | clock GHz | MFMA busy frac |", "|---|---|---|---|---|---|---|---|"]
+
+        def mean(c, k):
+            v = cnt[c].get(k, [])
+            return sum(v) / len(v) if v else 0.0
+
+        for k in cnt["SQ_LDS_IDX_ACTIVE"]:
+            if "rocclr" in k or "Functor" in k:
+                continue
+            n = _short(k)
+            a_, bc = mean("SQ_LDS_IDX_ACTIVE", k), mean("SQ_LDS_BANK_CONFLICT", k)
+            mb, clocks = mean("SQ_VALU_MFMA_BUSY_CYCLES", k), mean("GRBM_GUI_ACTIVE", k) / NUM_XCDS
+            t = avg.get(n)
+            L.append("| %s | %.4g | %.4g | %s | %.4g | %.4g | %s | %s |" % (
+                n, a_, bc, "%.3f" % (bc / a_) if a_ else "-", mb, clocks,
+                "%.2f" % (clocks / (t * 1e3)) if t else "-",
+                "%.3f" % (mb / (NUM_SIMDS * clocks)) if (clocks and mb) else "-"))
     if traffic is not None:
         L += ["", "attention traffic_bytes_per_launch: %d" % int(traffic)]
     out = os.path.join(out_dir or os.path.join(ROOT, "profiles"), "kernels_%s.md" % wl)

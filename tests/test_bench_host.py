@@ -59,6 +59,14 @@ def _profile_dir(tmp_path, with_pmc=True):
         _write_csv(str(base / ("pmc_mfma_%s" % WL) / "host" / "pmc_counter_collection.csv"), hdr,
                    [[2, 2, ATTN, "SQ_INSTS_VALU_MFMA_MOPS_BF16", 2.0e9],
                     [4, 4, EST, "SQ_INSTS_VALU_MFMA_MOPS_BF16", 0.125e9]])
+        # LDS / MFMA busy pass: the attention's GRBM_GUI_ACTIVE over 8 XCDs is
+        # 1.3e6 clocks (1.625 GHz over its 800 us), its MFMA pipes busy 1.0e9
+        # SIMD-cycles of 1024 x 1.3e6
+        _write_csv(str(base / ("pmc_lds_%s" % WL) / "host" / "pmc_counter_collection.csv"), hdr,
+                   [[2, 2, ATTN, "SQ_LDS_IDX_ACTIVE", 1.0e8], [2, 2, ATTN, "SQ_LDS_BANK_CONFLICT", 5.0e4],
+                    [2, 2, ATTN, "SQ_VALU_MFMA_BUSY_CYCLES", 1.0e9], [2, 2, ATTN, "GRBM_GUI_ACTIVE", 1.04e7],
+                    [4, 4, EST, "SQ_LDS_IDX_ACTIVE", 6.0e6], [4, 4, EST, "SQ_LDS_BANK_CONFLICT", 3.0e6],
+                    [4, 4, EST, "SQ_VALU_MFMA_BUSY_CYCLES", 6.5e7], [4, 4, EST, "GRBM_GUI_ACTIVE", 1.0e6]])
     return str(base)
 
 
@@ -104,6 +112,14 @@ def test_summary_calibrates_bytes_and_rates(tmp_path):
     est = [r for r in text.splitlines() if r.startswith("| est_gemm_bf16<")]
     assert [c.strip() for c in est[2].strip("|").split("|")][1] == "64.0"  # 0.125e9 x 512
 
+    # LDS / MFMA busy cycles
+    lds = [c.strip() for c in rows[3].strip("|").split("|")]
+    assert lds[3] == "0.001"            # 5e4 conflict cycles of 1e8 LDS-active cycles (0.0005)
+    assert float(lds[5]) == pytest.approx(1.3e6, rel=1e-3)   # shader clocks per XCD
+    assert lds[6] == "1.62" or lds[6] == "1.63"              # 1.3e6 clocks over 800 us
+    assert float(lds[7]) == pytest.approx(1.0e9 / (1024 * 1.3e6), abs=1e-3)
+    assert [c.strip() for c in est[3].strip("|").split("|")][3] == "0.500"
+
 
 def test_traffic_read_back_is_tied_to_the_attention_source(tmp_path):
     out = tmp_path / "profiles"
@@ -126,6 +142,7 @@ def test_summary_without_counters_has_durations_only(tmp_path):
     text = (out / ("kernels_%s.md" % WL)).read_text()
     assert "## Kernel durations" in text
     assert "## HBM traffic" not in text and "traffic_bytes_per_launch" not in text
+    assert "## LDS and MFMA busy" not in text
     assert bench.profiled_traffic(WL, profiles_dir=str(out)) is None
 
 
