@@ -217,6 +217,7 @@ __device__ __forceinline__ float pair_sum(float v) {
 #define XATTN_EST_BK 32
 #endif
 constexpr int kEstSmallWaves = 8;
+constexpr int kEstSmallPerCu = 2;  // 128 x 128 workgroups per CU (64 KiB of LDS each)
 // Big tiles: 256 x 256 over 8 waves, 2 stage buffers of 64 reduction
 // elements (measured at 32K: 4 buffers of 32 elements 0.082 ms, 2 of 32
 // 0.088, 2 of 64 0.078)
@@ -302,8 +303,19 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(WPE))) 
     b = lo;
     const int per_head = (a.tile_base[b + 1] - a.tile_base[b]) / a.hq;
     int rem = logical - a.tile_base[b];
-    h = rem / per_head;
-    rem -= h * per_head;
+    if (a.group_chunk > 0) {
+      // grouped order: the heads of a kv group take the same tile one after
+      // the other, so that they read its K tile in the same round
+      const int G = a.group;
+      const int gi = rem / (per_head * G);
+      rem -= gi * (per_head * G);
+      const int t = rem / G;
+      h = gi * G + (rem - t * G);
+      rem = t;
+    } else {
+      h = rem / per_head;
+      rem -= h * per_head;
+    }
     const int lq_ = a.cu_q[b + 1] - a.cu_q[b], lk_ = a.cu_k[b + 1] - a.cu_k[b];
     const int R_ = lq_ / S, C_ = lk_ / S, os_ = (lk_ - lq_) / S;
     const int cbase = a.jb0 * RB, cend = min((a.jb0 + a.jb_count) * RB, C_);
@@ -318,6 +330,34 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(WPE))) 
       }
       rem -= nbx;
     }
+  } else if (a.group_chunk > 0) {
+    // (sequence, kv group) blocks of units; inside a block, chunks of CC
+    // column tiles with every row tile and every head of the group, so that
+    // the units reading one K column tile run in the same round on one XCD
+    // (with head-major units a launch of several rounds read each K tile
+    // once per head: 146 instead of 96 MiB at 32K)
+    const int G = a.group, hkv_ = a.hq / a.group;
+    const int CC = a.group_chunk;
+    const int per_group = ntx * nty * G;
+    const int bg = logical / per_group;
+    const int rem = logical - bg * per_group;
+    const int full = (ntx / CC) * CC * nty * G;
+    int c, r2, width;
+    if (rem < full) {
+      c = rem / (CC * nty * G);
+      r2 = rem - c * (CC * nty * G);
+      width = CC;
+    } else {
+      c = ntx / CC;
+      r2 = rem - full;
+      width = ntx - c * CC;
+    }
+    by = r2 / (G * width);
+    const int r3 = r2 - by * (G * width);
+    const int hg = r3 / width;
+    bx = c * CC + (r3 - hg * width);
+    b = bg / hkv_;
+    h = (bg - b * hkv_) * G + hg;
   } else {
     bx = logical % ntx;
     by = (logical / ntx) % nty;
@@ -752,6 +792,16 @@ bool est_tile_table(EstArgs& a, int S, int tr, int tc, int batch) {
   return true;
 }
 
+// Column tiles per chunk of the grouped unit order (EstArgs::group_chunk)
+// for a launch of n workgroups, per_cu of which share a CU: 0 (head-major
+// units) when every XCD's units fit one round, else enough column tiles
+// that one chunk -- all row tiles of all heads of a kv group -- fills one
+// XCD's 32 CUs.
+int est_group_chunk(long long n, int per_cu, int tiles_r, int group) {
+  if (n <= 256ll * per_cu) return 0;
+  return std::max(1, 32 * per_cu / (tiles_r * group));
+}
+
 template <int D, int S>
 hipError_t est_dispatch(const EstArgs& a, int dtype, int batch, hipStream_t st) {
   constexpr int RB = kBlock / S;
@@ -771,6 +821,7 @@ hipError_t est_dispatch(const EstArgs& a, int dtype, int batch, hipStream_t st) 
       if (nbig >= 256 * kEstBigPerCu) {
         a2.tiles_c = (int)big.x;
         a2.tiles_r = (int)big.y;
+        a2.group_chunk = est_group_chunk(nbig, kEstBigPerCu, a2.tiles_r, a.group);  // (with a table: > 0 = grouped)
         if (a2.n_tab > 0)
           hipLaunchKernelGGL((est_gemm_bf16<D, S, TR, TC, NW, XATTN_EST_BIG_NBUF, XATTN_EST_BIG_BK, true, XATTN_EST_BIG_WPE>),
                              dim3((unsigned)nbig), dim3(64 * NW), 0, st, a2);
@@ -781,6 +832,7 @@ hipError_t est_dispatch(const EstArgs& a, int dtype, int batch, hipStream_t st) 
         a2.tiles_c = (a.jb_count * RB + kEstTile - 1) / kEstTile;
         a2.tiles_r = (a.max_r + kEstTile - 1) / kEstTile;
         long long n = (long long)a2.tiles_c * a2.tiles_r * batch * a.hq;
+        a2.group_chunk = est_group_chunk(n, kEstSmallPerCu, a2.tiles_r, a.group);
         if (batch > 1 && est_tile_table(a2, S, kEstTile, kEstTile, batch)) n = a2.tile_base[batch];
         else a2.n_tab = 0;
         if (n > 0 && a2.n_tab > 0)

@@ -32,6 +32,11 @@ struct EstArgs {
   long long k_bytes;  // bytes addressable from k.base
   int tiles_c;        // big-tile GEMM: column tiles per head (set by the launcher)
   int tiles_r;        // big-tile GEMM: row tiles per head
+  // > 0: grouped unit order (set by the launcher).  Without a tile table:
+  // (sequence, kv group) blocks, each in chunks of group_chunk column tiles
+  // holding every row tile and head of the group; with one: within a
+  // sequence, the heads of a kv group take each tile one after the other.
+  int group_chunk;
   // Host copies of cu_q / cu_k (launcher only).  With them the launcher
   // gives the tile GEMM one workgroup per tile that has work, numbered
   // (sequence, head, row tile, column tile) with tile_base[b] the number of
